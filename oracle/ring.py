@@ -1,0 +1,171 @@
+"""Chunked ring all-reduce, simulated step by step on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): imported by tests,
+``smoke()`` and the CPU-baseline leg of the benchmark, never by the product.
+
+What the pages fix
+------------------
+* An all-reduce takes one equal-size tensor from every rank and gives every
+  rank the elementwise reduction ("Distributed Training", section "Data
+  parallelism and all-reduce"; CS336 Lecture 8, "Collective Operations").
+* The reduction is Sum or Mean; with Mean every replica receives the average
+  gradient (Burn distributed guide, reduction configuration section).
+* The ring strategy: peers form a ring and pass slices of the tensor around
+  it (Burn collective blog, "Methods", Ring); a ring all-reduce is a
+  reduce-scatter followed by an all-gather, each moving (W-1)/W of the model
+  per device ("Distributed Training", "Sharded data parallelism" on FSDP's
+  communication volume, and the printed traffic of "How to Apply It").
+* Float32 sums taken in a different order differ in the last digits
+  ("Distributed Training", Pitfalls, "Reproducibility"), so the order of
+  additions is part of the result and is fixed here.
+
+Readings where the pages are silent (each listed in the design notes)
+---------------------------------------------------------------------
+* Ring direction: rank r sends to rank (r + 1) mod P.
+* Chunks: chunk length L = ceil(n / C); chunk j covers
+  [min(jL, n), min((j+1)L, n)) and starts its reduce-scatter at rank
+  j mod P.  With C = P this is the textbook ring; C = kP pipelines k rounds.
+* Partial sums travel in the accumulation type (fp32 for fp32 and bf16
+  inputs, fp64 for fp64 inputs); bf16 inputs are widened exactly first.
+* Mean divides once, by P, at the chunk's owner after the full sum, with a
+  correctly rounded IEEE division in the accumulation type.
+* Output conversion to bf16 rounds to nearest even (``oracle.bf16``).
+
+Parity status: the association order itself is a reading (no page shows
+the step schedule); it is pinned by the tests against an independently
+derived closed-form fold, hand-worked examples, exact integer sums, the
+recursive-summation error bound and the pages' printed traffic figures.
+"""
+
+import numpy as np
+
+from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
+
+SUM = "sum"
+MEAN = "mean"
+
+
+def chunk_length(n, chunking):
+    """Length L = ceil(n / C) of every chunk but possibly the trailing ones."""
+    if chunking < 1:
+        raise ValueError("chunking must be >= 1")
+    return -(-n // chunking) if n > 0 else 0
+
+
+def chunk_start_ranks(n, chunking, P):
+    """Start rank of the reduce-scatter for every element (int64 array).
+
+    Element i lies in chunk floor(i / L); that chunk starts at rank
+    (chunk mod P).  Reading of the Ring strategy in the Burn collective blog,
+    "Methods".
+    """
+    L = chunk_length(n, chunking)
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    return (np.arange(n, dtype=np.int64) // L) % P
+
+
+def _widen(X, in_dtype):
+    """Rank inputs -> (P, n) array in the accumulation type."""
+    if in_dtype == "f32":
+        return np.array(X, dtype=np.float32, copy=True)
+    if in_dtype == "f64":
+        return np.array(X, dtype=np.float64, copy=True)
+    if in_dtype == "bf16":
+        return bf16_bits_to_f32(np.asarray(X, dtype=np.uint16)).copy()
+    raise ValueError(f"unknown input dtype {in_dtype!r}")
+
+
+def _narrow(A, out_dtype):
+    if out_dtype in ("f32", "f64"):
+        return A.astype(np.float32 if out_dtype == "f32" else np.float64)
+    if out_dtype == "bf16":
+        return f32_to_bf16_bits(A.astype(np.float32))
+    raise ValueError(f"unknown output dtype {out_dtype!r}")
+
+
+def ring_allreduce(X, op=SUM, chunking=None, in_dtype="f32", out_dtype=None):
+    """All-reduce P rank buffers by simulating the ring one step at a time.
+
+    X: array-like of shape (P, n) -- rank r's buffer is X[r].  For
+    ``in_dtype="bf16"`` the entries are raw bfloat16 bit patterns (uint16).
+    op: ``"sum"`` or ``"mean"``.  chunking: C >= 1 (default P).
+    Returns (Y, sent): Y of shape (P, n) in ``out_dtype`` (default: the input
+    dtype) holding every rank's result, and ``sent[r]`` = number of elements
+    rank r put on the wire over the whole all-reduce.
+    """
+    A = _widen(X, in_dtype)
+    if A.ndim != 2:
+        raise ValueError("X must have shape (P, n)")
+    P, n = A.shape
+    if P < 1:
+        raise ValueError("P must be >= 1")
+    if op not in (SUM, MEAN):
+        raise ValueError(f"unknown op {op!r}")
+    C = P if chunking is None else int(chunking)
+    L = chunk_length(n, C)
+    chunks = [(min(j * L, n), min((j + 1) * L, n)) for j in range(C)]
+    start = [j % P for j in range(C)]
+    owner = [(s + P - 1) % P for s in start]
+    sent = np.zeros(P, dtype=np.int64)
+
+    # Reduce-scatter: P-1 steps.  Every send of a step reads the buffers as
+    # they stood at the start of the step (S), so the sends are simultaneous.
+    for t in range(P - 1):
+        S = A.copy()
+        for r in range(P):
+            dst = (r + 1) % P
+            for j, (lo, hi) in enumerate(chunks):
+                if start[j] == (r - t) % P:
+                    A[dst, lo:hi] = S[r, lo:hi] + A[dst, lo:hi]
+                    sent[r] += hi - lo
+
+    # Mean: the owner of each chunk now holds the full sum; divide once.
+    if op == MEAN:
+        div = A.dtype.type(P)
+        for j, (lo, hi) in enumerate(chunks):
+            A[owner[j], lo:hi] = A[owner[j], lo:hi] / div
+
+    # All-gather: P-1 steps of forwarding the owner's finished chunk.
+    for t in range(P - 1):
+        S = A.copy()
+        for r in range(P):
+            dst = (r + 1) % P
+            for j, (lo, hi) in enumerate(chunks):
+                if owner[j] == (r - t) % P:
+                    A[dst, lo:hi] = S[r, lo:hi]
+                    sent[r] += hi - lo
+
+    return _narrow(A, out_dtype or in_dtype), sent
+
+
+def ring_allreduce_sampled(V, start, op=SUM, in_dtype="f32", out_dtype=None):
+    """The same ring, for elements taken out of a larger buffer.
+
+    V: shape (P, m) -- the P rank values of m sampled elements.
+    start: shape (m,) -- each element's reduce-scatter start rank (from
+    ``chunk_start_ranks`` of the full buffer, evaluated at the sampled
+    indices).  Elements do not interact in an all-reduce, so simulating the
+    ring on the sample gives exactly the values the full-buffer ring gives at
+    those indices.  Returns Y of shape (P, m).
+    """
+    A = _widen(V, in_dtype)
+    P, m = A.shape
+    start = np.asarray(start, dtype=np.int64)
+    if start.shape != (m,):
+        raise ValueError("start must have one entry per sampled element")
+    cols = np.arange(m)
+    for t in range(P - 1):
+        S = A.copy()
+        src = (start + t) % P
+        dst = (src + 1) % P
+        A[dst, cols] = S[src, cols] + A[dst, cols]
+    owner = (start + P - 1) % P
+    if op == MEAN:
+        A[owner, cols] = A[owner, cols] / A.dtype.type(P)
+    for t in range(P - 1):
+        S = A.copy()
+        src = (owner + t) % P
+        dst = (src + 1) % P
+        A[dst, cols] = S[src, cols]
+    return _narrow(A, out_dtype or in_dtype)
