@@ -1,0 +1,19 @@
+"""MI355X-native gradient all-reduce for data-parallel training.
+
+P ranks' gradient buffers are combined elementwise with Sum or Mean in the
+order of a chunked ring (reduce-scatter then all-gather), every rank ending
+with the same result; on one GPU the ranks are P buffers in HBM.  The work
+runs in the HIP library ``libddp_allreduce.so`` (C ABI in
+include/ddp_allreduce.h); this package is its Python binding.
+"""
+
+from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, ddp_bucket_pack,
+                  ddp_bucket_unpack, allreduce_ring_emulated, allreduce_fused_sgd, allreduce,
+                  allreduce_sgd)
+from .bucketer import GradBucketer
+
+__all__ = [
+    "SUM", "MEAN", "F32", "BF16", "MAX_RANKS", "DdpError", "ddp_bucket_plan", "ddp_bucket_pack",
+    "ddp_bucket_unpack", "allreduce_ring_emulated", "allreduce_fused_sgd", "allreduce",
+    "allreduce_sgd", "GradBucketer",
+]

@@ -1,0 +1,172 @@
+"""Python binding of the C ABI: the same entry points, argument marshalling
+only.  Every step of the all-reduce runs in the HIP library; PyTorch is used
+here for device memory, pointers and the current stream.
+
+Raw entry points (same names and argument order as the C header, pointers as
+Python ints, stream as an int handle or None):
+    ddp_bucket_plan, ddp_bucket_pack, ddp_bucket_unpack,
+    allreduce_ring_emulated, allreduce_fused_sgd
+Tensor-level helpers:
+    allreduce(tensors, op, chunking, out)            -> list of outputs
+    allreduce_sgd(grads, w, v, lr, mu, op, chunking, out)
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _native as N
+
+SUM = N.DDP_SUM
+MEAN = N.DDP_MEAN
+F32 = N.DDP_F32
+BF16 = N.DDP_BF16
+MAX_RANKS = N.DDP_MAX_RANKS
+
+
+class DdpError(RuntimeError):
+    """A non-OK status from the library; ``status`` holds the code."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{N.STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != N.DDP_OK:
+        raise DdpError(status, N.last_error())
+
+
+def _op(op):
+    if op in (SUM, MEAN):
+        return op
+    return {"sum": SUM, "mean": MEAN}[op]
+
+
+# ----------------------------------------------------------- raw entry ----
+
+SEGMENT_DTYPE = np.dtype([("tensor", "<i4"), ("bucket", "<i4"), ("src_off", "<i8"),
+                          ("dst_off", "<i8"), ("len", "<i8")])
+assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(N.Segment)
+
+
+def ddp_bucket_plan(numels, dtype, bucket_bytes):
+    """Plan buckets (host only).  Returns (segments, n_buckets, total_elems,
+    fingerprint); segments is a numpy structured array in the C layout."""
+    numels = np.ascontiguousarray(numels, dtype=np.int64)
+    T = int(numels.size)
+    c_numels = numels.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    n_segs = ctypes.c_int64(0)
+    n_buckets = ctypes.c_int32(0)
+    total = ctypes.c_int64(0)
+    fp = ctypes.c_uint64(0)
+    lib = N.lib()
+    _check(lib.ddp_bucket_plan(c_numels, T, dtype, bucket_bytes, None, 0, ctypes.byref(n_segs),
+                               ctypes.byref(n_buckets), ctypes.byref(total), ctypes.byref(fp)))
+    segs = np.zeros(n_segs.value, dtype=SEGMENT_DTYPE)
+    _check(lib.ddp_bucket_plan(c_numels, T, dtype, bucket_bytes,
+                               segs.ctypes.data_as(ctypes.POINTER(N.Segment)), segs.size,
+                               ctypes.byref(n_segs), ctypes.byref(n_buckets),
+                               ctypes.byref(total), ctypes.byref(fp)))
+    return segs, n_buckets.value, total.value, fp.value
+
+
+def ddp_bucket_pack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors, rank_bucket,
+                    bucket_len, stream=None):
+    _check(N.lib().ddp_bucket_pack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors,
+                                   N.pointer_array(rank_bucket), bucket_len, stream))
+
+
+def ddp_bucket_unpack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors, rank_bucket,
+                      bucket_len, stream=None):
+    _check(N.lib().ddp_bucket_unpack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors,
+                                     N.pointer_array(rank_bucket), bucket_len, stream))
+
+
+def allreduce_ring_emulated(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n,
+                            stream=None):
+    _check(N.lib().allreduce_ring_emulated(_op(op), P, chunking, N.pointer_array(rank_in),
+                                           in_dtype, N.pointer_array(rank_out), out_dtype, n,
+                                           stream))
+
+
+def allreduce_fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu,
+                        rank_grad_out, out_dtype, stream=None):
+    out = N.pointer_array(rank_grad_out) if rank_grad_out is not None else None
+    _check(N.lib().allreduce_fused_sgd(_op(op), P, chunking, N.pointer_array(rank_grad),
+                                       grad_dtype, n, master_w, momentum, lr, mu, out,
+                                       out_dtype, stream))
+
+
+# --------------------------------------------------------- torch level ----
+
+def torch_dtype_code(dtype):
+    import torch
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported element type {dtype}")
+
+
+def current_stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _rank_tensors(tensors, what):
+    tensors = list(tensors)
+    if not 1 <= len(tensors) <= MAX_RANKS:
+        raise ValueError(f"{what}: need 1..{MAX_RANKS} rank tensors, got {len(tensors)}")
+    t0 = tensors[0]
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{what}: tensors must live on the GPU")
+        if t.device != t0.device or t.dtype != t0.dtype or t.numel() != t0.numel():
+            raise ValueError(f"{what}: every rank needs the same device, dtype and size")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: tensors must be contiguous")
+    return tensors
+
+
+def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None):
+    """All-reduce a list of P equal-size GPU tensors (one per rank) in the
+    chunked ring order.  ``out``: list of P output tensors ("in place" when
+    they are the inputs); default: new tensors of ``out_dtype`` (default the
+    input dtype).  Enqueued on the current stream; returns the outputs."""
+    import torch
+    tensors = _rank_tensors(tensors, "allreduce")
+    P = len(tensors)
+    if out is None:
+        dt = out_dtype or tensors[0].dtype
+        out = [torch.empty(tensors[0].shape, dtype=dt, device=tensors[0].device) for _ in range(P)]
+    out = _rank_tensors(out, "allreduce out")
+    if len(out) != P or out[0].numel() != tensors[0].numel():
+        raise ValueError("allreduce: out must match the inputs")
+    allreduce_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
+                            torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
+                            torch_dtype_code(out[0].dtype), tensors[0].numel(),
+                            current_stream(tensors[0].device))
+    return out
+
+
+def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):
+    """All-reduce the rank gradients, then one SGD-momentum step on the
+    float32 master weights ``w`` and momentum ``v`` (updated in place).
+    ``out``: optional list of P tensors receiving the reduced gradient."""
+    import torch
+    grads = _rank_tensors(grads, "allreduce_sgd")
+    for t in (w, v):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != grads[0].numel() \
+                or t.device != grads[0].device:
+            raise ValueError("allreduce_sgd: w and v must be contiguous float32 tensors of the "
+                             "gradient's size on its device")
+    out_ptrs, out_code = None, F32
+    if out is not None:
+        out = _rank_tensors(out, "allreduce_sgd out")
+        out_ptrs = [t.data_ptr() for t in out]
+        out_code = torch_dtype_code(out[0].dtype)
+    allreduce_fused_sgd(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
+                        torch_dtype_code(grads[0].dtype), grads[0].numel(), w.data_ptr(),
+                        v.data_ptr(), lr, mu, out_ptrs, out_code, current_stream(grads[0].device))
+    return out

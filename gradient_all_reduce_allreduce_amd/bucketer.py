@@ -1,0 +1,91 @@
+"""Gradient bucketer: ragged per-parameter gradients <-> fixed-size buckets.
+
+DDP packs gradients into buckets (25 MB by default), filled in the reverse
+order of the parameters, and every rank reduces the buckets in the same
+order ("Distributed Training", "Data parallelism and all-reduce").  The plan
+comes from the library's ``ddp_bucket_plan``; pack and unpack run as HIP
+kernels for all P ranks in one launch each.  This class only owns the
+torch-allocated tables the kernels read (the device copy of the segment
+table and the per-rank tensor pointer tables).
+"""
+
+import math
+
+import numpy as np
+
+from . import api
+
+
+class GradBucketer:
+    def __init__(self, shapes, dtype, bucket_bytes=25 << 20, device="cuda"):
+        import torch
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.numels = [int(math.prod(s)) for s in self.shapes]
+        self.dtype = dtype
+        self.code = api.torch_dtype_code(dtype)
+        self.elem_bytes = torch.empty(0, dtype=dtype).element_size()
+        self.bucket_bytes = int(bucket_bytes)
+        self.bucket_elems = self.bucket_bytes // self.elem_bytes
+        segs, nb, total, fp = api.ddp_bucket_plan(self.numels, self.code, self.bucket_bytes)
+        self.segments = segs
+        self.n_buckets = nb
+        self.total = total
+        self.fingerprint = fp
+        self.bucket_lengths = [min(self.bucket_elems, total - b * self.bucket_elems)
+                               for b in range(nb)]
+        first = np.searchsorted(segs["bucket"], np.arange(nb + 1), side="left")
+        self._seg_first = [int(x) for x in first]
+        self.device = torch.device(device)
+        self.segs_dev = None
+        if segs.size:
+            self.segs_dev = torch.from_numpy(segs.view(np.uint8).copy()).to(self.device)
+
+    def bucket_len(self, b):
+        return self.bucket_lengths[b]
+
+    def segment_range(self, b):
+        """(first segment index, count) of bucket b in the segment table."""
+        return self._seg_first[b], self._seg_first[b + 1] - self._seg_first[b]
+
+    def check_rank_tensors(self, rank_tensors):
+        """Every rank must hold tensors of exactly the planned shapes (the
+        emulated "same order on every rank" rule)."""
+        for r, ts in enumerate(rank_tensors):
+            if len(ts) != len(self.shapes):
+                raise ValueError(f"rank {r}: {len(ts)} tensors, plan has {len(self.shapes)}")
+            for t, (x, s) in enumerate(zip(ts, self.shapes)):
+                if tuple(x.shape) != s or x.dtype != self.dtype or not x.is_contiguous() \
+                        or x.device != self.device:
+                    raise ValueError(f"rank {r} tensor {t} does not match the plan")
+
+    def pointer_table(self, rank_tensors):
+        """Device table [P * T] of the tensors' addresses, rank-major."""
+        import torch
+        self.check_rank_tensors(rank_tensors)
+        ptrs = [x.data_ptr() for ts in rank_tensors for x in ts]
+        return torch.tensor(ptrs, dtype=torch.int64).to(self.device)
+
+    def alloc_buckets(self, P):
+        """P bucket buffers of full bucket capacity."""
+        import torch
+        return [torch.empty(self.bucket_elems, dtype=self.dtype, device=self.device)
+                for _ in range(P)]
+
+    def _seg_ptr(self, b):
+        first, count = self.segment_range(b)
+        return self.segs_dev.data_ptr() + first * api.SEGMENT_DTYPE.itemsize, count
+
+    def pack(self, table, b, rank_buckets):
+        """Gather bucket b of every rank (pointer table from ``pointer_table``)
+        into ``rank_buckets`` on the current stream."""
+        ptr, count = self._seg_ptr(b)
+        api.ddp_bucket_pack(len(rank_buckets), self.code, ptr, count, table.data_ptr(),
+                            len(self.shapes), [x.data_ptr() for x in rank_buckets],
+                            self.bucket_len(b), api.current_stream(self.device))
+
+    def unpack(self, table, b, rank_buckets):
+        """Scatter bucket b of every rank back into its tensors."""
+        ptr, count = self._seg_ptr(b)
+        api.ddp_bucket_unpack(len(rank_buckets), self.code, ptr, count, table.data_ptr(),
+                              len(self.shapes), [x.data_ptr() for x in rank_buckets],
+                              self.bucket_len(b), api.current_stream(self.device))

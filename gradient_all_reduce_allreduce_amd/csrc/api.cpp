@@ -1,0 +1,336 @@
+// api.cpp -- the C ABI declared in include/ddp_allreduce.h.
+//
+// Everything here runs on the host: argument validation (complete before
+// any device work is enqueued), the bucket plan, error reporting, and the
+// hand-off to the kernel launchers.  No HIP call is made before validation
+// succeeds, so every error path can be exercised on a machine without a GPU.
+#include <stdint.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return DDP_OK;
+}
+
+bool valid_dtype(int d) { return d == DDP_F32 || d == DDP_BF16; }
+int elem_bytes(int d) { return d == DDP_BF16 ? 2 : 4; }
+
+struct Buf {
+    uintptr_t lo;
+    uintptr_t hi;   // one past the end
+    int es;
+    const char* what;
+    int index;
+};
+
+// Two buffers may be disjoint or alias exactly (same start, same element
+// size, same length); anything else is a partial overlap.
+int check_overlaps(const std::vector<Buf>& bufs) {
+    for (size_t i = 0; i < bufs.size(); ++i) {
+        for (size_t j = i + 1; j < bufs.size(); ++j) {
+            const Buf& a = bufs[i];
+            const Buf& b = bufs[j];
+            if (a.lo >= a.hi || b.lo >= b.hi) continue;
+            const bool overlap = a.lo < b.hi && b.lo < a.hi;
+            if (!overlap) continue;
+            const bool exact = a.lo == b.lo && a.hi == b.hi && a.es == b.es;
+            if (!exact) {
+                return fail(DDP_E_OVERLAP, "%s[%d] and %s[%d] overlap without aliasing exactly", a.what,
+                            a.index, b.what, b.index);
+            }
+        }
+    }
+    return DDP_OK;
+}
+
+int check_ranks(int32_t P) {
+    if (P < 1 || P > DDP_MAX_RANKS) return fail(DDP_E_ARG, "P = %d outside 1..%d", P, DDP_MAX_RANKS);
+    return DDP_OK;
+}
+
+int check_ptr_array(const void* const* arr, int32_t P, const char* what) {
+    if (arr == nullptr) return fail(DDP_E_ARG, "%s is NULL", what);
+    for (int r = 0; r < P; ++r) {
+        if (arr[r] == nullptr) return fail(DDP_E_ARG, "%s[%d] is NULL", what, r);
+        if (reinterpret_cast<uintptr_t>(arr[r]) & 15u)
+            return fail(DDP_E_ALIGN, "%s[%d] is not 16-byte aligned", what, r);
+    }
+    return DDP_OK;
+}
+
+int hip_fail(int code, const char* msg) {
+    return fail(DDP_E_HIP, "HIP error %d in %s", code, msg ? msg : "?");
+}
+
+// Shared validation of the reduction calls.
+int validate_reduce(int op, int32_t P, int32_t chunking, const void* const* in, int in_dtype,
+                    void* const* out, int out_dtype, int64_t n, bool out_required) {
+    if (op != DDP_SUM && op != DDP_MEAN) return fail(DDP_E_ARG, "unknown reduce op %d", op);
+    int s = check_ranks(P);
+    if (s) return s;
+    if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
+    if (n < 0) return fail(DDP_E_ARG, "n = %lld is negative", static_cast<long long>(n));
+    if (!valid_dtype(in_dtype)) return fail(DDP_E_ARG, "unknown input dtype %d", in_dtype);
+    if (!valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown output dtype %d", out_dtype);
+    if ((s = check_ptr_array(in, P, "rank_in"))) return s;
+    if (out_required || out != nullptr) {
+        if ((s = check_ptr_array(const_cast<const void* const*>(out), P, "rank_out"))) return s;
+    }
+    return DDP_OK;
+}
+
+void add_rank_bufs(std::vector<Buf>& bufs, const void* const* arr, int32_t P, int64_t n, int es,
+                   const char* what) {
+    for (int r = 0; r < P; ++r) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(arr[r]);
+        bufs.push_back({lo, lo + static_cast<uintptr_t>(n) * es, es, what, r});
+    }
+}
+
+uint64_t fnv1a(uint64_t h, const void* data, size_t len) {
+    const unsigned char* p = static_cast<const unsigned char*>(data);
+    for (size_t i = 0; i < len; ++i) {
+        h ^= p[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ddp_last_error(void) { return g_last_error.c_str(); }
+
+int ddp_bucket_plan(const int64_t* numels, int32_t n_tensors, ddp_dtype dtype, int64_t bucket_bytes,
+                    ddp_segment* segs, int64_t segs_cap, int64_t* n_segs, int32_t* n_buckets,
+                    int64_t* total_elems, uint64_t* fingerprint) {
+    if (n_tensors < 0) return fail(DDP_E_ARG, "n_tensors = %d is negative", n_tensors);
+    if (n_tensors > 0 && numels == nullptr) return fail(DDP_E_ARG, "numels is NULL");
+    if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (bucket_bytes <= 0 || bucket_bytes % 16 != 0)
+        return fail(DDP_E_ARG, "bucket_bytes = %lld must be a positive multiple of 16",
+                    static_cast<long long>(bucket_bytes));
+    if (n_segs == nullptr) return fail(DDP_E_ARG, "n_segs is NULL");
+    if (segs_cap < 0) return fail(DDP_E_ARG, "segs_cap is negative");
+    const int64_t es = elem_bytes(dtype);
+    const int64_t E = bucket_bytes / es;
+
+    int64_t total = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        if (numels[t] < 0) return fail(DDP_E_ARG, "numels[%d] is negative", t);
+        if (numels[t] > INT64_MAX / 4 - total) return fail(DDP_E_ARG, "total element count overflows");
+        total += numels[t];
+    }
+    const int64_t buckets = (total + E - 1) / E;
+    if (buckets > INT32_MAX) return fail(DDP_E_ARG, "more than 2^31-1 buckets");
+
+    // Reverse parameter order; the flat range is cut every E elements.
+    int64_t count = 0;
+    int64_t flat = 0;
+    for (int32_t t = n_tensors - 1; t >= 0; --t) {
+        int64_t remaining = numels[t];
+        int64_t src = 0;
+        while (remaining > 0) {
+            const int64_t b = flat / E;
+            const int64_t off = flat - b * E;
+            const int64_t take = remaining < E - off ? remaining : E - off;
+            if (segs != nullptr && count < segs_cap) {
+                ddp_segment& s = segs[count];
+                s.tensor = t;
+                s.bucket = static_cast<int32_t>(b);
+                s.src_off = src;
+                s.dst_off = off;
+                s.len = take;
+            }
+            ++count;
+            src += take;
+            flat += take;
+            remaining -= take;
+        }
+    }
+    *n_segs = count;
+    if (n_buckets) *n_buckets = static_cast<int32_t>(buckets);
+    if (total_elems) *total_elems = total;
+    if (fingerprint) {
+        uint64_t h = 14695981039346656037ull;
+        const int32_t d = dtype;
+        h = fnv1a(h, &d, sizeof d);
+        h = fnv1a(h, &bucket_bytes, sizeof bucket_bytes);
+        h = fnv1a(h, &n_tensors, sizeof n_tensors);
+        if (n_tensors > 0) h = fnv1a(h, numels, sizeof(int64_t) * static_cast<size_t>(n_tensors));
+        *fingerprint = h;
+    }
+    if (segs != nullptr && count > segs_cap)
+        return fail(DDP_E_PLAN, "segment capacity %lld < %lld needed", static_cast<long long>(segs_cap),
+                    static_cast<long long>(count));
+    return ok();
+}
+
+static int bucket_copy(bool pack, int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
+                       int64_t n_segs, const void* const* tensor_ptrs_dev, int32_t n_tensors,
+                       const void* const* rank_bucket, int64_t bucket_len, void* stream) {
+    int s = check_ranks(P);
+    if (s) return s;
+    if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (bucket_len < 0) return fail(DDP_E_ARG, "bucket_len is negative");
+    if (n_segs < 0) return fail(DDP_E_ARG, "n_segs is negative");
+    if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
+    if (bucket_len > 0 && n_segs == 0) return fail(DDP_E_PLAN, "a non-empty bucket needs segments");
+    if (n_segs > bucket_len) return fail(DDP_E_PLAN, "more segments than bucket elements");
+    if (bucket_len > 0 && (segs_dev == nullptr || tensor_ptrs_dev == nullptr))
+        return fail(DDP_E_ARG, "segment table or tensor pointer table is NULL");
+    if ((s = check_ptr_array(rank_bucket, P, "rank_bucket"))) return s;
+    const int es = elem_bytes(dtype);
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_bucket, P, bucket_len, es, "rank_bucket");
+    for (size_t i = 0; i < bufs.size(); ++i)
+        for (size_t j = i + 1; j < bufs.size(); ++j)
+            if (bufs[i].lo < bufs[j].hi && bufs[j].lo < bufs[i].hi)
+                return fail(DDP_E_OVERLAP, "rank_bucket[%d] and rank_bucket[%d] overlap", bufs[i].index,
+                            bufs[j].index);
+    if (bucket_len == 0) return ok();
+
+    ddp::CopyLaunch l{};
+    l.P = P;
+    l.elem_bytes = es;
+    l.pack = pack ? 1 : 0;
+    l.segs = segs_dev;
+    l.n_segs = n_segs;
+    l.tensors = tensor_ptrs_dev;
+    l.n_tensors = n_tensors;
+    for (int r = 0; r < P; ++r) l.bucket[r] = const_cast<void*>(rank_bucket[r]);
+    l.bucket_len = bucket_len;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_bucket_copy(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+int ddp_bucket_pack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev, int64_t n_segs,
+                    const void* const* tensor_ptrs_dev, int32_t n_tensors, void* const* rank_bucket,
+                    int64_t bucket_len, void* stream) {
+    return bucket_copy(true, P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors,
+                       const_cast<const void* const*>(rank_bucket), bucket_len, stream);
+}
+
+int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev, int64_t n_segs,
+                      void* const* tensor_ptrs_dev, int32_t n_tensors, const void* const* rank_bucket,
+                      int64_t bucket_len, void* stream) {
+    return bucket_copy(false, P, dtype, segs_dev, n_segs, const_cast<const void* const*>(tensor_ptrs_dev),
+                       n_tensors, rank_bucket, bucket_len, stream);
+}
+
+int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
+                            ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                            void* stream) {
+    int s = validate_reduce(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, true);
+    if (s) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
+    if ((s = check_overlaps(bufs))) return s;
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.sgd = 0;
+    l.write_out = 1;
+    for (int r = 0; r < P; ++r) {
+        l.in[r] = rank_in[r];
+        l.out[r] = rank_out[r];
+    }
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_reduce(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
+                        ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr,
+                        float mu, void* const* rank_grad_out, ddp_dtype out_dtype, void* stream) {
+    int s = validate_reduce(op, P, chunking, rank_grad, grad_dtype, rank_grad_out, out_dtype, n, false);
+    if (s) return s;
+    if (master_w == nullptr || momentum == nullptr) return fail(DDP_E_ARG, "master_w or momentum is NULL");
+    if ((reinterpret_cast<uintptr_t>(master_w) | reinterpret_cast<uintptr_t>(momentum)) & 15u)
+        return fail(DDP_E_ALIGN, "master_w or momentum is not 16-byte aligned");
+    if (!(lr == lr) || !(mu == mu) || lr > 3.4e38f || lr < -3.4e38f || mu > 3.4e38f || mu < -3.4e38f)
+        return fail(DDP_E_ARG, "lr and mu must be finite");
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_grad, P, n, elem_bytes(grad_dtype), "rank_grad");
+    if (rank_grad_out)
+        add_rank_bufs(bufs, const_cast<const void* const*>(rank_grad_out), P, n, elem_bytes(out_dtype),
+                      "rank_grad_out");
+    if ((s = check_overlaps(bufs))) return s;
+    // The optimizer state may not alias anything, not even exactly.
+    const uintptr_t wl = reinterpret_cast<uintptr_t>(master_w);
+    const uintptr_t vl = reinterpret_cast<uintptr_t>(momentum);
+    const uintptr_t bytes = static_cast<uintptr_t>(n) * 4;
+    if (n > 0) {
+        if (wl < vl + bytes && vl < wl + bytes) return fail(DDP_E_OVERLAP, "master_w and momentum overlap");
+        for (const Buf& b : bufs) {
+            if (b.lo < wl + bytes && wl < b.hi)
+                return fail(DDP_E_OVERLAP, "master_w overlaps %s[%d]", b.what, b.index);
+            if (b.lo < vl + bytes && vl < b.hi)
+                return fail(DDP_E_OVERLAP, "momentum overlaps %s[%d]", b.what, b.index);
+        }
+    }
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = grad_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.sgd = 1;
+    l.write_out = rank_grad_out != nullptr;
+    for (int r = 0; r < P; ++r) {
+        l.in[r] = rank_grad[r];
+        l.out[r] = rank_grad_out ? rank_grad_out[r] : nullptr;
+    }
+    l.w = master_w;
+    l.v = momentum;
+    l.lr = lr;
+    l.mu = mu;
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_reduce(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// bucket_copy.hip -- gather a bucket out of ragged gradient tensors (pack)
+// and scatter it back (unpack), all P ranks in one launch, for gfx950.
+//
+// DDP packs gradients into fixed-size buckets before the all-reduce and
+// every rank fills them in the same order ("Distributed Training", "Data
+// parallelism and all-reduce"; FSDP's flattened units, "Sharded data
+// parallelism").  The segment table of a bucket says which piece of which
+// tensor occupies which range of the bucket.
+//
+// A pure copy: bound by HBM bandwidth, 2 * bucket bytes per rank.  Each
+// workgroup walks tiles of the bucket (16-byte vectors on the bucket side,
+// always aligned); for a tile it stages the overlapping segments in LDS, so
+// that each lane finds its segment with a short binary search in LDS
+// instead of a chain of dependent global loads.  A vector that lies inside
+// one segment whose tensor address is 16-byte aligned moves as one 16-byte
+// access; vectors across a segment boundary or misaligned on the tensor
+// side move element by element.  Every bucket element is written exactly
+// once (the segments tile the bucket), so no synchronisation between
+// workgroups is needed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace ddp {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;
+constexpr int kVecPerLane = 2;   // 16-byte vectors per lane and tile
+
+struct CopyArgs {
+    const ddp_segment* segs;
+    int64_t n_segs;
+    const void* const* tensors;   // [P * n_tensors], rank-major
+    int32_t n_tensors;
+    int32_t es;                   // element bytes, 2 or 4
+    void* bucket[kMaxRanks];
+    int64_t bucket_len;
+    int64_t tile_elems;           // elements per tile (multiple of 16 / es)
+    int64_t tiles;
+};
+
+__device__ __forceinline__ void copy_elem(char* dst, const char* src, int es) {
+    if (es == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+    } else {
+        *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+    }
+}
+
+// Largest index g in [0, count) with dst[g] <= e (dst sorted ascending,
+// dst[0] <= e).
+__device__ __forceinline__ int lds_find(const int64_t* dst, int count, int64_t e) {
+    int lo = 0;
+    int hi = count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (dst[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <bool PACK>
+__global__ __launch_bounds__(kBlock) void bucket_copy_kernel(CopyArgs a) {
+    __shared__ int64_t s_dst[kBlock];
+    __shared__ int64_t s_len[kBlock];
+    __shared__ char* s_ten[kBlock];
+
+    const int tid = threadIdx.x;
+    const int rank = blockIdx.y;
+    char* const bucket = static_cast<char*>(a.bucket[rank]);
+    const void* const* tensors = a.tensors + static_cast<int64_t>(rank) * a.n_tensors;
+    const int es = a.es;
+    const int ve = 16 / es;   // elements per 16-byte vector
+
+    for (int64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+        const int64_t lo = tile * a.tile_elems;
+        const int64_t hi = lo + a.tile_elems < a.bucket_len ? lo + a.tile_elems : a.bucket_len;
+
+        // First segment holding element lo (same search in every lane).
+        int64_t f = 0;
+        {
+            int64_t l = 0;
+            int64_t h = a.n_segs - 1;
+            while (l < h) {
+                const int64_t mid = (l + h + 1) >> 1;
+                if (a.segs[mid].dst_off <= lo) l = mid; else h = mid - 1;
+            }
+            f = l;
+        }
+
+        while (true) {
+            const int64_t k = f + tid;
+            const bool valid = k < a.n_segs && a.segs[k].dst_off < hi;
+            if (valid) {
+                const ddp_segment sg = a.segs[k];
+                s_dst[tid] = sg.dst_off;
+                s_len[tid] = sg.len;
+                s_ten[tid] = static_cast<char*>(const_cast<void*>(tensors[sg.tensor])) + sg.src_off * es;
+            }
+            const int count = __syncthreads_count(valid);   // valid lanes form a prefix
+            const int64_t cov_lo = s_dst[0] > lo ? s_dst[0] : lo;
+            const int64_t last_end = s_dst[count - 1] + s_len[count - 1];
+            const int64_t cov_hi = last_end < hi ? last_end : hi;
+
+#pragma unroll
+            for (int u = 0; u < kVecPerLane; ++u) {
+                const int64_t e0 = lo + static_cast<int64_t>(u * kBlock + tid) * ve;
+                int64_t b = e0 > cov_lo ? e0 : cov_lo;
+                const int64_t e1 = e0 + ve < cov_hi ? e0 + ve : cov_hi;
+                if (b >= e1) continue;
+                int g = lds_find(s_dst, count, b);
+                char* bk = bucket + e0 * es;
+                char* tn = s_ten[g] + (e0 - s_dst[g]) * es;
+                const bool whole = b == e0 && e1 == e0 + ve && e1 <= s_dst[g] + s_len[g] &&
+                                   (reinterpret_cast<uintptr_t>(tn) & 15u) == 0;
+                if (whole) {
+                    if (PACK) {
+                        *reinterpret_cast<u32x4*>(bk) = *reinterpret_cast<const u32x4*>(tn);
+                    } else {
+                        *reinterpret_cast<u32x4*>(tn) = *reinterpret_cast<const u32x4*>(bk);
+                    }
+                    continue;
+                }
+                for (int64_t e = b; e < e1; ++e) {
+                    while (e >= s_dst[g] + s_len[g]) ++g;
+                    char* pb = bucket + e * es;
+                    char* pt = s_ten[g] + (e - s_dst[g]) * es;
+                    if (PACK) copy_elem(pb, pt, es); else copy_elem(pt, pb, es);
+                }
+            }
+            __syncthreads();   // LDS is restaged below or by the next tile
+            if (count < kBlock || last_end >= hi) break;
+            f += count;
+        }
+    }
+}
+
+}  // namespace
+
+int launch_bucket_copy(const CopyLaunch& l, const char** msg) {
+    if (l.bucket_len <= 0) return 0;
+    CopyArgs a{};
+    a.segs = l.segs;
+    a.n_segs = l.n_segs;
+    a.tensors = l.tensors;
+    a.n_tensors = l.n_tensors;
+    a.es = l.elem_bytes;
+    for (int r = 0; r < l.P; ++r) a.bucket[r] = l.bucket[r];
+    a.bucket_len = l.bucket_len;
+    a.tile_elems = static_cast<int64_t>(kBlock) * kVecPerLane * (16 / l.elem_bytes);
+    a.tiles = (l.bucket_len + a.tile_elems - 1) / a.tile_elems;
+
+    int dev = 0;
+    int cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) {
+        *msg = "hipDeviceGetAttribute(MultiprocessorCount)";
+        return static_cast<int>(e == hipSuccess ? hipErrorInvalidValue : e);
+    }
+    // About eight resident workgroups per CU in total, shared by the ranks.
+    int64_t gx = (static_cast<int64_t>(cus) * 8 + l.P - 1) / l.P;
+    if (gx > a.tiles) gx = a.tiles;
+    if (gx < 1) gx = 1;
+    const void* fn = l.pack ? reinterpret_cast<const void*>(&bucket_copy_kernel<true>)
+                            : reinterpret_cast<const void*>(&bucket_copy_kernel<false>);
+    void* args[] = {&a};
+    e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(l.P)), dim3(kBlock),
+                        args, 0, static_cast<hipStream_t>(l.stream));
+    if (e != hipSuccess) {
+        *msg = "hipLaunchKernel(bucket_copy)";
+        return static_cast<int>(e);
+    }
+    return 0;
+}
+
+}  // namespace ddp

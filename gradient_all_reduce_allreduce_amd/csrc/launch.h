@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernel
+// translation units.  Not installed, not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/ddp_allreduce.h"
+
+namespace ddp {
+
+constexpr int kMaxRanks = DDP_MAX_RANKS;
+
+// Everything the fused ring-reduce kernel needs; validated by the caller.
+struct RingLaunch {
+    int P;
+    int chunking;
+    int op;            // DDP_SUM / DDP_MEAN
+    int in_bf16;       // input element type is bf16
+    int out_bf16;      // output element type is bf16
+    int sgd;           // apply the momentum step to w, v
+    int write_out;     // write the reduced gradient to out[]
+    const void* in[kMaxRanks];
+    void* out[kMaxRanks];
+    float* w;
+    float* v;
+    float lr;
+    float mu;
+    int64_t n;
+    void* stream;
+};
+
+// Returns 0 on success, else a HIP error code; *msg names the failing call.
+int launch_ring_reduce(const RingLaunch& l, const char** msg);
+
+// 16-byte vectors of each rank a lane keeps in flight per tile: P * U loads.
+constexpr int ring_vectors_per_lane(int P) {
+    return P <= 2 ? 8 : (P <= 4 ? 4 : (P <= 8 ? 2 : 1));
+}
+
+// Kernel entry points, one function per (input, output) element type pair;
+// defined in ring_reduce_<in>_<out>.hip.  scalar: the one-element-per-lane
+// variant for chunks shorter than a tile.
+const void* ring_kernel_f32_f32(int P, int sgd, int scalar);
+const void* ring_kernel_f32_bf16(int P, int sgd, int scalar);
+const void* ring_kernel_bf16_f32(int P, int sgd, int scalar);
+const void* ring_kernel_bf16_bf16(int P, int sgd, int scalar);
+
+struct CopyLaunch {
+    int P;
+    int elem_bytes;    // 2 or 4
+    int pack;          // 1: tensors -> bucket, 0: bucket -> tensors
+    const ddp_segment* segs;
+    int64_t n_segs;
+    const void* const* tensors;   // device array [P * n_tensors]
+    int32_t n_tensors;
+    void* bucket[kMaxRanks];
+    int64_t bucket_len;
+    void* stream;
+};
+
+int launch_bucket_copy(const CopyLaunch& l, const char** msg);
+
+}  // namespace ddp

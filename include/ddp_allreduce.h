@@ -1,0 +1,227 @@
+/*
+ * ddp_allreduce.h -- C ABI of the MI355X (gfx950) gradient all-reduce library.
+ *
+ * What it computes.  Data-parallel training gives every rank (one replica of
+ * the model) the gradient of its own shard of the batch; an all-reduce then
+ * combines the ranks' equal-size gradient tensors elementwise so that every
+ * rank holds the same sum or mean ("Distributed Training",
+ * computervisiononline.com/explains/distributed-training, section "Data
+ * parallelism and all-reduce"; CS336 "Lecture 8 - Parallelism", rd.me/cs336/
+ * lec8, "Collective Operations").  The reduction is ReduceOperation Sum or
+ * Mean (Burn distributed guide, pgsm.cn/news/420861, reduction configuration
+ * section).  The order of the floating-point additions is that of a ring
+ * (Burn collective blog, cielbird.github.io/blog/burn-distributed, "Methods",
+ * Ring): a reduce-scatter followed by an all-gather.
+ *
+ * How it runs.  All P ranks live on one GPU as P buffers in HBM, and one
+ * kernel performs, for every element, exactly the additions the ring would
+ * perform over P GPUs, in the same order, then writes the result to every
+ * rank's output.  The order is fixed as follows: with C chunks of length
+ * L = ceil(n / C), element i belongs to chunk j = floor(i / L), whose ring
+ * starts at rank s = j mod P and travels r -> r + 1, so
+ *     result[i] = (((x_s[i] + x_{s+1}[i]) + x_{s+2}[i]) + ... + x_{s+P-1}[i])
+ * (rank indices mod P), every addition a float32 addition rounded to
+ * nearest even.  Mean then divides by P once, correctly rounded.  bf16
+ * inputs are widened to float32 exactly before the first addition; bf16
+ * outputs are rounded to nearest even, NaN kept quiet.  No FMA contraction
+ * and no flushing of subnormals anywhere.
+ *
+ * Conventions shared by every call.
+ *   - Device memory is owned by the caller (allocated through PyTorch or
+ *     hipMalloc).  The library allocates no device memory and keeps no
+ *     device state between calls.
+ *   - "Host array of device pointers" means a plain C array in host memory
+ *     whose entries are device addresses; it is read during the call only.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Device work is enqueued on it and the call returns before it runs: the
+ *     caller keeps every buffer alive and unmodified until the stream reaches
+ *     that point (the pages' CollectiveTensor must be resolved before use;
+ *     here resolving means synchronizing the stream or an event on it).
+ *   - Every call validates its arguments before launching anything and
+ *     returns a ddp_status; on any error nothing has been enqueued.  The
+ *     library never aborts and never prints; ddp_last_error() gives a message
+ *     for the calling thread's most recent failure.
+ *   - Device buffers must be 16-byte aligned.  Two buffers of one call may
+ *     either be disjoint or start at the same address with the same element
+ *     size (exact aliasing, e.g. an in-place all-reduce); any other overlap
+ *     is rejected.
+ */
+#ifndef DDP_ALLREDUCE_H
+#define DDP_ALLREDUCE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest number of emulated ranks a call accepts. */
+#define DDP_MAX_RANKS 16
+
+typedef enum ddp_status {
+    DDP_OK = 0,
+    DDP_E_ARG = -1,          /* invalid argument (P, chunking, n, null pointer, enum) */
+    DDP_E_UNSUPPORTED = -2,  /* valid but unsupported combination */
+    DDP_E_ALIGN = -3,        /* a device buffer is not 16-byte aligned */
+    DDP_E_OVERLAP = -4,      /* two buffers overlap other than by exact aliasing */
+    DDP_E_PLAN = -5,         /* bucket plan inconsistent or capacity too small */
+    DDP_E_HIP = -6           /* the HIP runtime reported an error */
+} ddp_status;
+
+/* ReduceOperation of the Burn distributed guide (reduction configuration
+ * section): Sum adds the ranks' tensors, Mean gives every replica the
+ * average (torch's ReduceOp.SUM / AVG in CS336 Lecture 8). */
+typedef enum ddp_reduce_op { DDP_SUM = 0, DDP_MEAN = 1 } ddp_reduce_op;
+
+/* Element types.  Accumulation is always float32. */
+typedef enum ddp_dtype { DDP_F32 = 0, DDP_BF16 = 1 } ddp_dtype;
+
+/* One piece of one tensor inside one bucket, in elements: elements
+ * [src_off, src_off + len) of tensor `tensor` (flattened in C order) occupy
+ * [dst_off, dst_off + len) of bucket `bucket`. */
+typedef struct ddp_segment {
+    int32_t tensor;
+    int32_t bucket;
+    int64_t src_off;
+    int64_t dst_off;
+    int64_t len;
+} ddp_segment;
+
+/*
+ * ddp_bucket_plan -- host only, no device work.
+ *
+ * Plans fixed-size gradient buckets as DDP does ("Distributed Training",
+ * "Data parallelism and all-reduce": gradients packed into buckets, filled
+ * in the reverse order of the model's parameters, every rank reducing the
+ * buckets in the same order).  Tensors are laid end to end in reverse
+ * parameter order and the flat range is cut every E = bucket_bytes /
+ * sizeof(dtype) elements, so every bucket but the last holds exactly E
+ * elements and a tensor may straddle buckets.  Zero-size tensors produce no
+ * segment.
+ *
+ *   numels       host array [n_tensors], element counts in parameter order
+ *   dtype        element type (sets the element size)
+ *   bucket_bytes bucket capacity in bytes; a positive multiple of 16
+ *   segs         host array [segs_cap] to receive the segments, in bucket
+ *                order and by increasing dst_off within a bucket; may be NULL
+ *                to query the count only
+ *   n_segs       out: number of segments (always written on DDP_OK and on
+ *                DDP_E_PLAN for a too-small capacity)
+ *   n_buckets    out: number of buckets (may be NULL)
+ *   total_elems  out: sum of numels (may be NULL)
+ *   fingerprint  out: 64-bit FNV-1a hash of (dtype, bucket_bytes, numels);
+ *                equal on every rank that planned the same parameter list
+ *                (may be NULL)
+ * Errors: DDP_E_ARG (negative counts, NULL numels with n_tensors > 0, bad
+ * dtype, bucket_bytes not a positive multiple of 16, more than 2^31-1
+ * buckets), DDP_E_PLAN (segs_cap too small; *n_segs holds the need).
+ */
+int ddp_bucket_plan(const int64_t* numels, int32_t n_tensors, ddp_dtype dtype,
+                    int64_t bucket_bytes, ddp_segment* segs, int64_t segs_cap,
+                    int64_t* n_segs, int32_t* n_buckets, int64_t* total_elems,
+                    uint64_t* fingerprint);
+
+/*
+ * ddp_bucket_pack / ddp_bucket_unpack -- device copies, all P ranks in one
+ * launch.
+ *
+ * Pack gathers every rank's pieces of one bucket out of its separately
+ * allocated gradient tensors into that rank's flat bucket buffer; unpack
+ * scatters a bucket back into the tensors.  ("Distributed Training": DDP
+ * packs gradients into buckets; FSDP flattens a unit's parameters into one
+ * tensor, "Sharded data parallelism".)  Bit-exact copies.
+ *
+ *   P               number of ranks, 1..DDP_MAX_RANKS
+ *   dtype           element type of tensors and buckets
+ *   segs_dev        DEVICE array [n_segs]: the segments of this one bucket as
+ *                   returned by ddp_bucket_plan (same bucket index, sorted by
+ *                   dst_off, tiling [0, bucket_len) exactly).  The library
+ *                   does not read it on the host: a table that is not a
+ *                   bucket's slice of a plan for these tensors is undefined
+ *                   behaviour.
+ *   n_segs          number of segments, >= 0
+ *   tensor_ptrs_dev DEVICE array [P * n_tensors] of device pointers,
+ *                   rank-major: entry r * n_tensors + t is rank r's tensor t
+ *                   (contiguous, any alignment of its element type)
+ *   n_tensors       number of tensors per rank, >= 1
+ *   rank_bucket     host array [P] of device pointers to the bucket buffers
+ *                   (bucket_len elements each, 16-byte aligned, pairwise
+ *                   disjoint)
+ *   bucket_len      elements in this bucket, >= 0 (0: nothing is launched)
+ * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
+ */
+int ddp_bucket_pack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
+                    int64_t n_segs, const void* const* tensor_ptrs_dev,
+                    int32_t n_tensors, void* const* rank_bucket,
+                    int64_t bucket_len, void* stream);
+
+int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
+                      int64_t n_segs, void* const* tensor_ptrs_dev,
+                      int32_t n_tensors, const void* const* rank_bucket,
+                      int64_t bucket_len, void* stream);
+
+/*
+ * allreduce_ring_emulated -- the all-reduce of P rank buffers of n elements
+ * in the chunked ring order described at the top of this header.
+ *
+ * Every rank contributes a tensor of the same size and every rank receives
+ * the result ("Distributed Training", "Data parallelism and all-reduce");
+ * the ring is a reduce-scatter followed by an all-gather (the same page,
+ * "Sharded data parallelism", on the ring's communication volume).
+ *
+ *   op        DDP_SUM or DDP_MEAN
+ *   P         number of ranks, 1..DDP_MAX_RANKS
+ *   chunking  number of ring chunks C >= 1 (C = P is the textbook ring)
+ *   rank_in   host array [P] of device pointers, n elements of in_dtype each
+ *   in_dtype  DDP_F32 or DDP_BF16
+ *   rank_out  host array [P] of device pointers, n elements of out_dtype
+ *             each; rank_out[r] may equal rank_in[r] when the element sizes
+ *             match (in-place all-reduce)
+ *   out_dtype DDP_F32 or DDP_BF16
+ *   n         elements per rank, >= 0 (0: nothing is launched)
+ * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
+ */
+int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
+                            const void* const* rank_in, ddp_dtype in_dtype,
+                            void* const* rank_out, ddp_dtype out_dtype,
+                            int64_t n, void* stream);
+
+/*
+ * allreduce_fused_sgd -- the same all-reduce, followed in the same kernel by
+ * one SGD-with-momentum step on a float32 master copy of the weights.
+ *
+ * After the all-reduce every replica holds the same gradient and takes the
+ * same local optimizer step (CS336 Lecture 8, "Data Parallelism (DDP)");
+ * mixed precision keeps float32 master weights and accumulates in float32
+ * ("Distributed Training", Related, "Mixed-Precision Training").  Since the
+ * replicas are identical, one copy of (w, v) stands for all of them.  With
+ * g the reduced gradient in float32 (after the Mean division, before any
+ * output rounding), each element does, with one rounding per operation:
+ *     v = mu * v;  v = v + g;  w = w - lr * v
+ * (heavy-ball momentum, no dampening, no Nesterov, no weight decay).
+ *
+ *   rank_grad      host array [P] of device pointers, n elements of grad_dtype
+ *   master_w       device pointer, n floats, updated in place
+ *   momentum       device pointer, n floats, updated in place
+ *   lr, mu         learning rate and momentum factor (finite)
+ *   rank_grad_out  host array [P] of device pointers to receive the reduced
+ *                  gradient as out_dtype, or NULL to skip writing it
+ *   other arguments as for allreduce_ring_emulated.  master_w and momentum
+ *   must be disjoint from each other and from every gradient buffer.
+ * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
+ */
+int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
+                        const void* const* rank_grad, ddp_dtype grad_dtype,
+                        int64_t n, float* master_w, float* momentum, float lr,
+                        float mu, void* const* rank_grad_out,
+                        ddp_dtype out_dtype, void* stream);
+
+/* Message describing the calling thread's most recent non-OK status
+ * ("" if none).  The pointer stays valid until the thread's next call. */
+const char* ddp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDP_ALLREDUCE_H */

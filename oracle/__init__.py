@@ -33,14 +33,15 @@ Modules:
 Parity status of each function is stated in its module header.
 """
 
-from .ring import (SUM, MEAN, chunk_length, chunk_start_ranks, ring_allreduce,
-                   ring_allreduce_sampled)
+from .ring import (SUM, MEAN, chunk_length, chunk_start_ranks, chunk_start_ranks_at,
+                   ring_allreduce, ring_allreduce_sampled)
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .sgd import sgd_momentum
 from .bucket import bucket_plan, pack, unpack
 
 __all__ = [
-    "SUM", "MEAN", "chunk_length", "chunk_start_ranks", "ring_allreduce",
+    "SUM", "MEAN", "chunk_length", "chunk_start_ranks", "chunk_start_ranks_at",
+    "ring_allreduce",
     "ring_allreduce_sampled", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "sgd_momentum", "bucket_plan", "pack", "unpack",
 ]

@@ -59,10 +59,18 @@ def chunk_start_ranks(n, chunking, P):
     (chunk mod P).  Reading of the Ring strategy in the Burn collective blog,
     "Methods".
     """
+    return chunk_start_ranks_at(n, chunking, P, np.arange(n, dtype=np.int64))
+
+
+def chunk_start_ranks_at(n, chunking, P, idx):
+    """Start ranks of the elements with the given indices of an n-element
+    buffer (the same rule as ``chunk_start_ranks``, without materialising
+    all n of them)."""
     L = chunk_length(n, chunking)
-    if n == 0:
+    idx = np.asarray(idx, dtype=np.int64)
+    if idx.size == 0:
         return np.zeros(0, dtype=np.int64)
-    return (np.arange(n, dtype=np.int64) // L) % P
+    return (idx // L) % P
 
 
 def _widen(X, in_dtype):

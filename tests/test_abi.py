@@ -1,0 +1,212 @@
+"""Host-side checks of the C ABI: no GPU needed, no device work launched.
+
+* the library loads and exports every function the header declares;
+* the bucket plan equals the oracle's plan, element for element;
+* every validation rule returns its status before anything is enqueued.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddp_allreduce.h")
+
+ddp = pytest.importorskip("gradient_all_reduce_allreduce_amd")
+from gradient_all_reduce_allreduce_amd import _native as N  # noqa: E402
+from gradient_all_reduce_allreduce_amd.api import DdpError  # noqa: E402
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for want in ("ddp_bucket_plan", "ddp_bucket_pack", "ddp_bucket_unpack",
+                 "allreduce_ring_emulated", "allreduce_fused_sgd", "ddp_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_header_function():
+    lib = ctypes.CDLL(N.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_has_the_same_names():
+    for name in header_functions():
+        if name == "ddp_last_error":
+            continue
+        assert callable(getattr(ddp, name)), name
+
+
+# ------------------------------------------------------------------ plan ----
+
+def _plan_tuples(segs):
+    return [(int(s["tensor"]), int(s["bucket"]), int(s["src_off"]), int(s["dst_off"]),
+             int(s["len"])) for s in segs]
+
+
+@pytest.mark.parametrize("case", ["resnet50", "vit_b16", "ragged", "tiny", "zeros", "empty"])
+def test_plan_equals_oracle(case):
+    if case == "tiny":
+        numels, eb, bb = [15, 7, 0, 32, 1, 33], 4, 48
+    elif case == "zeros":
+        numels, eb, bb = [0, 0, 5, 0], 2, 16
+    elif case == "empty":
+        numels, eb, bb = [], 4, 64
+    elif case == "ragged":
+        numels, eb, bb = workloads.ragged_sizes(), 4, 25 << 20
+    else:
+        shapes = workloads.model_shapes(case)
+        numels = [workloads.numel(s) for s in shapes]
+        eb, bb = (4, 25 << 20) if case == "resnet50" else (2, 25 << 20)
+    dtype = ddp.F32 if eb == 4 else ddp.BF16
+    segs, nb, total, fp = ddp.ddp_bucket_plan(numels, dtype, bb)
+    want, lengths = oracle.bucket_plan(numels, eb, bb)
+    assert _plan_tuples(segs) == [tuple(int(v) for v in s) for s in want]
+    assert nb == len(lengths) and total == sum(numels)
+
+
+def test_plan_fingerprint():
+    a = ddp.ddp_bucket_plan([10, 20, 30], ddp.F32, 64)[3]
+    assert a == ddp.ddp_bucket_plan([10, 20, 30], ddp.F32, 64)[3]
+    assert a != ddp.ddp_bucket_plan([10, 30, 20], ddp.F32, 64)[3]
+    assert a != ddp.ddp_bucket_plan([10, 20, 30], ddp.F32, 128)[3]
+    assert a != ddp.ddp_bucket_plan([10, 20, 30], ddp.BF16, 64)[3]
+
+
+def test_plan_errors():
+    lib = N.lib()
+    numels = (ctypes.c_int64 * 2)(5, 7)
+    n = ctypes.c_int64(0)
+    assert lib.ddp_bucket_plan(numels, 2, ddp.F32, 24, None, 0, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_ARG          # not a multiple of 16
+    assert lib.ddp_bucket_plan(numels, 2, ddp.F32, 0, None, 0, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_plan(numels, 2, 7, 16, None, 0, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_ARG          # bad dtype
+    assert lib.ddp_bucket_plan(None, 2, ddp.F32, 16, None, 0, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_plan(numels, -1, ddp.F32, 16, None, 0, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_ARG
+    neg = (ctypes.c_int64 * 2)(5, -7)
+    assert lib.ddp_bucket_plan(neg, 2, ddp.F32, 16, None, 0, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_ARG
+    segs = (N.Segment * 1)()
+    assert lib.ddp_bucket_plan(numels, 2, ddp.F32, 16, segs, 1, ctypes.byref(n), None, None,
+                               None) == N.DDP_E_PLAN
+    assert n.value == 4                                       # 12 elements, 4 per bucket
+    assert "capacity" in N.last_error()
+
+
+# ------------------------------------------------------------ validation ----
+
+A = 0x7f0000000000            # fake, 16-byte aligned device addresses; never touched
+MB = 1 << 20
+
+
+def ar(op=0, P=2, C=2, ins=None, it=0, outs=None, ot=0, n=16):
+    ins = ins if ins is not None else [A + r * MB for r in range(P)]
+    outs = outs if outs is not None else [A + 64 * MB + r * MB for r in range(P)]
+    return N.lib().allreduce_ring_emulated(
+        op, P, C, N.pointer_array(ins) if ins != "null" else None, it,
+        N.pointer_array(outs) if outs != "null" else None, ot, n, None)
+
+
+def test_allreduce_argument_errors():
+    assert ar(op=2) == N.DDP_E_ARG
+    assert ar(P=0) == N.DDP_E_ARG
+    assert ar(P=17, ins=[A + r * MB for r in range(17)],
+              outs=[A + 64 * MB + r * MB for r in range(17)]) == N.DDP_E_ARG
+    assert ar(C=0) == N.DDP_E_ARG
+    assert ar(n=-1) == N.DDP_E_ARG
+    assert ar(it=3) == N.DDP_E_ARG
+    assert ar(ot=-1) == N.DDP_E_ARG
+    assert ar(ins="null") == N.DDP_E_ARG
+    assert ar(outs="null") == N.DDP_E_ARG
+    assert ar(ins=[A, 0]) == N.DDP_E_ARG
+    assert "rank_in[1] is NULL" in N.last_error()
+
+
+def test_allreduce_alignment_errors():
+    assert ar(ins=[A, A + MB + 4]) == N.DDP_E_ALIGN
+    assert ar(outs=[A + 64 * MB + 8, A + 65 * MB]) == N.DDP_E_ALIGN
+
+
+def test_allreduce_overlap_rules():
+    n = 1024
+    # partial overlap between two inputs
+    assert ar(ins=[A, A + 16], n=n) == N.DDP_E_OVERLAP
+    # output partially over another rank's input
+    assert ar(ins=[A, A + MB], outs=[A + MB + 64, A + 2 * MB], n=n) == N.DDP_E_OVERLAP
+    # bf16 input aliased by an f32 output of the same start: different
+    # element sizes, rejected
+    assert ar(ins=[A, A + MB], it=1, outs=[A, A + MB], ot=0, n=n) == N.DDP_E_OVERLAP
+    # exact in-place aliasing and n = 0 are accepted; n = 0 launches nothing
+    assert ar(ins=[A, A + MB], outs=[A, A + MB], n=0) == N.DDP_OK
+    assert N.last_error() == ""
+
+
+def test_zero_length_is_a_no_op():
+    assert ar(n=0) == N.DDP_OK
+
+
+def sgd(P=2, C=2, grads=None, gt=0, n=16, w=A + 200 * MB, v=A + 300 * MB, lr=1e-3, mu=0.9,
+        outs=None, ot=0, op=1):
+    grads = grads if grads is not None else [A + r * MB for r in range(P)]
+    return N.lib().allreduce_fused_sgd(op, P, C, N.pointer_array(grads), gt, n, w, v, lr, mu,
+                                       N.pointer_array(outs) if outs else None, ot, None)
+
+
+def test_fused_sgd_errors():
+    assert sgd(w=None) == N.DDP_E_ARG
+    assert sgd(v=None) == N.DDP_E_ARG
+    assert sgd(w=A + 200 * MB + 4) == N.DDP_E_ALIGN
+    assert sgd(lr=float("nan")) == N.DDP_E_ARG
+    assert sgd(mu=float("inf")) == N.DDP_E_ARG
+    assert sgd(v=A + 200 * MB + 16, n=1024) == N.DDP_E_OVERLAP       # w and v overlap
+    assert sgd(w=A, n=1024) == N.DDP_E_OVERLAP                       # w aliases a gradient
+    assert sgd(outs=[A + 500 * MB, A + 500 * MB + 32], n=1024) == N.DDP_E_OVERLAP
+    assert sgd(n=0) == N.DDP_OK
+
+
+def test_pack_errors():
+    lib = N.lib()
+    buckets = N.pointer_array([A, A + MB])
+    assert lib.ddp_bucket_pack(0, 0, A, 1, A, 1, buckets, 16, None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_pack(2, 5, A, 1, A, 1, buckets, 16, None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_pack(2, 0, A, 0, A, 1, buckets, 16, None) == N.DDP_E_PLAN
+    assert lib.ddp_bucket_pack(2, 0, None, 1, A, 1, buckets, 16, None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_pack(2, 0, A, 1, A, 0, buckets, 16, None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_pack(2, 0, A, 1, A, 1, N.pointer_array([A, A + 8]), 16,
+                               None) == N.DDP_E_ALIGN
+    assert lib.ddp_bucket_pack(2, 0, A, 1, A, 1, N.pointer_array([A, A + 16]), 16,
+                               None) == N.DDP_E_OVERLAP
+    assert lib.ddp_bucket_unpack(2, 0, A, 1, A, 1, buckets, -1, None) == N.DDP_E_ARG
+    assert lib.ddp_bucket_pack(2, 0, A, 0, A, 1, buckets, 0, None) == N.DDP_OK
+
+
+def test_python_layer_raises_with_the_status():
+    with pytest.raises(DdpError) as e:
+        ddp.allreduce_ring_emulated("sum", 0, 1, [], ddp.F32, [], ddp.F32, 4)
+    assert e.value.status == N.DDP_E_ARG
+
+
+def test_last_error_is_per_thread():
+    import threading
+    assert ar(P=0) == N.DDP_E_ARG
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(N.last_error()))
+    t.start()
+    t.join()
+    assert seen == [""] and "P = 0" in N.last_error()
