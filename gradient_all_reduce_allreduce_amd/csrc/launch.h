@@ -32,9 +32,15 @@ struct RingLaunch {
 // Returns 0 on success, else a HIP error code; *msg names the failing call.
 int launch_ring_reduce(const RingLaunch& l, const char** msg);
 
-// 16-byte vectors of each rank a lane keeps in flight per tile: P * U loads.
+// Vectors of each rank a lane keeps in flight per tile: P * U loads.
 constexpr int ring_vectors_per_lane(int P) {
-    return P <= 2 ? 8 : (P <= 4 ? 4 : (P <= 8 ? 2 : 1));
+    return P <= 2 ? 4 : (P <= 8 ? 2 : 1);
+}
+
+// Elements per lane vector: 8 for bf16 -> bf16 (16-byte loads and stores),
+// otherwise 4 so that float32 outputs and momentum state move as 16 bytes.
+constexpr int ring_lane_elems(bool in_bf16, bool out_bf16, bool sgd) {
+    return (in_bf16 && out_bf16 && !sgd) ? 8 : 4;
 }
 
 // Kernel entry points, one function per (input, output) element type pair;

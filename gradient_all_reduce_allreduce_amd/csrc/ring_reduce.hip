@@ -3,9 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
-#include <unordered_map>
-
 #include "launch.h"
 #include "ring_reduce_impl.h"
 
@@ -13,7 +10,7 @@ namespace ddp {
 namespace {
 
 // Buffers longer than this go out in several launches so that lane offsets
-// stay 32-bit; a multiple of every vector width, so each launch's first
+// stay 32-bit; a multiple of every lane-vector width, so each launch's first
 // element stays 16-byte aligned.
 constexpr int64_t kMaxLaunchElems = int64_t(1) << 29;
 
@@ -24,62 +21,21 @@ const void* select_kernel(const RingLaunch& l, int scalar) {
     return l.out_bf16 ? ring_kernel_f32_bf16(l.P, l.sgd, scalar) : ring_kernel_f32_f32(l.P, l.sgd, scalar);
 }
 
-struct DeviceInfo {
-    int cus = 0;
-    std::unordered_map<const void*, int> blocks_per_cu;
-};
-
-std::mutex g_mutex;
-std::unordered_map<int, DeviceInfo> g_devices;
-
-// Resident workgroups of `fn` on the current device (CUs x blocks per CU),
-// or -(HIP error).
-int resident_blocks(const void* fn, const char** msg) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) {
-        *msg = "hipGetDevice";
-        return -static_cast<int>(e);
-    }
-    std::lock_guard<std::mutex> lock(g_mutex);
-    DeviceInfo& info = g_devices[dev];
-    if (info.cus == 0) {
-        int cus = 0;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess || cus <= 0) {
-            *msg = "hipDeviceGetAttribute(MultiprocessorCount)";
-            return -static_cast<int>(e == hipSuccess ? hipErrorInvalidValue : e);
-        }
-        info.cus = cus;
-    }
-    auto it = info.blocks_per_cu.find(fn);
-    if (it == info.blocks_per_cu.end()) {
-        int nb = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, rr::kBlock, 0);
-        if (e != hipSuccess || nb <= 0) {
-            *msg = "hipOccupancyMaxActiveBlocksPerMultiprocessor";
-            return -static_cast<int>(e == hipSuccess ? hipErrorInvalidValue : e);
-        }
-        it = info.blocks_per_cu.emplace(fn, nb).first;
-    }
-    return info.cus * it->second;
-}
-
 }  // namespace
 
 int launch_ring_reduce(const RingLaunch& l, const char** msg) {
     if (l.n <= 0) return 0;
-    const int64_t V = l.in_bf16 ? 8 : 4;
+    const int64_t V = ring_lane_elems(l.in_bf16 != 0, l.out_bf16 != 0, l.sgd != 0);
     const int64_t tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P) * V;
     const int64_t L = (l.n + l.chunking - 1) / l.chunking;
+    // Chunks shorter than a tile would put several start ranks in one tile:
+    // those calls use the one-element-per-lane kernel.
     const int scalar = L < tile ? 1 : 0;
     const void* fn = select_kernel(l, scalar);
     if (fn == nullptr) {
         *msg = "no kernel for this rank count";
         return static_cast<int>(hipErrorInvalidValue);
     }
-    const int slots = resident_blocks(fn, msg);
-    if (slots < 0) return -slots;
     const int ies = l.in_bf16 ? 2 : 4;
     const int oes = l.out_bf16 ? 2 : 4;
 
@@ -101,23 +57,13 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         a.mean = l.op == DDP_MEAN;
         a.write_out = l.write_out;
 
-        int64_t grid = 1;
+        int64_t grid;
         if (scalar) {
-            a.per_block = 0;
-            const int64_t need = (n + rr::kBlock - 1) / rr::kBlock;
-            grid = need < slots ? need : slots;
-        } else if (a.n_vec > 0) {
-            // Balanced contiguous shares in whole rows of 256 vectors, one
-            // share per resident workgroup.
-            const int64_t row = rr::kBlock * V;
-            const int64_t rows = (a.n_vec + row - 1) / row;
-            const int64_t rows_per_block = (rows + slots - 1) / slots;
-            a.per_block = static_cast<uint32_t>(rows_per_block * row);
-            grid = (a.n_vec + a.per_block - 1) / a.per_block;
+            grid = (n + rr::kBlock - 1) / rr::kBlock;
         } else {
-            a.per_block = static_cast<uint32_t>(rr::kBlock * V);
+            grid = (a.n_vec + tile - 1) / tile;   // one tile per workgroup
+            if (grid < 1) grid = 1;               // the tail still needs a workgroup
         }
-        if (grid < 1) grid = 1;
         void* args[] = {&a};
         const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(rr::kBlock), args, 0,
                                              static_cast<hipStream_t>(l.stream));

@@ -16,21 +16,27 @@
 //
 // The work is bound by HBM bandwidth: per element it reads P inputs, writes
 // P outputs and does P-1 float32 additions.  The design follows from that:
-//   * each workgroup of 256 lanes owns one contiguous, balanced share of the
-//     buffer and the grid equals the device's resident capacity, so every
-//     workgroup streams concurrently and all finish together;
-//   * each lane loads U 16-byte vectors from each of the P ranks per tile
-//     (P*U loads in flight) with non-temporal hints, folds them in registers
-//     and stores 16-byte vectors non-temporally: the data is touched once,
-//     so nothing is staged in LDS and no cache lines are kept;
+//   * one workgroup of 256 lanes per tile and as many workgroups as tiles;
+//     the dispatcher balances tiles over the CUs and XCDs as they free up
+//     (measured faster than fixed per-workgroup shares of the buffer);
+//   * each lane loads U vectors of V elements from each of the P ranks (P*U
+//     loads in flight) with non-temporal hints, folds them in registers and
+//     stores them non-temporally.  Every lane store is 16 bytes wide when
+//     the output or the momentum state is float32 (V = 4), so a wave writes
+//     1 KiB contiguous per instruction; bf16 -> bf16 moves 8 elements per
+//     lane.  The data is touched once, so nothing is staged in LDS and no
+//     cache lines are kept;
 //   * addresses are a per-rank base in SGPRs plus one 32-bit lane offset
 //     shared by all ranks (the host splits buffers over 2^29 elements into
 //     several launches), which keeps VGPRs for data;
-//   * the reduce-scatter start rank is uniform over a tile except where a
-//     chunk boundary falls inside it; chunks are at least a tile long on
-//     this path, so such a tile holds two start ranks and is folded in both
-//     orders, selecting per element.  Chunks shorter than a tile go to a
-//     one-element-per-lane kernel;
+//   * the reduce-scatter start rank s is uniform over a tile except where a
+//     chunk boundary falls inside it, so the lanes load rank (s + k) mod P
+//     into register k -- the rotation happens in the scalar pointer loads --
+//     and one fixed fold serves every start rank.  Chunks are at least a
+//     tile long on this path, so a tile holds at most two start ranks; the
+//     second order is the same registers folded from k = 1, selected per
+//     element.  Chunks shorter than a tile go to a one-element-per-lane
+//     kernel;
 //   * bf16 inputs are widened exactly (a shift) inside the fold, float32
 //     accumulation throughout, no FMA contraction, subnormals kept.
 #pragma once
@@ -58,8 +64,7 @@ struct RingArgs {
     int64_t base;        // global index of this launch's first element
     int64_t L;           // chunk length ceil(n_total / C)
     uint32_t n;          // elements in this launch (< 2^29)
-    uint32_t n_vec;      // elements covered by whole 16-byte input vectors
-    uint32_t per_block;  // elements per workgroup, a multiple of 256 * V
+    uint32_t n_vec;      // elements covered by whole lane vectors
     int32_t mean;
     int32_t write_out;
 };
@@ -119,105 +124,111 @@ __device__ __forceinline__ void momentum_step(float g, float& w, float& v, float
     v = vn;
 }
 
-// ---- the fold: ((x_S + x_{S+1}) + ...) + x_{S+P-1}, rank indices mod P ---
+// The kernel reads its arguments straight from the kernarg segment (address
+// space 4).  A uniform index into the rank-pointer arrays then compiles to a
+// scalar load, with no private copy of the argument block.
+typedef const __attribute__((address_space(4))) RingArgs* KArgs;
 
-template <int P, int S, bool BF16, int U, int V>
-__device__ __forceinline__ void fold_from(const u32x4 (&x)[P][U], float (&acc)[U][V]) {
+__device__ __forceinline__ KArgs kernel_args() {
+    return (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+}
+
+// ---- the fold -------------------------------------------------------------
+//
+// x[k] holds rank (s + k) mod P, s the chunk's start rank, so the ring's
+// order is the fixed fold ((x[0] + x[1]) + x[2]) + ... + x[P-1].  SHIFT
+// folds the same registers as if the start rank were s + SHIFT:
+// ((x[SHIFT] + x[SHIFT+1]) + ...), indices mod P.
+
+template <int P, int SHIFT, bool BF16, int U, int V>
+__device__ __forceinline__ void fold(const u32x4 (&x)[P][U], float (&acc)[U][V]) {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            float s = elem<BF16>(x[S][u], e);
+            float s = elem<BF16>(x[SHIFT % P][u], e);
 #pragma unroll
-            for (int k = 1; k < P; ++k) s = s + elem<BF16>(x[(S + k) % P][u], e);
+            for (int k = 1; k < P; ++k) s = s + elem<BF16>(x[(SHIFT + k) % P][u], e);
             acc[u][e] = s;
         }
     }
 }
 
-// s is uniform across the workgroup: a chain of scalar branches.
-template <int P, int S, bool BF16, int U, int V>
-__device__ __forceinline__ void fold_uniform(int s, const u32x4 (&x)[P][U], float (&acc)[U][V]) {
-    if constexpr (S + 1 < P) {
-        if (s == S) {
-            fold_from<P, S, BF16, U, V>(x, acc);
-        } else {
-            fold_uniform<P, S + 1, BF16, U, V>(s, x, acc);
-        }
-    } else {
-        fold_from<P, S, BF16, U, V>(x, acc);
-    }
-}
-
-template <int P, int S>
-__device__ __forceinline__ float fold_scalar_from(const float (&xs)[P]) {
-#pragma clang fp contract(off)
-    float s = xs[S];
-#pragma unroll
-    for (int k = 1; k < P; ++k) s = s + xs[(S + k) % P];
-    return s;
-}
-
-// s may differ between lanes.
-template <int P, int S>
-__device__ __forceinline__ float fold_scalar(int s, const float (&xs)[P]) {
-    if constexpr (S + 1 < P) {
-        if (s == S) return fold_scalar_from<P, S>(xs);
-        return fold_scalar<P, S + 1>(s, xs);
-    } else {
-        return fold_scalar_from<P, S>(xs);
-    }
+__device__ __forceinline__ int rank_at(int s, int k, int P) {
+    const int r = s + k;
+    return r >= P ? r - P : r;
 }
 
 // ---- one element per lane: tails and chunks shorter than a tile ----------
 
 template <int P, bool INB, bool OUTB, bool SGD>
-__device__ __forceinline__ void process_element(const RingArgs a, uint32_t i) {
+__device__ __forceinline__ void process_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    float xs[P];
+    const int s = static_cast<int>(((a->base + i) / a->L) % P);
+    float g;
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
+    for (int k = 0; k < P; ++k) {
+        const void* p = a->in[rank_at(s, k, P)];   // per-lane pointer choice
+        float xk;
         if constexpr (INB) {
-            const uint16_t h = static_cast<const uint16_t*>(a.in[r])[i];
-            xs[r] = __uint_as_float(static_cast<uint32_t>(h) << 16);
+            xk = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
         } else {
-            xs[r] = static_cast<const float*>(a.in[r])[i];
+            xk = static_cast<const float*>(p)[i];
         }
+        g = k == 0 ? xk : g + xk;
     }
-    const int s = static_cast<int>(((a.base + i) / a.L) % P);
-    float g = fold_scalar<P, 0>(s, xs);
-    if (a.mean) g = mean_of<P>(g);
+    if (a->mean) g = mean_of<P>(g);
     if constexpr (SGD) {
-        float w = a.w[i];
-        float v = a.v[i];
-        momentum_step(g, w, v, a.lr, a.mu);
-        a.w[i] = w;
-        a.v[i] = v;
-        if (!a.write_out) return;
+        float w = a->w[i];
+        float v = a->v[i];
+        momentum_step(g, w, v, a->lr, a->mu);
+        a->w[i] = w;
+        a->v[i] = v;
+        if (!a->write_out) return;
     }
 #pragma unroll
     for (int r = 0; r < P; ++r) {
         if constexpr (OUTB) {
-            static_cast<uint16_t*>(a.out[r])[i] = static_cast<uint16_t>(bf16_bits(g));
+            static_cast<uint16_t*>(a->out[r])[i] = static_cast<uint16_t>(bf16_bits(g));
         } else {
-            static_cast<float*>(a.out[r])[i] = g;
+            static_cast<float*>(a->out[r])[i] = g;
         }
     }
 }
 
 // ---- the vector path ------------------------------------------------------
 
-// One tile: U rows of 256 16-byte vectors per rank.  FULL: every vector of
-// the tile lies below blk_end (no per-vector predicate).
-template <int P, bool INB, bool OUTB, bool SGD, int U, bool FULL>
-__device__ __forceinline__ void process_tile(const RingArgs a, uint32_t t0, uint32_t blk_end) {
+template <int W>
+__device__ __forceinline__ u32x4 load_lane(const void* p) {
+    if constexpr (W == 4) {
+        return load16(p);
+    } else {
+        const u32x2 h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        return u32x4{h[0], h[1], 0u, 0u};
+    }
+}
+
+// One tile = U rows of 256 lane vectors of V elements per rank, processed
+// by one workgroup.  FULL: the whole tile lies below n_vec.
+template <int P, bool INB, bool OUTB, bool SGD, bool FULL>
+__device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
 #pragma clang fp contract(off)
-    constexpr int V = INB ? 8 : 4;        // elements per 16-byte input vector
-    constexpr uint32_t IES = INB ? 2 : 4; // input element bytes
-    constexpr uint32_t OES = OUTB ? 2 : 4;
+    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int V = ring_lane_elems(INB, OUTB, SGD);
+    constexpr uint32_t IES = INB ? 2 : 4;   // input element bytes
+    constexpr uint32_t OES = OUTB ? 2 : 4;  // output element bytes
+    constexpr int WIN = V * IES / 4;        // input words per lane vector (2 or 4)
     constexpr uint32_t TILE = static_cast<uint32_t>(kBlock) * U * V;
     const uint32_t tid = threadIdx.x;
+    const uint32_t n_vec = a->n_vec;
+
+    // Chunks are at least TILE long on this path, so the tile holds one
+    // start rank, or two with the boundary at element `split` of the launch.
+    const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
+    const int64_t j0 = (a->base + t0) / a->L;
+    const int64_t j1 = (a->base + last) / a->L;
+    const int s0 = static_cast<int>(j0 % P);
 
     u32x4 x[P][U];
     float ws[U][V];
@@ -226,39 +237,33 @@ __device__ __forceinline__ void process_tile(const RingArgs a, uint32_t t0, uint
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t i0 = t0 + (u * kBlock + tid) * V;
-        ok[u] = FULL || (i0 < blk_end);
+        ok[u] = FULL || (i0 < n_vec);
         if (ok[u]) {
 #pragma unroll
-            for (int r = 0; r < P; ++r) x[r][u] = load16(static_cast<const char*>(a.in[r]) + i0 * IES);
+            for (int k = 0; k < P; ++k)
+                x[k][u] = load_lane<WIN>(static_cast<const char*>(a->in[rank_at(s0, k, P)]) + i0 * IES);
             if constexpr (SGD) {
+                static_assert(V == 4, "the momentum state moves as one 16-byte vector per lane");
+                const u32x4 wq = load16(reinterpret_cast<const char*>(a->w) + i0 * 4u);
+                const u32x4 vq = load16(reinterpret_cast<const char*>(a->v) + i0 * 4u);
 #pragma unroll
-                for (int q = 0; q < V / 4; ++q) {
-                    const u32x4 wq = load16(reinterpret_cast<const char*>(a.w) + (i0 + 4 * q) * 4u);
-                    const u32x4 vq = load16(reinterpret_cast<const char*>(a.v) + (i0 + 4 * q) * 4u);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ws[u][4 * q + e] = __uint_as_float(wq[e]);
-                        vs[u][4 * q + e] = __uint_as_float(vq[e]);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    ws[u][e] = __uint_as_float(wq[e]);
+                    vs[u][e] = __uint_as_float(vq[e]);
                 }
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < P; ++r) x[r][u] = u32x4{0u, 0u, 0u, 0u};
+            for (int k = 0; k < P; ++k) x[k][u] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 
-    // Chunks are at least TILE long here, so the tile holds one start rank,
-    // or two with the boundary at element `split` of the launch.
     float acc[U][V];
-    const uint32_t last = FULL ? t0 + TILE - 1 : ((t0 + TILE < blk_end ? t0 + TILE : blk_end) - 1);
-    const int64_t j0 = (a.base + t0) / a.L;
-    const int64_t j1 = (a.base + last) / a.L;
-    fold_uniform<P, 0, INB, U, V>(static_cast<int>(j0 % P), x, acc);
+    fold<P, 0, INB, U, V>(x, acc);
     if (j1 != j0) {
         float acc2[U][V];
-        fold_uniform<P, 0, INB, U, V>(static_cast<int>(j1 % P), x, acc2);
-        const uint32_t split = static_cast<uint32_t>(j1 * a.L - a.base);
+        fold<P, 1, INB, U, V>(x, acc2);
+        const uint32_t split = static_cast<uint32_t>(j1 * a->L - a->base);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -268,84 +273,82 @@ __device__ __forceinline__ void process_tile(const RingArgs a, uint32_t t0, uint
         }
     }
 
+    const bool mean = a->mean != 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
         const uint32_t i0 = t0 + (u * kBlock + tid) * V;
         float g[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) g[e] = a.mean ? mean_of<P>(acc[u][e]) : acc[u][e];
+        for (int e = 0; e < V; ++e) g[e] = mean ? mean_of<P>(acc[u][e]) : acc[u][e];
         if constexpr (SGD) {
+            u32x4 wq, vq;
 #pragma unroll
-            for (int e = 0; e < V; ++e) momentum_step(g[e], ws[u][e], vs[u][e], a.lr, a.mu);
-#pragma unroll
-            for (int q = 0; q < V / 4; ++q) {
-                u32x4 wq, vq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    wq[e] = __float_as_uint(ws[u][4 * q + e]);
-                    vq[e] = __float_as_uint(vs[u][4 * q + e]);
-                }
-                store16(reinterpret_cast<char*>(a.w) + (i0 + 4 * q) * 4u, wq);
-                store16(reinterpret_cast<char*>(a.v) + (i0 + 4 * q) * 4u, vq);
+            for (int e = 0; e < 4; ++e) {
+                momentum_step(g[e], ws[u][e], vs[u][e], a->lr, a->mu);
+                wq[e] = __float_as_uint(ws[u][e]);
+                vq[e] = __float_as_uint(vs[u][e]);
             }
-            if (!a.write_out) continue;
+            store16(reinterpret_cast<char*>(a->w) + i0 * 4u, wq);
+            store16(reinterpret_cast<char*>(a->v) + i0 * 4u, vq);
+            if (!a->write_out) continue;
         }
-        if constexpr (OUTB) {
-            if constexpr (V == 8) {
-                u32x4 o;
+        if constexpr (OUTB && V == 8) {
+            u32x4 o;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
+            for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-                for (int r = 0; r < P; ++r) store16(static_cast<char*>(a.out[r]) + i0 * OES, o);
-            } else {
-                u32x2 o;
+            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+        } else if constexpr (OUTB) {
+            u32x2 o;
 #pragma unroll
-                for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
+            for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-                for (int r = 0; r < P; ++r) store8(static_cast<char*>(a.out[r]) + i0 * OES, o);
-            }
+            for (int r = 0; r < P; ++r) store8(static_cast<char*>(a->out[r]) + i0 * OES, o);
         } else {
+            u32x4 o;
 #pragma unroll
-            for (int q = 0; q < V / 4; ++q) {
-                u32x4 o;
+            for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[4 * q + e]);
-#pragma unroll
-                for (int r = 0; r < P; ++r) store16(static_cast<char*>(a.out[r]) + (i0 + 4 * q) * OES, o);
-            }
+            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
         }
     }
 }
 
+// One tile per workgroup and as many workgroups as tiles: the hardware
+// dispatcher hands tiles to whichever CU is free, which balances the load
+// across CUs and XCDs better than fixed per-workgroup shares.
 template <int P, bool INB, bool OUTB, bool SGD>
-__global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs a) {
-    constexpr int U = ring_vectors_per_lane(P);
-    constexpr int V = INB ? 8 : 4;
-    constexpr uint32_t TILE = static_cast<uint32_t>(kBlock) * U * V;
-    const uint32_t begin = blockIdx.x * a.per_block;
-    const uint32_t end = begin + a.per_block < a.n_vec ? begin + a.per_block : a.n_vec;
-    uint32_t t0 = begin;
-    for (; t0 + TILE <= end; t0 += TILE) process_tile<P, INB, OUTB, SGD, U, true>(a, t0, end);
-    if (t0 < end) process_tile<P, INB, OUTB, SGD, U, false>(a, t0, end);
+__global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
+    constexpr uint32_t TILE =
+        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(INB, OUTB, SGD);
+    const KArgs a = kernel_args();
+    const uint32_t t0 = blockIdx.x * TILE;
+    const uint32_t n_vec = a->n_vec;
+    if (t0 + TILE <= n_vec) {
+        process_tile<P, INB, OUTB, SGD, true>(a, t0);
+    } else if (t0 < n_vec) {
+        process_tile<P, INB, OUTB, SGD, false>(a, t0);
+    }
     if (blockIdx.x == gridDim.x - 1) {
-        const uint32_t i = a.n_vec + threadIdx.x;
-        if (i < a.n) process_element<P, INB, OUTB, SGD>(a, i);
+        const uint32_t i = n_vec + threadIdx.x;
+        if (i < a->n) process_element<P, INB, OUTB, SGD>(a, i);
     }
 }
 
 // Chunks shorter than a tile (C large against n): one element per lane.
 template <int P, bool INB, bool OUTB, bool SGD>
-__global__ __launch_bounds__(kBlock) void ring_reduce_scalar_kernel(RingArgs a) {
-    for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < a.n; i += gridDim.x * kBlock)
-        process_element<P, INB, OUTB, SGD>(a, i);
+__global__ __launch_bounds__(kBlock) void ring_reduce_scalar_kernel(RingArgs) {
+    const KArgs a = kernel_args();
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < a->n) process_element<P, INB, OUTB, SGD>(a, i);
 }
 
 template <bool INB, bool OUTB, bool SGD, bool SCALAR>
 const void* ring_kernel_for(int P) {
     switch (P) {
-#define DDP_CASE(p)                                                                              \
-    case p:                                                                                      \
+#define DDP_CASE(p)                                                                                  \
+    case p:                                                                                          \
         return SCALAR ? reinterpret_cast<const void*>(&ring_reduce_scalar_kernel<p, INB, OUTB, SGD>) \
                       : reinterpret_cast<const void*>(&ring_reduce_kernel<p, INB, OUTB, SGD>);
         DDP_CASE(1) DDP_CASE(2) DDP_CASE(3) DDP_CASE(4)
@@ -361,7 +364,6 @@ const void* ring_kernel_for(int P) {
 }  // namespace rr
 }  // namespace ddp
 
-// Defines ddp::ring_kernel_<name>(P, sgd, scalar) for one type pair.
 #define DDP_RING_TYPE_PAIR(name, INB, OUTB)                                              \
     namespace ddp {                                                                      \
     const void* ring_kernel_##name(int P, int sgd, int scalar) {                         \
