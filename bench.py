@@ -1,0 +1,244 @@
+"""Benchmark: the data-parallel gradient all-reduce on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (the configuration the headline metric is quoted on): P = 8
+emulated ranks, each holding a ResNet-50-shaped gradient set of 161 fp32
+tensors (25,557,032 parameters) drawn from N(0, 0.01), laid out as views of
+25 MiB buckets filled in reverse parameter order (3 full buckets and a
+partial tail).  One step all-reduces every bucket with Mean in the chunked
+ring order (8 chunks), every rank receiving its own copy of the result.
+
+Metric: effective HBM GB/s = algorithmic bytes / time, where the algorithmic
+bytes of one all-reduce of n elements over P ranks are P*n*(s_in + s_out)
+(every rank's input read once, every rank's output written once).  Inputs
+are resident in HBM before the timed region; the step streams 1.6 GB, far
+more than the 256 MB last-level cache, and two buffer sets alternate.
+
+Prints one JSON line with the step throughput, the dominant kernel's
+roofline (its own launches timed with HIP events on the stream they run on)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "all-reduce effective HBM GB/s per bucket (P ranks) and % of MI355X HBM peak"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ring_reduce_p8_f32_resnet50_traffic.md")
+KERNEL_SOURCES = ["ring_reduce_impl.h", "ring_reduce.hip", "ring_reduce_f32_f32.hip", "launch.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gradient_all_reduce_allreduce_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    otherwise None."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip().lstrip("- ").strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(grads_host, bucket_lens, P, C, min_seconds=10.0, max_passes=20):
+    """The oracle (NumPy, single thread) on whole buckets of the same
+    gradient set, bucket after bucket and pass after pass, until at least
+    min_seconds have passed (bounded by max_passes over the set)."""
+    import oracle
+    done_bytes = 0
+    t0 = time.perf_counter()
+    buckets = 0
+    for _ in range(max_passes):
+        for X in grads_host:
+            oracle.ring_allreduce(X, "mean", C)
+            buckets += 1
+            done_bytes += X.shape[0] * X.shape[1] * 8
+            if time.perf_counter() - t0 > min_seconds:
+                break
+        if time.perf_counter() - t0 > min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{buckets} bucket all-reduces over the {len(bucket_lens)} buckets of the "
+                  f"same gradient set (P={P}, fp32, Mean, C={C}), stepwise ring simulation in NumPy, "
+                  f"{dt:.1f} s; host has {os.cpu_count()} cores",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (a kernel of known "
+                         "traffic, to scale the memory counters of a profiler run)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the P ranks are emulated as P buffers in one "
+              f"GPU's HBM; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gradient_all_reduce_allreduce_amd as ddp
+    import workloads
+
+    if args.calibrate_copy:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": a.numel() * 4,
+                          "bytes_written": b.numel() * 4, "launches": 10}))
+        return 0
+
+    cfg = workloads.CONFIGS["cfg2"]
+    P, C = cfg["P"], cfg["chunking"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = workloads.model_shapes("resnet50")
+    plan = ddp.GradBucketer(shapes, torch.float32, cfg["bucket_bytes"], device=dev)
+    E = plan.bucket_elems
+    lens = [plan.bucket_len(k) for k in range(plan.n_buckets)]
+
+    # Two buffer sets of inputs and outputs, each an arena of P rows padded
+    # to whole buckets (grads as bucket views: bucket k of rank r is
+    # row r, elements [k*E, k*E + len_k)).
+    sets = []
+    for s in range(2):
+        g = plan.alloc_arena(P)
+        for r in range(P):
+            workloads.torch_normal_(g[r], cfg["dist"][1], seed=1000 * s + r)
+        sets.append((g, plan.alloc_arena(P)))
+    views = []
+    for g, o in sets:
+        views.append([([plan.bucket_view(g[r], k) for r in range(P)],
+                       [plan.bucket_view(o[r], k) for r in range(P)], n)
+                      for k, n in enumerate(lens)])
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        for k, (ins, outs, n) in enumerate(views[i % 2]):
+            if events is not None:
+                events[k][0].record(stream)
+            ddp.allreduce(ins, "mean", C, out=outs)
+            if events is not None:
+                events[k][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region 1: the step throughput, K steps bracketed by events.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    bytes_step = sum(P * n * (4 + 4) for n in lens)
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+
+    # Timed region 2: the same K steps with an event pair around every
+    # launch of the dominant (only) kernel, on the stream it runs on.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in lens] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    durs = [[ev[i][k][0].elapsed_time(ev[i][k][1]) for k in range(len(lens))]
+            for i in range(args.steps)]
+    launches = args.steps * len(lens)
+    avg_ms = sum(map(sum, durs)) / launches
+    avg_bytes = bytes_step / len(lens)
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    full = [d for row in durs for k, d in enumerate(row) if lens[k] == E]
+    full_gbs = P * E * 8 / (sum(full) / len(full) * 1e-3) / 1e9 if full else None
+    traffic = measured_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "resnet50-gradient-set all-reduce: P=8 ranks x 161 fp32 tensors "
+                        "(25,557,032 params) N(0,0.01), 25 MiB buckets (3 full + tail of "
+                        "5,896,232), grads as bucket views of a per-rank arena padded to "
+                        "whole buckets, Mean, 8 ring chunks",
+            "P": P, "chunking": C, "op": "mean", "bucket_bytes": cfg["bucket_bytes"],
+            "buckets": len(lens), "elements_per_rank": plan.total,
+            "bytes_per_step": bytes_step,
+        },
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ring_reduce_kernel<P=8, f32 -> f32>",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(avg_bytes),
+            "full_bucket_gbs": round(full_gbs, 1) if full_gbs else None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        g = sets[0][0]
+        host = [np.ascontiguousarray(g[:, k * E:k * E + n].cpu().numpy()) for k, n in enumerate(lens)]
+        del sets, views
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(host, lens, P, C)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -65,6 +65,35 @@ class GradBucketer:
         ptrs = [x.data_ptr() for ts in rank_tensors for x in ts]
         return torch.tensor(ptrs, dtype=torch.int64).to(self.device)
 
+    def alloc_arena(self, P):
+        """One [P, n_buckets * E] tensor holding every rank's gradients in
+        bucket order (DDP's "gradients as bucket views" layout: no pack or
+        unpack copies).  Each rank's row is padded to whole buckets, so rank
+        r's copy of bucket k starts at r * n_buckets * bucket_bytes +
+        k * bucket_bytes: the P copies the all-reduce reads at the same
+        offset sit a whole multiple of the bucket size apart."""
+        import torch
+        return torch.empty(P, max(1, self.n_buckets) * self.bucket_elems, dtype=self.dtype,
+                           device=self.device)
+
+    def bucket_view(self, arena_row, b):
+        """Bucket b of one rank's arena row (its live elements only)."""
+        lo = b * self.bucket_elems
+        return arena_row[lo:lo + self.bucket_len(b)]
+
+    def tensor_views(self, arena_row):
+        """The rank's per-parameter gradient tensors as views of its arena
+        row (parameter order, planned shapes)."""
+        views = [None] * len(self.shapes)
+        offs = {}
+        flat = 0
+        for t in reversed(range(len(self.shapes))):
+            offs[t] = flat
+            flat += self.numels[t]
+        for t, s in enumerate(self.shapes):
+            views[t] = arena_row[offs[t]:offs[t] + self.numels[t]].view(s)
+        return views
+
     def alloc_buckets(self, P):
         """P bucket buffers of full bucket capacity."""
         import torch

@@ -19,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libddp_allreduce.so")
+PATTERNS = os.path.join(PKG, "hbm_patterns")     # HBM access-pattern benchmark
 SOURCES = ["api.cpp", "ring_reduce.hip", "ring_reduce_f32_f32.hip",
            "ring_reduce_f32_bf16.hip", "ring_reduce_bf16_f32.hip",
            "ring_reduce_bf16_bf16.hip", "bucket_copy.hip"]
@@ -43,11 +44,22 @@ def _compile(src):
     return obj
 
 
+def _compile_patterns():
+    cmd = [HIPCC, *COMMON, *DEVICE, os.path.join(CSRC, "hbm_patterns.hip"), "-o",
+           PATTERNS + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(PATTERNS + ".tmp", PATTERNS)
+
+
 def build(verbose=False):
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        patterns = ex.submit(_compile_patterns)
         objs = list(ex.map(_compile, SOURCES))
+        patterns.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

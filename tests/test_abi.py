@@ -210,3 +210,22 @@ def test_last_error_is_per_thread():
     t.start()
     t.join()
     assert seen == [""] and "P = 0" in N.last_error()
+
+
+def test_bucket_views_match_pack_layout():
+    """Gradients as views of a rank's arena row sit exactly where packing
+    separate tensors would put them (host-only: CPU tensors)."""
+    import torch
+    shapes = [(3, 5), (7,), (0,), (4, 4, 2), (1,), (33,), (1000,)]
+    b = ddp.GradBucketer(shapes, torch.float32, 256, device="cpu")
+    arena = b.alloc_arena(2)
+    assert arena.shape == (2, b.n_buckets * b.bucket_elems)
+    rng = np.random.default_rng(0)
+    for r in range(2):
+        views = b.tensor_views(arena[r])
+        host = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+        for v, h in zip(views, host):
+            v.copy_(torch.from_numpy(h))
+        want = oracle.pack(host, 4, 256)
+        for k in range(b.n_buckets):
+            assert np.array_equal(b.bucket_view(arena[r], k).numpy(), want[k])

@@ -1,0 +1,132 @@
+"""GPU parity of bucket pack / unpack against the oracle's pack (the
+definition: concatenate the reversed, flattened tensors and cut every E
+elements), bit for bit, including tensors whose addresses are not 16-byte
+aligned, zero-size tensors, straddling tensors and the partial tail bucket;
+and pack -> all-reduce -> unpack against the oracle's composition."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import DEV, assert_same_bits, oracle_ring
+
+pytestmark = pytest.mark.gpu
+ddp = pytest.importorskip("gradient_all_reduce_allreduce_amd")
+
+
+def make_rank_tensors(P, shapes, dtype, seed, misalign=0):
+    """Per rank, separately allocated tensors; with misalign > 0 every
+    tensor is a view starting `misalign` elements into its own storage."""
+    rng = np.random.default_rng(seed)
+    host, dev = [], []
+    for r in range(P):
+        hs, ds = [], []
+        for s in shapes:
+            x = rng.standard_normal(s).astype(np.float32)
+            if dtype == torch.bfloat16:
+                x = workloads.to_bf16_bits(x.reshape(-1)).reshape(s)
+            hs.append(x)
+            n = int(np.prod(s, dtype=np.int64))
+            store = torch.empty(n + misalign, dtype=dtype, device=DEV)
+            t = store[misalign:misalign + n].view(s)
+            src = torch.from_numpy(x.view(np.int16) if dtype == torch.bfloat16 else x)
+            t.copy_(src.to(DEV).view(dtype) if dtype == torch.bfloat16 else src.to(DEV))
+            ds.append(t)
+        host.append(hs)
+        dev.append(ds)
+    return host, dev
+
+
+def bits(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+SHAPES = [(3, 5), (7,), (0,), (4, 4, 2), (1,), (33,), (1000,), (17, 3), (4096,), (2,), (513,)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("misalign", [0, 1, 3])
+@pytest.mark.parametrize("bucket_bytes", [64, 1024, 16 << 10])
+def test_pack_unpack_equal_oracle(dtype, misalign, bucket_bytes):
+    P = 3
+    host, dev = make_rank_tensors(P, SHAPES, dtype, seed=misalign + bucket_bytes, misalign=misalign)
+    b = ddp.GradBucketer(SHAPES, dtype, bucket_bytes, device=DEV)
+    es = 2 if dtype == torch.bfloat16 else 4
+    table = b.pointer_table(dev)
+    bufs = b.alloc_buckets(P)
+    want = [oracle.pack(host[r], es, bucket_bytes) for r in range(P)]
+    assert len(want[0]) == b.n_buckets
+    for k in range(b.n_buckets):
+        b.pack(table, k, bufs)
+        torch.cuda.synchronize()
+        for r in range(P):
+            got = bits(bufs[r][:b.bucket_len(k)])
+            assert np.array_equal(got, want[r][k]), (k, r)
+    # unpack the oracle's buckets into zeroed tensors
+    for ts in dev:
+        for t in ts:
+            t.zero_()
+    for k in range(b.n_buckets):
+        for r in range(P):
+            src = torch.from_numpy(want[r][k].view(np.int16) if dtype == torch.bfloat16 else want[r][k])
+            bufs[r][:b.bucket_len(k)].copy_(src.to(DEV).view(dtype) if dtype == torch.bfloat16
+                                            else src.to(DEV))
+        b.unpack(table, k, bufs)
+    torch.cuda.synchronize()
+    for r in range(P):
+        for t, (x, h) in enumerate(zip(dev[r], host[r])):
+            assert np.array_equal(bits(x), h), (r, t)
+
+
+def test_pack_many_small_segments_per_tile():
+    """More than 256 segments overlap one tile: the LDS staging rounds."""
+    P = 2
+    shapes = [(1,)] * 300 + [(2,)] * 300 + [(5,)] * 100
+    host, dev = make_rank_tensors(P, shapes, torch.float32, seed=4)
+    b = ddp.GradBucketer(shapes, torch.float32, 1 << 20, device=DEV)
+    table = b.pointer_table(dev)
+    bufs = b.alloc_buckets(P)
+    b.pack(table, 0, bufs)
+    torch.cuda.synchronize()
+    want = [oracle.pack(host[r], 4, 1 << 20) for r in range(P)]
+    for r in range(P):
+        assert np.array_equal(bits(bufs[r][:b.bucket_len(0)]), want[r][0])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pack_allreduce_unpack_equals_oracle(dtype):
+    P = 4
+    shapes = [(s,) for s in workloads.ragged_sizes(count=40, lo=10, hi=20000, seed=3)]
+    host, dev = make_rank_tensors(P, shapes, dtype, seed=9)
+    es = 2 if dtype == torch.bfloat16 else 4
+    name = "bf16" if es == 2 else "f32"
+    bb = 64 << 10
+    b = ddp.GradBucketer(shapes, dtype, bb, device=DEV)
+    table = b.pointer_table(dev)
+    bufs = b.alloc_buckets(P)
+    for k in range(b.n_buckets):
+        b.pack(table, k, bufs)
+        n = b.bucket_len(k)
+        ddp.allreduce([x[:n] for x in bufs], "sum", P, out=[x[:n] for x in bufs])
+        b.unpack(table, k, bufs)
+    torch.cuda.synchronize()
+    packed = [oracle.pack(host[r], es, bb) for r in range(P)]
+    reduced = []
+    for k in range(len(packed[0])):
+        X = np.stack([packed[r][k] for r in range(P)])
+        reduced.append(oracle_ring(X, "sum", P, in_dtype=name))
+    for r in range(P):
+        want = oracle.unpack([reduced[k][r] for k in range(len(reduced))], shapes)
+        for t, x in enumerate(dev[r]):
+            assert_same_bits(bits(x).reshape(-1), want[t].reshape(-1), f"rank {r} tensor {t}")
+
+
+def test_plan_mismatch_is_rejected():
+    b = ddp.GradBucketer([(4,), (8,)], torch.float32, 64, device=DEV)
+    bad = [[torch.zeros(4, device=DEV), torch.zeros(9, device=DEV)]]
+    with pytest.raises(ValueError):
+        b.pointer_table(bad)

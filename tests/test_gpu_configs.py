@@ -1,0 +1,219 @@
+"""The five workloads at their full sizes, in the launch configuration the
+benchmark times.  Whole-buffer properties are checked on the GPU (every
+rank's output identical); values are checked against the oracle on sampled
+elements -- the first and last of every bucket, both sides of every chunk
+boundary, and a seeded random sample -- which the oracle simulates one ring
+per element."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import DEV, assert_same_bits
+
+pytestmark = pytest.mark.gpu
+ddp = pytest.importorskip("gradient_all_reduce_allreduce_amd")
+
+
+def sample_indices(n, C, rng, k=4000):
+    L = -(-n // C)
+    parts = [np.arange(min(n, 64)), np.arange(max(0, n - 64), n), rng.integers(0, n, k)]
+    for j in range(1, C):
+        b = j * L
+        parts.append(np.arange(max(0, b - 16), min(n, b + 16)))
+    return np.unique(np.concatenate(parts)).astype(np.int64)
+
+
+def host_values(rows, idx):
+    """rows: list of P device tensors (1-D); values at idx as (P, m) numpy."""
+    it = torch.from_numpy(idx).to(DEV)
+    out = []
+    for t in rows:
+        v = t[it]
+        out.append(v.view(torch.int16).cpu().numpy().view(np.uint16) if v.dtype == torch.bfloat16
+                   else v.cpu().numpy())
+    return np.stack(out)
+
+
+def all_ranks_equal(rows):
+    ref = rows[0].view(torch.int16) if rows[0].dtype == torch.bfloat16 else rows[0].view(torch.int32)
+    for t in rows[1:]:
+        x = t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+        if not torch.equal(ref, x):
+            return False
+    return True
+
+
+def fill_arena(P, total, dtype, std, seed_base):
+    arena = torch.empty(P, total, dtype=dtype, device=DEV)
+    step = 1 << 26
+    for r in range(P):
+        for lo in range(0, total, step):
+            hi = min(total, lo + step)
+            workloads.torch_normal_(arena[r, lo:hi], std, seed=seed_base + 1000 * r + lo // step)
+    return arena
+
+
+def test_config2_resnet50_buckets():
+    """P=8, ResNet-50 gradient set (161 tensors, 25,557,032 fp32), 25 MiB
+    buckets, Mean, gradients laid out as bucket views of one [P, total]
+    arena."""
+    cfg = workloads.CONFIGS["cfg2"]
+    P, C = cfg["P"], cfg["chunking"]
+    shapes = workloads.model_shapes("resnet50")
+    b = ddp.GradBucketer(shapes, torch.float32, cfg["bucket_bytes"], device=DEV)
+    assert (b.n_buckets, b.total) == (4, 25_557_032)
+    grads = fill_arena(P, b.total, torch.float32, 0.01, seed_base=20)
+    out = torch.empty_like(grads)
+    rng = np.random.default_rng(2)
+    checks = []
+    for k in range(b.n_buckets):
+        lo, n = k * b.bucket_elems, b.bucket_len(k)
+        idx = sample_indices(n, C, rng)
+        checks.append((lo, n, idx, host_values([grads[r, lo:lo + n] for r in range(P)], idx)))
+        ddp.allreduce([grads[r, lo:lo + n] for r in range(P)], "mean", C,
+                      out=[out[r, lo:lo + n] for r in range(P)])
+    torch.cuda.synchronize()
+    assert all_ranks_equal([out[r] for r in range(P)])
+    for lo, n, idx, V in checks:
+        want = oracle.ring_allreduce_sampled(V, oracle.chunk_start_ranks_at(n, C, P, idx), "mean")
+        got = host_values([out[r, lo:lo + n] for r in range(P)], idx)
+        assert_same_bits(got, want, f"bucket at {lo}")
+    # second run: identical bits
+    out2 = torch.empty_like(grads)
+    for k in range(b.n_buckets):
+        lo, n = k * b.bucket_elems, b.bucket_len(k)
+        ddp.allreduce([grads[r, lo:lo + n] for r in range(P)], "mean", C,
+                      out=[out2[r, lo:lo + n] for r in range(P)])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+
+
+def test_config3_vit_bf16_fused_sgd():
+    """P=8, ViT-B/16 gradient set (152 tensors, 86,567,656 bf16), Mean with
+    fp32 accumulation, fused SGD-momentum (0.9, lr 1e-3) on fp32 master
+    weights, 25 MiB buckets."""
+    cfg = workloads.CONFIGS["cfg3"]
+    P, C, sg = cfg["P"], cfg["chunking"], cfg["sgd"]
+    b = ddp.GradBucketer(workloads.model_shapes("vit_b16"), torch.bfloat16, cfg["bucket_bytes"],
+                         device=DEV)
+    assert (b.n_buckets, b.total) == (7, 86_567_656)
+    grads = fill_arena(P, b.total, torch.bfloat16, 1e-3, seed_base=30)
+    w = torch.empty(b.total, dtype=torch.float32, device=DEV)
+    v = torch.empty(b.total, dtype=torch.float32, device=DEV)
+    workloads.torch_normal_(w, sg["w_std"], seed=31)
+    workloads.torch_normal_(v, sg["v_std"], seed=32)
+    gout = torch.empty_like(grads)
+    rng = np.random.default_rng(3)
+    checks = []
+    for k in range(b.n_buckets):
+        lo, n = k * b.bucket_elems, b.bucket_len(k)
+        idx = sample_indices(n, C, rng)
+        it = torch.from_numpy(idx + lo).to(DEV)
+        checks.append((lo, n, idx, host_values([grads[r, lo:lo + n] for r in range(P)], idx),
+                       w[it].cpu().numpy(), v[it].cpu().numpy()))
+        ddp.allreduce_sgd([grads[r, lo:lo + n] for r in range(P)], w[lo:lo + n], v[lo:lo + n],
+                          sg["lr"], sg["mu"], "mean", C,
+                          out=[gout[r, lo:lo + n] for r in range(P)])
+    torch.cuda.synchronize()
+    assert all_ranks_equal([gout[r] for r in range(P)])
+    for lo, n, idx, V, w0, v0 in checks:
+        start = oracle.chunk_start_ranks_at(n, C, P, idx)
+        g32 = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="f32")[0]
+        ow, ov = oracle.sgd_momentum(g32, w0, v0, sg["lr"], sg["mu"])
+        it = torch.from_numpy(idx + lo).to(DEV)
+        assert_same_bits(w[it].cpu().numpy(), ow, f"w bucket at {lo}")
+        assert_same_bits(v[it].cpu().numpy(), ov, f"v bucket at {lo}")
+        gb = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="bf16")
+        assert_same_bits(host_values([gout[r, lo:lo + n] for r in range(P)], idx), gb,
+                         f"grads bucket at {lo}")
+
+
+def test_config4_ragged_pack_allreduce_unpack():
+    """P=4, 2,000 separately allocated fp32 tensors per rank with log-uniform
+    sizes in [1e3, 4e6], U[-1, 1], Sum, 25 MiB buckets with a partial tail:
+    pack -> all-reduce -> unpack for every bucket, in place."""
+    cfg = workloads.CONFIGS["cfg4"]
+    P, C = cfg["P"], cfg["chunking"]
+    sizes = workloads.ragged_sizes()
+    shapes = [(s,) for s in sizes]
+    b = ddp.GradBucketer(shapes, torch.float32, cfg["bucket_bytes"], device=DEV)
+    assert b.total == sum(sizes) and b.bucket_len(b.n_buckets - 1) < b.bucket_elems
+    tensors = []
+    for r in range(P):
+        ts = []
+        for t, s in enumerate(sizes):
+            x = torch.empty(s, dtype=torch.float32, device=DEV)
+            workloads.torch_uniform_(x, -1.0, 1.0, seed=40_000 * (r + 1) + t)
+            ts.append(x)
+        tensors.append(ts)
+    # samples: (tensor, offset) pairs, mapped to bucket positions by the
+    # oracle's own plan
+    segs, lengths = oracle.bucket_plan(sizes, 4, cfg["bucket_bytes"])
+    rng = np.random.default_rng(4)
+    picks = []
+    for t in sorted(set(rng.integers(0, len(sizes), 300).tolist()) | {0, len(sizes) - 1}):
+        for off in {0, sizes[t] - 1, int(rng.integers(0, sizes[t]))}:
+            picks.append((t, off))
+    seg_of = {}
+    for (t, bk, src, dst, ln) in segs:
+        seg_of.setdefault(t, []).append((src, ln, bk, dst))
+    pos = []
+    for t, off in picks:
+        for src, ln, bk, dst in seg_of[t]:
+            if src <= off < src + ln:
+                pos.append((bk, dst + off - src))
+    V = np.array([[tensors[r][t][off].item() for (t, off) in picks] for r in range(P)],
+                 np.float32)
+    table = b.pointer_table(tensors)
+    bufs = b.alloc_buckets(P)
+    for k in range(b.n_buckets):
+        n = b.bucket_len(k)
+        b.pack(table, k, bufs)
+        ddp.allreduce([x[:n] for x in bufs], "sum", C, out=[x[:n] for x in bufs])
+        b.unpack(table, k, bufs)
+    torch.cuda.synchronize()
+    start = np.array([oracle.chunk_start_ranks_at(lengths[bk], C, P, [d])[0] for bk, d in pos])
+    want = oracle.ring_allreduce_sampled(V, start, "sum")
+    got = np.array([[tensors[r][t][off].item() for (t, off) in picks] for r in range(P)],
+                   np.float32)
+    assert_same_bits(got, want, "ragged samples")
+    for t in (0, len(sizes) // 2, len(sizes) - 1):
+        for r in range(1, P):
+            assert torch.equal(tensors[r][t].view(torch.int32), tensors[0][t].view(torch.int32))
+
+
+def test_config5_transformer_bf16_to_f32_100MiB():
+    """P=8, 2,017,529,856-parameter dense transformer gradient set in bf16
+    (32.3 GB of rank inputs), N(0, 1e-4), Mean, fp32 outputs (64.6 GB),
+    100 MiB buckets."""
+    cfg = workloads.CONFIGS["cfg5"]
+    P, C = cfg["P"], cfg["chunking"]
+    b = ddp.GradBucketer(workloads.model_shapes("transformer_2b"), torch.bfloat16,
+                         cfg["bucket_bytes"], device=DEV)
+    assert (b.n_buckets, b.total) == (39, 2_017_529_856)
+    grads = fill_arena(P, b.total, torch.bfloat16, 1e-4, seed_base=50)
+    out = torch.empty(P, b.total, dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(5)
+    sampled = {0, b.n_buckets // 2, b.n_buckets - 1}
+    checks = []
+    for k in range(b.n_buckets):
+        lo, n = k * b.bucket_elems, b.bucket_len(k)
+        if k in sampled:
+            idx = sample_indices(n, C, rng)
+            checks.append((lo, n, idx, host_values([grads[r, lo:lo + n] for r in range(P)], idx)))
+        ddp.allreduce([grads[r, lo:lo + n] for r in range(P)], "mean", C,
+                      out=[out[r, lo:lo + n] for r in range(P)])
+    torch.cuda.synchronize()
+    for k in sampled:
+        lo, n = k * b.bucket_elems, b.bucket_len(k)
+        assert all_ranks_equal([out[r, lo:lo + n] for r in range(P)])
+    for lo, n, idx, V in checks:
+        want = oracle.ring_allreduce_sampled(V, oracle.chunk_start_ranks_at(n, C, P, idx), "mean",
+                                             in_dtype="bf16", out_dtype="f32")
+        got = host_values([out[r, lo:lo + n] for r in range(P)], idx)
+        assert_same_bits(got, want, f"bucket at {lo}")
+    del grads, out
+    torch.cuda.empty_cache()
