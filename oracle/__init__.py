@@ -25,7 +25,8 @@ pages it follows:
   Operations" and "Data Parallelism (DDP)".
 
 Modules:
-    ring    -- the chunked ring all-reduce simulated step by step
+    ring    -- the chunked ring all-reduce simulated step by step, and its
+               two halves (reduce-scatter, all-gather) on their own
     bf16    -- bfloat16 <-> float32 conversions by definition
     sgd     -- SGD with momentum on fp32 master weights
     bucket  -- reverse-order gradient bucketing, pack and unpack
@@ -33,15 +34,16 @@ Modules:
 Parity status of each function is stated in its module header.
 """
 
-from .ring import (SUM, MEAN, chunk_length, chunk_start_ranks, chunk_start_ranks_at,
-                   ring_allreduce, ring_allreduce_sampled)
+from .ring import (SUM, MEAN, chunk_length, chunk_owners, chunk_start_ranks,
+                   chunk_start_ranks_at, ring_all_gather, ring_allreduce,
+                   ring_allreduce_sampled, ring_reduce_scatter)
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .sgd import sgd_momentum
 from .bucket import bucket_plan, pack, unpack
 
 __all__ = [
-    "SUM", "MEAN", "chunk_length", "chunk_start_ranks", "chunk_start_ranks_at",
-    "ring_allreduce",
+    "SUM", "MEAN", "chunk_length", "chunk_owners", "chunk_start_ranks",
+    "chunk_start_ranks_at", "ring_all_gather", "ring_allreduce", "ring_reduce_scatter",
     "ring_allreduce_sampled", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "sgd_momentum", "bucket_plan", "pack", "unpack",
 ]

@@ -92,6 +92,52 @@ def _narrow(A, out_dtype):
     raise ValueError(f"unknown output dtype {out_dtype!r}")
 
 
+def _chunks(n, P, C):
+    L = chunk_length(n, C)
+    chunks = [(min(j * L, n), min((j + 1) * L, n)) for j in range(C)]
+    start = [j % P for j in range(C)]
+    owner = [(s + P - 1) % P for s in start]
+    return chunks, start, owner
+
+
+def _reduce_scatter_steps(A, chunks, start, sent):
+    """The P-1 reduce-scatter steps, in place on A (P, n).  Every send of a
+    step reads the buffers as they stood at the start of the step (S), so
+    the sends are simultaneous."""
+    P = A.shape[0]
+    for t in range(P - 1):
+        S = A.copy()
+        for r in range(P):
+            dst = (r + 1) % P
+            for j, (lo, hi) in enumerate(chunks):
+                if start[j] == (r - t) % P:
+                    A[dst, lo:hi] = S[r, lo:hi] + A[dst, lo:hi]
+                    sent[r] += hi - lo
+
+
+def _all_gather_steps(A, chunks, owner, sent):
+    """The P-1 all-gather steps: the owner's finished chunk is forwarded
+    around the ring."""
+    P = A.shape[0]
+    for t in range(P - 1):
+        S = A.copy()
+        for r in range(P):
+            dst = (r + 1) % P
+            for j, (lo, hi) in enumerate(chunks):
+                if owner[j] == (r - t) % P:
+                    A[dst, lo:hi] = S[r, lo:hi]
+                    sent[r] += hi - lo
+
+
+def _check(A, op):
+    if A.ndim != 2:
+        raise ValueError("X must have shape (P, n)")
+    if A.shape[0] < 1:
+        raise ValueError("P must be >= 1")
+    if op not in (SUM, MEAN):
+        raise ValueError(f"unknown op {op!r}")
+
+
 def ring_allreduce(X, op=SUM, chunking=None, in_dtype="f32", out_dtype=None):
     """All-reduce P rank buffers by simulating the ring one step at a time.
 
@@ -103,30 +149,13 @@ def ring_allreduce(X, op=SUM, chunking=None, in_dtype="f32", out_dtype=None):
     rank r put on the wire over the whole all-reduce.
     """
     A = _widen(X, in_dtype)
-    if A.ndim != 2:
-        raise ValueError("X must have shape (P, n)")
+    _check(A, op)
     P, n = A.shape
-    if P < 1:
-        raise ValueError("P must be >= 1")
-    if op not in (SUM, MEAN):
-        raise ValueError(f"unknown op {op!r}")
     C = P if chunking is None else int(chunking)
-    L = chunk_length(n, C)
-    chunks = [(min(j * L, n), min((j + 1) * L, n)) for j in range(C)]
-    start = [j % P for j in range(C)]
-    owner = [(s + P - 1) % P for s in start]
+    chunks, start, owner = _chunks(n, P, C)
     sent = np.zeros(P, dtype=np.int64)
 
-    # Reduce-scatter: P-1 steps.  Every send of a step reads the buffers as
-    # they stood at the start of the step (S), so the sends are simultaneous.
-    for t in range(P - 1):
-        S = A.copy()
-        for r in range(P):
-            dst = (r + 1) % P
-            for j, (lo, hi) in enumerate(chunks):
-                if start[j] == (r - t) % P:
-                    A[dst, lo:hi] = S[r, lo:hi] + A[dst, lo:hi]
-                    sent[r] += hi - lo
+    _reduce_scatter_steps(A, chunks, start, sent)
 
     # Mean: the owner of each chunk now holds the full sum; divide once.
     if op == MEAN:
@@ -134,17 +163,57 @@ def ring_allreduce(X, op=SUM, chunking=None, in_dtype="f32", out_dtype=None):
         for j, (lo, hi) in enumerate(chunks):
             A[owner[j], lo:hi] = A[owner[j], lo:hi] / div
 
-    # All-gather: P-1 steps of forwarding the owner's finished chunk.
-    for t in range(P - 1):
-        S = A.copy()
-        for r in range(P):
-            dst = (r + 1) % P
-            for j, (lo, hi) in enumerate(chunks):
-                if owner[j] == (r - t) % P:
-                    A[dst, lo:hi] = S[r, lo:hi]
-                    sent[r] += hi - lo
-
+    _all_gather_steps(A, chunks, owner, sent)
     return _narrow(A, out_dtype or in_dtype), sent
+
+
+def chunk_owners(n, chunking, P):
+    """Owner rank of every element: the rank where the chunk's reduce-scatter
+    ends, (start + P - 1) mod P."""
+    return (chunk_start_ranks(n, chunking, P) + P - 1) % P
+
+
+def ring_reduce_scatter(X, op=SUM, chunking=None, in_dtype="f32", out_dtype=None):
+    """The first half of the ring on its own: P-1 reduce-scatter steps, then
+    Mean at each chunk's owner.  ("Distributed Training", "Sharded data
+    parallelism": FSDP reduce-scatters the gradients so that each rank ends
+    holding its shard; CS336 Lecture 8, "Collective Operations": each rank
+    receives a unique chunk of the reduced tensor.)
+
+    Returns (Y, owner, sent): Y (P, n) in ``out_dtype`` is every rank's
+    buffer after the steps -- only Y[owner[i], i] is the finished reduction
+    of element i, the other entries are partial sums of the ring --, owner
+    (n,) the owning rank of each element, sent[r] the elements rank r sent.
+    """
+    A = _widen(X, in_dtype)
+    _check(A, op)
+    P, n = A.shape
+    C = P if chunking is None else int(chunking)
+    chunks, start, owner = _chunks(n, P, C)
+    sent = np.zeros(P, dtype=np.int64)
+    _reduce_scatter_steps(A, chunks, start, sent)
+    if op == MEAN:
+        div = A.dtype.type(P)
+        for j, (lo, hi) in enumerate(chunks):
+            A[owner[j], lo:hi] = A[owner[j], lo:hi] / div
+    return _narrow(A, out_dtype or in_dtype), chunk_owners(n, C, P), sent
+
+
+def ring_all_gather(B, chunking=None):
+    """The second half of the ring on its own: P-1 steps forwarding each
+    chunk from its owner, so every rank ends with the owner's values.
+    (CS336 Lecture 8, "Collective Operations": all-gather gives every rank
+    the complete tensor.)  B: (P, n) array of any dtype; only
+    B[owner[i], i] matters.  Returns (Y, sent)."""
+    A = np.array(B, copy=True)
+    if A.ndim != 2 or A.shape[0] < 1:
+        raise ValueError("B must have shape (P, n)")
+    P, n = A.shape
+    C = P if chunking is None else int(chunking)
+    chunks, _, owner = _chunks(n, P, C)
+    sent = np.zeros(P, dtype=np.int64)
+    _all_gather_steps(A, chunks, owner, sent)
+    return A, sent
 
 
 def ring_allreduce_sampled(V, start, op=SUM, in_dtype="f32", out_dtype=None):

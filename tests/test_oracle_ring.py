@@ -274,3 +274,55 @@ def test_float64_accumulation():
     Y, _ = oracle.ring_allreduce(X, "sum", 4, in_dtype="f64")
     assert Y.dtype == np.float64
     assert np.array_equal(Y[0], fold_closed_form(X, 4))
+
+
+# ------------------------------------------------ the ring's two halves ----
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 8])
+def test_reduce_scatter_then_all_gather_is_the_all_reduce(P):
+    for n, C in ((37, P), (100, 2 * P + 1), (64, 1)):
+        X = workloads.rank_buffers(P, n, dist="wide", seed=P + n)
+        for op in ("sum", "mean"):
+            R, owner, s1 = oracle.ring_reduce_scatter(X, op, C)
+            G, s2 = oracle.ring_all_gather(R, C)
+            Y, s = oracle.ring_allreduce(X, op, C)
+            assert np.array_equal(bits(G), bits(Y))
+            assert np.array_equal(s1 + s2, s)
+            # the owner holds the finished value
+            assert np.array_equal(bits(R[owner, np.arange(n)]), bits(Y[0]))
+
+
+def test_reduce_scatter_owner_rule():
+    """Chunk j starts at rank j mod P and ends at its owner, one rank
+    before the start."""
+    own = oracle.chunk_owners(12, 4, 4)
+    assert own.tolist() == [3, 3, 3, 0, 0, 0, 1, 1, 1, 2, 2, 2]
+
+
+def test_all_gather_copies_the_owner_values():
+    P, n, C = 4, 20, 4
+    B = np.arange(P * n, dtype=np.int64).reshape(P, n)
+    G, sent = oracle.ring_all_gather(B, C)
+    own = oracle.chunk_owners(n, C, P)
+    for r in range(P):
+        assert G[r].tolist() == B[own, np.arange(n)].tolist()
+    assert np.all(sent * P == (P - 1) * n)
+
+
+def test_fully_sharded_traffic_matches_pages(golden_dir):
+    """Full sharding moves two all-gathers and a reduce-scatter per step,
+    3(W-1)/W model sizes per device; the pages print 2.625 at W=8 and 2.953
+    at W=64, 1.5 times the replicated ring all-reduce."""
+    with open(os.path.join(golden_dir, "pages_printed.json")) as f:
+        pr = json.load(f)
+    full = pr["ring_traffic_fully_sharded"]["model_sizes_per_device"]
+    for W in (8, 64):
+        n = W * 3
+        X = np.zeros((W, n), np.float32)
+        _, _, rs = oracle.ring_reduce_scatter(X, "sum", W)
+        _, ag = oracle.ring_all_gather(X, W)
+        per_device = (2 * ag + rs) / n
+        assert np.all(per_device == per_device[0])
+        assert f"{per_device[0]:.3f}" == full[str(W)]
+        rep = pr["ring_traffic_replicated"]["model_sizes_per_device"][str(W)]
+        assert f"{per_device[0] / float(rep):.2f}" == "1.50"
