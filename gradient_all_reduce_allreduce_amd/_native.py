@@ -59,6 +59,11 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,
         ctypes.c_int, ctypes.c_void_p]),
+    "reducescatter_ring_emulated": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
+        ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),
+    "allgather_ring_emulated": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),
     "ddp_last_error": (ctypes.c_char_p, []),
 }
 

@@ -98,6 +98,18 @@ def allreduce_fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, mom
                                        out_dtype, stream))
 
 
+def reducescatter_ring_emulated(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n,
+                                stream=None):
+    _check(N.lib().reducescatter_ring_emulated(_op(op), P, chunking, N.pointer_array(rank_in),
+                                               in_dtype, N.pointer_array(rank_out), out_dtype, n,
+                                               stream))
+
+
+def allgather_ring_emulated(P, chunking, rank_buf, dtype, n, stream=None):
+    _check(N.lib().allgather_ring_emulated(P, chunking, N.pointer_array(rank_buf), dtype, n,
+                                           stream))
+
+
 # --------------------------------------------------------- torch level ----
 
 def torch_dtype_code(dtype):
@@ -148,6 +160,36 @@ def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None):
                             torch_dtype_code(out[0].dtype), tensors[0].numel(),
                             current_stream(tensors[0].device))
     return out
+
+
+def reduce_scatter(tensors, op="sum", chunking=None, out=None, out_dtype=None):
+    """Reduce-scatter: out[owner(i)][i] receives element i's reduction
+    (owner = the rank where the chunk's ring ends); every other element of
+    ``out`` is left as it was.  Returns ``out``."""
+    import torch
+    tensors = _rank_tensors(tensors, "reduce_scatter")
+    P = len(tensors)
+    if out is None:
+        dt = out_dtype or tensors[0].dtype
+        out = [torch.empty(tensors[0].shape, dtype=dt, device=tensors[0].device) for _ in range(P)]
+    out = _rank_tensors(out, "reduce_scatter out")
+    if len(out) != P or out[0].numel() != tensors[0].numel():
+        raise ValueError("reduce_scatter: out must match the inputs")
+    reducescatter_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
+                                torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
+                                torch_dtype_code(out[0].dtype), tensors[0].numel(),
+                                current_stream(tensors[0].device))
+    return out
+
+
+def all_gather(tensors, chunking=None):
+    """All-gather in place: every rank receives each element from the rank
+    that owns it.  Returns the tensors."""
+    tensors = _rank_tensors(tensors, "all_gather")
+    allgather_ring_emulated(len(tensors), chunking or len(tensors),
+                            [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
+                            tensors[0].numel(), current_stream(tensors[0].device))
+    return tensors
 
 
 def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):

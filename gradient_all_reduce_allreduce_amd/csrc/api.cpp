@@ -333,4 +333,66 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const voi
     return ok();
 }
 
+int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
+                                ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                                void* stream) {
+    int s = validate_reduce(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, true);
+    if (s) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
+    if ((s = check_overlaps(bufs))) return s;
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.mode = ddp::kReduceScatter;
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    for (int r = 0; r < P; ++r) {
+        l.in[r] = rank_in[r];
+        l.out[r] = rank_out[r];
+    }
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_reduce(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf, ddp_dtype dtype, int64_t n,
+                            void* stream) {
+    int s = check_ranks(P);
+    if (s) return s;
+    if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
+    if (n < 0) return fail(DDP_E_ARG, "n = %lld is negative", static_cast<long long>(n));
+    if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if ((s = check_ptr_array(const_cast<const void* const*>(rank_buf), P, "rank_buf"))) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_buf), P, n, elem_bytes(dtype), "rank_buf");
+    for (size_t i = 0; i < bufs.size(); ++i)
+        for (size_t j = i + 1; j < bufs.size(); ++j)
+            if (n > 0 && bufs[i].lo < bufs[j].hi && bufs[j].lo < bufs[i].hi)
+                return fail(DDP_E_OVERLAP, "rank_buf[%d] and rank_buf[%d] overlap", bufs[i].index,
+                            bufs[j].index);
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.mode = ddp::kAllGather;
+    l.P = P;
+    l.chunking = chunking;
+    l.in_bf16 = dtype == DDP_BF16;
+    l.out_bf16 = dtype == DDP_BF16;
+    for (int r = 0; r < P; ++r) l.out[r] = rank_buf[r];
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_reduce(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
 }  // extern "C"

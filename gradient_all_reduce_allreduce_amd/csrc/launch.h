@@ -11,7 +11,11 @@ namespace ddp {
 constexpr int kMaxRanks = DDP_MAX_RANKS;
 
 // Everything the fused ring-reduce kernel needs; validated by the caller.
+// What one launch sequence computes.
+enum RingMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+
 struct RingLaunch {
+    int mode;          // RingMode
     int P;
     int chunking;
     int op;            // DDP_SUM / DDP_MEAN
@@ -50,6 +54,12 @@ const void* ring_kernel_f32_f32(int P, int sgd, int scalar);
 const void* ring_kernel_f32_bf16(int P, int sgd, int scalar);
 const void* ring_kernel_bf16_f32(int P, int sgd, int scalar);
 const void* ring_kernel_bf16_bf16(int P, int sgd, int scalar);
+const void* ring_rs_kernel_f32_f32(int P, int scalar);
+const void* ring_rs_kernel_f32_bf16(int P, int scalar);
+const void* ring_rs_kernel_bf16_f32(int P, int scalar);
+const void* ring_rs_kernel_bf16_bf16(int P, int scalar);
+// All-gather kernels by element size (2 or 4 bytes); ring_allgather.hip.
+const void* ring_ag_kernel(int elem_bytes, int P, int scalar);
 
 struct CopyLaunch {
     int P;

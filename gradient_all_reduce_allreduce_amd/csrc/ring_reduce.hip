@@ -1,5 +1,6 @@
-// ring_reduce.hip -- host-side launch of the ring all-reduce kernels
-// (device code in ring_reduce_impl.h).
+// ring_reduce.hip -- host-side launch of the ring kernels (device code in
+// ring_reduce_impl.h): the fused all-reduce (optionally with SGD), and the
+// reduce-scatter and all-gather halves on their own.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,21 +16,43 @@ namespace {
 constexpr int64_t kMaxLaunchElems = int64_t(1) << 29;
 
 const void* select_kernel(const RingLaunch& l, int scalar) {
-    if (l.in_bf16) {
-        return l.out_bf16 ? ring_kernel_bf16_bf16(l.P, l.sgd, scalar) : ring_kernel_bf16_f32(l.P, l.sgd, scalar);
+    const int P = l.P;
+    switch (l.mode) {
+        case kReduceScatter:
+            if (l.in_bf16) return l.out_bf16 ? ring_rs_kernel_bf16_bf16(P, scalar) : ring_rs_kernel_bf16_f32(P, scalar);
+            return l.out_bf16 ? ring_rs_kernel_f32_bf16(P, scalar) : ring_rs_kernel_f32_f32(P, scalar);
+        case kAllGather:
+            return ring_ag_kernel(l.out_bf16 ? 2 : 4, P, scalar);
+        default:
+            if (l.in_bf16) {
+                return l.out_bf16 ? ring_kernel_bf16_bf16(P, l.sgd, scalar) : ring_kernel_bf16_f32(P, l.sgd, scalar);
+            }
+            return l.out_bf16 ? ring_kernel_f32_bf16(P, l.sgd, scalar) : ring_kernel_f32_f32(P, l.sgd, scalar);
     }
-    return l.out_bf16 ? ring_kernel_f32_bf16(l.P, l.sgd, scalar) : ring_kernel_f32_f32(l.P, l.sgd, scalar);
+}
+
+// Elements per lane vector and per tile of the vector kernel of this mode.
+void tile_shape(const RingLaunch& l, int64_t* V, int64_t* tile) {
+    if (l.mode == kAllGather) {
+        *V = l.out_bf16 ? 8 : 4;
+        *tile = static_cast<int64_t>(rr::kBlock) * *V;
+        return;
+    }
+    const bool sgd = l.mode == kAllReduce && l.sgd;
+    *V = ring_lane_elems(l.in_bf16 != 0, l.out_bf16 != 0, sgd);
+    *tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P) * *V;
 }
 
 }  // namespace
 
 int launch_ring_reduce(const RingLaunch& l, const char** msg) {
     if (l.n <= 0) return 0;
-    const int64_t V = ring_lane_elems(l.in_bf16 != 0, l.out_bf16 != 0, l.sgd != 0);
-    const int64_t tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P) * V;
+    if (l.mode == kAllGather && l.P == 1) return 0;   // one rank already holds everything
+    int64_t V = 4, tile = 0;
+    tile_shape(l, &V, &tile);
     const int64_t L = (l.n + l.chunking - 1) / l.chunking;
     // Chunks shorter than a tile would put several start ranks in one tile:
-    // those calls use the one-element-per-lane kernel.
+    // those calls use the one-element-per-lane kernels.
     const int scalar = L < tile ? 1 : 0;
     const void* fn = select_kernel(l, scalar);
     if (fn == nullptr) {
@@ -43,7 +66,7 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         const int64_t n = l.n - base < kMaxLaunchElems ? l.n - base : kMaxLaunchElems;
         rr::RingArgs a{};
         for (int r = 0; r < l.P; ++r) {
-            a.in[r] = static_cast<const char*>(l.in[r]) + base * ies;
+            a.in[r] = l.in[r] ? static_cast<const char*>(l.in[r]) + base * ies : nullptr;
             a.out[r] = l.out[r] ? static_cast<char*>(l.out[r]) + base * oes : nullptr;
         }
         a.w = l.w ? l.w + base : nullptr;
@@ -68,7 +91,7 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(rr::kBlock), args, 0,
                                              static_cast<hipStream_t>(l.stream));
         if (e != hipSuccess) {
-            *msg = "hipLaunchKernel(ring_reduce)";
+            *msg = "hipLaunchKernel(ring)";
             return static_cast<int>(e);
         }
     }

@@ -344,6 +344,235 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_scalar_kernel(RingArgs) {
     if (i < a->n) process_element<P, INB, OUTB, SGD>(a, i);
 }
 
+// ---- the ring's two halves as separate passes ------------------------------
+//
+// Reduce-scatter: element i's finished reduction is written to its owner
+// only, owner = (s + P - 1) mod P, the rank where the chunk's reduce-scatter
+// ends -- in the rotated load order that is register P-1.  The owner's copy
+// is stored with ordinary (cache-allocating) stores, so an all-gather that
+// follows finds it in the last-level cache.  All-gather: every rank other
+// than the owner receives the owner's value.  Tiles that straddle a chunk
+// boundary take the per-element path (at most C-1 tiles per call).
+
+template <int P, bool INB, bool OUTB>
+__device__ __forceinline__ void rs_element(KArgs a, uint32_t i) {
+#pragma clang fp contract(off)
+    const int s = static_cast<int>(((a->base + i) / a->L) % P);
+    float g;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        const void* p = a->in[rank_at(s, k, P)];
+        float xk;
+        if constexpr (INB) {
+            xk = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+        } else {
+            xk = static_cast<const float*>(p)[i];
+        }
+        g = k == 0 ? xk : g + xk;
+    }
+    if (a->mean) g = mean_of<P>(g);
+    void* o = a->out[rank_at(s, P - 1, P)];
+    if constexpr (OUTB) {
+        static_cast<uint16_t*>(o)[i] = static_cast<uint16_t>(bf16_bits(g));
+    } else {
+        static_cast<float*>(o)[i] = g;
+    }
+}
+
+template <int P, int ES>
+__device__ __forceinline__ void ag_element(KArgs a, uint32_t i) {
+    const int s = static_cast<int>(((a->base + i) / a->L) % P);
+    const int o = rank_at(s, P - 1, P);
+    if constexpr (ES == 2) {
+        const uint16_t v = static_cast<const uint16_t*>(a->out[o])[i];
+#pragma unroll
+        for (int r = 0; r < P; ++r)
+            if (r != o) static_cast<uint16_t*>(a->out[r])[i] = v;
+    } else {
+        const uint32_t v = static_cast<const uint32_t*>(a->out[o])[i];
+#pragma unroll
+        for (int r = 0; r < P; ++r)
+            if (r != o) static_cast<uint32_t*>(a->out[r])[i] = v;
+    }
+}
+
+template <int P, bool INB, bool OUTB, bool FULL>
+__device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
+#pragma clang fp contract(off)
+    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int V = ring_lane_elems(INB, OUTB, false);
+    constexpr uint32_t IES = INB ? 2 : 4;
+    constexpr uint32_t OES = OUTB ? 2 : 4;
+    constexpr int WIN = V * IES / 4;
+    constexpr uint32_t TILE = static_cast<uint32_t>(kBlock) * U * V;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t n_vec = a->n_vec;
+    const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
+    const int64_t j0 = (a->base + t0) / a->L;
+    const int64_t j1 = (a->base + last) / a->L;
+    if (j0 != j1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i0 = t0 + (u * kBlock + tid) * V;
+            if (FULL || i0 < n_vec) {
+                for (int e = 0; e < V; ++e) rs_element<P, INB, OUTB>(a, i0 + e);
+            }
+        }
+        return;
+    }
+    const int s0 = static_cast<int>(j0 % P);
+    u32x4 x[P][U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i0 = t0 + (u * kBlock + tid) * V;
+        ok[u] = FULL || (i0 < n_vec);
+        if (ok[u]) {
+#pragma unroll
+            for (int k = 0; k < P; ++k)
+                x[k][u] = load_lane<WIN>(static_cast<const char*>(a->in[rank_at(s0, k, P)]) + i0 * IES);
+        } else {
+#pragma unroll
+            for (int k = 0; k < P; ++k) x[k][u] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float acc[U][V];
+    fold<P, 0, INB, U, V>(x, acc);
+    char* const owner = static_cast<char*>(a->out[rank_at(s0, P - 1, P)]);
+    const bool mean = a->mean != 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        const uint32_t i0 = t0 + (u * kBlock + tid) * V;
+        float g[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) g[e] = mean ? mean_of<P>(acc[u][e]) : acc[u][e];
+        if constexpr (OUTB && V == 8) {
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
+            *reinterpret_cast<u32x4*>(owner + i0 * OES) = o;
+        } else if constexpr (OUTB) {
+            u32x2 o;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
+            *reinterpret_cast<u32x2*>(owner + i0 * OES) = o;
+        } else {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
+            *reinterpret_cast<u32x4*>(owner + i0 * OES) = o;
+        }
+    }
+}
+
+template <int P, int ES, bool FULL>
+__device__ __forceinline__ void ag_tile(KArgs a, uint32_t t0) {
+    constexpr int V = 16 / ES;
+    constexpr uint32_t TILE = static_cast<uint32_t>(kBlock) * V;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t n_vec = a->n_vec;
+    const uint32_t i0 = t0 + tid * V;
+    const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
+    const int64_t j0 = (a->base + t0) / a->L;
+    const int64_t j1 = (a->base + last) / a->L;
+    if (!FULL && i0 >= n_vec) return;
+    if (j0 != j1) {
+        for (int e = 0; e < V; ++e) ag_element<P, ES>(a, i0 + e);
+        return;
+    }
+    const int o = rank_at(static_cast<int>(j0 % P), P - 1, P);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a->out[o]) + i0 * ES);
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        if (r == o) continue;
+        store16(static_cast<char*>(a->out[r]) + i0 * ES, y);
+    }
+}
+
+template <int P, bool INB, bool OUTB>
+__global__ __launch_bounds__(kBlock) void ring_rs_kernel(RingArgs) {
+    constexpr uint32_t TILE =
+        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(INB, OUTB, false);
+    const KArgs a = kernel_args();
+    const uint32_t t0 = blockIdx.x * TILE;
+    const uint32_t n_vec = a->n_vec;
+    if (t0 + TILE <= n_vec) {
+        rs_tile<P, INB, OUTB, true>(a, t0);
+    } else if (t0 < n_vec) {
+        rs_tile<P, INB, OUTB, false>(a, t0);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        const uint32_t i = n_vec + threadIdx.x;
+        if (i < a->n) rs_element<P, INB, OUTB>(a, i);
+    }
+}
+
+template <int P, bool INB, bool OUTB>
+__global__ __launch_bounds__(kBlock) void ring_rs_scalar_kernel(RingArgs) {
+    const KArgs a = kernel_args();
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < a->n) rs_element<P, INB, OUTB>(a, i);
+}
+
+template <int P, int ES>
+__global__ __launch_bounds__(kBlock) void ring_ag_kernel(RingArgs) {
+    constexpr uint32_t TILE = static_cast<uint32_t>(kBlock) * (16 / ES);
+    const KArgs a = kernel_args();
+    const uint32_t t0 = blockIdx.x * TILE;
+    const uint32_t n_vec = a->n_vec;
+    if (t0 + TILE <= n_vec) {
+        ag_tile<P, ES, true>(a, t0);
+    } else if (t0 < n_vec) {
+        ag_tile<P, ES, false>(a, t0);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        const uint32_t i = n_vec + threadIdx.x;
+        if (i < a->n) ag_element<P, ES>(a, i);
+    }
+}
+
+template <int P, int ES>
+__global__ __launch_bounds__(kBlock) void ring_ag_scalar_kernel(RingArgs) {
+    const KArgs a = kernel_args();
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < a->n) ag_element<P, ES>(a, i);
+}
+
+template <bool INB, bool OUTB, bool SCALAR>
+const void* ring_rs_kernel_for(int P) {
+    switch (P) {
+#define DDP_CASE(p)                                                                       \
+    case p:                                                                               \
+        return SCALAR ? reinterpret_cast<const void*>(&ring_rs_scalar_kernel<p, INB, OUTB>) \
+                      : reinterpret_cast<const void*>(&ring_rs_kernel<p, INB, OUTB>);
+        DDP_CASE(1) DDP_CASE(2) DDP_CASE(3) DDP_CASE(4)
+        DDP_CASE(5) DDP_CASE(6) DDP_CASE(7) DDP_CASE(8)
+        DDP_CASE(9) DDP_CASE(10) DDP_CASE(11) DDP_CASE(12)
+        DDP_CASE(13) DDP_CASE(14) DDP_CASE(15) DDP_CASE(16)
+#undef DDP_CASE
+        default:
+            return nullptr;
+    }
+}
+
+template <int ES, bool SCALAR>
+const void* ring_ag_kernel_for(int P) {
+    switch (P) {
+#define DDP_CASE(p)                                                                 \
+    case p:                                                                         \
+        return SCALAR ? reinterpret_cast<const void*>(&ring_ag_scalar_kernel<p, ES>) \
+                      : reinterpret_cast<const void*>(&ring_ag_kernel<p, ES>);
+        DDP_CASE(1) DDP_CASE(2) DDP_CASE(3) DDP_CASE(4)
+        DDP_CASE(5) DDP_CASE(6) DDP_CASE(7) DDP_CASE(8)
+        DDP_CASE(9) DDP_CASE(10) DDP_CASE(11) DDP_CASE(12)
+        DDP_CASE(13) DDP_CASE(14) DDP_CASE(15) DDP_CASE(16)
+#undef DDP_CASE
+        default:
+            return nullptr;
+    }
+}
+
 template <bool INB, bool OUTB, bool SGD, bool SCALAR>
 const void* ring_kernel_for(int P) {
     switch (P) {
@@ -364,6 +593,8 @@ const void* ring_kernel_for(int P) {
 }  // namespace rr
 }  // namespace ddp
 
+// Defines ddp::ring_kernel_<name>(P, sgd, scalar) and
+// ddp::ring_rs_kernel_<name>(P, scalar) for one type pair.
 #define DDP_RING_TYPE_PAIR(name, INB, OUTB)                                              \
     namespace ddp {                                                                      \
     const void* ring_kernel_##name(int P, int sgd, int scalar) {                         \
@@ -371,5 +602,9 @@ const void* ring_kernel_for(int P) {
                                : rr::ring_kernel_for<INB, OUTB, true, false>(P);         \
         return scalar ? rr::ring_kernel_for<INB, OUTB, false, true>(P)                   \
                       : rr::ring_kernel_for<INB, OUTB, false, false>(P);                 \
+    }                                                                                    \
+    const void* ring_rs_kernel_##name(int P, int scalar) {                               \
+        return scalar ? rr::ring_rs_kernel_for<INB, OUTB, true>(P)                       \
+                      : rr::ring_rs_kernel_for<INB, OUTB, false>(P);                     \
     }                                                                                    \
     }

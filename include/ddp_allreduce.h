@@ -216,6 +216,51 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
                         float mu, void* const* rank_grad_out,
                         ddp_dtype out_dtype, void* stream);
 
+/*
+ * reducescatter_ring_emulated -- the first half of the ring on its own.
+ *
+ * Every rank ends holding the finished reduction of the chunks it owns
+ * ("Distributed Training", "Sharded data parallelism": FSDP reduce-scatters
+ * gradients so that each rank keeps its shard; CS336 Lecture 8, "Collective
+ * Operations": each rank receives a unique chunk of the reduced tensor).
+ * The chunk that starts its ring at rank s is owned by rank (s + P - 1) mod P,
+ * where its reduce-scatter ends.  For every element i the call writes the
+ * reduction (the same value, bit for bit, that allreduce_ring_emulated
+ * produces, Mean applied) to rank_out[owner(i)][i] only; every other
+ * element of every rank_out buffer is left untouched.  (In a real ring the
+ * other ranks would hold partial sums there.)
+ *
+ * Arguments, layout, ownership and errors as for allreduce_ring_emulated.
+ * reducescatter_ring_emulated followed by allgather_ring_emulated on
+ * rank_out equals allreduce_ring_emulated bit for bit.
+ */
+int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
+                                const void* const* rank_in, ddp_dtype in_dtype,
+                                void* const* rank_out, ddp_dtype out_dtype,
+                                int64_t n, void* stream);
+
+/*
+ * allgather_ring_emulated -- the second half of the ring on its own.
+ *
+ * Gives every rank the complete tensor (CS336 Lecture 8, "Collective
+ * Operations"; FSDP all-gathers a unit's parameters, "Distributed Training",
+ * "Sharded data parallelism").  With the chunk ownership of
+ * reducescatter_ring_emulated (chunk length ceil(n / C), chunk j owned by
+ * rank (j + P - 1) mod P), every element i is copied bit for bit from
+ * rank_buf[owner(i)][i] into the same position of every other rank's
+ * buffer.
+ *
+ *   P         number of ranks, 1..DDP_MAX_RANKS (P = 1: nothing to do)
+ *   chunking  C >= 1
+ *   rank_buf  host array [P] of device pointers, n elements of dtype each,
+ *             16-byte aligned, pairwise disjoint
+ *   dtype     DDP_F32 or DDP_BF16 (only the element size matters)
+ *   n         elements per rank, >= 0
+ * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
+ */
+int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf,
+                            ddp_dtype dtype, int64_t n, void* stream);
+
 /* Message describing the calling thread's most recent non-OK status
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* ddp_last_error(void);

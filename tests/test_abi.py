@@ -229,3 +229,25 @@ def test_bucket_views_match_pack_layout():
         want = oracle.pack(host, 4, 256)
         for k in range(b.n_buckets):
             assert np.array_equal(b.bucket_view(arena[r], k).numpy(), want[k])
+
+
+def test_reduce_scatter_and_all_gather_errors():
+    lib = N.lib()
+    ins = N.pointer_array([A, A + MB])
+    outs = N.pointer_array([A + 64 * MB, A + 65 * MB])
+    assert lib.reducescatter_ring_emulated(0, 0, 2, ins, 0, outs, 0, 16, None) == N.DDP_E_ARG
+    assert lib.reducescatter_ring_emulated(0, 2, 0, ins, 0, outs, 0, 16, None) == N.DDP_E_ARG
+    assert lib.reducescatter_ring_emulated(0, 2, 2, ins, 0, N.pointer_array([A, A + 8]), 0, 16,
+                                           None) == N.DDP_E_ALIGN
+    assert lib.reducescatter_ring_emulated(0, 2, 2, ins, 0, N.pointer_array([A + 16, A + MB]), 0,
+                                           1024, None) == N.DDP_E_OVERLAP
+    assert lib.reducescatter_ring_emulated(0, 2, 2, ins, 0, ins, 0, 0, None) == N.DDP_OK
+    assert lib.allgather_ring_emulated(0, 2, outs, 0, 16, None) == N.DDP_E_ARG
+    assert lib.allgather_ring_emulated(2, 0, outs, 0, 16, None) == N.DDP_E_ARG
+    assert lib.allgather_ring_emulated(2, 2, outs, 3, 16, None) == N.DDP_E_ARG
+    assert lib.allgather_ring_emulated(2, 2, None, 0, 16, None) == N.DDP_E_ARG
+    assert lib.allgather_ring_emulated(2, 2, N.pointer_array([A, A + 4]), 0, 16,
+                                       None) == N.DDP_E_ALIGN
+    assert lib.allgather_ring_emulated(2, 2, N.pointer_array([A, A]), 0, 16,
+                                       None) == N.DDP_E_OVERLAP
+    assert lib.allgather_ring_emulated(2, 2, outs, 1, 0, None) == N.DDP_OK

@@ -1,0 +1,91 @@
+"""GPU parity of the ring's two halves as separate calls: the reduce-scatter
+writes each element's reduction into its owner's buffer only (bit for bit the
+oracle's reduce-scatter at the owner), the all-gather copies each element from
+its owner to every other rank, and reduce-scatter followed by all-gather is
+the fused all-reduce bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import DEV, assert_same_bits, to_device, to_host, torch_dtype
+
+pytestmark = pytest.mark.gpu
+ddp = pytest.importorskip("gradient_all_reduce_allreduce_amd")
+
+SENTINEL_F32 = np.uint32(0x7FBADBAD)       # a NaN pattern no reduction produces here
+SENTINEL_BF16 = np.uint16(0x7FBA)
+
+
+def draw(P, n, dtype, seed):
+    X = workloads.rank_buffers(P, n, dist="wide", seed=seed)
+    return workloads.to_bf16_bits(X) if dtype == "bf16" else X
+
+
+def sentinel_tensors(P, n, dtype):
+    if dtype == "bf16":
+        h = np.full((P, n), SENTINEL_BF16, np.uint16)
+    else:
+        h = np.full((P, n), SENTINEL_F32, np.uint32).view(np.float32)
+    return to_device(h, dtype), h
+
+
+def raw(a):
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"),
+                                  ("f32", "bf16")])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+def test_reduce_scatter_writes_only_the_owner(pair, P):
+    it, ot = pair
+    for n in (1, 9, 4099, 70001):
+        for C in sorted({1, P, 2 * P + 1, n}):
+            for op in ("sum", "mean"):
+                X = draw(P, n, it, seed=P * 13 + n + C)
+                outs, before = sentinel_tensors(P, n, ot)
+                ddp.reduce_scatter(to_device(X, it), op, C, out=outs)
+                torch.cuda.synchronize()
+                got = to_host(outs)
+                R, owner, _ = oracle.ring_reduce_scatter(X, op, C, in_dtype=it, out_dtype=ot)
+                cols = np.arange(n)
+                tag = f"{it}->{ot} P={P} n={n} C={C} {op}"
+                assert_same_bits(got[owner, cols], R[owner, cols], tag)
+                mask = np.ones((P, n), bool)
+                mask[owner, cols] = False
+                assert np.array_equal(raw(got)[mask], raw(before)[mask]), tag
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P", [1, 2, 5, 8, 16])
+def test_all_gather_copies_from_the_owner(dtype, P):
+    for n in (1, 7, 4101, 70003):
+        for C in sorted({1, P, 3 * P + 1, n}):
+            B = draw(P, n, dtype, seed=P + n + C)
+            bufs = to_device(B, dtype)
+            ddp.all_gather(bufs, C)
+            torch.cuda.synchronize()
+            want, _ = oracle.ring_all_gather(B, C)
+            assert np.array_equal(raw(to_host(bufs)), raw(want)), (dtype, P, n, C)
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_reduce_scatter_then_all_gather_is_the_all_reduce(pair, P):
+    it, ot = pair
+    for n, C in ((1_000_003, P), (262_147, 3 * P), (6_553_600, P)):
+        X = draw(P, n, it, seed=n + P)
+        fused = ddp.allreduce(to_device(X, it), "mean", C, out_dtype=torch_dtype(ot))
+        ins = to_device(X, it)
+        outs = [torch.empty(n, dtype=torch_dtype(ot), device=DEV) for _ in range(P)]
+        ddp.reduce_scatter(ins, "mean", C, out=outs)
+        ddp.all_gather(outs, C)
+        torch.cuda.synchronize()
+        assert_same_bits(to_host(outs), to_host(fused), f"{it}->{ot} P={P} n={n} C={C}")
+        if it == ot:    # in place: rank buffers are both input and output
+            ddp.reduce_scatter(ins, "mean", C, out=ins)
+            ddp.all_gather(ins, C)
+            torch.cuda.synchronize()
+            assert_same_bits(to_host(ins), to_host(fused), "in place")
