@@ -64,6 +64,9 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),
     "allgather_ring_emulated": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),
+    "allreduce_ring_stepwise": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p]),
     "ddp_last_error": (ctypes.c_char_p, []),
 }
 

@@ -110,6 +110,11 @@ def allgather_ring_emulated(P, chunking, rank_buf, dtype, n, stream=None):
                                            stream))
 
 
+def allreduce_ring_stepwise(op, P, chunking, rank_buf, dtype, n, sent_dev=None, stream=None):
+    _check(N.lib().allreduce_ring_stepwise(_op(op), P, chunking, N.pointer_array(rank_buf),
+                                           dtype, n, sent_dev, stream))
+
+
 # --------------------------------------------------------- torch level ----
 
 def torch_dtype_code(dtype):
@@ -189,6 +194,22 @@ def all_gather(tensors, chunking=None):
     allgather_ring_emulated(len(tensors), chunking or len(tensors),
                             [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
                             tensors[0].numel(), current_stream(tensors[0].device))
+    return tensors
+
+
+def allreduce_stepwise(tensors, op="sum", chunking=None, sent=None):
+    """All-reduce fp32 rank tensors in place, one ring step per launch.
+    ``sent``: optional int64 GPU tensor of P counters, increased by the
+    elements each rank sends.  Returns the tensors."""
+    import torch
+    tensors = _rank_tensors(tensors, "allreduce_stepwise")
+    if sent is not None and (sent.dtype != torch.int64 or sent.numel() != len(tensors)
+                             or not sent.is_cuda or not sent.is_contiguous()):
+        raise ValueError("allreduce_stepwise: sent must be a contiguous int64 GPU tensor of P")
+    allreduce_ring_stepwise(op, len(tensors), chunking or len(tensors),
+                            [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
+                            tensors[0].numel(), sent.data_ptr() if sent is not None else None,
+                            current_stream(tensors[0].device))
     return tensors
 
 

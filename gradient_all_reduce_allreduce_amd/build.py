@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libddp_allreduce.so")
 PATTERNS = os.path.join(PKG, "hbm_patterns")     # HBM access-pattern benchmark
 SOURCES = ["api.cpp", "ring_reduce.hip", "ring_reduce_f32_f32.hip",
            "ring_reduce_f32_bf16.hip", "ring_reduce_bf16_f32.hip",
-           "ring_reduce_bf16_bf16.hip", "ring_allgather.hip", "bucket_copy.hip"]
+           "ring_reduce_bf16_bf16.hip", "ring_allgather.hip", "ring_step.hip",
+           "bucket_copy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -395,4 +395,44 @@ int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf, 
     return ok();
 }
 
+int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void* const* rank_buf,
+                            ddp_dtype dtype, int64_t n, uint64_t* sent_dev, void* stream) {
+    if (op != DDP_SUM && op != DDP_MEAN) return fail(DDP_E_ARG, "unknown reduce op %d", op);
+    int s = check_ranks(P);
+    if (s) return s;
+    if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
+    if (n < 0) return fail(DDP_E_ARG, "n = %lld is negative", static_cast<long long>(n));
+    if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (dtype != DDP_F32)
+        return fail(DDP_E_UNSUPPORTED, "the stepwise ring keeps partial sums in the rank buffers, "
+                                       "which must therefore be float32");
+    if ((s = check_ptr_array(const_cast<const void* const*>(rank_buf), P, "rank_buf"))) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_buf), P, n, 4, "rank_buf");
+    if (sent_dev != nullptr) {
+        if (reinterpret_cast<uintptr_t>(sent_dev) & 7u) return fail(DDP_E_ALIGN, "sent is not 8-byte aligned");
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(sent_dev);
+        bufs.push_back({lo, lo + static_cast<uintptr_t>(P) * 8, 8, "sent", 0});
+    }
+    for (size_t i = 0; i < bufs.size(); ++i)
+        for (size_t j = i + 1; j < bufs.size(); ++j)
+            if (n > 0 && bufs[i].lo < bufs[j].hi && bufs[j].lo < bufs[i].hi)
+                return fail(DDP_E_OVERLAP, "%s[%d] and %s[%d] overlap", bufs[i].what, bufs[i].index,
+                            bufs[j].what, bufs[j].index);
+    if (n == 0) return ok();
+
+    ddp::StepLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    for (int r = 0; r < P; ++r) l.buf[r] = static_cast<float*>(rank_buf[r]);
+    l.sent = sent_dev;
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_stepwise(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
 }  // extern "C"

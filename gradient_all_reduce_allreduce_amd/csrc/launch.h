@@ -61,6 +61,19 @@ const void* ring_rs_kernel_bf16_bf16(int P, int scalar);
 // All-gather kernels by element size (2 or 4 bytes); ring_allgather.hip.
 const void* ring_ag_kernel(int elem_bytes, int P, int scalar);
 
+// The ring one step per launch (ring_step.hip): fp32 rank buffers, in place.
+struct StepLaunch {
+    int P;
+    int chunking;
+    int op;
+    float* buf[kMaxRanks];
+    uint64_t* sent;    // device [P] counters of elements sent, or null
+    int64_t n;
+    void* stream;
+};
+
+int launch_ring_stepwise(const StepLaunch& l, const char** msg);
+
 struct CopyLaunch {
     int P;
     int elem_bytes;    // 2 or 4

@@ -261,6 +261,35 @@ int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
 int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf,
                             ddp_dtype dtype, int64_t n, void* stream);
 
+/*
+ * allreduce_ring_stepwise -- the same all-reduce, one ring step per launch.
+ *
+ * The ring as the pages describe it: peers pass slices of the tensor around
+ * the ring (Burn collective blog, "Methods", Ring), P-1 reduce-scatter steps
+ * then P-1 all-gather steps ("Distributed Training", "Sharded data
+ * parallelism"; its "How to Apply It" prints the resulting traffic,
+ * 2(W-1)/W model sizes per device).  Launch t of the reduce-scatter moves the
+ * chunk that started at rank s from rank s+t to rank s+t+1, which adds it to
+ * its own copy; the last one ends at the chunk's owner, which applies Mean;
+ * the all-gather launches then copy the finished chunk around the ring.
+ * The result is bit for bit that of allreduce_ring_emulated.
+ *
+ *   rank_buf  host array [P] of device pointers, n float32 each, in place:
+ *             the inputs, and on completion every rank's result; 16-byte
+ *             aligned, pairwise disjoint
+ *   dtype     DDP_F32 only (partial sums live in the rank buffers and stay
+ *             float32); DDP_BF16 returns DDP_E_UNSUPPORTED
+ *   sent_dev  device array [P] of uint64, 8-byte aligned, or NULL; rank r's
+ *             entry is increased by the number of elements rank r sends
+ *             (the caller clears it first)
+ *   other arguments as for allreduce_ring_emulated.  2(P-1) launches (more
+ *   for n over 2^29).
+ * Errors: DDP_E_ARG, DDP_E_UNSUPPORTED, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
+ */
+int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking,
+                            void* const* rank_buf, ddp_dtype dtype, int64_t n,
+                            uint64_t* sent_dev, void* stream);
+
 /* Message describing the calling thread's most recent non-OK status
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* ddp_last_error(void);

@@ -251,3 +251,15 @@ def test_reduce_scatter_and_all_gather_errors():
     assert lib.allgather_ring_emulated(2, 2, N.pointer_array([A, A]), 0, 16,
                                        None) == N.DDP_E_OVERLAP
     assert lib.allgather_ring_emulated(2, 2, outs, 1, 0, None) == N.DDP_OK
+
+
+def test_stepwise_errors():
+    lib = N.lib()
+    bufs = N.pointer_array([A, A + MB])
+    assert lib.allreduce_ring_stepwise(0, 2, 2, bufs, 1, 16, None, None) == N.DDP_E_UNSUPPORTED
+    assert lib.allreduce_ring_stepwise(0, 2, 2, bufs, 0, 16, A + 200 * MB + 4, None) == N.DDP_E_ALIGN
+    assert lib.allreduce_ring_stepwise(0, 2, 2, bufs, 0, 1024, A + 64, None) == N.DDP_E_OVERLAP
+    assert lib.allreduce_ring_stepwise(0, 2, 2, N.pointer_array([A, A]), 0, 16, None,
+                                       None) == N.DDP_E_OVERLAP
+    assert lib.allreduce_ring_stepwise(3, 2, 2, bufs, 0, 16, None, None) == N.DDP_E_ARG
+    assert lib.allreduce_ring_stepwise(0, 2, 2, bufs, 0, 0, None, None) == N.DDP_OK
