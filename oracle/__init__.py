@@ -30,6 +30,7 @@ Modules:
     bf16    -- bfloat16 <-> float32 conversions by definition
     sgd     -- SGD with momentum on fp32 master weights
     bucket  -- reverse-order gradient bucketing, pack and unpack
+    tree    -- the centralized and b-ary tree all-reduce
 
 Parity status of each function is stated in its module header.
 """
@@ -37,6 +38,7 @@ Parity status of each function is stated in its module header.
 from .ring import (SUM, MEAN, chunk_length, chunk_owners, chunk_start_ranks,
                    chunk_start_ranks_at, ring_all_gather, ring_allreduce,
                    ring_allreduce_sampled, ring_reduce_scatter)
+from .tree import tree_allreduce, tree_parents
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .sgd import sgd_momentum
 from .bucket import bucket_plan, pack, unpack
@@ -45,5 +47,5 @@ __all__ = [
     "SUM", "MEAN", "chunk_length", "chunk_owners", "chunk_start_ranks",
     "chunk_start_ranks_at", "ring_all_gather", "ring_allreduce", "ring_reduce_scatter",
     "ring_allreduce_sampled", "bf16_bits_to_f32", "f32_to_bf16_bits",
-    "sgd_momentum", "bucket_plan", "pack", "unpack",
+    "sgd_momentum", "bucket_plan", "pack", "unpack", "tree_allreduce", "tree_parents",
 ]
