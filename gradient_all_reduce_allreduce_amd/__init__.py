@@ -10,7 +10,7 @@ include/ddp_allreduce.h); this package is its Python binding.
 from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, ddp_bucket_pack,
                   ddp_bucket_unpack, allreduce_ring_emulated, allreduce_fused_sgd,
                   reducescatter_ring_emulated, allgather_ring_emulated, allreduce_ring_stepwise,
-                  allreduce, allreduce_stepwise,
+                  allreduce_tree_emulated, allreduce, allreduce_stepwise, allreduce_tree,
                   allreduce_sgd, reduce_scatter, all_gather)
 from .bucketer import GradBucketer
 
@@ -18,6 +18,7 @@ __all__ = [
     "SUM", "MEAN", "F32", "BF16", "MAX_RANKS", "DdpError", "ddp_bucket_plan", "ddp_bucket_pack",
     "ddp_bucket_unpack", "allreduce_ring_emulated", "allreduce_fused_sgd",
     "reducescatter_ring_emulated", "allgather_ring_emulated", "allreduce_ring_stepwise",
-    "allreduce", "allreduce_stepwise", "allreduce_sgd",
+    "allreduce_tree_emulated", "allreduce", "allreduce_stepwise", "allreduce_tree",
+    "allreduce_sgd",
     "reduce_scatter", "all_gather", "GradBucketer",
 ]

@@ -115,6 +115,13 @@ def allreduce_ring_stepwise(op, P, chunking, rank_buf, dtype, n, sent_dev=None, 
                                            dtype, n, sent_dev, stream))
 
 
+def allreduce_tree_emulated(op, P, branching, rank_in, in_dtype, rank_out, out_dtype, n,
+                            stream=None):
+    _check(N.lib().allreduce_tree_emulated(_op(op), P, branching, N.pointer_array(rank_in),
+                                           in_dtype, N.pointer_array(rank_out), out_dtype, n,
+                                           stream))
+
+
 # --------------------------------------------------------- torch level ----
 
 def torch_dtype_code(dtype):
@@ -161,6 +168,25 @@ def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None):
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("allreduce: out must match the inputs")
     allreduce_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
+                            torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
+                            torch_dtype_code(out[0].dtype), tensors[0].numel(),
+                            current_stream(tensors[0].device))
+    return out
+
+
+def allreduce_tree(tensors, op="sum", branching=2, out=None, out_dtype=None):
+    """All-reduce along the b-ary tree (branching >= P-1: the centralized
+    strategy).  Arguments as for ``allreduce``."""
+    import torch
+    tensors = _rank_tensors(tensors, "allreduce_tree")
+    P = len(tensors)
+    if out is None:
+        dt = out_dtype or tensors[0].dtype
+        out = [torch.empty(tensors[0].shape, dtype=dt, device=tensors[0].device) for _ in range(P)]
+    out = _rank_tensors(out, "allreduce_tree out")
+    if len(out) != P or out[0].numel() != tensors[0].numel():
+        raise ValueError("allreduce_tree: out must match the inputs")
+    allreduce_tree_emulated(op, P, branching, [t.data_ptr() for t in tensors],
                             torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
                             torch_dtype_code(out[0].dtype), tensors[0].numel(),
                             current_stream(tensors[0].device))

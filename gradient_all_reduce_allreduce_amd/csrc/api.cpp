@@ -435,4 +435,38 @@ int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void*
     return ok();
 }
 
+int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching, const void* const* rank_in,
+                            ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                            void* stream) {
+    if (branching < 1) return fail(DDP_E_ARG, "branching = %d, must be >= 1", branching);
+    int s = validate_reduce(op, P, 1, rank_in, in_dtype, rank_out, out_dtype, n, true);
+    if (s) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
+    if ((s = check_overlaps(bufs))) return s;
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.mode = ddp::kTree;
+    l.P = P;
+    l.chunking = 1;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.write_out = 1;
+    // b-ary heap: the parent of rank c >= 1 is (c - 1) / b.
+    for (int c = 1; c < P; ++c) l.parents |= static_cast<uint64_t>((c - 1) / branching) << (4 * c);
+    for (int r = 0; r < P; ++r) {
+        l.in[r] = rank_in[r];
+        l.out[r] = rank_out[r];
+    }
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_reduce(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
 }  // extern "C"

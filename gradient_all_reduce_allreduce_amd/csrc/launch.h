@@ -12,7 +12,7 @@ constexpr int kMaxRanks = DDP_MAX_RANKS;
 
 // Everything the fused ring-reduce kernel needs; validated by the caller.
 // What one launch sequence computes.
-enum RingMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+enum RingMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2, kTree = 3 };
 
 struct RingLaunch {
     int mode;          // RingMode
@@ -29,6 +29,7 @@ struct RingLaunch {
     float* v;
     float lr;
     float mu;
+    uint64_t parents;  // kTree: parent of rank c in bits [4c, 4c+4)
     int64_t n;
     void* stream;
 };
@@ -58,6 +59,10 @@ const void* ring_rs_kernel_f32_f32(int P, int scalar);
 const void* ring_rs_kernel_f32_bf16(int P, int scalar);
 const void* ring_rs_kernel_bf16_f32(int P, int scalar);
 const void* ring_rs_kernel_bf16_bf16(int P, int scalar);
+const void* tree_kernel_f32_f32(int P);
+const void* tree_kernel_f32_bf16(int P);
+const void* tree_kernel_bf16_f32(int P);
+const void* tree_kernel_bf16_bf16(int P);
 // All-gather kernels by element size (2 or 4 bytes); ring_allgather.hip.
 const void* ring_ag_kernel(int elem_bytes, int P, int scalar);
 

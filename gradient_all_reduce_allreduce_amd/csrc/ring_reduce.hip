@@ -23,6 +23,9 @@ const void* select_kernel(const RingLaunch& l, int scalar) {
             return l.out_bf16 ? ring_rs_kernel_f32_bf16(P, scalar) : ring_rs_kernel_f32_f32(P, scalar);
         case kAllGather:
             return ring_ag_kernel(l.out_bf16 ? 2 : 4, P, scalar);
+        case kTree:
+            if (l.in_bf16) return l.out_bf16 ? tree_kernel_bf16_bf16(P) : tree_kernel_bf16_f32(P);
+            return l.out_bf16 ? tree_kernel_f32_bf16(P) : tree_kernel_f32_f32(P);
         default:
             if (l.in_bf16) {
                 return l.out_bf16 ? ring_kernel_bf16_bf16(P, l.sgd, scalar) : ring_kernel_bf16_f32(P, l.sgd, scalar);
@@ -50,10 +53,11 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
     if (l.mode == kAllGather && l.P == 1) return 0;   // one rank already holds everything
     int64_t V = 4, tile = 0;
     tile_shape(l, &V, &tile);
-    const int64_t L = (l.n + l.chunking - 1) / l.chunking;
+    const int64_t L = l.mode == kTree ? l.n : (l.n + l.chunking - 1) / l.chunking;
     // Chunks shorter than a tile would put several start ranks in one tile:
-    // those calls use the one-element-per-lane kernels.
-    const int scalar = L < tile ? 1 : 0;
+    // those calls use the one-element-per-lane kernels.  (The tree's order
+    // does not depend on the element.)
+    const int scalar = l.mode != kTree && L < tile ? 1 : 0;
     const void* fn = select_kernel(l, scalar);
     if (fn == nullptr) {
         *msg = "no kernel for this rank count";
@@ -79,6 +83,7 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         a.n_vec = static_cast<uint32_t>(n - n % V);
         a.mean = l.op == DDP_MEAN;
         a.write_out = l.write_out;
+        a.parents = l.parents;
 
         int64_t grid;
         if (scalar) {

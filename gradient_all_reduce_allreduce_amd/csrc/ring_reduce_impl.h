@@ -67,6 +67,7 @@ struct RingArgs {
     uint32_t n_vec;      // elements covered by whole lane vectors
     int32_t mean;
     int32_t write_out;
+    uint64_t parents;    // tree strategy: 4 bits per rank c >= 1, its parent
 };
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
@@ -573,6 +574,166 @@ const void* ring_ag_kernel_for(int P) {
     }
 }
 
+// ---- centralized and tree strategies ----------------------------------------
+//
+// The reduce runs along a tree over the ranks (Burn collective blog,
+// "Methods", Tree; Centralized is the tree whose root has every other rank as
+// a child): every node adds its children's partial sums to its own value in
+// increasing child order, children before parents, then the root's value is
+// broadcast.  The tree's shape arrives as a parent table (4 bits per rank);
+// parents[c] < c, so walking the parents from the highest rank down finishes
+// every child before its parent.  Register indices are compile-time; the
+// shape only decides, with uniform branches, which of the P(P-1)/2 possible
+// edges are taken.  The order does not depend on the element, so there are
+// no chunk boundaries and no per-element start ranks.
+
+template <int P, bool BF16, int U, int V>
+__device__ __forceinline__ void tree_fold(const u32x4 (&x)[P][U], uint64_t parents, float (&acc)[U][V]) {
+#pragma clang fp contract(off)
+    float part[P][U][V];
+#pragma unroll
+    for (int r = 0; r < P; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e) part[r][u][e] = elem<BF16>(x[r][u], e);
+#pragma unroll
+    for (int p = P - 2; p >= 0; --p) {
+#pragma unroll
+        for (int c = p + 1; c < P; ++c) {
+            if (static_cast<int>((parents >> (4 * c)) & 15u) == p) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) part[p][u][e] = part[p][u][e] + part[c][u][e];
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[u][e] = part[0][u][e];
+}
+
+template <int P, bool INB, bool OUTB>
+__device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
+#pragma clang fp contract(off)
+    float part[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        if constexpr (INB) {
+            part[r] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a->in[r])[i]) << 16);
+        } else {
+            part[r] = static_cast<const float*>(a->in[r])[i];
+        }
+    }
+    const uint64_t parents = a->parents;
+#pragma unroll
+    for (int p = P - 2; p >= 0; --p)
+#pragma unroll
+        for (int c = p + 1; c < P; ++c)
+            if (static_cast<int>((parents >> (4 * c)) & 15u) == p) part[p] = part[p] + part[c];
+    float g = part[0];
+    if (a->mean) g = mean_of<P>(g);
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        if constexpr (OUTB) {
+            static_cast<uint16_t*>(a->out[r])[i] = static_cast<uint16_t>(bf16_bits(g));
+        } else {
+            static_cast<float*>(a->out[r])[i] = g;
+        }
+    }
+}
+
+template <int P, bool INB, bool OUTB, bool FULL>
+__device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
+#pragma clang fp contract(off)
+    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int V = ring_lane_elems(INB, OUTB, false);
+    constexpr uint32_t IES = INB ? 2 : 4;
+    constexpr uint32_t OES = OUTB ? 2 : 4;
+    constexpr int WIN = V * IES / 4;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t n_vec = a->n_vec;
+    u32x4 x[P][U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i0 = t0 + (u * kBlock + tid) * V;
+        ok[u] = FULL || (i0 < n_vec);
+        if (ok[u]) {
+#pragma unroll
+            for (int r = 0; r < P; ++r) x[r][u] = load_lane<WIN>(static_cast<const char*>(a->in[r]) + i0 * IES);
+        } else {
+#pragma unroll
+            for (int r = 0; r < P; ++r) x[r][u] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float acc[U][V];
+    tree_fold<P, INB, U, V>(x, a->parents, acc);
+    const bool mean = a->mean != 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        const uint32_t i0 = t0 + (u * kBlock + tid) * V;
+        float g[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) g[e] = mean ? mean_of<P>(acc[u][e]) : acc[u][e];
+        if constexpr (OUTB && V == 8) {
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
+#pragma unroll
+            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+        } else if constexpr (OUTB) {
+            u32x2 o;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
+#pragma unroll
+            for (int r = 0; r < P; ++r) store8(static_cast<char*>(a->out[r]) + i0 * OES, o);
+        } else {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
+#pragma unroll
+            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+        }
+    }
+}
+
+template <int P, bool INB, bool OUTB>
+__global__ __launch_bounds__(kBlock) void tree_reduce_kernel(RingArgs) {
+    constexpr uint32_t TILE =
+        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(INB, OUTB, false);
+    const KArgs a = kernel_args();
+    const uint32_t t0 = blockIdx.x * TILE;
+    const uint32_t n_vec = a->n_vec;
+    if (t0 + TILE <= n_vec) {
+        tree_tile<P, INB, OUTB, true>(a, t0);
+    } else if (t0 < n_vec) {
+        tree_tile<P, INB, OUTB, false>(a, t0);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        const uint32_t i = n_vec + threadIdx.x;
+        if (i < a->n) tree_element<P, INB, OUTB>(a, i);
+    }
+}
+
+template <bool INB, bool OUTB>
+const void* tree_kernel_for(int P) {
+    switch (P) {
+#define DDP_CASE(p) \
+    case p: return reinterpret_cast<const void*>(&tree_reduce_kernel<p, INB, OUTB>);
+        DDP_CASE(1) DDP_CASE(2) DDP_CASE(3) DDP_CASE(4)
+        DDP_CASE(5) DDP_CASE(6) DDP_CASE(7) DDP_CASE(8)
+        DDP_CASE(9) DDP_CASE(10) DDP_CASE(11) DDP_CASE(12)
+        DDP_CASE(13) DDP_CASE(14) DDP_CASE(15) DDP_CASE(16)
+#undef DDP_CASE
+        default:
+            return nullptr;
+    }
+}
+
 template <bool INB, bool OUTB, bool SGD, bool SCALAR>
 const void* ring_kernel_for(int P) {
     switch (P) {
@@ -593,8 +754,9 @@ const void* ring_kernel_for(int P) {
 }  // namespace rr
 }  // namespace ddp
 
-// Defines ddp::ring_kernel_<name>(P, sgd, scalar) and
-// ddp::ring_rs_kernel_<name>(P, scalar) for one type pair.
+// Defines ddp::ring_kernel_<name>(P, sgd, scalar),
+// ddp::ring_rs_kernel_<name>(P, scalar) and ddp::tree_kernel_<name>(P) for
+// one type pair.
 #define DDP_RING_TYPE_PAIR(name, INB, OUTB)                                              \
     namespace ddp {                                                                      \
     const void* ring_kernel_##name(int P, int sgd, int scalar) {                         \
@@ -607,4 +769,5 @@ const void* ring_kernel_for(int P) {
         return scalar ? rr::ring_rs_kernel_for<INB, OUTB, true>(P)                       \
                       : rr::ring_rs_kernel_for<INB, OUTB, false>(P);                     \
     }                                                                                    \
+    const void* tree_kernel_##name(int P) { return rr::tree_kernel_for<INB, OUTB>(P); }  \
     }

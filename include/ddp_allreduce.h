@@ -290,6 +290,31 @@ int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking,
                             void* const* rank_buf, ddp_dtype dtype, int64_t n,
                             uint64_t* sent_dev, void* stream);
 
+/*
+ * allreduce_tree_emulated -- the all-reduce along a tree instead of a ring.
+ *
+ * The Tree strategy arranges the peers in a b-tree that reduces in parallel
+ * (O(log_b N)); the Centralized strategy sends every tensor to a root that
+ * aggregates and broadcasts the result (Burn collective blog, "Methods");
+ * both are a reduce followed by a broadcast (same page, "Local ring
+ * downfall").  The tree is the b-ary heap over the ranks: rank 0 is the root
+ * and the children of rank i are ranks b*i+1 ... b*i+b.  Every rank adds its
+ * children's partial sums to its own value in increasing child order, after
+ * all of them have arrived; the root applies Mean; every rank receives the
+ * root's value.  Partial sums are float32.  branching >= P-1 makes every
+ * rank a child of the root: the Centralized strategy, whose additions run
+ * in rank order (the same order as allreduce_ring_emulated with one chunk).
+ *
+ *   branching  b >= 1 (b = 1 is a chain)
+ *   other arguments, layout, ownership and errors as for
+ *   allreduce_ring_emulated (there is no chunking: the tree's order is the
+ *   same for every element).
+ */
+int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching,
+                            const void* const* rank_in, ddp_dtype in_dtype,
+                            void* const* rank_out, ddp_dtype out_dtype,
+                            int64_t n, void* stream);
+
 /* Message describing the calling thread's most recent non-OK status
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* ddp_last_error(void);

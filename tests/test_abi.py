@@ -263,3 +263,16 @@ def test_stepwise_errors():
                                        None) == N.DDP_E_OVERLAP
     assert lib.allreduce_ring_stepwise(3, 2, 2, bufs, 0, 16, None, None) == N.DDP_E_ARG
     assert lib.allreduce_ring_stepwise(0, 2, 2, bufs, 0, 0, None, None) == N.DDP_OK
+
+
+def test_tree_errors():
+    lib = N.lib()
+    ins = N.pointer_array([A, A + MB])
+    outs = N.pointer_array([A + 64 * MB, A + 65 * MB])
+    assert lib.allreduce_tree_emulated(0, 2, 0, ins, 0, outs, 0, 16, None) == N.DDP_E_ARG
+    assert lib.allreduce_tree_emulated(0, 17, 2, ins, 0, outs, 0, 16, None) == N.DDP_E_ARG
+    assert lib.allreduce_tree_emulated(0, 2, 2, ins, 0, N.pointer_array([A + 8, A + MB]), 0, 16,
+                                       None) == N.DDP_E_ALIGN
+    assert lib.allreduce_tree_emulated(0, 2, 2, ins, 0, N.pointer_array([A + 16, A + MB]), 0,
+                                       1024, None) == N.DDP_E_OVERLAP
+    assert lib.allreduce_tree_emulated(1, 2, 5, ins, 0, outs, 1, 0, None) == N.DDP_OK
