@@ -39,6 +39,11 @@ class Segment(ctypes.Structure):
                 ("len", ctypes.c_int64)]
 
 
+class TensorTiles(ctypes.Structure):
+    """ddp_tensor_tiles: a tensor's element count and first tile."""
+    _fields_ = [("numel", ctypes.c_int64), ("first_tile", ctypes.c_int64)]
+
+
 _c_void_pp = ctypes.POINTER(ctypes.c_void_p)
 _SIGNATURES = {
     "ddp_bucket_plan": (ctypes.c_int, [
@@ -70,6 +75,14 @@ _SIGNATURES = {
     "allreduce_tree_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
         ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),
+    "ddp_multi_plan": (ctypes.c_int, [
+        ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+        ctypes.POINTER(TensorTiles), ctypes.POINTER(ctypes.c_int64),
+        ctypes.POINTER(ctypes.c_int64)]),
+    "allreduce_multi_ring_emulated": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_void_p]),
     "ddp_last_error": (ctypes.c_char_p, []),
 }
 

@@ -122,6 +122,31 @@ def allreduce_tree_emulated(op, P, branching, rank_in, in_dtype, rank_out, out_d
                                            stream))
 
 
+TILES_DTYPE = np.dtype([("numel", "<i8"), ("first_tile", "<i8")])
+
+
+def ddp_multi_plan(numels, P, in_dtype, out_dtype):
+    """Tile plan of a multi-tensor all-reduce (host only).  Returns (tiles,
+    total_tiles, tile_elems); tiles is a numpy structured array in the C
+    layout."""
+    numels = np.ascontiguousarray(numels, dtype=np.int64)
+    tiles = np.zeros(numels.size, dtype=TILES_DTYPE)
+    total = ctypes.c_int64(0)
+    tile = ctypes.c_int64(0)
+    _check(N.lib().ddp_multi_plan(numels.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                  numels.size, P, in_dtype, out_dtype,
+                                  tiles.ctypes.data_as(ctypes.POINTER(N.TensorTiles)),
+                                  ctypes.byref(total), ctypes.byref(tile)))
+    return tiles, total.value, tile.value
+
+
+def allreduce_multi_ring_emulated(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems,
+                                  in_ptrs_dev, in_dtype, out_ptrs_dev, out_dtype, stream=None):
+    _check(N.lib().allreduce_multi_ring_emulated(_op(op), P, chunking, n_tensors, tiles_dev,
+                                                 total_tiles, tile_elems, in_ptrs_dev, in_dtype,
+                                                 out_ptrs_dev, out_dtype, stream))
+
+
 # --------------------------------------------------------- torch level ----
 
 def torch_dtype_code(dtype):
@@ -237,6 +262,71 @@ def allreduce_stepwise(tensors, op="sum", chunking=None, sent=None):
                             tensors[0].numel(), sent.data_ptr() if sent is not None else None,
                             current_stream(tensors[0].device))
     return tensors
+
+
+class MultiAllReduce:
+    """All-reduce many tensors per rank in one launch (the per-parameter
+    small-message path).  Plans once for a list of shapes; ``__call__`` takes
+    P lists of T tensors (rank-major) and optional P output lists."""
+
+    def __init__(self, shapes, P, dtype, out_dtype=None, device="cuda"):
+        import torch
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.P = P
+        self.dtype = dtype
+        self.out_dtype = out_dtype or dtype
+        self.device = torch.device(device)
+        numels = [int(np.prod(s, dtype=np.int64)) for s in self.shapes]
+        self.tiles, self.total_tiles, self.tile_elems = ddp_multi_plan(
+            numels, P, torch_dtype_code(dtype), torch_dtype_code(self.out_dtype))
+        self.tiles_dev = torch.from_numpy(self.tiles.view(np.uint8).copy()).to(self.device)
+
+    def _table(self, lists, dtype):
+        import torch
+        if len(lists) != self.P:
+            raise ValueError(f"need {self.P} rank lists")
+        ptrs = []
+        for ts in lists:
+            if len(ts) != len(self.shapes):
+                raise ValueError("every rank needs one tensor per planned shape")
+            for x, s in zip(ts, self.shapes):
+                if tuple(x.shape) != s or x.dtype != dtype or not x.is_contiguous() \
+                        or x.device != self.device:
+                    raise ValueError("tensor does not match the plan")
+                ptrs.append(x.data_ptr())
+        return torch.tensor(ptrs, dtype=torch.int64).to(self.device)
+
+    def bind(self, rank_lists, out=None):
+        """Validate the tensors once and upload their pointer tables; returns
+        a launcher ``run(op="sum", chunking=None)`` that enqueues the whole
+        multi-tensor all-reduce with one call.  The tensors (and ``out``,
+        default: new tensors) must stay alive while the launcher is used."""
+        import torch
+        if out is None:
+            out = [[torch.empty(s, dtype=self.out_dtype, device=self.device) for s in self.shapes]
+                   for _ in range(self.P)]
+        tin = self._table(rank_lists, self.dtype)
+        tout = self._table(out, self.out_dtype)
+        args = (self.P, len(self.shapes), self.tiles_dev.data_ptr(), self.total_tiles,
+                self.tile_elems, tin.data_ptr(), torch_dtype_code(self.dtype), tout.data_ptr(),
+                torch_dtype_code(self.out_dtype))
+        stream = current_stream(self.device)
+
+        def run(op="sum", chunking=None):
+            P, T, tiles, total, tile, pin, dtin, pout, dtout = args
+            allreduce_multi_ring_emulated(op, P, chunking or P, T, tiles, total, tile, pin, dtin,
+                                          pout, dtout, stream)
+            return out
+
+        run.tables = (tin, tout)      # kept alive with the launcher
+        run.out = out
+        return run
+
+    def __call__(self, rank_lists, op="sum", chunking=None, out=None):
+        """bind() and launch once."""
+        run = self.bind(rank_lists, out)
+        self._last = run              # the tables must outlive the launch
+        return run(op, chunking)
 
 
 def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):

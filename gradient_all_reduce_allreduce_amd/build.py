@@ -23,7 +23,7 @@ PATTERNS = os.path.join(PKG, "hbm_patterns")     # HBM access-pattern benchmark
 SOURCES = ["api.cpp", "ring_reduce.hip", "ring_reduce_f32_f32.hip",
            "ring_reduce_f32_bf16.hip", "ring_reduce_bf16_f32.hip",
            "ring_reduce_bf16_bf16.hip", "ring_allgather.hip", "ring_step.hip",
-           "bucket_copy.hip"]
+           "multi_tensor.hip", "bucket_copy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

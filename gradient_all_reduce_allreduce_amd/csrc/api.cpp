@@ -469,4 +469,63 @@ int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching, cons
     return ok();
 }
 
+int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtype in_dtype,
+                   ddp_dtype out_dtype, ddp_tensor_tiles* tiles, int64_t* total_tiles, int64_t* tile_elems) {
+    int s = check_ranks(P);
+    if (s) return s;
+    if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
+    if (numels == nullptr || tiles == nullptr || total_tiles == nullptr || tile_elems == nullptr)
+        return fail(DDP_E_ARG, "NULL pointer argument");
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown dtype");
+    const int64_t tile = ddp::multi_tile_elems(P, in_dtype == DDP_BF16, out_dtype == DDP_BF16);
+    int64_t next = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        if (numels[t] < 0) return fail(DDP_E_ARG, "numels[%d] is negative", t);
+        if (numels[t] > (int64_t(1) << 29))
+            return fail(DDP_E_UNSUPPORTED, "numels[%d] = %lld is over 2^29 elements", t,
+                        static_cast<long long>(numels[t]));
+        tiles[t].numel = numels[t];
+        tiles[t].first_tile = next;
+        next += (numels[t] + tile - 1) / tile;
+    }
+    *total_tiles = next;
+    *tile_elems = tile;
+    return ok();
+}
+
+int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
+                                  const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
+                                  const void* const* in_ptrs_dev, ddp_dtype in_dtype, void* const* out_ptrs_dev,
+                                  ddp_dtype out_dtype, void* stream) {
+    if (op != DDP_SUM && op != DDP_MEAN) return fail(DDP_E_ARG, "unknown reduce op %d", op);
+    int s = check_ranks(P);
+    if (s) return s;
+    if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
+    if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown dtype");
+    if (total_tiles < 0 || total_tiles > INT32_MAX) return fail(DDP_E_ARG, "total_tiles out of range");
+    if (tiles_dev == nullptr || in_ptrs_dev == nullptr || out_ptrs_dev == nullptr)
+        return fail(DDP_E_ARG, "NULL table");
+    if (tile_elems != ddp::multi_tile_elems(P, in_dtype == DDP_BF16, out_dtype == DDP_BF16))
+        return fail(DDP_E_PLAN, "tile_elems does not match this P and these dtypes");
+    if (total_tiles == 0) return ok();
+
+    ddp::MultiLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.T = n_tensors;
+    l.tiles = tiles_dev;
+    l.in = in_ptrs_dev;
+    l.out = out_ptrs_dev;
+    l.total_tiles = total_tiles;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_multi_ring(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
 }  // extern "C"

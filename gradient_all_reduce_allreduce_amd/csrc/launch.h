@@ -79,6 +79,24 @@ struct StepLaunch {
 
 int launch_ring_stepwise(const StepLaunch& l, const char** msg);
 
+// Many tensors in one launch (multi_tensor.hip).
+struct MultiLaunch {
+    int P;
+    int chunking;
+    int op;
+    int in_bf16;
+    int out_bf16;
+    int32_t T;
+    const ddp_tensor_tiles* tiles;
+    const void* const* in;
+    void* const* out;
+    int64_t total_tiles;
+    void* stream;
+};
+
+int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16);
+int launch_multi_ring(const MultiLaunch& l, const char** msg);
+
 struct CopyLaunch {
     int P;
     int elem_bytes;    // 2 or 4

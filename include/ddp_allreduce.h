@@ -87,6 +87,13 @@ typedef struct ddp_segment {
     int64_t len;
 } ddp_segment;
 
+/* One tensor of a multi-tensor all-reduce: its element count and the index
+ * of its first tile in the launch (from ddp_multi_plan). */
+typedef struct ddp_tensor_tiles {
+    int64_t numel;
+    int64_t first_tile;
+} ddp_tensor_tiles;
+
 /*
  * ddp_bucket_plan -- host only, no device work.
  *
@@ -314,6 +321,55 @@ int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching,
                             const void* const* rank_in, ddp_dtype in_dtype,
                             void* const* rank_out, ddp_dtype out_dtype,
                             int64_t n, void* stream);
+
+/*
+ * ddp_multi_plan -- host only: lay out the tiles of a multi-tensor
+ * all-reduce.
+ *
+ * Without buckets every parameter's gradient is all-reduced on its own
+ * (CS336 Lecture 8, "Data Parallelism (DDP)"), and small collectives use
+ * the hardware badly ("Distributed Training", "Communication costs"); the
+ * multi-tensor call below reduces all of them in one launch.  This plan
+ * gives tensor t a run of tiles starting at tiles[t].first_tile.
+ *
+ *   numels       host array [n_tensors], each 0 .. 2^29 elements
+ *   P, in_dtype, out_dtype   as for the all-reduce (they set the tile size)
+ *   tiles        host array [n_tensors] to receive the plan
+ *   total_tiles  out: tiles of all tensors (the launch's workgroups)
+ *   tile_elems   out: elements per tile (pass it back to the all-reduce)
+ * Errors: DDP_E_ARG (bad counts, pointers, P or dtypes), DDP_E_UNSUPPORTED
+ * (a tensor over 2^29 elements: use the single-tensor call).
+ */
+int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P,
+                   ddp_dtype in_dtype, ddp_dtype out_dtype, ddp_tensor_tiles* tiles,
+                   int64_t* total_tiles, int64_t* tile_elems);
+
+/*
+ * allreduce_multi_ring_emulated -- n_tensors independent all-reduces in one
+ * launch; tensor t gives, bit for bit, what allreduce_ring_emulated gives
+ * for it alone (same P, op and chunking; its own chunk length
+ * ceil(numel_t / C)).
+ *
+ *   tiles_dev    DEVICE array [n_tensors]: the plan of ddp_multi_plan for
+ *                these tensors, P and dtypes (the library does not read it
+ *                on the host; any other table is undefined behaviour)
+ *   total_tiles, tile_elems   the values ddp_multi_plan returned
+ *                (tile_elems is checked against this call's tile size)
+ *   in_ptrs_dev  DEVICE array [P * n_tensors] of device pointers,
+ *                rank-major (entry r * n_tensors + t = rank r's tensor t)
+ *   out_ptrs_dev DEVICE array [P * n_tensors] of device pointers, same
+ *                layout; an output may be its input (in place)
+ *   Tensors need only the alignment of their element type; 16-byte
+ *   aligned ones move as 16-byte vectors.  Buffers of different tensors or
+ *   ranks must not overlap (not checked: the tables live on the device).
+ * Errors: DDP_E_ARG, DDP_E_PLAN (tile_elems mismatch), DDP_E_HIP.
+ */
+int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
+                                  int32_t n_tensors, const ddp_tensor_tiles* tiles_dev,
+                                  int64_t total_tiles, int64_t tile_elems,
+                                  const void* const* in_ptrs_dev, ddp_dtype in_dtype,
+                                  void* const* out_ptrs_dev, ddp_dtype out_dtype,
+                                  void* stream);
 
 /* Message describing the calling thread's most recent non-OK status
  * ("" if none).  The pointer stays valid until the thread's next call. */

@@ -276,3 +276,26 @@ def test_tree_errors():
     assert lib.allreduce_tree_emulated(0, 2, 2, ins, 0, N.pointer_array([A + 16, A + MB]), 0,
                                        1024, None) == N.DDP_E_OVERLAP
     assert lib.allreduce_tree_emulated(1, 2, 5, ins, 0, outs, 1, 0, None) == N.DDP_OK
+
+
+def test_multi_plan():
+    tiles, total, tile = ddp.ddp_multi_plan([0, 1, 2048, 2049, 5], 8, ddp.F32, ddp.F32)
+    assert tile == 256 * 2 * 4
+    assert tiles["numel"].tolist() == [0, 1, 2048, 2049, 5]
+    assert tiles["first_tile"].tolist() == [0, 0, 1, 2, 4]
+    assert total == 5
+    _, _, tile_b = ddp.ddp_multi_plan([10], 8, ddp.BF16, ddp.BF16)
+    assert tile_b == 256 * 2 * 8
+    lib = N.lib()
+    with pytest.raises(DdpError) as e:
+        ddp.ddp_multi_plan([(1 << 29) + 1], 4, ddp.F32, ddp.F32)
+    assert e.value.status == N.DDP_E_UNSUPPORTED
+    with pytest.raises(DdpError):
+        ddp.ddp_multi_plan([-1], 4, ddp.F32, ddp.F32)
+    # a tile size from another plan is rejected before any launch
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 1, 4096, A, 0, A, 0,
+                                             None) == N.DDP_E_PLAN
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, None, 1, 2048, A, 0, A, 0,
+                                             None) == N.DDP_E_ARG
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 0, 2048, A, 0, A, 0,
+                                             None) == N.DDP_OK
