@@ -93,12 +93,162 @@ def cpu_baseline(grads_host, bucket_lens, P, C, min_seconds=10.0, max_passes=20)
     }
 
 
+def _time(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def run_suite(steps, warmup):
+    """Every entry point at the shape of its workload; one JSON line each.
+    Rates are algorithmic bytes (what the method must read and write) over
+    time, with the inputs resident in HBM."""
+    import torch
+
+    import gradient_all_reduce_allreduce_amd as ddp
+    import workloads
+
+    dev = torch.device("cuda:0")
+
+    def report(name, ms, nbytes, **extra):
+        line = {"suite": name, "ms": round(ms, 4), "algorithmic_bytes": int(nbytes),
+                "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        line.update(extra)
+        print(json.dumps(line), flush=True)
+
+    def arena_sets(plan, P, n_sets=2, std=0.01, out_dtype=None):
+        sets = []
+        for s_ in range(n_sets):
+            g = plan.alloc_arena(P)
+            for r in range(P):
+                workloads.torch_normal_(g[r], std, seed=77 * s_ + r)
+            o = torch.empty(g.shape, dtype=out_dtype or g.dtype, device=dev)
+            E = plan.bucket_elems
+            sets.append([([plan.bucket_view(g[r], k) for r in range(P)],
+                          [o[r, k * E:k * E + plan.bucket_len(k)] for r in range(P)])
+                         for k in range(plan.n_buckets)])
+        return sets
+
+    # config 2, bucket views (the headline step), the multi-tensor launch
+    # over the 161 separate per-parameter tensors, and pack/unpack
+    P = 8
+    shapes = workloads.model_shapes("resnet50")
+    plan = ddp.GradBucketer(shapes, torch.float32, 25 << 20, device=dev)
+    nbytes = P * plan.total * 8
+    sets = arena_sets(plan, P)
+    report("cfg2 resnet50 p8 f32 mean, bucket views",
+           _time(lambda i: [ddp.allreduce(a, "mean", P, out=o) for a, o in sets[i % 2]], steps, warmup),
+           nbytes)
+    report("cfg2 resnet50 p8 f32 mean, tree b=2 on bucket views",
+           _time(lambda i: [ddp.allreduce_tree(a, "mean", 2, out=o) for a, o in sets[i % 2]], steps, warmup),
+           nbytes)
+    report("cfg2 resnet50 p8 f32 mean, stepwise ring (2(P-1) launches per bucket, in place)",
+           _time(lambda i: [ddp.allreduce_stepwise(o, "mean", P) for _, o in sets[i % 2]],
+                 max(2, steps // 10), 2), nbytes, note="moves 35n floats per bucket against 16n")
+    del sets
+    tensors = [[torch.empty(s_, device=dev).normal_(0, 0.01) for s_ in shapes] for _ in range(P)]
+    outs = [[torch.empty(s_, device=dev) for s_ in shapes] for _ in range(P)]
+    run = ddp.MultiAllReduce(shapes, P, torch.float32, device=dev).bind(tensors, outs)
+    report("cfg2 resnet50 p8 f32 mean, 161 separate tensors, one multi-tensor launch",
+           _time(lambda i: run("mean"), steps, warmup), nbytes)
+    table = plan.pointer_table(tensors)
+    bufs = plan.alloc_buckets(P)
+
+    def packed_step(i):
+        for k in range(plan.n_buckets):
+            n = plan.bucket_len(k)
+            plan.pack(table, k, bufs)
+            ddp.allreduce([x[:n] for x in bufs], "mean", P, out=[x[:n] for x in bufs])
+            plan.unpack(table, k, bufs)
+    ms = _time(packed_step, steps, warmup)
+    report("cfg2 resnet50 p8 f32 mean, pack -> all-reduce -> unpack", ms, nbytes,
+           with_copies_gbps=round(3 * nbytes / (ms * 1e-3) / 1e9, 1),
+           note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
+    del tensors, outs, run, table, bufs
+    torch.cuda.empty_cache()
+
+    # config 3: ViT-B/16 bf16 gradients, Mean, fused SGD-momentum
+    plan = ddp.GradBucketer(workloads.model_shapes("vit_b16"), torch.bfloat16, 25 << 20, device=dev)
+    sets = arena_sets(plan, P, std=1e-3)
+    w = torch.empty(plan.total, device=dev).normal_(0, 0.02)
+    v = torch.zeros(plan.total, device=dev)
+    E = plan.bucket_elems
+
+    def sgd_step(i, with_out):
+        for k, (a, o) in enumerate(sets[i % 2]):
+            lo, n = k * E, plan.bucket_len(k)
+            ddp.allreduce_sgd(a, w[lo:lo + n], v[lo:lo + n], 1e-3, 0.9, "mean", P,
+                              out=o if with_out else None)
+    report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum (w, v fp32), no gradient output",
+           _time(lambda i: sgd_step(i, False), steps, warmup), P * plan.total * 2 + 16 * plan.total)
+    report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum, gradients also written (bf16)",
+           _time(lambda i: sgd_step(i, True), steps, warmup), P * plan.total * 4 + 16 * plan.total)
+    del sets, w, v
+    torch.cuda.empty_cache()
+
+    # config 4: 2,000 ragged fp32 tensors, P=4, Sum, 25 MiB buckets
+    P4 = 4
+    sizes = workloads.ragged_sizes()
+    shapes4 = [(n,) for n in sizes]
+    plan = ddp.GradBucketer(shapes4, torch.float32, 25 << 20, device=dev)
+    tensors = [[torch.empty(n, device=dev).uniform_(-1, 1) for n in sizes] for _ in range(P4)]
+    table = plan.pointer_table(tensors)
+    bufs = plan.alloc_buckets(P4)
+    nbytes4 = P4 * plan.total * 8
+
+    def ragged_step(i):
+        for k in range(plan.n_buckets):
+            n = plan.bucket_len(k)
+            plan.pack(table, k, bufs)
+            ddp.allreduce([x[:n] for x in bufs], "sum", P4, out=[x[:n] for x in bufs])
+            plan.unpack(table, k, bufs)
+    ms = _time(ragged_step, max(2, steps // 20), 1)
+    report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, pack -> all-reduce -> unpack "
+           f"({plan.n_buckets} buckets)", ms, nbytes4,
+           with_copies_gbps=round(3 * nbytes4 / (ms * 1e-3) / 1e9, 1))
+    run = ddp.MultiAllReduce(shapes4, P4, torch.float32, device=dev).bind(tensors, tensors)
+    report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, one multi-tensor launch, in place",
+           _time(lambda i: run("sum"), max(2, steps // 20), 1), nbytes4)
+    del tensors, table, bufs, run
+    torch.cuda.empty_cache()
+
+    # config 5: 2B-parameter transformer, bf16 in, fp32 out, 100 MiB buckets
+    plan = ddp.GradBucketer(workloads.model_shapes("transformer_2b"), torch.bfloat16, 100 << 20,
+                            device=dev)
+    g = plan.alloc_arena(P)
+    for r in range(P):
+        workloads.torch_normal_(g[r], 1e-4, seed=500 + r)
+    o = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    E = plan.bucket_elems
+    views = [([plan.bucket_view(g[r], k) for r in range(P)],
+              [o[r, k * E:k * E + plan.bucket_len(k)] for r in range(P)]) for k in range(plan.n_buckets)]
+    report(f"cfg5 transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets)",
+           _time(lambda i: [ddp.allreduce(a, "mean", P, out=b) for a, b in views], 3, 1),
+           P * plan.total * 6)
+    del g, o, views
+    torch.cuda.empty_cache()
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the headline line, time every entry point at the shape "
+                         "of its workload (one JSON line each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (a kernel of known "
                          "traffic, to scale the memory counters of a profiler run)")
@@ -123,6 +273,9 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": a.numel() * 4,
                           "bytes_written": b.numel() * 4, "launches": 10}))
         return 0
+
+    if args.suite:
+        return run_suite(args.steps, args.warmup)
 
     cfg = workloads.CONFIGS["cfg2"]
     P, C = cfg["P"], cfg["chunking"]

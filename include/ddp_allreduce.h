@@ -186,6 +186,9 @@ int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
  *             match (in-place all-reduce)
  *   out_dtype DDP_F32 or DDP_BF16
  *   n         elements per rank, >= 0 (0: nothing is launched)
+ * One launch per 2^29 elements; for bf16 inputs with float32 outputs the
+ * call runs as a reduce-scatter pass followed by an all-gather pass (see
+ * below), which is faster for that shape and gives the same bits.
  * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
  */
 int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
