@@ -14,7 +14,9 @@
 //             = 1.6 GiB, more than the last-level cache), with the 16
 //             buffers (a) separately allocated, (b) packed back to back in
 //             one allocation, (c) in one allocation with an extra 4 KiB
-//             between neighbours.
+//             between neighbours; each with 2 vectors per lane and a common
+//             store order, and with 1 vector per lane and the store order
+//             rotated per wave.
 // Every kernel uses one tile of 256 lanes x U vectors per workgroup and as
 // many workgroups as tiles.  Output: one line per measurement, GB/s of bytes
 // moved (read + written).
@@ -81,6 +83,34 @@ struct Streams8 {
     const u32x4* in[8];
     u32x4* out[8];
 };
+
+// The same pattern with one 16-byte vector per lane and the order of the 8
+// output stores rotated by the wave index (each wave starts at another
+// output stream).
+__global__ __launch_bounds__(kBlock) void red8_rotated_kernel(Streams8 p, uint32_t nvec) {
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i >= nvec) return;
+    u32x4 x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(p.in[r] + i);
+    u32x4 s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float acc = __uint_as_float(x[0][k]);
+#pragma unroll
+        for (int r = 1; r < 8; ++r) acc = acc + __uint_as_float(x[r][k]);
+        s[k] = __float_as_uint(acc);
+    }
+    const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * (kBlock / 64) + threadIdx.x / 64) & 7));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int want = (q + rot) & 7;
+        u32x4* o = p.out[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) o = want == j ? p.out[j] : o;
+        __builtin_nontemporal_store(s, o + i);
+    }
+}
 
 __global__ __launch_bounds__(kBlock) void red8_kernel(Streams8 p, uint32_t nvec) {
     const uint32_t t = blockIdx.x * (kBlock * kU);
@@ -183,6 +213,9 @@ int main() {
         ms = time_ms([&](int i) { red8_kernel<<<grid_for(rv), kBlock>>>(ps[i % sets], rv); });
         std::printf("red8  %-38s: %7.0f GB/s (%.1f us per 25 MiB x 16 streams)\n", names[layout],
                     16.0 * rb / ms / 1e6, ms * 1e3);
+        ms = time_ms([&](int i) { red8_rotated_kernel<<<(rv + kBlock - 1) / kBlock, kBlock>>>(ps[i % sets], rv); });
+        std::printf("red8  %-38s: %7.0f GB/s (%.1f us) one vector per lane, rotated stores\n",
+                    names[layout], 16.0 * rb / ms / 1e6, ms * 1e3);
     }
     for (char* p : separate) CK(hipFree(p));
     CK(hipFree(arena));

@@ -37,9 +37,11 @@ struct RingLaunch {
 // Returns 0 on success, else a HIP error code; *msg names the failing call.
 int launch_ring_reduce(const RingLaunch& l, const char** msg);
 
-// Vectors of each rank a lane keeps in flight per tile: P * U loads.
+// Vectors of each rank a lane keeps in flight per tile: P * U loads.  One
+// vector per lane (a 1,024- or 2,048-element tile of 256 lanes) measured
+// fastest from P = 3 up; P <= 2 keeps more loads in flight with U = 4.
 constexpr int ring_vectors_per_lane(int P) {
-    return P <= 2 ? 4 : (P <= 8 ? 2 : 1);
+    return P <= 2 ? 4 : 1;
 }
 
 // Elements per lane vector: 8 for bf16 -> bf16 (16-byte loads and stores),

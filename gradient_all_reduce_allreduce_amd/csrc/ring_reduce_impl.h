@@ -161,6 +161,25 @@ __device__ __forceinline__ int rank_at(int s, int k, int P) {
     return r >= P ? r - P : r;
 }
 
+// Every output rank receives the same value, so the order of the P stores
+// is free.  Each wave starts at a different rank (its wave index mod P):
+// the waves in flight then write to all P output streams at once instead
+// of all to the same one (measured about 2% faster than a common order).
+__device__ __forceinline__ int store_rotation(int P) {
+    const int wave = static_cast<int>(blockIdx.x * (kBlock / 64) + threadIdx.x / 64);
+    return __builtin_amdgcn_readfirstlane(wave % P);
+}
+
+// Output pointer of rank (rot + q) mod P, chosen with scalar selects.
+template <int P>
+__device__ __forceinline__ char* rotated_out(KArgs a, int rot, int q) {
+    const int want = rank_at(rot, q, P);
+    char* p = static_cast<char*>(a->out[0]);
+#pragma unroll
+    for (int j = 1; j < P; ++j) p = want == j ? static_cast<char*>(a->out[j]) : p;
+    return p;
+}
+
 // ---- one element per lane: tails and chunks shorter than a tile ----------
 
 template <int P, bool INB, bool OUTB, bool SGD>
@@ -275,6 +294,7 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
     }
 
     const bool mean = a->mean != 0;
+    const int rot = store_rotation(P);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -299,19 +319,19 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int r = 0; r < P; ++r) store8(static_cast<char*>(a->out[r]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store8(rotated_out<P>(a, rot, q) + i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
         }
     }
 }
@@ -672,6 +692,7 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     float acc[U][V];
     tree_fold<P, INB, U, V>(x, a->parents, acc);
     const bool mean = a->mean != 0;
+    const int rot = store_rotation(P);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -684,19 +705,19 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int r = 0; r < P; ++r) store8(static_cast<char*>(a->out[r]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store8(rotated_out<P>(a, rot, q) + i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int r = 0; r < P; ++r) store16(static_cast<char*>(a->out[r]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
         }
     }
 }

@@ -279,13 +279,15 @@ def test_tree_errors():
 
 
 def test_multi_plan():
-    tiles, total, tile = ddp.ddp_multi_plan([0, 1, 2048, 2049, 5], 8, ddp.F32, ddp.F32)
-    assert tile == 256 * 2 * 4
-    assert tiles["numel"].tolist() == [0, 1, 2048, 2049, 5]
+    _, _, tile = ddp.ddp_multi_plan([1], 8, ddp.F32, ddp.F32)
+    sizes = [0, 1, tile, tile + 1, 5]
+    tiles, total, _ = ddp.ddp_multi_plan(sizes, 8, ddp.F32, ddp.F32)
+    assert tile % 1024 == 0                  # whole 256-lane rows of 4 floats
+    assert tiles["numel"].tolist() == sizes
     assert tiles["first_tile"].tolist() == [0, 0, 1, 2, 4]
     assert total == 5
     _, _, tile_b = ddp.ddp_multi_plan([10], 8, ddp.BF16, ddp.BF16)
-    assert tile_b == 256 * 2 * 8
+    assert tile_b == 2 * tile                # bf16 -> bf16 moves 8 elements per lane
     lib = N.lib()
     with pytest.raises(DdpError) as e:
         ddp.ddp_multi_plan([(1 << 29) + 1], 4, ddp.F32, ddp.F32)
@@ -293,9 +295,9 @@ def test_multi_plan():
     with pytest.raises(DdpError):
         ddp.ddp_multi_plan([-1], 4, ddp.F32, ddp.F32)
     # a tile size from another plan is rejected before any launch
-    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 1, 4096, A, 0, A, 0,
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 1, tile + 4, A, 0, A, 0,
                                              None) == N.DDP_E_PLAN
-    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, None, 1, 2048, A, 0, A, 0,
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, None, 1, tile, A, 0, A, 0,
                                              None) == N.DDP_E_ARG
-    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 0, 2048, A, 0, A, 0,
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 0, tile, A, 0, A, 0,
                                              None) == N.DDP_OK
