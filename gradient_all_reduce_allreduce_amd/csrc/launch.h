@@ -39,9 +39,11 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg);
 
 // Vectors of each rank a lane keeps in flight per tile: P * U loads.  One
 // vector per lane (a 1,024- or 2,048-element tile of 256 lanes) measured
-// fastest from P = 3 up; P <= 2 keeps more loads in flight with U = 4.
-constexpr int ring_vectors_per_lane(int P) {
-    return P <= 2 ? 4 : 1;
+// fastest from P = 3 up; P <= 2 keeps more loads in flight with U = 4.  The
+// fused optimizer step, whose outputs are the two 16-byte state vectors
+// instead of P gradient copies, keeps two vectors per lane in flight.
+constexpr int ring_vectors_per_lane(int P, bool sgd) {
+    return P <= 2 ? 4 : (sgd ? 2 : 1);
 }
 
 // Elements per lane vector: 8 for bf16 -> bf16 (16-byte loads and stores),

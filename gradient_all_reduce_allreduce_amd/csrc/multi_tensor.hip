@@ -74,7 +74,7 @@ __device__ __forceinline__ void multi_element(KMulti a, int t, uint32_t i, int64
 template <int P, bool INB, bool OUTB>
 __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
 #pragma clang fp contract(off)
-    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int U = ring_vectors_per_lane(P, false);
     constexpr int V = ring_lane_elems(INB, OUTB, false);
     constexpr uint32_t IES = INB ? 2 : 4;
     constexpr uint32_t OES = OUTB ? 2 : 4;
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     float acc[U][V];
     rr::fold<P, 0, INB, U, V>(x, acc);
     const bool mean = a->mean != 0;
+    const int rot = rr::store_rotation(P);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -142,22 +143,25 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = rr::bf16_bits(g[2 * k]) | (rr::bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int r = 0; r < P; ++r)
-                rr::store16(static_cast<char*>(a->out[static_cast<int64_t>(r) * T + t]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q)
+                rr::store16(static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]) +
+                            i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = rr::bf16_bits(g[2 * k]) | (rr::bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int r = 0; r < P; ++r)
-                rr::store8(static_cast<char*>(a->out[static_cast<int64_t>(r) * T + t]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q)
+                rr::store8(static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]) +
+                            i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int r = 0; r < P; ++r)
-                rr::store16(static_cast<char*>(a->out[static_cast<int64_t>(r) * T + t]) + i0 * OES, o);
+            for (int q = 0; q < P; ++q)
+                rr::store16(static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]) +
+                            i0 * OES, o);
         }
     }
 }
@@ -180,7 +184,7 @@ const void* multi_kernel_for(int P) {
 }  // namespace
 
 int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16) {
-    return static_cast<int64_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(in_bf16, out_bf16, false);
+    return static_cast<int64_t>(kBlock) * ring_vectors_per_lane(P, false) * ring_lane_elems(in_bf16, out_bf16, false);
 }
 
 int launch_multi_ring(const MultiLaunch& l, const char** msg) {

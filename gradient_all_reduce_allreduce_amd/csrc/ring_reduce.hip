@@ -43,7 +43,7 @@ void tile_shape(const RingLaunch& l, int64_t* V, int64_t* tile) {
     }
     const bool sgd = l.mode == kAllReduce && l.sgd;
     *V = ring_lane_elems(l.in_bf16 != 0, l.out_bf16 != 0, sgd);
-    *tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P) * *V;
+    *tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P, sgd) * *V;
 }
 
 }  // namespace

@@ -234,7 +234,7 @@ __device__ __forceinline__ u32x4 load_lane(const void* p) {
 template <int P, bool INB, bool OUTB, bool SGD, bool FULL>
 __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
 #pragma clang fp contract(off)
-    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int U = ring_vectors_per_lane(P, SGD);
     constexpr int V = ring_lane_elems(INB, OUTB, SGD);
     constexpr uint32_t IES = INB ? 2 : 4;   // input element bytes
     constexpr uint32_t OES = OUTB ? 2 : 4;  // output element bytes
@@ -342,7 +342,7 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
 template <int P, bool INB, bool OUTB, bool SGD>
 __global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
     constexpr uint32_t TILE =
-        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(INB, OUTB, SGD);
+        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P, SGD) * ring_lane_elems(INB, OUTB, SGD);
     const KArgs a = kernel_args();
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
@@ -420,7 +420,7 @@ __device__ __forceinline__ void ag_element(KArgs a, uint32_t i) {
 template <int P, bool INB, bool OUTB, bool FULL>
 __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
 #pragma clang fp contract(off)
-    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int U = ring_vectors_per_lane(P, false);
     constexpr int V = ring_lane_elems(INB, OUTB, false);
     constexpr uint32_t IES = INB ? 2 : 4;
     constexpr uint32_t OES = OUTB ? 2 : 4;
@@ -504,17 +504,22 @@ __device__ __forceinline__ void ag_tile(KArgs a, uint32_t t0) {
     }
     const int o = rank_at(static_cast<int>(j0 % P), P - 1, P);
     const u32x4 y = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a->out[o]) + i0 * ES);
+    // the P-1 other ranks, starting at a rank that differs from wave to wave
+    const int rot = P > 1 ? store_rotation(P - 1) : 0;
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-        if (r == o) continue;
-        store16(static_cast<char*>(a->out[r]) + i0 * ES, y);
+    for (int q = 0; q < P - 1; ++q) {
+        const int r = rank_at(o, 1 + rank_at(rot, q, P - 1), P);
+        char* p = static_cast<char*>(a->out[0]);
+#pragma unroll
+        for (int j = 1; j < P; ++j) p = r == j ? static_cast<char*>(a->out[j]) : p;
+        store16(p + i0 * ES, y);
     }
 }
 
 template <int P, bool INB, bool OUTB>
 __global__ __launch_bounds__(kBlock) void ring_rs_kernel(RingArgs) {
     constexpr uint32_t TILE =
-        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(INB, OUTB, false);
+        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P, false) * ring_lane_elems(INB, OUTB, false);
     const KArgs a = kernel_args();
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
@@ -668,7 +673,7 @@ __device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
 template <int P, bool INB, bool OUTB, bool FULL>
 __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
 #pragma clang fp contract(off)
-    constexpr int U = ring_vectors_per_lane(P);
+    constexpr int U = ring_vectors_per_lane(P, false);
     constexpr int V = ring_lane_elems(INB, OUTB, false);
     constexpr uint32_t IES = INB ? 2 : 4;
     constexpr uint32_t OES = OUTB ? 2 : 4;
@@ -725,7 +730,7 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
 template <int P, bool INB, bool OUTB>
 __global__ __launch_bounds__(kBlock) void tree_reduce_kernel(RingArgs) {
     constexpr uint32_t TILE =
-        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P) * ring_lane_elems(INB, OUTB, false);
+        static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P, false) * ring_lane_elems(INB, OUTB, false);
     const KArgs a = kernel_args();
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
