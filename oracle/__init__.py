@@ -31,6 +31,7 @@ Modules:
     sgd     -- SGD with momentum on fp32 master weights
     bucket  -- reverse-order gradient bucketing, pack and unpack
     tree    -- the centralized and b-ary tree all-reduce
+    hierarchical -- the two-level (local / global) all-reduce
 
 Parity status of each function is stated in its module header.
 """
@@ -39,6 +40,7 @@ from .ring import (SUM, MEAN, chunk_length, chunk_owners, chunk_start_ranks,
                    chunk_start_ranks_at, ring_all_gather, ring_allreduce,
                    ring_allreduce_sampled, ring_reduce_scatter)
 from .tree import tree_allreduce, tree_parents
+from .hierarchical import hierarchical_allreduce
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .sgd import sgd_momentum
 from .bucket import bucket_plan, pack, unpack
@@ -48,4 +50,5 @@ __all__ = [
     "chunk_start_ranks_at", "ring_all_gather", "ring_allreduce", "ring_reduce_scatter",
     "ring_allreduce_sampled", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "sgd_momentum", "bucket_plan", "pack", "unpack", "tree_allreduce", "tree_parents",
+    "hierarchical_allreduce",
 ]
