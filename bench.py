@@ -154,6 +154,14 @@ def run_suite(steps, warmup):
     report("cfg2 resnet50 p8 f32 mean, tree b=2 on bucket views",
            _time(lambda i: [ddp.allreduce_tree(a, "mean", 2, out=o) for a, o in sets[i % 2]], steps, warmup),
            nbytes)
+    report("cfg2 resnet50 p8 f32 mean, two-level 2 nodes x 4: ring in the nodes, ring over them",
+           _time(lambda i: [ddp.allreduce_hierarchical(a, 2, "mean", ("ring", None), ("ring", None), out=o)
+                            for a, o in sets[i % 2]], steps, warmup),
+           nbytes)
+    report("cfg2 resnet50 p8 f32 mean, two-level 4 nodes x 2: tree in the nodes, ring over them",
+           _time(lambda i: [ddp.allreduce_hierarchical(a, 4, "mean", ("tree", 2), ("ring", None), out=o)
+                            for a, o in sets[i % 2]], steps, warmup),
+           nbytes)
     report("cfg2 resnet50 p8 f32 mean, stepwise ring (2(P-1) launches per bucket, in place)",
            _time(lambda i: [ddp.allreduce_stepwise(o, "mean", P) for _, o in sets[i % 2]],
                  max(2, steps // 10), 2), nbytes, note="moves 35n floats per bucket against 16n")

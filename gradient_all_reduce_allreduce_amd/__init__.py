@@ -12,7 +12,8 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   reducescatter_ring_emulated, allgather_ring_emulated, allreduce_ring_stepwise,
                   allreduce_tree_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
-                  allreduce_sgd, reduce_scatter, all_gather)
+                  allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
+                  allreduce_hierarchical)
 from .bucketer import GradBucketer
 
 __all__ = [
@@ -22,5 +23,6 @@ __all__ = [
     "allreduce_tree_emulated", "ddp_multi_plan", "allreduce_multi_ring_emulated", "allreduce",
     "allreduce_stepwise", "allreduce_tree", "MultiAllReduce",
     "allreduce_sgd",
-    "reduce_scatter", "all_gather", "GradBucketer",
+    "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",
+    "allreduce_hierarchical",
 ]

@@ -75,6 +75,10 @@ _SIGNATURES = {
     "allreduce_tree_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
         ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),
+    "allreduce_hierarchical_emulated": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int,
+        ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_void_p]),
     "ddp_multi_plan": (ctypes.c_int, [
         ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
         ctypes.POINTER(TensorTiles), ctypes.POINTER(ctypes.c_int64),

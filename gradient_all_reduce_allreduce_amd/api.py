@@ -5,10 +5,14 @@ here for device memory, pointers and the current stream.
 Raw entry points (same names and argument order as the C header, pointers as
 Python ints, stream as an int handle or None):
     ddp_bucket_plan, ddp_bucket_pack, ddp_bucket_unpack,
-    allreduce_ring_emulated, allreduce_fused_sgd
+    allreduce_ring_emulated, allreduce_fused_sgd, reducescatter_ring_emulated,
+    allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
+    allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated
 Tensor-level helpers:
     allreduce(tensors, op, chunking, out)            -> list of outputs
     allreduce_sgd(grads, w, v, lr, mu, op, chunking, out)
+    reduce_scatter, all_gather, allreduce_stepwise, allreduce_tree,
+    allreduce_hierarchical, MultiAllReduce
 """
 
 import ctypes
@@ -122,6 +126,25 @@ def allreduce_tree_emulated(op, P, branching, rank_in, in_dtype, rank_out, out_d
                                            stream))
 
 
+STRATEGY_RING = 0
+STRATEGY_TREE = 1
+STRATEGY_CENTRALIZED = 2
+_STRATEGIES = {"ring": STRATEGY_RING, "tree": STRATEGY_TREE, "centralized": STRATEGY_CENTRALIZED}
+
+
+def _strategy(st):
+    return st if isinstance(st, int) else _STRATEGIES[st]
+
+
+def allreduce_hierarchical_emulated(op, nodes, local_ranks, local_strategy, local_param,
+                                    global_strategy, global_param, rank_in, in_dtype, rank_out,
+                                    out_dtype, n, stream=None):
+    _check(N.lib().allreduce_hierarchical_emulated(
+        _op(op), nodes, local_ranks, _strategy(local_strategy), local_param or 0,
+        _strategy(global_strategy), global_param or 0, N.pointer_array(rank_in), in_dtype,
+        N.pointer_array(rank_out), out_dtype, n, stream))
+
+
 TILES_DTYPE = np.dtype([("numel", "<i8"), ("first_tile", "<i8")])
 
 
@@ -215,6 +238,32 @@ def allreduce_tree(tensors, op="sum", branching=2, out=None, out_dtype=None):
                             torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
                             torch_dtype_code(out[0].dtype), tensors[0].numel(),
                             current_stream(tensors[0].device))
+    return out
+
+
+def allreduce_hierarchical(tensors, nodes, op="sum", local=("ring", None), global_=("ring", None),
+                           out=None, out_dtype=None):
+    """Two-level all-reduce: ``nodes`` nodes of len(tensors) / nodes ranks
+    (node-major), each level with its own strategy, given as (name,
+    parameter) with name "ring" (parameter: chunk count, None = the level's
+    member count), "tree" (branching) or "centralized".  Other arguments as
+    for ``allreduce``."""
+    import torch
+    tensors = _rank_tensors(tensors, "allreduce_hierarchical")
+    P = len(tensors)
+    if nodes < 1 or P % nodes:
+        raise ValueError("allreduce_hierarchical: nodes must divide the rank count")
+    if out is None:
+        dt = out_dtype or tensors[0].dtype
+        out = [torch.empty(tensors[0].shape, dtype=dt, device=tensors[0].device) for _ in range(P)]
+    out = _rank_tensors(out, "allreduce_hierarchical out")
+    if len(out) != P or out[0].numel() != tensors[0].numel():
+        raise ValueError("allreduce_hierarchical: out must match the inputs")
+    allreduce_hierarchical_emulated(op, nodes, P // nodes, local[0], local[1], global_[0], global_[1],
+                                    [t.data_ptr() for t in tensors],
+                                    torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
+                                    torch_dtype_code(out[0].dtype), tensors[0].numel(),
+                                    current_stream(tensors[0].device))
     return out
 
 

@@ -484,6 +484,86 @@ int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching, cons
     return ok();
 }
 
+namespace {
+
+// Fold-register parent of register c >= 1 of a two-level strategy: the
+// registers are node blocks of Lr in the global order.  Within a block, a
+// tree links peer l to peer (l - 1) / b; a ring or centralized level links
+// every peer to the block's first register (a left fold from it).  A
+// block's first register is linked the same way to the first registers of
+// the other blocks.
+int level_parent(int c, int Lr, ddp_strategy local, int32_t local_param, ddp_strategy global,
+                 int32_t global_param) {
+    const int gi = c / Lr;
+    const int li = c % Lr;
+    if (li > 0) return gi * Lr + (local == DDP_STRATEGY_TREE ? (li - 1) / local_param : 0);
+    return (global == DDP_STRATEGY_TREE ? (gi - 1) / global_param : 0) * Lr;
+}
+
+int check_strategy(ddp_strategy st, int32_t param, const char* level) {
+    switch (st) {
+        case DDP_STRATEGY_RING:
+            if (param < 0) return fail(DDP_E_ARG, "%s ring chunk count %d is negative", level, param);
+            return DDP_OK;
+        case DDP_STRATEGY_TREE:
+            if (param < 1) return fail(DDP_E_ARG, "%s tree branching %d, must be >= 1", level, param);
+            return DDP_OK;
+        case DDP_STRATEGY_CENTRALIZED:
+            return DDP_OK;
+        default:
+            return fail(DDP_E_ARG, "unknown %s strategy %d", level, static_cast<int>(st));
+    }
+}
+
+}  // namespace
+
+int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t local_ranks,
+                                    ddp_strategy local_strategy, int32_t local_param,
+                                    ddp_strategy global_strategy, int32_t global_param,
+                                    const void* const* rank_in, ddp_dtype in_dtype, void* const* rank_out,
+                                    ddp_dtype out_dtype, int64_t n, void* stream) {
+    if (nodes < 1 || local_ranks < 1 || nodes > DDP_MAX_RANKS || local_ranks > DDP_MAX_RANKS ||
+        nodes * local_ranks > DDP_MAX_RANKS)
+        return fail(DDP_E_ARG, "nodes = %d x local_ranks = %d, need both >= 1 and a product <= %d", nodes,
+                    local_ranks, DDP_MAX_RANKS);
+    int s = check_strategy(local_strategy, local_param, "local");
+    if (s) return s;
+    if ((s = check_strategy(global_strategy, global_param, "global"))) return s;
+    const int P = nodes * local_ranks;
+    if ((s = validate_reduce(op, P, 1, rank_in, in_dtype, rank_out, out_dtype, n, true))) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
+    if ((s = check_overlaps(bufs))) return s;
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.mode = ddp::kTree;
+    l.P = P;
+    l.chunking = 1;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.write_out = 1;
+    l.groups = nodes;
+    if (local_strategy == DDP_STRATEGY_RING) l.local_chunking = local_param > 0 ? local_param : local_ranks;
+    if (global_strategy == DDP_STRATEGY_RING) l.global_chunking = global_param > 0 ? global_param : nodes;
+    for (int c = 1; c < P; ++c)
+        l.parents |= static_cast<uint64_t>(
+                         level_parent(c, local_ranks, local_strategy, local_param, global_strategy, global_param))
+                     << (4 * c);
+    for (int r = 0; r < P; ++r) {
+        l.in[r] = rank_in[r];
+        l.out[r] = rank_out[r];
+    }
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_ring_reduce(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
 int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtype in_dtype,
                    ddp_dtype out_dtype, ddp_tensor_tiles* tiles, int64_t* total_tiles, int64_t* tile_elems) {
     int s = check_ranks(P);

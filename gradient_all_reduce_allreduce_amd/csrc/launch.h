@@ -29,7 +29,10 @@ struct RingLaunch {
     float* v;
     float lr;
     float mu;
-    uint64_t parents;  // kTree: parent of rank c in bits [4c, 4c+4)
+    uint64_t parents;  // kTree: parent of fold register c in bits [4c, 4c+4)
+    int groups;        // kTree: G nodes of P / G ranks, node-major (0 means 1)
+    int local_chunking;   // kTree: chunk count of a ring within the nodes, 0 = fixed order
+    int global_chunking;  // kTree: chunk count of a ring over the nodes, 0 = fixed order
     int64_t n;
     void* stream;
 };
@@ -63,10 +66,10 @@ const void* ring_rs_kernel_f32_f32(int P, int scalar);
 const void* ring_rs_kernel_f32_bf16(int P, int scalar);
 const void* ring_rs_kernel_bf16_f32(int P, int scalar);
 const void* ring_rs_kernel_bf16_bf16(int P, int scalar);
-const void* tree_kernel_f32_f32(int P);
-const void* tree_kernel_f32_bf16(int P);
-const void* tree_kernel_bf16_f32(int P);
-const void* tree_kernel_bf16_bf16(int P);
+const void* tree_kernel_f32_f32(int P, int scalar);
+const void* tree_kernel_f32_bf16(int P, int scalar);
+const void* tree_kernel_bf16_f32(int P, int scalar);
+const void* tree_kernel_bf16_bf16(int P, int scalar);
 // All-gather kernels by element size (2 or 4 bytes); ring_allgather.hip.
 const void* ring_ag_kernel(int elem_bytes, int P, int scalar);
 

@@ -24,8 +24,8 @@ const void* select_kernel(const RingLaunch& l, int scalar) {
         case kAllGather:
             return ring_ag_kernel(l.out_bf16 ? 2 : 4, P, scalar);
         case kTree:
-            if (l.in_bf16) return l.out_bf16 ? tree_kernel_bf16_bf16(P) : tree_kernel_bf16_f32(P);
-            return l.out_bf16 ? tree_kernel_f32_bf16(P) : tree_kernel_f32_f32(P);
+            if (l.in_bf16) return l.out_bf16 ? tree_kernel_bf16_bf16(P, scalar) : tree_kernel_bf16_f32(P, scalar);
+            return l.out_bf16 ? tree_kernel_f32_bf16(P, scalar) : tree_kernel_f32_f32(P, scalar);
         default:
             if (l.in_bf16) {
                 return l.out_bf16 ? ring_kernel_bf16_bf16(P, l.sgd, scalar) : ring_kernel_bf16_f32(P, l.sgd, scalar);
@@ -53,11 +53,21 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
     if (l.mode == kAllGather && l.P == 1) return 0;   // one rank already holds everything
     int64_t V = 4, tile = 0;
     tile_shape(l, &V, &tile);
-    const int64_t L = l.mode == kTree ? l.n : (l.n + l.chunking - 1) / l.chunking;
+    // Chunk lengths: the ring's; for the tree strategies those of a ring
+    // within the nodes (L) and over the nodes (Lg), or a length beyond any
+    // index where a level's order is fixed.
+    const int64_t kFixed = int64_t(1) << 62;
+    const int groups = l.groups > 0 ? l.groups : 1;
+    int64_t L, Lg = kFixed;
+    if (l.mode == kTree) {
+        L = l.local_chunking > 0 ? (l.n + l.local_chunking - 1) / l.local_chunking : kFixed;
+        Lg = l.global_chunking > 0 ? (l.n + l.global_chunking - 1) / l.global_chunking : kFixed;
+    } else {
+        L = (l.n + l.chunking - 1) / l.chunking;
+    }
     // Chunks shorter than a tile would put several start ranks in one tile:
-    // those calls use the one-element-per-lane kernels.  (The tree's order
-    // does not depend on the element.)
-    const int scalar = l.mode != kTree && L < tile ? 1 : 0;
+    // those calls use the one-element-per-lane kernels.
+    const int scalar = (L < Lg ? L : Lg) < tile ? 1 : 0;
     const void* fn = select_kernel(l, scalar);
     if (fn == nullptr) {
         *msg = "no kernel for this rank count";
@@ -84,6 +94,9 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         a.mean = l.op == DDP_MEAN;
         a.write_out = l.write_out;
         a.parents = l.parents;
+        a.Lg = Lg;
+        a.groups = groups;
+        a.group_size = l.P / groups;
 
         int64_t grid;
         if (scalar) {

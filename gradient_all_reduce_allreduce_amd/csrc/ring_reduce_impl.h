@@ -67,7 +67,10 @@ struct RingArgs {
     uint32_t n_vec;      // elements covered by whole lane vectors
     int32_t mean;
     int32_t write_out;
-    uint64_t parents;    // tree strategy: 4 bits per rank c >= 1, its parent
+    uint64_t parents;    // tree strategies: 4 bits per fold register c >= 1, its parent register
+    int64_t Lg;          // two-level strategies: chunk length of the ring over nodes
+    int32_t groups;      // two-level strategies: G nodes of group_size ranks, node-major
+    int32_t group_size;
 };
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
@@ -599,18 +602,48 @@ const void* ring_ag_kernel_for(int P) {
     }
 }
 
-// ---- centralized and tree strategies ----------------------------------------
+// ---- centralized, tree and two-level strategies ---------------------------
 //
-// The reduce runs along a tree over the ranks (Burn collective blog,
-// "Methods", Tree; Centralized is the tree whose root has every other rank as
-// a child): every node adds its children's partial sums to its own value in
-// increasing child order, children before parents, then the root's value is
-// broadcast.  The tree's shape arrives as a parent table (4 bits per rank);
-// parents[c] < c, so walking the parents from the highest rank down finishes
-// every child before its parent.  Register indices are compile-time; the
-// shape only decides, with uniform branches, which of the P(P-1)/2 possible
-// edges are taken.  The order does not depend on the element, so there are
-// no chunk boundaries and no per-element start ranks.
+// The reduce runs along a tree over P fold registers (Burn collective blog,
+// "Methods", Tree; Centralized is the tree whose root has every other member
+// as a child): every register adds its children's partial sums to its own
+// value in increasing child order, children before parents, and the root's
+// value is broadcast.  The shape arrives as a parent table (4 bits per
+// register); parents[c] < c, so walking the registers from the highest down
+// finishes every child before its parent.  Register indices are
+// compile-time; the shape only decides, with uniform branches, which of the
+// P(P-1)/2 possible edges are taken.
+//
+// The same fold serves the two-level strategies (same blog, "Local strategy
+// and global strategy", "Local ring downfall"): P = G nodes of Lr ranks,
+// rank g*Lr + l being peer l of node g.  The registers hold node blocks in
+// the global order, each block the node's peers in the local order; a local
+// tree links the peers of a block, a ring or centralized level links them to
+// the block's first register (a left fold from it), and the blocks' first
+// registers are linked the same way at the global level.  A ring level
+// rotates its order per chunk: its members start at (chunk mod members), so
+// register k holds a rank that depends on the element's local and global
+// chunk -- uniform over a tile except where a chunk boundary falls inside
+// it.  Fixed orders pass chunk lengths beyond any index.  A single-level
+// tree is the case G = 1.
+
+// The rank held by each fold register when the local order starts at peer
+// s_l and the global order at node s_g.
+template <int P>
+__device__ __forceinline__ void level_ranks(int G, int Lr, int s_l, int s_g, int (&rank)[P]) {
+    int li = s_l;
+    int gi = s_g;
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+        rank[k] = gi * Lr + li;
+        li = li + 1 == Lr ? 0 : li + 1;
+        if (++cnt == Lr) {
+            cnt = 0;
+            gi = gi + 1 == G ? 0 : gi + 1;
+        }
+    }
+}
 
 template <int P, bool BF16, int U, int V>
 __device__ __forceinline__ void tree_fold(const u32x4 (&x)[P][U], uint64_t parents, float (&acc)[U][V]) {
@@ -643,13 +676,19 @@ __device__ __forceinline__ void tree_fold(const u32x4 (&x)[P][U], uint64_t paren
 template <int P, bool INB, bool OUTB>
 __device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
+    const int64_t gi = a->base + i;
+    const int G = a->groups;
+    const int Lr = a->group_size;
+    int rank[P];
+    level_ranks<P>(G, Lr, static_cast<int>((gi / a->L) % Lr), static_cast<int>((gi / a->Lg) % G), rank);
     float part[P];
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
+    for (int k = 0; k < P; ++k) {
+        const void* p = a->in[rank[k]];
         if constexpr (INB) {
-            part[r] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a->in[r])[i]) << 16);
+            part[k] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
         } else {
-            part[r] = static_cast<const float*>(a->in[r])[i];
+            part[k] = static_cast<const float*>(p)[i];
         }
     }
     const uint64_t parents = a->parents;
@@ -678,8 +717,26 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     constexpr uint32_t IES = INB ? 2 : 4;
     constexpr uint32_t OES = OUTB ? 2 : 4;
     constexpr int WIN = V * IES / 4;
+    constexpr uint32_t TILE = static_cast<uint32_t>(kBlock) * U * V;
     const uint32_t tid = threadIdx.x;
     const uint32_t n_vec = a->n_vec;
+    const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
+    const int64_t jl = (a->base + t0) / a->L;
+    const int64_t jg = (a->base + t0) / a->Lg;
+    if (jl != (a->base + last) / a->L || jg != (a->base + last) / a->Lg) {
+        // a local or global chunk boundary inside the tile: element by element
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i0 = t0 + (u * kBlock + tid) * V;
+            if (FULL || i0 < n_vec)
+                for (int e = 0; e < V; ++e) tree_element<P, INB, OUTB>(a, i0 + e);
+        }
+        return;
+    }
+    const int G = a->groups;
+    const int Lr = a->group_size;
+    int rank[P];
+    level_ranks<P>(G, Lr, static_cast<int>(jl % Lr), static_cast<int>(jg % G), rank);
     u32x4 x[P][U];
     bool ok[U];
 #pragma unroll
@@ -688,7 +745,8 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
         ok[u] = FULL || (i0 < n_vec);
         if (ok[u]) {
 #pragma unroll
-            for (int r = 0; r < P; ++r) x[r][u] = load_lane<WIN>(static_cast<const char*>(a->in[r]) + i0 * IES);
+            for (int k = 0; k < P; ++k)
+                x[k][u] = load_lane<WIN>(static_cast<const char*>(a->in[rank[k]]) + i0 * IES);
         } else {
 #pragma unroll
             for (int r = 0; r < P; ++r) x[r][u] = u32x4{0u, 0u, 0u, 0u};
@@ -745,11 +803,21 @@ __global__ __launch_bounds__(kBlock) void tree_reduce_kernel(RingArgs) {
     }
 }
 
-template <bool INB, bool OUTB>
+// Local or global chunks shorter than a tile: one element per lane.
+template <int P, bool INB, bool OUTB>
+__global__ __launch_bounds__(kBlock) void tree_reduce_scalar_kernel(RingArgs) {
+    const KArgs a = kernel_args();
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < a->n) tree_element<P, INB, OUTB>(a, i);
+}
+
+template <bool INB, bool OUTB, bool SCALAR>
 const void* tree_kernel_for(int P) {
     switch (P) {
-#define DDP_CASE(p) \
-    case p: return reinterpret_cast<const void*>(&tree_reduce_kernel<p, INB, OUTB>);
+#define DDP_CASE(p)                                                                           \
+    case p:                                                                                   \
+        return SCALAR ? reinterpret_cast<const void*>(&tree_reduce_scalar_kernel<p, INB, OUTB>) \
+                      : reinterpret_cast<const void*>(&tree_reduce_kernel<p, INB, OUTB>);
         DDP_CASE(1) DDP_CASE(2) DDP_CASE(3) DDP_CASE(4)
         DDP_CASE(5) DDP_CASE(6) DDP_CASE(7) DDP_CASE(8)
         DDP_CASE(9) DDP_CASE(10) DDP_CASE(11) DDP_CASE(12)
@@ -781,7 +849,7 @@ const void* ring_kernel_for(int P) {
 }  // namespace ddp
 
 // Defines ddp::ring_kernel_<name>(P, sgd, scalar),
-// ddp::ring_rs_kernel_<name>(P, scalar) and ddp::tree_kernel_<name>(P) for
+// ddp::ring_rs_kernel_<name>(P, scalar) and ddp::tree_kernel_<name>(P, scalar) for
 // one type pair.
 #define DDP_RING_TYPE_PAIR(name, INB, OUTB)                                              \
     namespace ddp {                                                                      \
@@ -795,5 +863,8 @@ const void* ring_kernel_for(int P) {
         return scalar ? rr::ring_rs_kernel_for<INB, OUTB, true>(P)                       \
                       : rr::ring_rs_kernel_for<INB, OUTB, false>(P);                     \
     }                                                                                    \
-    const void* tree_kernel_##name(int P) { return rr::tree_kernel_for<INB, OUTB>(P); }  \
+    const void* tree_kernel_##name(int P, int scalar) {                                  \
+        return scalar ? rr::tree_kernel_for<INB, OUTB, true>(P)                          \
+                      : rr::tree_kernel_for<INB, OUTB, false>(P);                        \
+    }                                                                                    \
     }

@@ -325,6 +325,54 @@ int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching,
                             void* const* rank_out, ddp_dtype out_dtype,
                             int64_t n, void* stream);
 
+/* The strategies of one level of a two-level all-reduce (Burn collective
+ * blog, "Methods"). */
+typedef enum ddp_strategy {
+    DDP_STRATEGY_RING = 0,         /* parameter: chunk count C >= 1, 0 = the level's member count */
+    DDP_STRATEGY_TREE = 1,         /* parameter: branching factor b >= 1 */
+    DDP_STRATEGY_CENTRALIZED = 2   /* parameter ignored */
+} ddp_strategy;
+
+/*
+ * allreduce_hierarchical_emulated -- the all-reduce split over two levels,
+ * each with its own strategy (Burn collective blog, "Local strategy and
+ * global strategy" and "Local ring downfall").
+ *
+ * The P = nodes * local_ranks ranks form `nodes` nodes of `local_ranks`
+ * peers, numbered node-major: rank g * local_ranks + l is peer l of node g.
+ * With a Tree or Centralized local strategy the steps are a local reduce to
+ * peer 0 of every node, a global all-reduce among those peers, and a local
+ * broadcast; with a Ring local strategy the local reduce is a local ring
+ * all-reduce (a ring cannot be split into a reduce and a broadcast), after
+ * which peer 0 holds the same node sum.  Each level sums in the order of its
+ * single-level strategy over its members (the node's peers in peer order;
+ * the nodes in node order):
+ *   Ring: C chunks of length ceil(n / C); the chunk holding element i
+ *     starts at member (chunk mod m) and adds the members in ring order
+ *     (as allreduce_ring_emulated over m members);
+ *   Tree: the b-ary heap of allreduce_tree_emulated over the members;
+ *   Centralized: the root adds the other members in order.
+ * Mean divides the global sum once by P (all ranks), correctly rounded;
+ * every rank receives the result.  Partial sums are float32 throughout.
+ * One node is the local strategy alone over P ranks; one peer per node is
+ * the global strategy alone.
+ *
+ *   nodes, local_ranks     >= 1 each, product <= DDP_MAX_RANKS
+ *   local_strategy, local_param    the strategy within every node and its
+ *                                  parameter (see ddp_strategy)
+ *   global_strategy, global_param  the strategy over the nodes
+ *   rank_in, in_dtype, rank_out, out_dtype, n, stream   as for
+ *   allreduce_ring_emulated, with P = nodes * local_ranks
+ * Errors: as for allreduce_ring_emulated; DDP_E_ARG also for an unknown
+ * strategy, a negative ring parameter or a tree branching below 1.
+ */
+int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t local_ranks,
+                                    ddp_strategy local_strategy, int32_t local_param,
+                                    ddp_strategy global_strategy, int32_t global_param,
+                                    const void* const* rank_in, ddp_dtype in_dtype,
+                                    void* const* rank_out, ddp_dtype out_dtype,
+                                    int64_t n, void* stream);
+
 /*
  * ddp_multi_plan -- host only: lay out the tiles of a multi-tensor
  * all-reduce.

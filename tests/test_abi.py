@@ -278,6 +278,35 @@ def test_tree_errors():
     assert lib.allreduce_tree_emulated(1, 2, 5, ins, 0, outs, 1, 0, None) == N.DDP_OK
 
 
+def test_hierarchical_errors():
+    lib = N.lib()
+    f = lib.allreduce_hierarchical_emulated
+    ins4 = N.pointer_array([A + r * MB for r in range(4)])
+    outs4 = N.pointer_array([A + (64 + r) * MB for r in range(4)])
+    RING, TREE, CEN = 0, 1, 2
+    # shapes: both counts >= 1, product <= 16
+    assert f(0, 0, 4, RING, 0, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    assert f(0, 2, 0, RING, 0, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    assert f(0, 4, 5, RING, 0, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    # strategies and their parameters
+    assert f(0, 2, 2, 3, 0, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    assert f(0, 2, 2, RING, 0, -1, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    assert f(0, 2, 2, RING, -1, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    assert f(0, 2, 2, TREE, 0, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    assert f(0, 2, 2, RING, 0, TREE, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    # buffers, as for the other all-reduces
+    assert f(0, 2, 2, CEN, 0, CEN, 0, ins4, 0, N.pointer_array([A + 8, A + MB, A + 2 * MB, A + 3 * MB]),
+             0, 16, None) == N.DDP_E_ALIGN
+    assert f(0, 2, 2, CEN, 0, CEN, 0, ins4, 0, N.pointer_array([A + 16, A + 65 * MB, A + 66 * MB,
+                                                                 A + 67 * MB]),
+             0, 1024, None) == N.DDP_E_OVERLAP
+    assert f(2, 2, 2, RING, 0, RING, 0, ins4, 0, outs4, 0, 16, None) == N.DDP_E_ARG
+    # n = 0 is a valid no-op
+    assert f(1, 2, 2, TREE, 2, RING, 3, ins4, 1, outs4, 0, 0, None) == N.DDP_OK
+    with pytest.raises(ValueError):
+        ddp.allreduce_hierarchical([], 1)
+
+
 def test_multi_plan():
     _, _, tile = ddp.ddp_multi_plan([1], 8, ddp.F32, ddp.F32)
     sizes = [0, 1, tile, tile + 1, 5]

@@ -1,0 +1,114 @@
+"""GPU parity of the two-level (local / global) all-reduce against the
+oracle's phase-by-phase simulation, bit for bit: every strategy pair, node
+shapes up to 16 ranks, chunk boundaries of either level inside tiles, chunks
+shorter than a tile, ragged tails, bf16, and a full 25 MiB bucket."""
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import assert_same_bits, to_device, to_host, torch_dtype
+
+pytestmark = pytest.mark.gpu
+ddp = pytest.importorskip("gradient_all_reduce_allreduce_amd")
+
+LOCALS = [("ring", None), ("ring", 3), ("tree", 2), ("tree", 1), ("centralized", None)]
+GLOBALS = [("ring", None), ("ring", 5), ("tree", 2), ("centralized", None)]
+
+
+def draw(P, n, dtype, seed):
+    X = workloads.rank_buffers(P, n, dist="wide", seed=seed)
+    return workloads.to_bf16_bits(X) if dtype == "bf16" else X
+
+
+def run(X, it, ot, op, G, local, glob):
+    out = ddp.allreduce_hierarchical(to_device(X, it), G, op, local, glob, out_dtype=torch_dtype(ot))
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def want(X, it, ot, op, G, local, glob):
+    return oracle.hierarchical_allreduce(X, op, nodes=G, local=local, global_=glob, in_dtype=it,
+                                         out_dtype=ot)
+
+
+@pytest.mark.parametrize("P,G", [(4, 2), (6, 2), (6, 3), (8, 2), (8, 4), (12, 3), (16, 4), (16, 8)])
+def test_every_strategy_pair_f32(P, G):
+    for n in (1, 9, 4101, 70001):
+        for li, local in enumerate(LOCALS):
+            for gi, glob in enumerate(GLOBALS):
+                op = ("sum", "mean")[(li + gi + n) % 2]
+                X = draw(P, n, "f32", seed=P * 100 + G * 10 + li * 4 + gi + n)
+                what = f"P={P} G={G} n={n} {local} {glob} {op}"
+                print(what, flush=True)
+                assert_same_bits(run(X, "f32", "f32", op, G, local, glob),
+                                 want(X, "f32", "f32", op, G, local, glob), what)
+
+
+@pytest.mark.parametrize("pair", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16")])
+@pytest.mark.parametrize("P,G", [(4, 2), (8, 2), (12, 4)])
+def test_element_types(pair, P, G):
+    it, ot = pair
+    for n in (9, 4101, 70001):
+        for local, glob in [(("ring", 3), ("ring", 5)), (("tree", 2), ("ring", None)),
+                            (("centralized", None), ("tree", 1))]:
+            for op in ("sum", "mean"):
+                X = draw(P, n, it, seed=P + G + n)
+                what = f"{it}->{ot} P={P} G={G} n={n} {local} {glob} {op}"
+                print(what, flush=True)
+                assert_same_bits(run(X, it, ot, op, G, local, glob), want(X, it, ot, op, G, local, glob),
+                                 what)
+
+
+def test_both_levels_rotate_inside_tiles():
+    """Local and global chunk boundaries at unaligned positions, so tiles
+    straddle either one or both, next to tiles that take the vector path."""
+    P, G = 8, 2
+    n = 3 * 65536 + 123
+    X = draw(P, n, "f32", seed=77)
+    for local, glob in [(("ring", 7), ("ring", 3)), (("ring", 4), ("ring", 2)), (("ring", 13), ("tree", 1))]:
+        assert_same_bits(run(X, "f32", "f32", "mean", G, local, glob),
+                         want(X, "f32", "f32", "mean", G, local, glob), f"{local} {glob}")
+
+
+def test_full_bucket_two_nodes_of_four():
+    """A full 25 MiB fp32 bucket of the ResNet-50 gradient set (6,553,600
+    elements x 8 ranks), as 2 nodes of 4: ring in the nodes and over them,
+    and tree in the nodes with a ring over them, Mean."""
+    P, G, n = 8, 2, 6_553_600
+    X = workloads.rank_buffers(P, n, dist="normal", scale=0.01, seed=2)
+    for local, glob in [(("ring", None), ("ring", None)), (("tree", 2), ("ring", 8))]:
+        assert_same_bits(run(X, "f32", "f32", "mean", G, local, glob),
+                         want(X, "f32", "f32", "mean", G, local, glob), f"{local} {glob}")
+
+
+@pytest.mark.parametrize("P", [4, 8])
+def test_single_levels_match_the_single_level_calls(P):
+    """One node is the local strategy alone, one peer per node the global
+    one: the two-level call then gives the single-level calls' bits."""
+    n = 1_000_003
+    X = draw(P, n, "f32", seed=P)
+    dev = to_device(X, "f32")
+    ring = to_host(ddp.allreduce(dev, "mean", 2 * P))
+    tree = to_host(ddp.allreduce_tree(dev, "mean", 2))
+    torch.cuda.synchronize()
+    assert_same_bits(to_host(ddp.allreduce_hierarchical(dev, 1, "mean", ("ring", 2 * P), ("tree", 3))), ring)
+    assert_same_bits(to_host(ddp.allreduce_hierarchical(dev, P, "mean", ("tree", 3), ("ring", 2 * P))), ring)
+    assert_same_bits(to_host(ddp.allreduce_hierarchical(dev, 1, "mean", ("tree", 2), ("ring", None))), tree)
+    assert_same_bits(to_host(ddp.allreduce_hierarchical(dev, P, "mean", ("ring", None), ("tree", 2))), tree)
+
+
+def test_in_place_and_deterministic():
+    P, G, n = 8, 4, 100_003
+    X = draw(P, n, "f32", seed=9)
+    first = None
+    for _ in range(2):
+        bufs = to_device(X, "f32")
+        ddp.allreduce_hierarchical(bufs, G, "sum", ("tree", 1), ("ring", 3), out=bufs)
+        torch.cuda.synchronize()
+        got = to_host(bufs)
+        if first is None:
+            first = got
+        assert_same_bits(got, first)
+    assert_same_bits(first, want(X, "f32", "f32", "sum", G, ("tree", 1), ("ring", 3)))
