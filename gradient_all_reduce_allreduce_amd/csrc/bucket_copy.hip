@@ -7,14 +7,19 @@
 // parallelism").  The segment table of a bucket says which piece of which
 // tensor occupies which range of the bucket.
 //
-// A pure copy: bound by HBM bandwidth, 2 * bucket bytes per rank.  Each
-// workgroup walks tiles of the bucket (16-byte vectors on the bucket side,
-// always aligned); for a tile it stages the overlapping segments in LDS, so
-// that each lane finds its segment with a short binary search in LDS
-// instead of a chain of dependent global loads.  A vector that lies inside
-// one segment whose tensor address is 16-byte aligned moves as one 16-byte
-// access; vectors across a segment boundary or misaligned on the tensor
-// side move element by element.  Every bucket element is written exactly
+// A pure copy: bound by HBM bandwidth, 2 * bucket bytes per rank.  One
+// workgroup per (tile of the bucket, rank), as many workgroups as tiles, so
+// that the dispatcher keeps every CU busy.  For its tile a workgroup stages
+// the overlapping segments in LDS (one uniform binary search in the segment
+// table finds the first), so that each lane finds the segment of each of
+// its vectors with a short binary search in LDS instead of a chain of
+// dependent global loads.  A vector (16 bytes on the bucket side, always
+// aligned) that lies inside one segment moves as one 16-byte access on the
+// bucket side and, on the tensor side, as one 16-byte access when the
+// tensor address is aligned, else as element-size accesses; a lane issues
+// all of those loads before its first store, so kVecPerLane vectors per
+// lane are in flight.  Vectors across a segment boundary move element by
+// element afterwards.  Every bucket element is written exactly
 // once (the segments tile the bucket), so no synchronisation between
 // workgroups is needed.
 #include <hip/hip_runtime.h>
@@ -28,7 +33,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
-constexpr int kVecPerLane = 2;   // 16-byte vectors per lane and tile
+constexpr int kVecPerLane = 8;   // 16-byte vectors per lane and tile
 
 struct CopyArgs {
     const ddp_segment* segs;
@@ -47,6 +52,37 @@ __device__ __forceinline__ void copy_elem(char* dst, const char* src, int es) {
         *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
     } else {
         *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+    }
+}
+
+// One 16-byte vector's worth of elements (4 float32 or 8 bf16) at an
+// address aligned only to the element size, and the inverse.
+__device__ __forceinline__ u32x4 load_elems(const char* p, int es) {
+    u32x4 v;
+    if (es == 4) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = q[j];
+    } else {
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = static_cast<uint32_t>(q[2 * j]) | (static_cast<uint32_t>(q[2 * j + 1]) << 16);
+    }
+    return v;
+}
+
+__device__ __forceinline__ void store_elems(char* p, u32x4 v, int es) {
+    if (es == 4) {
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = v[j];
+    } else {
+        uint16_t* q = reinterpret_cast<uint16_t*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            q[2 * j] = static_cast<uint16_t>(v[j] & 0xffffu);
+            q[2 * j + 1] = static_cast<uint16_t>(v[j] >> 16);
+        }
     }
 }
 
@@ -74,67 +110,101 @@ __global__ __launch_bounds__(kBlock) void bucket_copy_kernel(CopyArgs a) {
     const void* const* tensors = a.tensors + static_cast<int64_t>(rank) * a.n_tensors;
     const int es = a.es;
     const int ve = 16 / es;   // elements per 16-byte vector
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * a.tile_elems;
+    const int64_t hi = lo + a.tile_elems < a.bucket_len ? lo + a.tile_elems : a.bucket_len;
 
-    for (int64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
-        const int64_t lo = tile * a.tile_elems;
-        const int64_t hi = lo + a.tile_elems < a.bucket_len ? lo + a.tile_elems : a.bucket_len;
-
-        // First segment holding element lo (same search in every lane).
-        int64_t f = 0;
-        {
-            int64_t l = 0;
-            int64_t h = a.n_segs - 1;
-            while (l < h) {
-                const int64_t mid = (l + h + 1) >> 1;
-                if (a.segs[mid].dst_off <= lo) l = mid; else h = mid - 1;
-            }
-            f = l;
+    // First segment holding element lo (the same search in every lane).
+    int64_t f = 0;
+    {
+        int64_t l = 0;
+        int64_t h = a.n_segs - 1;
+        while (l < h) {
+            const int64_t mid = (l + h + 1) >> 1;
+            if (a.segs[mid].dst_off <= lo) l = mid; else h = mid - 1;
         }
+        f = l;
+    }
 
-        while (true) {
-            const int64_t k = f + tid;
-            const bool valid = k < a.n_segs && a.segs[k].dst_off < hi;
-            if (valid) {
-                const ddp_segment sg = a.segs[k];
-                s_dst[tid] = sg.dst_off;
-                s_len[tid] = sg.len;
-                s_ten[tid] = static_cast<char*>(const_cast<void*>(tensors[sg.tensor])) + sg.src_off * es;
-            }
-            const int count = __syncthreads_count(valid);   // valid lanes form a prefix
-            const int64_t cov_lo = s_dst[0] > lo ? s_dst[0] : lo;
-            const int64_t last_end = s_dst[count - 1] + s_len[count - 1];
-            const int64_t cov_hi = last_end < hi ? last_end : hi;
+    while (true) {
+        const int64_t k = f + tid;
+        const bool valid = k < a.n_segs && a.segs[k].dst_off < hi;
+        if (valid) {
+            const ddp_segment sg = a.segs[k];
+            s_dst[tid] = sg.dst_off;
+            s_len[tid] = sg.len;
+            s_ten[tid] = static_cast<char*>(const_cast<void*>(tensors[sg.tensor])) + sg.src_off * es;
+        }
+        const int count = __syncthreads_count(valid);   // valid lanes form a prefix
+        const int64_t cov_lo = s_dst[0] > lo ? s_dst[0] : lo;
+        const int64_t last_end = s_dst[count - 1] + s_len[count - 1];
+        const int64_t cov_hi = last_end < hi ? last_end : hi;
 
+        // Vectors inside one segment: every load first, then every store.
+        // The bucket side is always 16-byte aligned; the tensor side moves
+        // as one 16-byte access when aligned, else element by element.
+        u32x4 x[kVecPerLane];
+        char* tn[kVecPerLane];
+        int cls[kVecPerLane];   // 0 nothing here, 1 aligned, 2 misaligned tensor, 3 across segments
 #pragma unroll
-            for (int u = 0; u < kVecPerLane; ++u) {
-                const int64_t e0 = lo + static_cast<int64_t>(u * kBlock + tid) * ve;
-                int64_t b = e0 > cov_lo ? e0 : cov_lo;
-                const int64_t e1 = e0 + ve < cov_hi ? e0 + ve : cov_hi;
-                if (b >= e1) continue;
-                int g = lds_find(s_dst, count, b);
-                char* bk = bucket + e0 * es;
-                char* tn = s_ten[g] + (e0 - s_dst[g]) * es;
-                const bool whole = b == e0 && e1 == e0 + ve && e1 <= s_dst[g] + s_len[g] &&
-                                   (reinterpret_cast<uintptr_t>(tn) & 15u) == 0;
-                if (whole) {
-                    if (PACK) {
-                        *reinterpret_cast<u32x4*>(bk) = *reinterpret_cast<const u32x4*>(tn);
-                    } else {
-                        *reinterpret_cast<u32x4*>(tn) = *reinterpret_cast<const u32x4*>(bk);
+        for (int u = 0; u < kVecPerLane; ++u) {
+            const int64_t e0 = lo + static_cast<int64_t>(u * kBlock + tid) * ve;
+            const int64_t e1 = e0 + ve;
+            cls[u] = 0;
+            tn[u] = nullptr;
+            if (e0 < cov_hi && e1 > cov_lo) {
+                cls[u] = 3;
+                if (e0 >= cov_lo && e1 <= cov_hi) {
+                    const int g = lds_find(s_dst, count, e0);
+                    if (e1 <= s_dst[g] + s_len[g]) {
+                        tn[u] = s_ten[g] + (e0 - s_dst[g]) * es;
+                        cls[u] = (reinterpret_cast<uintptr_t>(tn[u]) & 15u) == 0 ? 1 : 2;
                     }
-                    continue;
-                }
-                for (int64_t e = b; e < e1; ++e) {
-                    while (e >= s_dst[g] + s_len[g]) ++g;
-                    char* pb = bucket + e * es;
-                    char* pt = s_ten[g] + (e - s_dst[g]) * es;
-                    if (PACK) copy_elem(pb, pt, es); else copy_elem(pt, pb, es);
                 }
             }
-            __syncthreads();   // LDS is restaged below or by the next tile
-            if (count < kBlock || last_end >= hi) break;
-            f += count;
+            const char* bk = bucket + e0 * es;
+            if (cls[u] == 1) {
+                x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(PACK ? tn[u] : bk));
+            } else if (cls[u] == 2) {
+                if (PACK) {
+                    x[u] = load_elems(tn[u], es);
+                } else {
+                    x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk));
+                }
+            }
         }
+#pragma unroll
+        for (int u = 0; u < kVecPerLane; ++u) {
+            char* bk = bucket + (lo + static_cast<int64_t>(u * kBlock + tid) * ve) * es;
+            if (cls[u] == 1) {
+                *reinterpret_cast<u32x4*>(PACK ? bk : tn[u]) = x[u];
+            } else if (cls[u] == 2) {
+                if (PACK) {
+                    *reinterpret_cast<u32x4*>(bk) = x[u];
+                } else {
+                    store_elems(tn[u], x[u], es);
+                }
+            }
+        }
+
+        // Vectors across a segment boundary, or partly covered by this
+        // round's segments: element by element.
+#pragma unroll
+        for (int u = 0; u < kVecPerLane; ++u) {
+            if (cls[u] != 3) continue;
+            const int64_t e0 = lo + static_cast<int64_t>(u * kBlock + tid) * ve;
+            const int64_t b = e0 > cov_lo ? e0 : cov_lo;
+            const int64_t e1 = e0 + ve < cov_hi ? e0 + ve : cov_hi;
+            int g = lds_find(s_dst, count, b);
+            for (int64_t e = b; e < e1; ++e) {
+                while (e >= s_dst[g] + s_len[g]) ++g;
+                char* pb = bucket + e * es;
+                char* pt = s_ten[g] + (e - s_dst[g]) * es;
+                if (PACK) copy_elem(pb, pt, es); else copy_elem(pt, pb, es);
+            }
+        }
+        __syncthreads();   // LDS is restaged below
+        if (count < kBlock || last_end >= hi) break;
+        f += count;
     }
 }
 
@@ -153,23 +223,15 @@ int launch_bucket_copy(const CopyLaunch& l, const char** msg) {
     a.tile_elems = static_cast<int64_t>(kBlock) * kVecPerLane * (16 / l.elem_bytes);
     a.tiles = (l.bucket_len + a.tile_elems - 1) / a.tile_elems;
 
-    int dev = 0;
-    int cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess || cus <= 0) {
-        *msg = "hipDeviceGetAttribute(MultiprocessorCount)";
-        return static_cast<int>(e == hipSuccess ? hipErrorInvalidValue : e);
+    if (a.tiles > 0x7fffffff) {
+        *msg = "bucket too long for one launch";
+        return static_cast<int>(hipErrorInvalidValue);
     }
-    // About eight resident workgroups per CU in total, shared by the ranks.
-    int64_t gx = (static_cast<int64_t>(cus) * 8 + l.P - 1) / l.P;
-    if (gx > a.tiles) gx = a.tiles;
-    if (gx < 1) gx = 1;
     const void* fn = l.pack ? reinterpret_cast<const void*>(&bucket_copy_kernel<true>)
                             : reinterpret_cast<const void*>(&bucket_copy_kernel<false>);
     void* args[] = {&a};
-    e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(l.P)), dim3(kBlock),
-                        args, 0, static_cast<hipStream_t>(l.stream));
+    const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.tiles), static_cast<unsigned>(l.P)),
+                                         dim3(kBlock), args, 0, static_cast<hipStream_t>(l.stream));
     if (e != hipSuccess) {
         *msg = "hipLaunchKernel(bucket_copy)";
         return static_cast<int>(e);
