@@ -19,9 +19,11 @@
 // tensor address is aligned, else as element-size accesses; a lane issues
 // all of those loads before its first store, so kVecPerLane vectors per
 // lane are in flight.  Vectors across a segment boundary move element by
-// element afterwards.  Every bucket element is written exactly
-// once (the segments tile the bucket), so no synchronisation between
-// workgroups is needed.
+// element afterwards.  Stores are ordinary (measured faster than
+// non-temporal ones here: the all-reduce that reads a packed bucket next
+// finds part of it in the last-level cache).  Every bucket element is
+// written exactly once (the segments tile the bucket), so no
+// synchronisation between workgroups is needed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

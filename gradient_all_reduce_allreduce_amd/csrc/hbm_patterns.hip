@@ -8,7 +8,8 @@
 // This program times, with hipEvents over 40 repetitions each:
 //   read   -- 2 GiB read with 16-byte non-temporal loads (XOR-folded)
 //   write  -- 2 GiB written with 16-byte stores, plain and non-temporal
-//   copy   -- 2 GiB read + 2 GiB written, 16-byte non-temporal accesses
+//   copy   -- 2 GiB read + 2 GiB written, 16-byte non-temporal loads, and
+//             non-temporal or ordinary stores
 //   red8   -- the all-reduce's own pattern: 8 input streams summed into 8
 //             identical output streams (25 MiB each, 4 rotating buffer sets
 //             = 1.6 GiB, more than the last-level cache), with the 16
@@ -16,7 +17,7 @@
 //             one allocation, (c) in one allocation with an extra 4 KiB
 //             between neighbours; each with 2 vectors per lane and a common
 //             store order, and with 1 vector per lane and the store order
-//             rotated per wave.
+//             rotated per wave (non-temporal or ordinary stores).
 // Every kernel uses one tile of 256 lanes x U vectors per workgroup and as
 // many workgroups as tiles.  Output: one line per measurement, GB/s of bytes
 // moved (read + written).
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(kBlock) void write_kernel(u32x4* a, uint32_t nvec) 
     }
 }
 
+template <bool NT>
 __global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* a, u32x4* b, uint32_t nvec) {
     const uint32_t t = blockIdx.x * (kBlock * kU);
     u32x4 x[kU];
@@ -75,7 +77,9 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* a, u32x4* b, 
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const uint32_t i = t + u * kBlock + threadIdx.x;
-        if (i < nvec) __builtin_nontemporal_store(x[u], b + i);
+        if (i < nvec) {
+            if (NT) __builtin_nontemporal_store(x[u], b + i); else b[i] = x[u];
+        }
     }
 }
 
@@ -86,7 +90,8 @@ struct Streams8 {
 
 // The same pattern with one 16-byte vector per lane and the order of the 8
 // output stores rotated by the wave index (each wave starts at another
-// output stream).
+// output stream); NT selects non-temporal or ordinary stores.
+template <bool NT>
 __global__ __launch_bounds__(kBlock) void red8_rotated_kernel(Streams8 p, uint32_t nvec) {
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i >= nvec) return;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kBlock) void red8_rotated_kernel(Streams8 p, uint32
         u32x4* o = p.out[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) o = want == j ? p.out[j] : o;
-        __builtin_nontemporal_store(s, o + i);
+        if (NT) __builtin_nontemporal_store(s, o + i); else o[i] = s;
     }
 }
 
@@ -179,9 +184,13 @@ int main() {
     ms = time_ms([&](int) { write_kernel<true><<<g, kBlock>>>(reinterpret_cast<u32x4*>(A), nvec); });
     std::printf("write nt          : %7.0f GB/s\n", big / ms / 1e6);
     ms = time_ms([&](int) {
-        copy_kernel<<<g, kBlock>>>(reinterpret_cast<const u32x4*>(A), reinterpret_cast<u32x4*>(B), nvec);
+        copy_kernel<true><<<g, kBlock>>>(reinterpret_cast<const u32x4*>(A), reinterpret_cast<u32x4*>(B), nvec);
     });
     std::printf("copy  nt          : %7.0f GB/s\n", 2.0 * big / ms / 1e6);
+    ms = time_ms([&](int) {
+        copy_kernel<false><<<g, kBlock>>>(reinterpret_cast<const u32x4*>(A), reinterpret_cast<u32x4*>(B), nvec);
+    });
+    std::printf("copy  nt load, plain store: %7.0f GB/s\n", 2.0 * big / ms / 1e6);
 
     const size_t rb = size_t(25) << 20;               // 25 MiB per stream
     const uint32_t rv = static_cast<uint32_t>(rb / 16);
@@ -213,8 +222,11 @@ int main() {
         ms = time_ms([&](int i) { red8_kernel<<<grid_for(rv), kBlock>>>(ps[i % sets], rv); });
         std::printf("red8  %-38s: %7.0f GB/s (%.1f us per 25 MiB x 16 streams)\n", names[layout],
                     16.0 * rb / ms / 1e6, ms * 1e3);
-        ms = time_ms([&](int i) { red8_rotated_kernel<<<(rv + kBlock - 1) / kBlock, kBlock>>>(ps[i % sets], rv); });
+        ms = time_ms([&](int i) { red8_rotated_kernel<true><<<(rv + kBlock - 1) / kBlock, kBlock>>>(ps[i % sets], rv); });
         std::printf("red8  %-38s: %7.0f GB/s (%.1f us) one vector per lane, rotated stores\n",
+                    names[layout], 16.0 * rb / ms / 1e6, ms * 1e3);
+        ms = time_ms([&](int i) { red8_rotated_kernel<false><<<(rv + kBlock - 1) / kBlock, kBlock>>>(ps[i % sets], rv); });
+        std::printf("red8  %-38s: %7.0f GB/s (%.1f us) one vector per lane, rotated plain stores\n",
                     names[layout], 16.0 * rb / ms / 1e6, ms * 1e3);
     }
     for (char* p : separate) CK(hipFree(p));
