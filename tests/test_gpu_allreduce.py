@@ -171,6 +171,64 @@ def test_more_than_one_launch():
     torch.cuda.empty_cache()
 
 
+def sampled_indices(n, C, extra=()):
+    """Indices around every chunk boundary, the launch split at 2^29, both
+    ends, and random ones."""
+    L = -(-n // C)
+    parts = [np.arange(0, 64), np.arange(n - 64, n), np.arange((1 << 29) - 40, (1 << 29) + 40),
+             np.random.default_rng(1).integers(0, n, 2000)]
+    parts += [np.arange(max(0, j * L - 40), min(n, j * L + 40)) for j in range(1, C)]
+    parts += list(extra)
+    return np.unique(np.concatenate(parts))
+
+
+def test_more_than_one_launch_bf16_to_f32_two_passes():
+    """bf16 -> fp32 runs as a reduce-scatter pass and an all-gather pass;
+    both carry the chunk order across the split at 2^29 elements."""
+    P, n, C = 3, (1 << 29) + 77, 4
+    ins = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    for r, t in enumerate(ins):
+        workloads.torch_normal_(t, 1.0, seed=200 + r)
+    outs = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    ddp.allreduce(ins, "mean", C, out=outs)
+    torch.cuda.synchronize()
+    idx = sampled_indices(n, C)
+    it = torch.from_numpy(idx).to(DEV)
+    V = np.stack([t[it].view(torch.int16).cpu().numpy().view(np.uint16) for t in ins])
+    start = oracle.chunk_start_ranks_at(n, C, P, idx)
+    want = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="f32")
+    got = np.stack([t[it].cpu().numpy() for t in outs])
+    assert_same_bits(got, want, "split launch, bf16 -> f32")
+    del ins, outs
+    torch.cuda.empty_cache()
+
+
+def test_more_than_one_launch_fused_sgd():
+    """The optimizer state is offset with the gradients at every launch."""
+    P, n, C = 3, (1 << 29) + 77, 3
+    grads = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    for r, t in enumerate(grads):
+        workloads.torch_normal_(t, 1e-3, seed=300 + r)
+    w = torch.empty(n, dtype=torch.float32, device=DEV)
+    v = torch.empty(n, dtype=torch.float32, device=DEV)
+    workloads.torch_normal_(w, 0.02, seed=310)
+    workloads.torch_normal_(v, 1e-3, seed=311)
+    idx = sampled_indices(n, C)
+    it = torch.from_numpy(idx).to(DEV)
+    w0 = w[it].cpu().numpy()
+    v0 = v[it].cpu().numpy()
+    ddp.allreduce_sgd(grads, w, v, 1e-3, 0.9, "mean", C)
+    torch.cuda.synchronize()
+    V = np.stack([t[it].view(torch.int16).cpu().numpy().view(np.uint16) for t in grads])
+    start = oracle.chunk_start_ranks_at(n, C, P, idx)
+    g = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="f32")[0]
+    w1, v1 = oracle.sgd_momentum(g, w0, v0, 1e-3, 0.9)
+    assert_same_bits(w[it].cpu().numpy(), w1, "split launch, w")
+    assert_same_bits(v[it].cpu().numpy(), v1, "split launch, v")
+    del grads, w, v
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------- fused SGD ----
 
 @pytest.mark.parametrize("gt,ot", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32")])

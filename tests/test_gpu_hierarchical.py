@@ -3,12 +3,13 @@ oracle's phase-by-phase simulation, bit for bit: every strategy pair, node
 shapes up to 16 ranks, chunk boundaries of either level inside tiles, chunks
 shorter than a tile, ragged tails, bf16, and a full 25 MiB bucket."""
 
+import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from gpu_helpers import assert_same_bits, to_device, to_host, torch_dtype
+from gpu_helpers import DEV, assert_same_bits, to_device, to_host, torch_dtype
 
 pytestmark = pytest.mark.gpu
 ddp = pytest.importorskip("gradient_all_reduce_allreduce_amd")
@@ -112,3 +113,30 @@ def test_in_place_and_deterministic():
             first = got
         assert_same_bits(got, first)
     assert_same_bits(first, want(X, "f32", "f32", "sum", G, ("tree", 1), ("ring", 3)))
+
+
+def test_more_than_one_launch():
+    """Over 2^29 elements the call is split into launches; the chunk order
+    of a rotating level runs across the split.  With one node the two-level
+    call is its local ring alone, with one peer per node its global ring
+    alone: both equal the flat ring, computed on sampled elements."""
+    P, n, C = 3, (1 << 29) + 77, 5
+    ins = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    for r, t in enumerate(ins):
+        workloads.torch_normal_(t, 1.0, seed=400 + r)
+    outs = [torch.empty_like(t) for t in ins]
+    L = -(-n // C)
+    idx = np.unique(np.concatenate(
+        [np.arange(0, 64), np.arange(n - 64, n), np.arange((1 << 29) - 40, (1 << 29) + 40),
+         np.random.default_rng(2).integers(0, n, 2000)] +
+        [np.arange(j * L - 40, j * L + 40) for j in range(1, C)]))
+    it = torch.from_numpy(idx).to(DEV)
+    V = np.stack([t[it].cpu().numpy() for t in ins])
+    expect = oracle.ring_allreduce_sampled(V, oracle.chunk_start_ranks_at(n, C, P, idx), "mean")
+    for G, local, glob in [(1, ("ring", C), ("tree", 2)), (P, ("tree", 2), ("ring", C))]:
+        ddp.allreduce_hierarchical(ins, G, "mean", local, glob, out=outs)
+        torch.cuda.synchronize()
+        got = np.stack([t[it].cpu().numpy() for t in outs])
+        assert_same_bits(got, expect, f"split launch G={G}")
+    del ins, outs
+    torch.cuda.empty_cache()
