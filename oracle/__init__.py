@@ -32,6 +32,8 @@ Modules:
     bucket  -- reverse-order gradient bucketing, pack and unpack
     tree    -- the centralized and b-ary tree all-reduce
     hierarchical -- the two-level (local / global) all-reduce
+    zero    -- ZeRO stage 1: reduce-scatter, the owner's optimizer step,
+               all-gather of the updated parameters
 
 Parity status of each function is stated in its module header.
 """
@@ -41,6 +43,7 @@ from .ring import (SUM, MEAN, chunk_length, chunk_owners, chunk_start_ranks,
                    ring_allreduce_sampled, ring_reduce_scatter)
 from .tree import tree_allreduce, tree_parents
 from .hierarchical import hierarchical_allreduce
+from .zero import zero1_sgd_step
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .sgd import sgd_momentum
 from .bucket import bucket_plan, pack, unpack
@@ -50,5 +53,5 @@ __all__ = [
     "chunk_start_ranks_at", "ring_all_gather", "ring_allreduce", "ring_reduce_scatter",
     "ring_allreduce_sampled", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "sgd_momentum", "bucket_plan", "pack", "unpack", "tree_allreduce", "tree_parents",
-    "hierarchical_allreduce",
+    "hierarchical_allreduce", "zero1_sgd_step",
 ]
