@@ -203,6 +203,13 @@ def run_suite(steps, warmup):
            _time(lambda i: sgd_step(i, False), steps, warmup), P * plan.total * 2 + 16 * plan.total)
     report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum, gradients also written (bf16)",
            _time(lambda i: sgd_step(i, True), steps, warmup), P * plan.total * 4 + 16 * plan.total)
+
+    def zero1_step(i):
+        for k, (a, o) in enumerate(sets[i % 2]):
+            lo, n = k * E, plan.bucket_len(k)
+            ddp.zero1_sgd_step(a, w[lo:lo + n], v[lo:lo + n], 1e-3, 0.9, o, "mean", P)
+    report("cfg3 vitb16 p8 bf16 mean, ZeRO stage 1 step (owner sgd-momentum, bf16 parameters to every rank)",
+           _time(zero1_step, steps, warmup), P * plan.total * 4 + 16 * plan.total)
     del sets, w, v
     torch.cuda.empty_cache()
 

@@ -13,7 +13,7 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   allreduce_tree_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
                   allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
-                  allreduce_hierarchical)
+                  allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step)
 from .bucketer import GradBucketer
 
 __all__ = [
@@ -24,5 +24,5 @@ __all__ = [
     "allreduce_stepwise", "allreduce_tree", "MultiAllReduce",
     "allreduce_sgd",
     "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",
-    "allreduce_hierarchical",
+    "allreduce_hierarchical", "zero1_sgd_step_emulated", "zero1_sgd_step",
 ]

@@ -5,12 +5,14 @@ here for device memory, pointers and the current stream.
 Raw entry points (same names and argument order as the C header, pointers as
 Python ints, stream as an int handle or None):
     ddp_bucket_plan, ddp_bucket_pack, ddp_bucket_unpack,
-    allreduce_ring_emulated, allreduce_fused_sgd, reducescatter_ring_emulated,
+    allreduce_ring_emulated, allreduce_fused_sgd, zero1_sgd_step_emulated,
+    reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
     allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated
 Tensor-level helpers:
     allreduce(tensors, op, chunking, out)            -> list of outputs
     allreduce_sgd(grads, w, v, lr, mu, op, chunking, out)
+    zero1_sgd_step(grads, w, v, lr, mu, params, op, chunking)
     reduce_scatter, all_gather, allreduce_stepwise, allreduce_tree,
     allreduce_hierarchical, MultiAllReduce
 """
@@ -100,6 +102,13 @@ def allreduce_fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, mom
     _check(N.lib().allreduce_fused_sgd(_op(op), P, chunking, N.pointer_array(rank_grad),
                                        grad_dtype, n, master_w, momentum, lr, mu, out,
                                        out_dtype, stream))
+
+
+def zero1_sgd_step_emulated(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu,
+                            rank_param_out, param_dtype, stream=None):
+    _check(N.lib().zero1_sgd_step_emulated(_op(op), P, chunking, N.pointer_array(rank_grad), grad_dtype,
+                                           n, master_w, momentum, lr, mu,
+                                           N.pointer_array(rank_param_out), param_dtype, stream))
 
 
 def reducescatter_ring_emulated(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n,
@@ -376,6 +385,29 @@ class MultiAllReduce:
         run = self.bind(rank_lists, out)
         self._last = run              # the tables must outlive the launch
         return run(op, chunking)
+
+
+def zero1_sgd_step(grads, w, v, lr, mu, params, op="mean", chunking=None):
+    """ZeRO stage 1 step: reduce-scatter the rank gradients, the momentum
+    step on the float32 master weights ``w`` and momentum ``v`` (updated in
+    place; element i is its chunk owner's shard), and all-gather of the
+    updated weights into every rank's ``params`` tensor (float32 or
+    bfloat16; may be the gradient tensors themselves).  Returns ``params``."""
+    import torch
+    grads = _rank_tensors(grads, "zero1_sgd_step")
+    params = _rank_tensors(params, "zero1_sgd_step params")
+    for t in (w, v):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != grads[0].numel() \
+                or t.device != grads[0].device:
+            raise ValueError("zero1_sgd_step: w and v must be contiguous float32 tensors of the "
+                             "gradient's size on its device")
+    if len(params) != len(grads) or params[0].numel() != grads[0].numel():
+        raise ValueError("zero1_sgd_step: one parameter tensor per rank, of the gradient's size")
+    zero1_sgd_step_emulated(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
+                            torch_dtype_code(grads[0].dtype), grads[0].numel(), w.data_ptr(),
+                            v.data_ptr(), lr, mu, [p.data_ptr() for p in params],
+                            torch_dtype_code(params[0].dtype), current_stream(grads[0].device))
+    return params
 
 
 def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):

@@ -293,9 +293,13 @@ int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const
     return ok();
 }
 
-int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
-                        ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr,
-                        float mu, void* const* rank_grad_out, ddp_dtype out_dtype, void* stream) {
+namespace {
+
+// The fused optimizer step; write_out: 0 nothing, 1 the reduced gradient,
+// 2 the updated weights, into rank_out.
+int fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
+              ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr, float mu,
+              void* const* rank_grad_out, ddp_dtype out_dtype, int write_out, void* stream) {
     int s = validate_reduce(op, P, chunking, rank_grad, grad_dtype, rank_grad_out, out_dtype, n, false);
     if (s) return s;
     if (master_w == nullptr || momentum == nullptr) return fail(DDP_E_ARG, "master_w or momentum is NULL");
@@ -331,7 +335,7 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const voi
     l.in_bf16 = grad_dtype == DDP_BF16;
     l.out_bf16 = out_dtype == DDP_BF16;
     l.sgd = 1;
-    l.write_out = rank_grad_out != nullptr;
+    l.write_out = rank_grad_out != nullptr ? write_out : 0;
     for (int r = 0; r < P; ++r) {
         l.in[r] = rank_grad[r];
         l.out[r] = rank_grad_out ? rank_grad_out[r] : nullptr;
@@ -346,6 +350,23 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const voi
     const int e = ddp::launch_ring_reduce(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
+}
+
+}  // namespace
+
+int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
+                        ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr,
+                        float mu, void* const* rank_grad_out, ddp_dtype out_dtype, void* stream) {
+    return fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu, rank_grad_out,
+                     out_dtype, 1, stream);
+}
+
+int zero1_sgd_step_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
+                            ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr,
+                            float mu, void* const* rank_param_out, ddp_dtype param_dtype, void* stream) {
+    if (rank_param_out == nullptr) return fail(DDP_E_ARG, "rank_param_out is NULL");
+    return fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu, rank_param_out,
+                     param_dtype, 2, stream);
 }
 
 int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,

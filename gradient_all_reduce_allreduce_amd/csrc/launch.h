@@ -22,7 +22,7 @@ struct RingLaunch {
     int in_bf16;       // input element type is bf16
     int out_bf16;      // output element type is bf16
     int sgd;           // apply the momentum step to w, v
-    int write_out;     // write the reduced gradient to out[]
+    int write_out;     // write to out[]: 1 the reduced gradient, 2 (with sgd) the updated weights
     const void* in[kMaxRanks];
     void* out[kMaxRanks];
     float* w;

@@ -12,7 +12,9 @@
 // distributed guide, ReduceOperation), optionally one SGD-momentum step on
 // float32 master weights (CS336 Lecture 8, "Data Parallelism (DDP)";
 // "Distributed Training", "Mixed-Precision Training"), and writes the
-// result to every rank (the all-gather).
+// result -- the reduced gradient, or after the step the updated weights
+// (ZeRO stage 1, "Distributed Training", "Sharded data parallelism") -- to
+// every rank (the all-gather).
 //
 // The work is bound by HBM bandwidth: per element it reads P inputs, writes
 // P outputs and does P-1 float32 additions.  The design follows from that:
@@ -66,7 +68,7 @@ struct RingArgs {
     uint32_t n;          // elements in this launch (< 2^29)
     uint32_t n_vec;      // elements covered by whole lane vectors
     int32_t mean;
-    int32_t write_out;
+    int32_t write_out;   // with SGD: 0 nothing, 1 the reduced gradient, 2 the updated weights
     uint64_t parents;    // tree strategies: 4 bits per fold register c >= 1, its parent register
     int64_t Lg;          // two-level strategies: chunk length of the ring over nodes
     int32_t groups;      // two-level strategies: G nodes of group_size ranks, node-major
@@ -209,6 +211,7 @@ __device__ __forceinline__ void process_element(KArgs a, uint32_t i) {
         a->w[i] = w;
         a->v[i] = v;
         if (!a->write_out) return;
+        if (a->write_out == 2) g = w;
     }
 #pragma unroll
     for (int r = 0; r < P; ++r) {
@@ -316,6 +319,10 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
             store16(reinterpret_cast<char*>(a->w) + i0 * 4u, wq);
             store16(reinterpret_cast<char*>(a->v) + i0 * 4u, vq);
             if (!a->write_out) continue;
+            if (a->write_out == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) g[e] = ws[u][e];
+            }
         }
         if constexpr (OUTB && V == 8) {
             u32x4 o;

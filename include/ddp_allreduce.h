@@ -227,6 +227,44 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
                         ddp_dtype out_dtype, void* stream);
 
 /*
+ * zero1_sgd_step_emulated -- one ZeRO stage 1 step: the optimizer state is
+ * sharded over the ranks and the updated parameters go to every rank.
+ *
+ * Stage 1 partitions the 32-bit master weights and the optimizer's moments
+ * across the data-parallel ranks, each rank updating only its partition;
+ * each parameter belongs to one rank, whose optimizer updates it, and the
+ * updated parameters are then sent to all ranks ("Distributed Training",
+ * "Sharded data parallelism: ZeRO and FSDP").  Here the partition is the
+ * ring's own: element i belongs to the owner of its chunk, where the
+ * reduce-scatter ends.  In one pass, for every element: the reduce-scatter
+ * in ring order (the same float32 value, Mean applied, as
+ * allreduce_ring_emulated), the owner's momentum step
+ *     v = mu * v;  v = v + g;  w = w - lr * v
+ * on its shard of master_w and momentum (one rounding per operation), and
+ * the all-gather of the updated weight, rounded to param_dtype (bf16:
+ * nearest even), into every rank's parameter buffer.  master_w and
+ * momentum hold the union of the P shards.  The update equals that of
+ * allreduce_fused_sgd bit for bit: stage 1 only partitions the state.
+ *
+ *   rank_grad        host array [P] of device pointers, n elements of grad_dtype
+ *   master_w         device pointer, n floats, updated in place
+ *   momentum         device pointer, n floats, updated in place
+ *   lr, mu           learning rate and momentum factor (finite)
+ *   rank_param_out   host array [P] of device pointers, n elements of
+ *                    param_dtype, receiving the updated parameters; entry r
+ *                    may be rank_grad[r] itself (exact aliasing)
+ *   other arguments as for allreduce_ring_emulated.  master_w and momentum
+ *   must be disjoint from each other and from every other buffer.
+ * Errors: DDP_E_ARG (also for a NULL rank_param_out), DDP_E_ALIGN,
+ * DDP_E_OVERLAP, DDP_E_HIP.
+ */
+int zero1_sgd_step_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
+                            const void* const* rank_grad, ddp_dtype grad_dtype,
+                            int64_t n, float* master_w, float* momentum, float lr,
+                            float mu, void* const* rank_param_out,
+                            ddp_dtype param_dtype, void* stream);
+
+/*
  * reducescatter_ring_emulated -- the first half of the ring on its own.
  *
  * Every rank ends holding the finished reduction of the chunks it owns

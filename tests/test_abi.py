@@ -180,6 +180,31 @@ def test_fused_sgd_errors():
     assert sgd(n=0) == N.DDP_OK
 
 
+def zero1(P=2, C=2, grads=None, gt=1, n=16, w=A + 200 * MB, v=A + 300 * MB, lr=1e-3, mu=0.9,
+          params="default", pt=1, op=1):
+    grads = grads if grads is not None else [A + r * MB for r in range(P)]
+    if params == "default":
+        params = [A + (400 + r) * MB for r in range(P)]
+    return N.lib().zero1_sgd_step_emulated(op, P, C, N.pointer_array(grads), gt, n, w, v, lr, mu,
+                                           N.pointer_array(params) if params else None, pt, None)
+
+
+def test_zero1_errors():
+    assert zero1(params=None) == N.DDP_E_ARG                         # the parameters are the output
+    assert zero1(w=None) == N.DDP_E_ARG
+    assert zero1(pt=7) == N.DDP_E_ARG
+    assert zero1(lr=float("nan")) == N.DDP_E_ARG
+    assert zero1(P=0) == N.DDP_E_ARG
+    assert zero1(w=A + 200 * MB + 8) == N.DDP_E_ALIGN
+    assert zero1(params=[A + 400 * MB + 2, A + 401 * MB]) == N.DDP_E_ALIGN
+    assert zero1(w=A + 400 * MB, n=1024) == N.DDP_E_OVERLAP           # w aliases a parameter buffer
+    assert zero1(params=[A + 400 * MB, A + 400 * MB + 64], n=1024) == N.DDP_E_OVERLAP
+    # parameters in place of bf16 gradients: exact aliasing, same element size
+    assert zero1(params=[A, A + MB], n=0) == N.DDP_OK
+    assert zero1(params=[A, A + MB], pt=0, n=1024) == N.DDP_E_OVERLAP  # f32 over bf16: not exact
+    assert zero1(n=0) == N.DDP_OK
+
+
 def test_pack_errors():
     lib = N.lib()
     buckets = N.pointer_array([A, A + MB])
