@@ -13,7 +13,8 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   allreduce_tree_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
                   allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
-                  allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step)
+                  allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step,
+                  allreduce_multi_fused_sgd)
 from .bucketer import GradBucketer
 
 __all__ = [
@@ -25,4 +26,5 @@ __all__ = [
     "allreduce_sgd",
     "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",
     "allreduce_hierarchical", "zero1_sgd_step_emulated", "zero1_sgd_step",
+    "allreduce_multi_fused_sgd",
 ]

@@ -8,7 +8,8 @@ Python ints, stream as an int handle or None):
     allreduce_ring_emulated, allreduce_fused_sgd, zero1_sgd_step_emulated,
     reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
-    allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated
+    allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
+    allreduce_multi_fused_sgd
 Tensor-level helpers:
     allreduce(tensors, op, chunking, out)            -> list of outputs
     allreduce_sgd(grads, w, v, lr, mu, op, chunking, out)
@@ -177,6 +178,14 @@ def allreduce_multi_ring_emulated(op, P, chunking, n_tensors, tiles_dev, total_t
     _check(N.lib().allreduce_multi_ring_emulated(_op(op), P, chunking, n_tensors, tiles_dev,
                                                  total_tiles, tile_elems, in_ptrs_dev, in_dtype,
                                                  out_ptrs_dev, out_dtype, stream))
+
+
+def allreduce_multi_fused_sgd(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems,
+                              in_ptrs_dev, grad_dtype, w_ptrs_dev, v_ptrs_dev, lr, mu, out_ptrs_dev,
+                              out_dtype, stream=None):
+    _check(N.lib().allreduce_multi_fused_sgd(_op(op), P, chunking, n_tensors, tiles_dev, total_tiles,
+                                             tile_elems, in_ptrs_dev, grad_dtype, w_ptrs_dev,
+                                             v_ptrs_dev, lr, mu, out_ptrs_dev, out_dtype, stream))
 
 
 # --------------------------------------------------------- torch level ----
@@ -378,6 +387,40 @@ class MultiAllReduce:
 
         run.tables = (tin, tout)      # kept alive with the launcher
         run.out = out
+        return run
+
+    def _state_table(self, ts):
+        import torch
+        if len(ts) != len(self.shapes):
+            raise ValueError("one optimizer-state tensor per planned shape")
+        for x, s in zip(ts, self.shapes):
+            if tuple(x.shape) != s or x.dtype != torch.float32 or not x.is_contiguous() \
+                    or x.device != self.device:
+                raise ValueError("optimizer state must be contiguous float32 tensors of the planned shapes")
+        return torch.tensor([x.data_ptr() for x in ts], dtype=torch.int64).to(self.device)
+
+    def bind_sgd(self, rank_grads, w, v, out=None):
+        """Like bind(), for the all-reduce fused with one SGD-momentum step
+        per tensor: ``w`` and ``v`` are lists of T float32 tensors (each
+        parameter's master weights and momentum, updated in place); ``out``:
+        optional P lists receiving the reduced gradients.  Returns
+        ``run(lr, mu, op="mean", chunking=None)``."""
+        tin = self._table(rank_grads, self.dtype)
+        tout = self._table(out, self.out_dtype) if out is not None else None
+        tw = self._state_table(w)
+        tv = self._state_table(v)
+        stream = current_stream(self.device)
+        T = len(self.shapes)
+
+        def run(lr, mu, op="mean", chunking=None):
+            allreduce_multi_fused_sgd(op, self.P, chunking or self.P, T, self.tiles_dev.data_ptr(),
+                                      self.total_tiles, self.tile_elems, tin.data_ptr(),
+                                      torch_dtype_code(self.dtype), tw.data_ptr(), tv.data_ptr(), lr, mu,
+                                      tout.data_ptr() if tout is not None else None,
+                                      torch_dtype_code(self.out_dtype), stream)
+            return out
+
+        run.tables = (tin, tout, tw, tv)   # kept alive with the launcher
         return run
 
     def __call__(self, rank_lists, op="sum", chunking=None, out=None):

@@ -609,10 +609,11 @@ int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtyp
     return ok();
 }
 
-int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
-                                  const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
-                                  const void* const* in_ptrs_dev, ddp_dtype in_dtype, void* const* out_ptrs_dev,
-                                  ddp_dtype out_dtype, void* stream) {
+namespace {
+
+int validate_multi(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
+                   const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
+                   const void* const* in_ptrs_dev, ddp_dtype in_dtype, ddp_dtype out_dtype) {
     if (op != DDP_SUM && op != DDP_MEAN) return fail(DDP_E_ARG, "unknown reduce op %d", op);
     int s = check_ranks(P);
     if (s) return s;
@@ -620,10 +621,58 @@ int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
     if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown dtype");
     if (total_tiles < 0 || total_tiles > INT32_MAX) return fail(DDP_E_ARG, "total_tiles out of range");
-    if (tiles_dev == nullptr || in_ptrs_dev == nullptr || out_ptrs_dev == nullptr)
-        return fail(DDP_E_ARG, "NULL table");
+    if (tiles_dev == nullptr || in_ptrs_dev == nullptr) return fail(DDP_E_ARG, "NULL table");
     if (tile_elems != ddp::multi_tile_elems(P, in_dtype == DDP_BF16, out_dtype == DDP_BF16))
         return fail(DDP_E_PLAN, "tile_elems does not match this P and these dtypes");
+    return DDP_OK;
+}
+
+}  // namespace
+
+int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
+                              const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
+                              const void* const* in_ptrs_dev, ddp_dtype grad_dtype, float* const* w_ptrs_dev,
+                              float* const* v_ptrs_dev, float lr, float mu, void* const* out_ptrs_dev,
+                              ddp_dtype out_dtype, void* stream) {
+    int s = validate_multi(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems, in_ptrs_dev, grad_dtype,
+                           out_dtype);
+    if (s) return s;
+    if (w_ptrs_dev == nullptr || v_ptrs_dev == nullptr) return fail(DDP_E_ARG, "NULL weight or momentum table");
+    if (!(lr == lr) || !(mu == mu) || lr > 3.4e38f || lr < -3.4e38f || mu > 3.4e38f || mu < -3.4e38f)
+        return fail(DDP_E_ARG, "lr and mu must be finite");
+    if (total_tiles == 0) return ok();
+
+    ddp::MultiLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = grad_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.T = n_tensors;
+    l.tiles = tiles_dev;
+    l.in = in_ptrs_dev;
+    l.out = out_ptrs_dev;
+    l.w = w_ptrs_dev;
+    l.v = v_ptrs_dev;
+    l.lr = lr;
+    l.mu = mu;
+    l.sgd = 1;
+    l.total_tiles = total_tiles;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = ddp::launch_multi_ring(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
+                                  const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
+                                  const void* const* in_ptrs_dev, ddp_dtype in_dtype, void* const* out_ptrs_dev,
+                                  ddp_dtype out_dtype, void* stream) {
+    int s = validate_multi(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems, in_ptrs_dev, in_dtype,
+                           out_dtype);
+    if (s) return s;
+    if (out_ptrs_dev == nullptr) return fail(DDP_E_ARG, "NULL table");
     if (total_tiles == 0) return ok();
 
     ddp::MultiLaunch l{};

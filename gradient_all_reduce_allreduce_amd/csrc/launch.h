@@ -96,7 +96,12 @@ struct MultiLaunch {
     int32_t T;
     const ddp_tensor_tiles* tiles;
     const void* const* in;
-    void* const* out;
+    void* const* out;           // may be null with sgd: no gradient output
+    float* const* w;            // sgd: [T] device table of master weights
+    float* const* v;            // sgd: [T] device table of momentum buffers
+    float lr;
+    float mu;
+    int sgd;
     int64_t total_tiles;
     void* stream;
 };

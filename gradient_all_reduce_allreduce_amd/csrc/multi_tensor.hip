@@ -11,9 +11,13 @@
 // allreduce_ring_emulated.  The host plan gives every tensor a run of tiles;
 // a workgroup finds its tensor by a binary search over the plan (uniform,
 // scalar loads) and then works like the single-tensor kernel: rotated rank
-// pointers, one fixed fold, P output stores.  Tiles of small tensors, tiles
-// across a chunk boundary and tensors not 16-byte aligned take a per-element
-// path whose rank pointers are read per lane.
+// pointers, one fixed fold, P output stores.  Optionally every tensor then
+// takes one SGD-momentum step on its float32 master weights and momentum,
+// as each replica's optimizer.step() does after the per-parameter
+// all-reduces (same lecture section), with or without writing the reduced
+// gradients.  Tiles of small tensors, tiles
+// across a chunk boundary and tensors (or optimizer state) not 16-byte
+// aligned take a per-element path whose rank pointers are read per lane.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,7 +34,11 @@ using rr::u32x4;
 struct MultiArgs {
     const ddp_tensor_tiles* tiles;   // [T], device
     const void* const* in;           // [P * T] device, rank-major
-    void* const* out;                // [P * T] device, rank-major
+    void* const* out;                // [P * T] device, rank-major; null: no output
+    float* const* w;                 // SGD: [T] device, master weights
+    float* const* v;                 // SGD: [T] device, momentum
+    float lr;
+    float mu;
     int32_t T;
     int32_t chunking;
     int32_t mean;
@@ -42,7 +50,7 @@ __device__ __forceinline__ KMulti multi_args() {
     return (KMulti)(__builtin_amdgcn_kernarg_segment_ptr());
 }
 
-template <int P, bool INB, bool OUTB>
+template <int P, bool INB, bool OUTB, bool SGD>
 __device__ __forceinline__ void multi_element(KMulti a, int t, uint32_t i, int64_t L) {
 #pragma clang fp contract(off)
     const int T = a->T;
@@ -60,6 +68,16 @@ __device__ __forceinline__ void multi_element(KMulti a, int t, uint32_t i, int64
         g = k == 0 ? xk : g + xk;
     }
     if (a->mean) g = rr::mean_of<P>(g);
+    if constexpr (SGD) {
+        float* wp = a->w[t];
+        float* vp = a->v[t];
+        float w = wp[i];
+        float v = vp[i];
+        rr::momentum_step(g, w, v, a->lr, a->mu);
+        wp[i] = w;
+        vp[i] = v;
+        if (a->out == nullptr) return;
+    }
 #pragma unroll
     for (int r = 0; r < P; ++r) {
         void* o = a->out[static_cast<int64_t>(r) * T + t];
@@ -71,7 +89,7 @@ __device__ __forceinline__ void multi_element(KMulti a, int t, uint32_t i, int64
     }
 }
 
-template <int P, bool INB, bool OUTB>
+template <int P, bool INB, bool OUTB, bool SGD>
 __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
 #pragma clang fp contract(off)
     constexpr int U = ring_vectors_per_lane(P, false);
@@ -103,22 +121,27 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     const int64_t j1 = (end - 1) / L;
     const uint32_t tid = threadIdx.x;
 
+    const bool write_out = !SGD || a->out != nullptr;
     bool vector_path = j0 == j1 && end - t0 == TILE;
     uintptr_t align = 0;
 #pragma unroll
     for (int r = 0; r < P; ++r) {
         align |= reinterpret_cast<uintptr_t>(a->in[static_cast<int64_t>(r) * T + t]);
-        align |= reinterpret_cast<uintptr_t>(a->out[static_cast<int64_t>(r) * T + t]);
+        if (write_out) align |= reinterpret_cast<uintptr_t>(a->out[static_cast<int64_t>(r) * T + t]);
     }
+    if constexpr (SGD) align |= reinterpret_cast<uintptr_t>(a->w[t]) | reinterpret_cast<uintptr_t>(a->v[t]);
     vector_path = vector_path && (align & 15u) == 0;
 
     if (!vector_path) {
-        for (uint32_t i = t0 + tid; i < end; i += kBlock) multi_element<P, INB, OUTB>(a, t, i, L);
+        for (uint32_t i = t0 + tid; i < end; i += kBlock) multi_element<P, INB, OUTB, SGD>(a, t, i, L);
         return;
     }
 
     const int s0 = static_cast<int>(j0 % P);
     u32x4 x[P][U];
+    constexpr int WV = SGD ? V / 4 : 1;   // 16-byte state vectors per lane vector
+    u32x4 wq[U][WV];
+    u32x4 vq[U][WV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -126,6 +149,13 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
         for (int k = 0; k < P; ++k) {
             const char* p = static_cast<const char*>(a->in[static_cast<int64_t>(rr::rank_at(s0, k, P)) * T + t]);
             x[k][u] = rr::load_lane<WIN>(p + i0 * IES);
+        }
+        if constexpr (SGD) {
+#pragma unroll
+            for (int q = 0; q < WV; ++q) {
+                wq[u][q] = rr::load16(reinterpret_cast<const char*>(a->w[t]) + (i0 + 4 * q) * 4u);
+                vq[u][q] = rr::load16(reinterpret_cast<const char*>(a->v[t]) + (i0 + 4 * q) * 4u);
+            }
         }
     }
     float acc[U][V];
@@ -138,6 +168,23 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
         float g[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) g[e] = mean ? rr::mean_of<P>(acc[u][e]) : acc[u][e];
+        if constexpr (SGD) {
+#pragma unroll
+            for (int q = 0; q < WV; ++q) {
+                u32x4 wn, vn;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float w = __uint_as_float(wq[u][q][e]);
+                    float v = __uint_as_float(vq[u][q][e]);
+                    rr::momentum_step(g[4 * q + e], w, v, a->lr, a->mu);
+                    wn[e] = __float_as_uint(w);
+                    vn[e] = __float_as_uint(v);
+                }
+                rr::store16(reinterpret_cast<char*>(a->w[t]) + (i0 + 4 * q) * 4u, wn);
+                rr::store16(reinterpret_cast<char*>(a->v[t]) + (i0 + 4 * q) * 4u, vn);
+            }
+            if (!write_out) continue;
+        }
         if constexpr (OUTB && V == 8) {
             u32x4 o;
 #pragma unroll
@@ -166,11 +213,11 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     }
 }
 
-template <bool INB, bool OUTB>
+template <bool INB, bool OUTB, bool SGD>
 const void* multi_kernel_for(int P) {
     switch (P) {
 #define DDP_CASE(p) \
-    case p: return reinterpret_cast<const void*>(&multi_ring_kernel<p, INB, OUTB>);
+    case p: return reinterpret_cast<const void*>(&multi_ring_kernel<p, INB, OUTB, SGD>);
         DDP_CASE(1) DDP_CASE(2) DDP_CASE(3) DDP_CASE(4)
         DDP_CASE(5) DDP_CASE(6) DDP_CASE(7) DDP_CASE(8)
         DDP_CASE(9) DDP_CASE(10) DDP_CASE(11) DDP_CASE(12)
@@ -189,8 +236,17 @@ int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16) {
 
 int launch_multi_ring(const MultiLaunch& l, const char** msg) {
     if (l.total_tiles <= 0) return 0;
-    const void* fn = l.in_bf16 ? (l.out_bf16 ? multi_kernel_for<true, true>(l.P) : multi_kernel_for<true, false>(l.P))
-                               : (l.out_bf16 ? multi_kernel_for<false, true>(l.P) : multi_kernel_for<false, false>(l.P));
+    const void* fn;
+    if (l.sgd) {
+        fn = l.in_bf16 ? (l.out_bf16 ? multi_kernel_for<true, true, true>(l.P) : multi_kernel_for<true, false, true>(l.P))
+                       : (l.out_bf16 ? multi_kernel_for<false, true, true>(l.P)
+                                     : multi_kernel_for<false, false, true>(l.P));
+    } else {
+        fn = l.in_bf16 ? (l.out_bf16 ? multi_kernel_for<true, true, false>(l.P)
+                                     : multi_kernel_for<true, false, false>(l.P))
+                       : (l.out_bf16 ? multi_kernel_for<false, true, false>(l.P)
+                                     : multi_kernel_for<false, false, false>(l.P));
+    }
     if (fn == nullptr) {
         *msg = "no multi-tensor kernel for this rank count";
         return static_cast<int>(hipErrorInvalidValue);
@@ -199,6 +255,10 @@ int launch_multi_ring(const MultiLaunch& l, const char** msg) {
     a.tiles = l.tiles;
     a.in = l.in;
     a.out = l.out;
+    a.w = l.w;
+    a.v = l.v;
+    a.lr = l.lr;
+    a.mu = l.mu;
     a.T = l.T;
     a.chunking = l.chunking;
     a.mean = l.op == DDP_MEAN;

@@ -460,6 +460,41 @@ int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
                                   void* const* out_ptrs_dev, ddp_dtype out_dtype,
                                   void* stream);
 
+/*
+ * allreduce_multi_fused_sgd -- the multi-tensor all-reduce followed, in the
+ * same launch, by one SGD-with-momentum step per tensor: the whole
+ * per-parameter data-parallel step (CS336 Lecture 8, "Data Parallelism
+ * (DDP)": every parameter's gradient is all-reduced with AVG, then every
+ * rank runs optimizer.step() locally on identical gradients).  Tensor t is
+ * reduced exactly as allreduce_multi_ring_emulated reduces it; with g its
+ * reduced float32 gradient (Mean applied, before any output rounding) each
+ * element then does, one rounding per operation,
+ *     v = mu * v;  v = v + g;  w = w - lr * v
+ * on the tensor's float32 master weights and momentum (one copy stands for
+ * the identical replicas), as allreduce_fused_sgd does.
+ *
+ *   tiles_dev, total_tiles, tile_elems   the plan of ddp_multi_plan for these
+ *                tensors, P, grad_dtype and out_dtype (out_dtype sets the
+ *                tile size even when no gradient is written)
+ *   in_ptrs_dev  DEVICE array [P * n_tensors] of gradient pointers,
+ *                rank-major, elements of grad_dtype
+ *   w_ptrs_dev, v_ptrs_dev   DEVICE arrays [n_tensors] of pointers to each
+ *                tensor's float32 master weights and momentum, updated in
+ *                place; they must not overlap any other buffer (not checked:
+ *                the tables live on the device)
+ *   lr, mu       learning rate and momentum factor (finite)
+ *   out_ptrs_dev DEVICE array [P * n_tensors] receiving the reduced
+ *                gradients as out_dtype, or NULL to skip writing them
+ * Errors: DDP_E_ARG, DDP_E_PLAN (tile_elems mismatch), DDP_E_HIP.
+ */
+int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
+                              int32_t n_tensors, const ddp_tensor_tiles* tiles_dev,
+                              int64_t total_tiles, int64_t tile_elems,
+                              const void* const* in_ptrs_dev, ddp_dtype grad_dtype,
+                              float* const* w_ptrs_dev, float* const* v_ptrs_dev,
+                              float lr, float mu, void* const* out_ptrs_dev,
+                              ddp_dtype out_dtype, void* stream);
+
 /* Message describing the calling thread's most recent non-OK status
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* ddp_last_error(void);

@@ -205,6 +205,18 @@ def test_zero1_errors():
     assert zero1(n=0) == N.DDP_OK
 
 
+def test_multi_fused_sgd_errors():
+    _, _, tile = ddp.ddp_multi_plan([1], 8, ddp.F32, ddp.F32)
+    f = N.lib().allreduce_multi_fused_sgd
+    assert f(1, 8, 8, 1, A, 1, tile, A, 0, None, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 1, tile, A, 0, A, None, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 1, tile, A, 0, A, A, float("nan"), 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 1, tile + 4, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_PLAN
+    assert f(1, 8, 8, 1, None, 1, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(5, 8, 8, 1, A, 1, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 0, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_OK
+
+
 def test_pack_errors():
     lib = N.lib()
     buckets = N.pointer_array([A, A + MB])

@@ -114,3 +114,125 @@ def test_per_parameter_ddp_step_on_a_tiny_mlp():
             assert_same_bits(out[r][t].cpu().numpy().reshape(-1), want[r], f"param {t}")
         d = np.linalg.norm(out[0][t].cpu().numpy() - full[t].numpy()) / np.linalg.norm(full[t].numpy())
         assert d < 1e-5
+
+
+# ------------------------------------------------- fused optimizer step ----
+
+def sgd_state(shapes, seed, misalign=0):
+    """Per tensor float32 master weights and momentum (host copies and
+    device tensors, optionally misaligned views)."""
+    rng = np.random.default_rng(seed)
+    host, dev = [], []
+    for s in shapes:
+        n = int(np.prod(s, dtype=np.int64))
+        pair_h, pair_d = [], []
+        for scale in (0.02, 1e-3):
+            x = (rng.standard_normal(n) * scale).astype(np.float32)
+            store = torch.empty(n + misalign, dtype=torch.float32, device=DEV)
+            t = store[misalign:misalign + n].view(s)
+            t.copy_(torch.from_numpy(x).view(s))
+            pair_h.append(x)
+            pair_d.append(t)
+        host.append(pair_h)
+        dev.append(pair_d)
+    return host, dev
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("P", [1, 3, 8])
+@pytest.mark.parametrize("misalign", [0, 1])
+@pytest.mark.parametrize("with_out", [False, True])
+def test_multi_fused_sgd_equals_oracle_per_tensor(pair, P, misalign, with_out):
+    """Every tensor: the oracle's ring on that tensor alone, then its
+    momentum step, bit for bit; the reduced gradients when asked for."""
+    it, ot = pair
+    tdt = torch.bfloat16 if it == "bf16" else torch.float32
+    odt = torch.bfloat16 if ot == "bf16" else torch.float32
+    shapes = [(1,), (7,), (64,), (3, 5), (1000,), (4096,), (4097,), (33, 129), (70001,), (0,)]
+    host, dev = make(P, shapes, tdt, seed=10 * P + misalign, misalign=misalign)
+    sh, sd = sgd_state(shapes, seed=P, misalign=misalign)
+    m = ddp.MultiAllReduce(shapes, P, tdt, odt, device=DEV)
+    out = [[torch.empty(s, dtype=odt, device=DEV) for s in shapes] for _ in range(P)] if with_out else None
+    run = m.bind_sgd(dev, [p[0] for p in sd], [p[1] for p in sd], out=out)
+    C = 2 * P + 1
+    run(1e-3, 0.9, "mean", C)
+    torch.cuda.synchronize()
+    for t, s in enumerate(shapes):
+        X = np.stack([host[r][t] for r in range(P)])
+        if X.shape[1] == 0:
+            continue
+        g = oracle_ring(X, "mean", C, in_dtype=it, out_dtype="f32")[0]
+        w1, v1 = oracle.sgd_momentum(g, sh[t][0], sh[t][1], 1e-3, 0.9)
+        what = f"{it}->{ot} P={P} t={t} misalign={misalign}"
+        assert_same_bits(sd[t][0].cpu().numpy().reshape(1, -1), w1[None], what + " w")
+        assert_same_bits(sd[t][1].cpu().numpy().reshape(1, -1), v1[None], what + " v")
+        if with_out:
+            want = oracle_ring(X, "mean", C, in_dtype=it, out_dtype=ot)
+            got = np.stack([bits_of(out[r][t]) for r in range(P)])
+            assert_same_bits(got, want, what + " grads")
+
+
+def test_multi_fused_sgd_equals_bucketed_fused_sgd():
+    """The per-parameter fused step on 161 ResNet-50 tensors updates the
+    weights exactly as the single-tensor fused step does per tensor."""
+    P = 8
+    shapes = workloads.resnet50_shapes()
+    _, dev = make(P, shapes, torch.float32, seed=6)
+    _, sd = sgd_state(shapes, seed=7)
+    ref = [(p[0].clone(), p[1].clone()) for p in sd]
+    m = ddp.MultiAllReduce(shapes, P, torch.float32, device=DEV)
+    m.bind_sgd(dev, [p[0] for p in sd], [p[1] for p in sd])(1e-3, 0.9, "mean", P)
+    for t in range(len(shapes)):
+        ddp.allreduce_sgd([dev[r][t].reshape(-1) for r in range(P)], ref[t][0].reshape(-1),
+                          ref[t][1].reshape(-1), 1e-3, 0.9, "mean", P)
+    torch.cuda.synchronize()
+    for t in range(len(shapes)):
+        assert torch.equal(sd[t][0].view(torch.int32), ref[t][0].view(torch.int32)), t
+        assert torch.equal(sd[t][1].view(torch.int32), ref[t][1].view(torch.int32)), t
+
+
+def test_per_parameter_ddp_training_steps_on_a_tiny_mlp():
+    """The lecture's DDP loop, every step on the GPU in one launch: each rank
+    computes its shard's gradients, all of them are all-reduced with AVG and
+    each replica's SGD-momentum step follows.  Over three steps the weights
+    track single-device training on the full batch (float32 round-off) and
+    match the oracle's ring + step bit for bit."""
+    W = 4
+    torch.manual_seed(0)
+    net = torch.nn.Sequential(torch.nn.Linear(16, 32), torch.nn.Tanh(), torch.nn.Linear(32, 3))
+    ref = torch.nn.Sequential(torch.nn.Linear(16, 32), torch.nn.Tanh(), torch.nn.Linear(32, 3))
+    ref.load_state_dict(net.state_dict())
+    opt = torch.optim.SGD(ref.parameters(), lr=0.1, momentum=0.9)
+    g = torch.Generator().manual_seed(1)
+    shapes = [tuple(p.shape) for p in net.parameters()]
+    w_dev = [p.detach().to(DEV).contiguous() for p in net.parameters()]
+    v_dev = [torch.zeros_like(p) for p in w_dev]
+    w_host = [p.detach().numpy().reshape(-1).copy() for p in net.parameters()]
+    v_host = [np.zeros_like(x) for x in w_host]
+    m = ddp.MultiAllReduce(shapes, W, torch.float32, device=DEV)
+    for step in range(3):
+        X = torch.randn(32, 16, generator=g)
+        y = torch.randint(0, 3, (32,), generator=g)
+        shard = []
+        for r in range(W):
+            with torch.no_grad():
+                for p, wd in zip(net.parameters(), w_dev):
+                    p.copy_(wd.cpu())
+            net.zero_grad()
+            F.cross_entropy(net(X[r::W]), y[r::W]).backward()
+            shard.append([p.grad.detach().clone() for p in net.parameters()])
+        dev = [[t.to(DEV) for t in shard[r]] for r in range(W)]
+        m.bind_sgd(dev, w_dev, v_dev)(0.1, 0.9, "mean", W)
+        torch.cuda.synchronize()
+        for t in range(len(shapes)):
+            Xs = np.stack([shard[r][t].numpy().reshape(-1) for r in range(W)])
+            gm, _ = oracle.ring_allreduce(Xs, "mean", W)
+            w_host[t], v_host[t] = oracle.sgd_momentum(gm[0], w_host[t], v_host[t], 0.1, 0.9)
+            assert_same_bits(w_dev[t].cpu().numpy().reshape(1, -1), w_host[t][None], f"step {step} w{t}")
+        opt.zero_grad()
+        F.cross_entropy(ref(X), y).backward()
+        opt.step()
+    for p, wd in zip(ref.parameters(), w_dev):
+        d = (np.linalg.norm(wd.cpu().numpy() - p.detach().numpy()) /
+             np.linalg.norm(p.detach().numpy()))
+        assert d < 1e-5, d
