@@ -10,10 +10,12 @@ namespace ddp {
 
 constexpr int kMaxRanks = DDP_MAX_RANKS;
 
-// Everything the fused ring-reduce kernel needs; validated by the caller.
-// What one launch sequence computes.
+// What one launch sequence computes: the ring all-reduce (optionally with
+// the fused optimizer step), one of its halves, or a fold along a tree
+// (tree, centralized and two-level strategies).
 enum RingMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2, kTree = 3 };
 
+// Everything launch_ring_reduce needs; validated by the caller (api.cpp).
 struct RingLaunch {
     int mode;          // RingMode
     int P;
