@@ -190,6 +190,13 @@ def run_suite(steps, warmup):
     report("cfg2 resnet50 p8 f32 mean, pack -> all-reduce -> unpack", ms, nbytes,
            with_copies_gbps=round(3 * nbytes / (ms * 1e-3) / 1e9, 1),
            note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
+    copy_bytes = P * plan.total * 4 * 2     # every rank's gradients read once and written once
+    report("cfg2 resnet50 p8 f32, pack alone (161 tensors -> 4 buckets, all ranks)",
+           _time(lambda i: [plan.pack(table, k, bufs) for k in range(plan.n_buckets)], steps, warmup),
+           copy_bytes)
+    report("cfg2 resnet50 p8 f32, unpack alone (4 buckets -> 161 tensors, all ranks)",
+           _time(lambda i: [plan.unpack(table, k, bufs) for k in range(plan.n_buckets)], steps, warmup),
+           copy_bytes)
     del tensors, outs, run, table, bufs
     torch.cuda.empty_cache()
 
@@ -238,7 +245,14 @@ def run_suite(steps, warmup):
     ms = _time(ragged_step, max(2, steps // 20), 1)
     report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, pack -> all-reduce -> unpack "
            f"({plan.n_buckets} buckets)", ms, nbytes4,
-           with_copies_gbps=round(3 * nbytes4 / (ms * 1e-3) / 1e9, 1))
+           with_copies_gbps=round(3 * nbytes4 / (ms * 1e-3) / 1e9, 1),
+           note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
+    report(f"cfg4 ragged {len(sizes)} tensors p4 f32, pack alone ({plan.n_buckets} buckets, all ranks)",
+           _time(lambda i: [plan.pack(table, k, bufs) for k in range(plan.n_buckets)], max(2, steps // 20), 1),
+           P4 * plan.total * 8)
+    report(f"cfg4 ragged {len(sizes)} tensors p4 f32, unpack alone ({plan.n_buckets} buckets, all ranks)",
+           _time(lambda i: [plan.unpack(table, k, bufs) for k in range(plan.n_buckets)], max(2, steps // 20), 1),
+           P4 * plan.total * 8)
     run = ddp.MultiAllReduce(shapes4, P4, torch.float32, device=dev).bind(tensors, tensors)
     report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, one multi-tensor launch, in place",
            _time(lambda i: run("sum"), max(2, steps // 20), 1), nbytes4)

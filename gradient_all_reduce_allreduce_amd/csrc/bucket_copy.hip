@@ -19,11 +19,12 @@
 // tensor address is aligned, else as element-size accesses; a lane issues
 // all of those loads before its first store, so kVecPerLane vectors per
 // lane are in flight.  Vectors across a segment boundary move element by
-// element afterwards.  Stores are ordinary (measured faster than
-// non-temporal ones here: the all-reduce that reads a packed bucket next
-// finds part of it in the last-level cache).  Every bucket element is
-// written exactly once (the segments tile the bucket), so no
-// synchronisation between workgroups is needed.
+// element afterwards.  Pack stores are ordinary (the all-reduce that reads
+// a packed bucket next finds part of it in the last-level cache), unpack
+// stores non-temporal (the tensors are not read again soon); both choices
+// measured faster than the other.  Every bucket element is written exactly
+// once (the segments tile the bucket), so no synchronisation between
+// workgroups is needed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,7 +36,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
-constexpr int kVecPerLane = 8;   // 16-byte vectors per lane and tile
+constexpr int kVecPerLane = 4;   // 16-byte vectors per lane and tile
 
 struct CopyArgs {
     const ddp_segment* segs;
@@ -73,17 +74,17 @@ __device__ __forceinline__ u32x4 load_elems(const char* p, int es) {
     return v;
 }
 
-__device__ __forceinline__ void store_elems(char* p, u32x4 v, int es) {
+__device__ __forceinline__ void store_elems_nt(char* p, u32x4 v, int es) {
     if (es == 4) {
         uint32_t* q = reinterpret_cast<uint32_t*>(p);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q[j] = v[j];
+        for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(static_cast<uint32_t>(v[j]), q + j);
     } else {
         uint16_t* q = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            q[2 * j] = static_cast<uint16_t>(v[j] & 0xffffu);
-            q[2 * j + 1] = static_cast<uint16_t>(v[j] >> 16);
+            __builtin_nontemporal_store(static_cast<uint16_t>(v[j] & 0xffffu), q + 2 * j);
+            __builtin_nontemporal_store(static_cast<uint16_t>(v[j] >> 16), q + 2 * j + 1);
         }
     }
 }
@@ -178,12 +179,16 @@ __global__ __launch_bounds__(kBlock) void bucket_copy_kernel(CopyArgs a) {
         for (int u = 0; u < kVecPerLane; ++u) {
             char* bk = bucket + (lo + static_cast<int64_t>(u * kBlock + tid) * ve) * es;
             if (cls[u] == 1) {
-                *reinterpret_cast<u32x4*>(PACK ? bk : tn[u]) = x[u];
+                if (PACK) {
+                    *reinterpret_cast<u32x4*>(bk) = x[u];
+                } else {
+                    __builtin_nontemporal_store(x[u], reinterpret_cast<u32x4*>(tn[u]));
+                }
             } else if (cls[u] == 2) {
                 if (PACK) {
                     *reinterpret_cast<u32x4*>(bk) = x[u];
                 } else {
-                    store_elems(tn[u], x[u], es);
+                    store_elems_nt(tn[u], x[u], es);
                 }
             }
         }

@@ -95,6 +95,16 @@ def test_pack_many_small_segments_per_tile():
     want = [oracle.pack(host[r], 4, 1 << 20) for r in range(P)]
     for r in range(P):
         assert np.array_equal(bits(bufs[r][:b.bucket_len(0)]), want[r][0])
+    # and back, into cleared tensors, through the same staging rounds
+    for r in range(P):
+        for t in dev[r]:
+            t.zero_()
+    b.unpack(table, 0, bufs)
+    torch.cuda.synchronize()
+    for r in range(P):
+        for t, x in zip(dev[r], host[r]):
+            assert np.array_equal(bits(t.reshape(-1)).view(np.uint32),
+                                  np.asarray(x, dtype=np.float32).reshape(-1).view(np.uint32))
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
