@@ -273,22 +273,7 @@ int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const
     l.n = n;
     l.stream = stream;
     const char* msg = nullptr;
-    int e = 0;
-    if (in_dtype == DDP_BF16 && out_dtype == DDP_F32) {
-        // Outputs twice as wide as the inputs: the reduce-scatter pass
-        // (P reads, one owner write) then the all-gather pass (one read,
-        // P-1 writes) separate reads from writes in time and measure faster
-        // than the single pass.  Same additions, same bits.
-        l.mode = ddp::kReduceScatter;
-        e = ddp::launch_ring_reduce(l, &msg);
-        if (e == 0) {
-            l.mode = ddp::kAllGather;
-            l.in_bf16 = 0;    // the all-gather moves float32 output elements
-            e = ddp::launch_ring_reduce(l, &msg);
-        }
-    } else {
-        e = ddp::launch_ring_reduce(l, &msg);
-    }
+    const int e = ddp::launch_ring_reduce(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
 }

@@ -37,6 +37,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 constexpr int kVecPerLane = 4;   // 16-byte vectors per lane and tile
+// LDS the kernel declares: the staged segments (s_dst, s_len, s_ten).
+constexpr unsigned kStaticLds = kBlock * (2 * sizeof(int64_t) + sizeof(char*));
 
 struct CopyArgs {
     const ddp_segment* segs;
@@ -238,7 +240,8 @@ int launch_bucket_copy(const CopyLaunch& l, const char** msg) {
                             : reinterpret_cast<const void*>(&bucket_copy_kernel<false>);
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.tiles), static_cast<unsigned>(l.P)),
-                                         dim3(kBlock), args, 0, static_cast<hipStream_t>(l.stream));
+                                         dim3(kBlock), args, lds_reserve(kCopyWgPerCu, kStaticLds),
+                                         static_cast<hipStream_t>(l.stream));
     if (e != hipSuccess) {
         *msg = "hipLaunchKernel(bucket_copy)";
         return static_cast<int>(e);

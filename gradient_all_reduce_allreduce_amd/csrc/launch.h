@@ -10,6 +10,42 @@ namespace ddp {
 
 constexpr int kMaxRanks = DDP_MAX_RANKS;
 
+// ---- launch shape -----------------------------------------------------------
+//
+// Every kernel here streams HBM with little arithmetic.  On MI355X the mix
+// of reads and writes of the all-reduce (P input streams, P output streams)
+// reaches its highest rate when few waves per CU keep requests in flight:
+// 6.39 TB/s at 4 one-wave workgroups per CU against 5.7 TB/s with the CUs
+// filled, in a plain 8-in/8-out streaming kernel.  A launch therefore
+// reserves LDS it never touches, so that at most the chosen number of its
+// workgroups fit on a CU at once; the dispatcher still hands tiles to
+// whichever CU frees up.  The limit only pays where a tile's first load
+// follows its start within a few dozen instructions: the multi-tensor and
+// bucket-copy kernels, which search a table first, and the two halves of
+// the ring measured slower with it, so they keep the hardware's occupancy.
+
+constexpr unsigned kLdsBytesPerCu = 160u * 1024u;   // CDNA4 compute unit
+
+// Dynamic LDS for a launch whose kernel already uses `static_bytes`, such
+// that at most `wg_per_cu` workgroups are resident per CU (0: no limit).
+constexpr unsigned lds_reserve(int wg_per_cu, unsigned static_bytes = 0) {
+    if (wg_per_cu <= 0) return 0u;
+    const unsigned per = (kLdsBytesPerCu / static_cast<unsigned>(wg_per_cu)) & ~1023u;
+    return per > static_bytes ? per - static_bytes : 0u;
+}
+
+// Lanes per workgroup of the ring, tree and multi-tensor kernels: one wave,
+// so that the resident waves of a CU start and finish tiles independently.
+constexpr int kRingBlock = 64;
+// Resident workgroups per CU for each kernel family (0: no limit).
+constexpr int kRingWgPerCu = 4;     // fused all-reduce, tree strategies
+constexpr int kSgdWgPerCu = 4;      // fused all-reduce + optimizer step
+constexpr int kRsWgPerCu = 0;       // reduce-scatter half
+constexpr int kAgWgPerCu = 0;       // all-gather half
+constexpr int kMultiWgPerCu = 0;    // many tensors in one launch
+constexpr int kStepWgPerCu = 0;     // one ring step per launch
+constexpr int kCopyWgPerCu = 0;     // bucket pack / unpack
+
 // What one launch sequence computes: the ring all-reduce (optionally with
 // the fused optimizer step), one of its halves, or a fold along a tree
 // (tree, centralized and two-level strategies).
@@ -43,10 +79,10 @@ struct RingLaunch {
 int launch_ring_reduce(const RingLaunch& l, const char** msg);
 
 // Vectors of each rank a lane keeps in flight per tile: P * U loads.  One
-// vector per lane (a 1,024- or 2,048-element tile of 256 lanes) measured
-// fastest from P = 3 up; P <= 2 keeps more loads in flight with U = 4.  The
-// fused optimizer step, whose outputs are the two 16-byte state vectors
-// instead of P gradient copies, keeps two vectors per lane in flight.
+// vector per lane (a tile of 256 or 512 elements per wave) measured fastest
+// from P = 3 up; P <= 2 keeps more loads in flight with U = 4.  The fused
+// optimizer step, whose outputs are the two 16-byte state vectors instead
+// of P gradient copies, keeps two vectors per lane in flight.
 constexpr int ring_vectors_per_lane(int P, bool sgd) {
     return P <= 2 ? 4 : (sgd ? 2 : 1);
 }

@@ -180,8 +180,8 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
                     wn[e] = __float_as_uint(w);
                     vn[e] = __float_as_uint(v);
                 }
-                rr::store16(reinterpret_cast<char*>(a->w[t]) + (i0 + 4 * q) * 4u, wn);
-                rr::store16(reinterpret_cast<char*>(a->v[t]) + (i0 + 4 * q) * 4u, vn);
+                rr::store16(a->w[t], n * 4u, (i0 + 4 * q) * 4u, wn);
+                rr::store16(a->v[t], n * 4u, (i0 + 4 * q) * 4u, vn);
             }
             if (!write_out) continue;
         }
@@ -191,24 +191,21 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
             for (int k = 0; k < 4; ++k) o[k] = rr::bf16_bits(g[2 * k]) | (rr::bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
             for (int q = 0; q < P; ++q)
-                rr::store16(static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]) +
-                            i0 * OES, o);
+                rr::store16(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t], n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = rr::bf16_bits(g[2 * k]) | (rr::bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
             for (int q = 0; q < P; ++q)
-                rr::store8(static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]) +
-                            i0 * OES, o);
+                rr::store8(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t], n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
             for (int q = 0; q < P; ++q)
-                rr::store16(static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]) +
-                            i0 * OES, o);
+                rr::store16(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t], n * OES, i0 * OES, o);
         }
     }
 }
@@ -263,7 +260,8 @@ int launch_multi_ring(const MultiLaunch& l, const char** msg) {
     a.chunking = l.chunking;
     a.mean = l.op == DDP_MEAN;
     void* args[] = {&a};
-    const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(l.total_tiles)), dim3(kBlock), args, 0,
+    const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(l.total_tiles)), dim3(kBlock), args,
+                                         lds_reserve(kMultiWgPerCu),
                                          static_cast<hipStream_t>(l.stream));
     if (e != hipSuccess) {
         *msg = "hipLaunchKernel(multi_ring)";

@@ -46,6 +46,16 @@ void tile_shape(const RingLaunch& l, int64_t* V, int64_t* tile) {
     *tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P, sgd) * *V;
 }
 
+// Resident workgroups per CU for the launches of this mode (launch.h).
+int wg_per_cu(const RingLaunch& l) {
+    switch (l.mode) {
+        case kReduceScatter: return kRsWgPerCu;
+        case kAllGather: return kAgWgPerCu;
+        case kTree: return kRingWgPerCu;
+        default: return l.sgd ? kSgdWgPerCu : kRingWgPerCu;
+    }
+}
+
 }  // namespace
 
 int launch_ring_reduce(const RingLaunch& l, const char** msg) {
@@ -82,6 +92,8 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         for (int r = 0; r < l.P; ++r) {
             a.in[r] = l.in[r] ? static_cast<const char*>(l.in[r]) + base * ies : nullptr;
             a.out[r] = l.out[r] ? static_cast<char*>(l.out[r]) + base * oes : nullptr;
+            a.in[r + l.P] = a.in[r];
+            a.out[r + l.P] = a.out[r];
         }
         a.w = l.w ? l.w + base : nullptr;
         a.v = l.v ? l.v + base : nullptr;
@@ -89,12 +101,14 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         a.mu = l.mu;
         a.base = base;
         a.L = L;
+        a.rcpL = 1.0 / static_cast<double>(L);
         a.n = static_cast<uint32_t>(n);
         a.n_vec = static_cast<uint32_t>(n - n % V);
         a.mean = l.op == DDP_MEAN;
         a.write_out = l.write_out;
         a.parents = l.parents;
         a.Lg = Lg;
+        a.rcpLg = 1.0 / static_cast<double>(Lg);
         a.groups = groups;
         a.group_size = l.P / groups;
 
@@ -106,8 +120,8 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
             if (grid < 1) grid = 1;               // the tail still needs a workgroup
         }
         void* args[] = {&a};
-        const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(rr::kBlock), args, 0,
-                                             static_cast<hipStream_t>(l.stream));
+        const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(rr::kBlock), args,
+                                             lds_reserve(wg_per_cu(l)), static_cast<hipStream_t>(l.stream));
         if (e != hipSuccess) {
             *msg = "hipLaunchKernel(ring)";
             return static_cast<int>(e);

@@ -54,23 +54,28 @@ namespace rr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlock = 256;
+constexpr int kBlock = kRingBlock;
 
 struct RingArgs {
-    const void* in[kMaxRanks];   // already offset to this launch's first element
-    void* out[kMaxRanks];
+    // Rank r's buffers, already offset to this launch's first element, at
+    // r and again at r + P: the P ranks from any start s are the P
+    // consecutive entries from s, one scalar load.
+    const void* in[2 * kMaxRanks];
+    void* out[2 * kMaxRanks];
     float* w;
     float* v;
     float lr;
     float mu;
     int64_t base;        // global index of this launch's first element
     int64_t L;           // chunk length ceil(n_total / C)
+    double rcpL;         // 1 / L, rounded (chunk_of)
     uint32_t n;          // elements in this launch (< 2^29)
     uint32_t n_vec;      // elements covered by whole lane vectors
     int32_t mean;
     int32_t write_out;   // with SGD: 0 nothing, 1 the reduced gradient, 2 the updated weights
     uint64_t parents;    // tree strategies: 4 bits per fold register c >= 1, its parent register
     int64_t Lg;          // two-level strategies: chunk length of the ring over nodes
+    double rcpLg;        // 1 / Lg, rounded
     int32_t groups;      // two-level strategies: G nodes of group_size ranks, node-major
     int32_t group_size;
 };
@@ -78,11 +83,25 @@ struct RingArgs {
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ void store16(void* p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+
+// Result stores go through a buffer resource over the destination (base in
+// SGPRs, a 32-bit lane offset), because the buffer form carries a cache
+// policy: device scope (sc1) without the non-temporal hint measured 2-3%
+// faster than non-temporal stores for the all-reduce's 8-in/8-out pattern
+// at the occupancy the launches use (6.39 against 6.22 TB/s), and faster
+// than ordinary stores (5.86).  The hardware drops stores at or beyond
+// `bytes` from the base.
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit format, no swizzle
+constexpr int kStoreDeviceScope = 16;      // cache-policy operand of the store: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferWord3);
 }
-__device__ __forceinline__ void store8(void* p, u32x2 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+__device__ __forceinline__ void store16(void* base, uint32_t bytes, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, buffer_over(base, bytes), off, 0, kStoreDeviceScope);
+}
+__device__ __forceinline__ void store8(void* base, uint32_t bytes, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, buffer_over(base, bytes), off, 0, kStoreDeviceScope);
 }
 
 // Element e of a 16-byte vector as float32.  A bf16 value is the upper half
@@ -166,6 +185,22 @@ __device__ __forceinline__ int rank_at(int s, int k, int P) {
     return r >= P ? r - P : r;
 }
 
+// The chunk holding global element x, floor(x / L), without a 64-bit
+// integer division (a long instruction sequence that would sit between a
+// tile's start and its first load): the product with the host-rounded
+// reciprocal is within one of the quotient for x < 2^52, and one
+// comparison each way makes it exact.  The quotient is below the chunk
+// count, an int.
+__device__ __forceinline__ int chunk_of(int64_t x, int64_t L, double rcpL) {
+    int j = static_cast<int>(static_cast<double>(x) * rcpL);
+    if (static_cast<int64_t>(j) * L > x) {
+        --j;
+    } else if (static_cast<int64_t>(j + 1) * L <= x) {
+        ++j;
+    }
+    return j;
+}
+
 // Every output rank receives the same value, so the order of the P stores
 // is free.  Each wave starts at a different rank (its wave index mod P):
 // the waves in flight then write to all P output streams at once instead
@@ -175,14 +210,20 @@ __device__ __forceinline__ int store_rotation(int P) {
     return __builtin_amdgcn_readfirstlane(wave % P);
 }
 
-// Output pointer of rank (rot + q) mod P, chosen with scalar selects.
+// The P output bases in store order, dst[q] = rank (rot + q) mod P, and
+// the P input bases in fold order, src[k] = rank (s + k) mod P: P
+// consecutive entries of the doubled pointer tables, read with one scalar
+// load each before the first store or load needs them.
 template <int P>
-__device__ __forceinline__ char* rotated_out(KArgs a, int rot, int q) {
-    const int want = rank_at(rot, q, P);
-    char* p = static_cast<char*>(a->out[0]);
+__device__ __forceinline__ void rotated_outs(KArgs a, int rot, char* (&dst)[P]) {
 #pragma unroll
-    for (int j = 1; j < P; ++j) p = want == j ? static_cast<char*>(a->out[j]) : p;
-    return p;
+    for (int q = 0; q < P; ++q) dst[q] = static_cast<char*>(a->out[rot + q]);
+}
+
+template <int P>
+__device__ __forceinline__ void rotated_ins(KArgs a, int s, const char* (&src)[P]) {
+#pragma unroll
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(a->in[s + k]);
 }
 
 // ---- one element per lane: tails and chunks shorter than a tile ----------
@@ -190,7 +231,7 @@ __device__ __forceinline__ char* rotated_out(KArgs a, int rot, int q) {
 template <int P, bool INB, bool OUTB, bool SGD>
 __device__ __forceinline__ void process_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    const int s = static_cast<int>(((a->base + i) / a->L) % P);
+    const int s = chunk_of(a->base + i, a->L, a->rcpL) % P;
     float g;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -238,7 +279,7 @@ __device__ __forceinline__ u32x4 load_lane(const void* p) {
 // One tile = U rows of 256 lane vectors of V elements per rank, processed
 // by one workgroup.  FULL: the whole tile lies below n_vec.
 template <int P, bool INB, bool OUTB, bool SGD, bool FULL>
-__device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
+__device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int j0) {
 #pragma clang fp contract(off)
     constexpr int U = ring_vectors_per_lane(P, SGD);
     constexpr int V = ring_lane_elems(INB, OUTB, SGD);
@@ -252,9 +293,11 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
     // Chunks are at least TILE long on this path, so the tile holds one
     // start rank, or two with the boundary at element `split` of the launch.
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int64_t j0 = (a->base + t0) / a->L;
-    const int64_t j1 = (a->base + last) / a->L;
-    const int s0 = static_cast<int>(j0 % P);
+    const int64_t next = static_cast<int64_t>(j0 + 1) * a->L;   // first element of chunk j0 + 1
+    const bool straddle = next <= a->base + last;
+    const int s0 = j0 % P;
+    const char* src[P];
+    rotated_ins<P>(a, s0, src);
 
     u32x4 x[P][U];
     float ws[U][V];
@@ -266,8 +309,7 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
         ok[u] = FULL || (i0 < n_vec);
         if (ok[u]) {
 #pragma unroll
-            for (int k = 0; k < P; ++k)
-                x[k][u] = load_lane<WIN>(static_cast<const char*>(a->in[rank_at(s0, k, P)]) + i0 * IES);
+            for (int k = 0; k < P; ++k) x[k][u] = load_lane<WIN>(src[k] + i0 * IES);
             if constexpr (SGD) {
                 static_assert(V == 4, "the momentum state moves as one 16-byte vector per lane");
                 const u32x4 wq = load16(reinterpret_cast<const char*>(a->w) + i0 * 4u);
@@ -286,10 +328,10 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
 
     float acc[U][V];
     fold<P, 0, INB, U, V>(x, acc);
-    if (j1 != j0) {
+    if (straddle) {
         float acc2[U][V];
         fold<P, 1, INB, U, V>(x, acc2);
-        const uint32_t split = static_cast<uint32_t>(j1 * a->L - a->base);
+        const uint32_t split = static_cast<uint32_t>(next - a->base);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -300,7 +342,8 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
     }
 
     const bool mean = a->mean != 0;
-    const int rot = store_rotation(P);
+    char* dst[P];
+    rotated_outs<P>(a, store_rotation(P), dst);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -316,8 +359,8 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
                 wq[e] = __float_as_uint(ws[u][e]);
                 vq[e] = __float_as_uint(vs[u][e]);
             }
-            store16(reinterpret_cast<char*>(a->w) + i0 * 4u, wq);
-            store16(reinterpret_cast<char*>(a->v) + i0 * 4u, vq);
+            store16(a->w, a->n * 4u, i0 * 4u, wq);
+            store16(a->v, a->n * 4u, i0 * 4u, vq);
             if (!a->write_out) continue;
             if (a->write_out == 2) {
 #pragma unroll
@@ -329,19 +372,19 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store8(rotated_out<P>(a, rot, q) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store8(dst[q], a->n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
         }
     }
 }
@@ -356,10 +399,13 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
     const KArgs a = kernel_args();
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
+    // The tile's chunk, computed before the branch so that its argument
+    // loads go out together with n_vec's.
+    const int j0 = chunk_of(a->base + t0, a->L, a->rcpL);
     if (t0 + TILE <= n_vec) {
-        process_tile<P, INB, OUTB, SGD, true>(a, t0);
+        process_tile<P, INB, OUTB, SGD, true>(a, t0, j0);
     } else if (t0 < n_vec) {
-        process_tile<P, INB, OUTB, SGD, false>(a, t0);
+        process_tile<P, INB, OUTB, SGD, false>(a, t0, j0);
     }
     if (blockIdx.x == gridDim.x - 1) {
         const uint32_t i = n_vec + threadIdx.x;
@@ -388,7 +434,7 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_scalar_kernel(RingArgs) {
 template <int P, bool INB, bool OUTB>
 __device__ __forceinline__ void rs_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    const int s = static_cast<int>(((a->base + i) / a->L) % P);
+    const int s = chunk_of(a->base + i, a->L, a->rcpL) % P;
     float g;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -412,7 +458,7 @@ __device__ __forceinline__ void rs_element(KArgs a, uint32_t i) {
 
 template <int P, int ES>
 __device__ __forceinline__ void ag_element(KArgs a, uint32_t i) {
-    const int s = static_cast<int>(((a->base + i) / a->L) % P);
+    const int s = chunk_of(a->base + i, a->L, a->rcpL) % P;
     const int o = rank_at(s, P - 1, P);
     if constexpr (ES == 2) {
         const uint16_t v = static_cast<const uint16_t*>(a->out[o])[i];
@@ -439,9 +485,8 @@ __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
     const uint32_t tid = threadIdx.x;
     const uint32_t n_vec = a->n_vec;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int64_t j0 = (a->base + t0) / a->L;
-    const int64_t j1 = (a->base + last) / a->L;
-    if (j0 != j1) {
+    const int j0 = chunk_of(a->base + t0, a->L, a->rcpL);
+    if (static_cast<int64_t>(j0 + 1) * a->L <= a->base + last) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -451,7 +496,9 @@ __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
         }
         return;
     }
-    const int s0 = static_cast<int>(j0 % P);
+    const int s0 = j0 % P;
+    const char* src[P];
+    rotated_ins<P>(a, s0, src);
     u32x4 x[P][U];
     bool ok[U];
 #pragma unroll
@@ -460,8 +507,7 @@ __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
         ok[u] = FULL || (i0 < n_vec);
         if (ok[u]) {
 #pragma unroll
-            for (int k = 0; k < P; ++k)
-                x[k][u] = load_lane<WIN>(static_cast<const char*>(a->in[rank_at(s0, k, P)]) + i0 * IES);
+            for (int k = 0; k < P; ++k) x[k][u] = load_lane<WIN>(src[k] + i0 * IES);
         } else {
 #pragma unroll
             for (int k = 0; k < P; ++k) x[k][u] = u32x4{0u, 0u, 0u, 0u};
@@ -505,25 +551,21 @@ __device__ __forceinline__ void ag_tile(KArgs a, uint32_t t0) {
     const uint32_t n_vec = a->n_vec;
     const uint32_t i0 = t0 + tid * V;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int64_t j0 = (a->base + t0) / a->L;
-    const int64_t j1 = (a->base + last) / a->L;
+    const int j0 = chunk_of(a->base + t0, a->L, a->rcpL);
     if (!FULL && i0 >= n_vec) return;
-    if (j0 != j1) {
+    if (static_cast<int64_t>(j0 + 1) * a->L <= a->base + last) {
         for (int e = 0; e < V; ++e) ag_element<P, ES>(a, i0 + e);
         return;
     }
-    const int o = rank_at(static_cast<int>(j0 % P), P - 1, P);
+    const int o = rank_at(j0 % P, P - 1, P);
     const u32x4 y = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a->out[o]) + i0 * ES);
     // the P-1 other ranks, starting at a rank that differs from wave to wave
     const int rot = P > 1 ? store_rotation(P - 1) : 0;
+    char* dst[P > 1 ? P - 1 : 1];
 #pragma unroll
-    for (int q = 0; q < P - 1; ++q) {
-        const int r = rank_at(o, 1 + rank_at(rot, q, P - 1), P);
-        char* p = static_cast<char*>(a->out[0]);
+    for (int q = 0; q < P - 1; ++q) dst[q] = static_cast<char*>(a->out[o + 1 + rank_at(rot, q, P - 1)]);
 #pragma unroll
-        for (int j = 1; j < P; ++j) p = r == j ? static_cast<char*>(a->out[j]) : p;
-        store16(p + i0 * ES, y);
-    }
+    for (int q = 0; q < P - 1; ++q) store16(dst[q], a->n * ES, i0 * ES, y);
 }
 
 template <int P, bool INB, bool OUTB>
@@ -687,7 +729,7 @@ __device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
     const int G = a->groups;
     const int Lr = a->group_size;
     int rank[P];
-    level_ranks<P>(G, Lr, static_cast<int>((gi / a->L) % Lr), static_cast<int>((gi / a->Lg) % G), rank);
+    level_ranks<P>(G, Lr, chunk_of(gi, a->L, a->rcpL) % Lr, chunk_of(gi, a->Lg, a->rcpLg) % G, rank);
     float part[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -728,9 +770,10 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     const uint32_t tid = threadIdx.x;
     const uint32_t n_vec = a->n_vec;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int64_t jl = (a->base + t0) / a->L;
-    const int64_t jg = (a->base + t0) / a->Lg;
-    if (jl != (a->base + last) / a->L || jg != (a->base + last) / a->Lg) {
+    const int jl = chunk_of(a->base + t0, a->L, a->rcpL);
+    const int jg = chunk_of(a->base + t0, a->Lg, a->rcpLg);
+    if (static_cast<int64_t>(jl + 1) * a->L <= a->base + last ||
+        static_cast<int64_t>(jg + 1) * a->Lg <= a->base + last) {
         // a local or global chunk boundary inside the tile: element by element
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -743,7 +786,7 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     const int G = a->groups;
     const int Lr = a->group_size;
     int rank[P];
-    level_ranks<P>(G, Lr, static_cast<int>(jl % Lr), static_cast<int>(jg % G), rank);
+    level_ranks<P>(G, Lr, jl % Lr, jg % G, rank);
     u32x4 x[P][U];
     bool ok[U];
 #pragma unroll
@@ -762,7 +805,8 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     float acc[U][V];
     tree_fold<P, INB, U, V>(x, a->parents, acc);
     const bool mean = a->mean != 0;
-    const int rot = store_rotation(P);
+    char* dst[P];
+    rotated_outs<P>(a, store_rotation(P), dst);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -775,19 +819,19 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store8(rotated_out<P>(a, rot, q) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store8(dst[q], a->n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(rotated_out<P>(a, rot, q) + i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
         }
     }
 }

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void ring_step_kernel(StepArgs) {
                         o[e] = __float_as_uint(v);
                     }
                 }
-                rr::store16(pd + i0 * 4u, o);
+                rr::store16(pd, a->n * 4u, i0 * 4u, o);
             }
             if (a->sent && tid == 0) atomicAdd(a->sent + src, static_cast<unsigned long long>(end - t0));
         }
@@ -190,7 +190,8 @@ int launch_ring_stepwise(const StepLaunch& l, const char** msg) {
                 int64_t grid = scalar ? (n + kBlock - 1) / kBlock : (a.n_vec + kStepTile - 1) / kStepTile;
                 if (grid < 1) grid = 1;
                 void* args[] = {&a};
-                const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kBlock), args, 0,
+                const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kBlock), args,
+                                                     lds_reserve(kStepWgPerCu),
                                                      static_cast<hipStream_t>(l.stream));
                 if (e != hipSuccess) {
                     *msg = "hipLaunchKernel(ring_step)";

@@ -348,7 +348,7 @@ def test_multi_plan():
     _, _, tile = ddp.ddp_multi_plan([1], 8, ddp.F32, ddp.F32)
     sizes = [0, 1, tile, tile + 1, 5]
     tiles, total, _ = ddp.ddp_multi_plan(sizes, 8, ddp.F32, ddp.F32)
-    assert tile % 1024 == 0                  # whole 256-lane rows of 4 floats
+    assert tile % 256 == 0                   # whole 64-lane rows of 4 floats
     assert tiles["numel"].tolist() == sizes
     assert tiles["first_tile"].tolist() == [0, 0, 1, 2, 4]
     assert total == 5
