@@ -14,7 +14,7 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
                   allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
                   allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step,
-                  allreduce_multi_fused_sgd)
+                  allreduce_multi_fused_sgd, ddp_set_wg_per_cu, KERNEL_FAMILIES)
 from .bucketer import GradBucketer
 
 __all__ = [
@@ -26,5 +26,5 @@ __all__ = [
     "allreduce_sgd",
     "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",
     "allreduce_hierarchical", "zero1_sgd_step_emulated", "zero1_sgd_step",
-    "allreduce_multi_fused_sgd",
+    "allreduce_multi_fused_sgd", "ddp_set_wg_per_cu", "KERNEL_FAMILIES",
 ]

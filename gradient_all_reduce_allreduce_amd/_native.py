@@ -30,6 +30,10 @@ DDP_F32 = 0
 DDP_BF16 = 1
 DDP_MAX_RANKS = 16
 
+# ddp_kernel_family
+KERNEL_FAMILIES = {"ring": 0, "ring_sgd": 1, "tree": 2, "reduce_scatter": 3, "all_gather": 4,
+                   "multi": 5, "bucket_copy": 6, "step": 7}
+
 
 class Segment(ctypes.Structure):
     """ddp_segment: elements [src_off, src_off+len) of tensor `tensor`
@@ -96,6 +100,7 @@ _SIGNATURES = {
         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_void_p]),
+    "ddp_set_wg_per_cu": (ctypes.c_int, [ctypes.c_int, ctypes.c_int32]),
     "ddp_last_error": (ctypes.c_char_p, []),
 }
 

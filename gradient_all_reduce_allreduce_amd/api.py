@@ -9,7 +9,7 @@ Python ints, stream as an int handle or None):
     reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
     allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
-    allreduce_multi_fused_sgd
+    allreduce_multi_fused_sgd, ddp_set_wg_per_cu
 Tensor-level helpers:
     allreduce(tensors, op, chunking, out)            -> list of outputs
     allreduce_sgd(grads, w, v, lr, mu, op, chunking, out)
@@ -186,6 +186,20 @@ def allreduce_multi_fused_sgd(op, P, chunking, n_tensors, tiles_dev, total_tiles
     _check(N.lib().allreduce_multi_fused_sgd(_op(op), P, chunking, n_tensors, tiles_dev, total_tiles,
                                              tile_elems, in_ptrs_dev, grad_dtype, w_ptrs_dev,
                                              v_ptrs_dev, lr, mu, out_ptrs_dev, out_dtype, stream))
+
+
+def ddp_set_wg_per_cu(family, wg_per_cu):
+    """Tuning knob: cap the resident workgroups per CU of one kernel family
+    (a name of ``KERNEL_FAMILIES`` or its ddp_kernel_family value) for later
+    launches; 0 = no cap, -1 = the built-in choice.  Results do not change."""
+    if isinstance(family, str):
+        if family not in N.KERNEL_FAMILIES:
+            raise ValueError(f"unknown kernel family {family!r}; one of {sorted(N.KERNEL_FAMILIES)}")
+        family = N.KERNEL_FAMILIES[family]
+    _check(N.lib().ddp_set_wg_per_cu(family, wg_per_cu))
+
+
+KERNEL_FAMILIES = dict(N.KERNEL_FAMILIES)
 
 
 # --------------------------------------------------------- torch level ----

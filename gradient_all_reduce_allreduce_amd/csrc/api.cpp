@@ -6,6 +6,7 @@
 // succeeds, so every error path can be exercised on a machine without a GPU.
 #include <stdint.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdarg>
 #include <cstdint>
@@ -19,6 +20,10 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// ddp_set_wg_per_cu: one cap per kernel family, -1 = the built-in choice.
+constexpr int kFamilies = DDP_KF_STEP + 1;
+std::atomic<int> g_wg_override[kFamilies] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
@@ -123,9 +128,24 @@ uint64_t fnv1a(uint64_t h, const void* data, size_t len) {
 
 }  // namespace
 
+namespace ddp {
+int wg_per_cu_override(int family) {
+    return family >= 0 && family < kFamilies ? g_wg_override[family].load(std::memory_order_relaxed) : -1;
+}
+}  // namespace ddp
+
 extern "C" {
 
 const char* ddp_last_error(void) { return g_last_error.c_str(); }
+
+int ddp_set_wg_per_cu(ddp_kernel_family family, int32_t wg_per_cu) {
+    const int f = static_cast<int>(family);
+    if (f < 0 || f >= kFamilies) return fail(DDP_E_ARG, "unknown kernel family %d", f);
+    if (!(wg_per_cu == -1 || wg_per_cu == 0 || (wg_per_cu >= 2 && wg_per_cu <= 64)))
+        return fail(DDP_E_ARG, "wg_per_cu = %d: expected -1, 0 or 2..64", wg_per_cu);
+    g_wg_override[f].store(wg_per_cu, std::memory_order_relaxed);
+    return ok();
+}
 
 int ddp_bucket_plan(const int64_t* numels, int32_t n_tensors, ddp_dtype dtype, int64_t bucket_bytes,
                     ddp_segment* segs, int64_t segs_cap, int64_t* n_segs, int32_t* n_buckets,

@@ -37,8 +37,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
 constexpr int kVecPerLane = 4;   // 16-byte vectors per lane and tile
-// LDS the kernel declares: the staged segments (s_dst, s_len, s_ten).
-constexpr unsigned kStaticLds = kBlock * (2 * sizeof(int64_t) + sizeof(char*));
 
 struct CopyArgs {
     const ddp_segment* segs;
@@ -217,6 +215,14 @@ __global__ __launch_bounds__(kBlock) void bucket_copy_kernel(CopyArgs a) {
     }
 }
 
+// Static LDS of a kernel; if the runtime cannot say, a bound above what the
+// staged-segment arrays take (256 entries of 24 bytes).
+unsigned static_lds(const void* fn) {
+    hipFuncAttributes at{};
+    if (hipFuncGetAttributes(&at, fn) != hipSuccess) return 8192u;
+    return static_cast<unsigned>(at.sharedSizeBytes);
+}
+
 }  // namespace
 
 int launch_bucket_copy(const CopyLaunch& l, const char** msg) {
@@ -238,9 +244,14 @@ int launch_bucket_copy(const CopyLaunch& l, const char** msg) {
     }
     const void* fn = l.pack ? reinterpret_cast<const void*>(&bucket_copy_kernel<true>)
                             : reinterpret_cast<const void*>(&bucket_copy_kernel<false>);
+    // The kernel's own LDS (the staged segments), as the compiler laid it
+    // out, counts against the per-CU share.
+    static const unsigned own_lds[2] = {static_lds(reinterpret_cast<const void*>(&bucket_copy_kernel<false>)),
+                                        static_lds(reinterpret_cast<const void*>(&bucket_copy_kernel<true>))};
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.tiles), static_cast<unsigned>(l.P)),
-                                         dim3(kBlock), args, lds_reserve(kCopyWgPerCu, kStaticLds),
+                                         dim3(kBlock), args, lds_reserve(wg_per_cu_for(DDP_KF_BUCKET_COPY, l.pack ? kPackWgPerCu : kUnpackWgPerCu),
+                                                           own_lds[l.pack ? 1 : 0]),
                                          static_cast<hipStream_t>(l.stream));
     if (e != hipSuccess) {
         *msg = "hipLaunchKernel(bucket_copy)";

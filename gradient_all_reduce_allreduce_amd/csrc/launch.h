@@ -14,37 +14,92 @@ constexpr int kMaxRanks = DDP_MAX_RANKS;
 //
 // Every kernel here streams HBM with little arithmetic.  On MI355X the mix
 // of reads and writes of the all-reduce (P input streams, P output streams)
-// reaches its highest rate when few waves per CU keep requests in flight:
-// 6.39 TB/s at 4 one-wave workgroups per CU against 5.7 TB/s with the CUs
-// filled, in a plain 8-in/8-out streaming kernel.  A launch therefore
-// reserves LDS it never touches, so that at most the chosen number of its
-// workgroups fit on a CU at once; the dispatcher still hands tiles to
-// whichever CU frees up.  The limit only pays where a tile's first load
-// follows its start within a few dozen instructions: the multi-tensor and
-// bucket-copy kernels, which search a table first, and the two halves of
-// the ring measured slower with it, so they keep the hardware's occupancy.
+// reaches its highest rate with few waves per CU keeping requests in
+// flight: a plain 8-in/8-out streaming kernel moves 6.36-6.42 TB/s with 3
+// or 4 one-wave workgroups per CU against 5.5 TB/s with the CUs filled.  A
+// launch therefore reserves LDS it never touches, so that at most a chosen
+// number of its workgroups fit on a CU at once; the dispatcher still hands
+// tiles to whichever CU frees up.  The best number depends on how many
+// bytes a wave moves per tile (the rank count and element types) and on
+// how long a tile takes to reach its first load, so it was measured for
+// each kernel family: the tables below hold the fastest of 2..16 on
+// 25 MiB buckets.  ddp_set_wg_per_cu overrides a family's choice.
 
 constexpr unsigned kLdsBytesPerCu = 160u * 1024u;   // CDNA4 compute unit
+// LDS goes to workgroups in granules of 1,280 bytes on this chip (measured:
+// a 53,760-byte request lets 3 workgroups share a CU, 54,272 bytes only 2),
+// so a request that is a multiple of the granule fits exactly
+// floor(160 KiB / request) workgroups per CU.
+constexpr unsigned kLdsGranule = 1280u;
 
-// Dynamic LDS for a launch whose kernel already uses `static_bytes`, such
-// that at most `wg_per_cu` workgroups are resident per CU (0: no limit).
+// Dynamic LDS for a launch whose kernel already uses `static_bytes` (its
+// own __shared__ arrays, as the compiler laid them out), such that at most
+// `wg_per_cu` workgroups are resident per CU (0: no limit).  Never fewer
+// than 2 per CU: a workgroup asking for the whole 160 KiB is refused.
 constexpr unsigned lds_reserve(int wg_per_cu, unsigned static_bytes = 0) {
     if (wg_per_cu <= 0) return 0u;
-    const unsigned per = (kLdsBytesPerCu / static_cast<unsigned>(wg_per_cu)) & ~1023u;
+    const unsigned k = static_cast<unsigned>(wg_per_cu < 2 ? 2 : wg_per_cu);
+    const unsigned per = kLdsBytesPerCu / k / kLdsGranule * kLdsGranule;
     return per > static_bytes ? per - static_bytes : 0u;
 }
 
 // Lanes per workgroup of the ring, tree and multi-tensor kernels: one wave,
 // so that the resident waves of a CU start and finish tiles independently.
 constexpr int kRingBlock = 64;
-// Resident workgroups per CU for each kernel family (0: no limit).
-constexpr int kRingWgPerCu = 4;     // fused all-reduce, tree strategies
-constexpr int kSgdWgPerCu = 4;      // fused all-reduce + optimizer step
-constexpr int kRsWgPerCu = 0;       // reduce-scatter half
-constexpr int kAgWgPerCu = 0;       // all-gather half
-constexpr int kMultiWgPerCu = 0;    // many tensors in one launch
+
+// The fused all-reduce: resident one-wave workgroups per CU by element
+// types and rank count P = 1..16 (index 0 unused; P = 1, a copy, takes
+// P = 2's value; P = 7, 9-11 and 13-15 interpolate the measured neighbours).
+// Rows: f32 -> f32, f32 -> bf16, bf16 -> f32, bf16 -> bf16.
+constexpr signed char kRingWg[4][17] = {
+    //   P: 1   2   3   4   5  6  7  8  9 10 11 12 13 14 15 16
+    {0, 4, 4, 12, 8, 8, 6, 5, 4, 4, 4, 3, 3, 3, 3, 3, 3},
+    {0, 12, 12, 16, 10, 10, 8, 6, 5, 5, 4, 4, 4, 4, 4, 4, 4},
+    {0, 6, 6, 16, 10, 10, 8, 6, 5, 5, 4, 4, 4, 3, 3, 3, 3},
+    {0, 6, 6, 12, 10, 8, 6, 6, 5, 5, 4, 4, 4, 3, 3, 3, 3},
+};
+// The all-reduce fused with the optimizer step (two lane vectors per tile),
+// by gradient type and whether the reduced gradients (or updated
+// parameters) are written to the ranks: rows bf16 without, bf16 with, f32
+// without, f32 with.
+constexpr signed char kSgdWg[4][17] = {
+    //   P: 1   2   3   4   5  6  7  8  9 10 11 12 13 14 15 16
+    {0, 6, 6, 10, 5, 6, 5, 5, 4, 4, 4, 5, 5, 4, 4, 4, 4},
+    {0, 5, 5, 8, 6, 6, 6, 5, 5, 5, 4, 4, 4, 4, 3, 3, 3},
+    {0, 8, 8, 10, 12, 10, 12, 10, 10, 10, 8, 8, 8, 8, 8, 8, 3},
+    {0, 3, 3, 6, 5, 4, 3, 3, 3, 3, 3, 2, 2, 2, 2, 2, 2},
+};
+constexpr int ring_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
+    return kRingWg[(in_bf16 ? 2 : 0) + (out_bf16 ? 1 : 0)][P];
+}
+constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
+    return kSgdWg[(grad_bf16 ? 0 : 2) + (writes_ranks ? 1 : 0)][P];
+}
+// The tree strategies walk a parent table before their first load and
+// measured best one workgroup above the ring (5 at P = 8, f32).
+constexpr int tree_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
+    return ring_wg_per_cu(P, in_bf16, out_bf16) + 1;
+}
+// Measured at P = 8, f32, ResNet-50 buckets; the multi-tensor kernel
+// searches its tile plan first and wants many more waves (16 at P = 8, 20
+// at P = 4, 20 with the optimizer step).  Bucket pack keeps the hardware's
+// occupancy (capping it only lost).
+constexpr int kRsWgPerCu = 10;      // reduce-scatter half
+constexpr int kAgWgPerCu = 12;      // all-gather half
+constexpr int multi_wg_per_cu(int P, bool sgd) { return sgd ? 20 : (P >= 6 ? 16 : 20); }
 constexpr int kStepWgPerCu = 0;     // one ring step per launch
-constexpr int kCopyWgPerCu = 0;     // bucket pack / unpack
+constexpr int kPackWgPerCu = 0;     // bucket pack (256-lane workgroups)
+constexpr int kUnpackWgPerCu = 5;   // bucket unpack (256-lane workgroups)
+
+// The cap ddp_set_wg_per_cu set for a family (ddp_kernel_family): -1 if
+// none (use the built-in choice), else the cap (0: no cap).  api.cpp.
+int wg_per_cu_override(int family);
+
+// The cap a launch of `family` uses: the override if set, else `builtin`.
+inline int wg_per_cu_for(int family, int builtin) {
+    const int o = wg_per_cu_override(family);
+    return o >= 0 ? o : builtin;
+}
 
 // What one launch sequence computes: the ring all-reduce (optionally with
 // the fused optimizer step), one of its halves, or a fold along a tree

@@ -261,7 +261,7 @@ int launch_multi_ring(const MultiLaunch& l, const char** msg) {
     a.mean = l.op == DDP_MEAN;
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(l.total_tiles)), dim3(kBlock), args,
-                                         lds_reserve(kMultiWgPerCu),
+                                         lds_reserve(wg_per_cu_for(DDP_KF_MULTI, multi_wg_per_cu(l.P, l.sgd != 0))),
                                          static_cast<hipStream_t>(l.stream));
     if (e != hipSuccess) {
         *msg = "hipLaunchKernel(multi_ring)";

@@ -46,13 +46,41 @@ void tile_shape(const RingLaunch& l, int64_t* V, int64_t* tile) {
     *tile = static_cast<int64_t>(rr::kBlock) * ring_vectors_per_lane(l.P, sgd) * *V;
 }
 
+// The 32-bit chunk map of a launch starting at global element `base` (see
+// rr::ChunkMap): chunks of L elements, their start member taken modulo M.
+// A launch holds at most 2^29 elements, so with d = L <= 2^30 every
+// t + off stays below 2^31.  A longer chunk leaves at most one boundary in
+// the launch, at local element tb; the divisor 2^30 with the origin shifted
+// to put a multiple of it at tb gives the same chunk steps.
+rr::ChunkMap chunk_map(int64_t base, int64_t L, int M) {
+    constexpr int64_t kCap = int64_t(1) << 30;
+    const int64_t first = base / L;
+    const int64_t within = base - first * L;   // the launch's first element, inside its chunk
+    rr::ChunkMap c;
+    if (L <= kCap) {
+        c.d = static_cast<uint32_t>(L);
+        c.off = static_cast<uint32_t>(within);
+    } else {
+        const int64_t tb = L - within;            // first element of the next chunk
+        c.d = static_cast<uint32_t>(kCap);
+        c.off = tb <= kCap ? static_cast<uint32_t>(kCap - tb) : 0u;
+    }
+    c.m = 0xffffffffu / c.d;
+    c.first = static_cast<uint32_t>(first % M);
+    return c;
+}
+
 // Resident workgroups per CU for the launches of this mode (launch.h).
 int wg_per_cu(const RingLaunch& l) {
+    const bool ib = l.in_bf16 != 0;
+    const bool ob = l.out_bf16 != 0;
     switch (l.mode) {
-        case kReduceScatter: return kRsWgPerCu;
-        case kAllGather: return kAgWgPerCu;
-        case kTree: return kRingWgPerCu;
-        default: return l.sgd ? kSgdWgPerCu : kRingWgPerCu;
+        case kReduceScatter: return wg_per_cu_for(DDP_KF_REDUCE_SCATTER, kRsWgPerCu);
+        case kAllGather: return wg_per_cu_for(DDP_KF_ALL_GATHER, kAgWgPerCu);
+        case kTree: return wg_per_cu_for(DDP_KF_TREE, tree_wg_per_cu(l.P, ib, ob));
+        default:
+            if (l.sgd) return wg_per_cu_for(DDP_KF_RING_SGD, sgd_wg_per_cu(l.P, ib, l.write_out != 0));
+            return wg_per_cu_for(DDP_KF_RING, ring_wg_per_cu(l.P, ib, ob));
     }
 }
 
@@ -99,16 +127,13 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         a.v = l.v ? l.v + base : nullptr;
         a.lr = l.lr;
         a.mu = l.mu;
-        a.base = base;
-        a.L = L;
-        a.rcpL = 1.0 / static_cast<double>(L);
+        a.ring = chunk_map(base, L, l.mode == kTree ? l.P / groups : l.P);
         a.n = static_cast<uint32_t>(n);
         a.n_vec = static_cast<uint32_t>(n - n % V);
         a.mean = l.op == DDP_MEAN;
         a.write_out = l.write_out;
         a.parents = l.parents;
-        a.Lg = Lg;
-        a.rcpLg = 1.0 / static_cast<double>(Lg);
+        a.global = chunk_map(base, Lg, groups);
         a.groups = groups;
         a.group_size = l.P / groups;
 

@@ -56,6 +56,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = kRingBlock;
 
+// Which chunk a launch-local element t belongs to, in 32-bit arithmetic:
+// q = floor((t + off) / d) chunks after the launch's first one, whose index
+// modulo the level's member count is `first`.  The host picks d and off so
+// that t + off < 2^31 for every element of the launch (chunk_map in
+// ring_reduce.hip): d is the chunk length, or 2^30 where a chunk is longer
+// than that (a launch then holds at most one chunk boundary, which the
+// shifted origin keeps in place).
+struct ChunkMap {
+    uint32_t d;          // divisor
+    uint32_t m;          // floor((2^32 - 1) / d)
+    uint32_t off;        // launch-local origin shift
+    uint32_t first;      // first chunk of the launch, modulo the member count
+};
+
 struct RingArgs {
     // Rank r's buffers, already offset to this launch's first element, at
     // r and again at r + P: the P ranks from any start s are the P
@@ -66,16 +80,13 @@ struct RingArgs {
     float* v;
     float lr;
     float mu;
-    int64_t base;        // global index of this launch's first element
-    int64_t L;           // chunk length ceil(n_total / C)
-    double rcpL;         // 1 / L, rounded (chunk_of)
+    ChunkMap ring;       // the ring's chunks (ring modes); the ring within the nodes (tree modes)
     uint32_t n;          // elements in this launch (< 2^29)
     uint32_t n_vec;      // elements covered by whole lane vectors
     int32_t mean;
     int32_t write_out;   // with SGD: 0 nothing, 1 the reduced gradient, 2 the updated weights
     uint64_t parents;    // tree strategies: 4 bits per fold register c >= 1, its parent register
-    int64_t Lg;          // two-level strategies: chunk length of the ring over nodes
-    double rcpLg;        // 1 / Lg, rounded
+    ChunkMap global;     // two-level strategies: the chunks of the ring over the nodes
     int32_t groups;      // two-level strategies: G nodes of group_size ranks, node-major
     int32_t group_size;
 };
@@ -185,20 +196,46 @@ __device__ __forceinline__ int rank_at(int s, int k, int P) {
     return r >= P ? r - P : r;
 }
 
-// The chunk holding global element x, floor(x / L), without a 64-bit
-// integer division (a long instruction sequence that would sit between a
-// tile's start and its first load): the product with the host-rounded
-// reciprocal is within one of the quotient for x < 2^52, and one
-// comparison each way makes it exact.  The quotient is below the chunk
-// count, an int.
-__device__ __forceinline__ int chunk_of(int64_t x, int64_t L, double rcpL) {
-    int j = static_cast<int>(static_cast<double>(x) * rcpL);
-    if (static_cast<int64_t>(j) * L > x) {
-        --j;
-    } else if (static_cast<int64_t>(j + 1) * L <= x) {
-        ++j;
+// Chunks from the launch's first one to the one holding launch-local
+// element t, and t's position within it (`rem`), for x = t + c.off < 2^31:
+// the high half of x * m is floor(x / d) or one less -- x * m / 2^32 lies in
+// (x / d - 2x / 2^32, x / d) -- so one comparison makes it exact.  With t
+// uniform over a wave these are a handful of scalar instructions between a
+// tile's start and its first load.
+__device__ __forceinline__ uint32_t chunk_steps(uint32_t t, const __attribute__((address_space(4))) ChunkMap& c,
+                                                uint32_t& rem) {
+    const uint32_t x = t + c.off;
+    uint32_t q = __umulhi(x, c.m);
+    uint32_t r = x - q * c.d;
+    if (r >= c.d) {
+        ++q;
+        r -= c.d;
     }
-    return j;
+    rem = r;
+    return q;
+}
+
+// The member (rank, or node, or peer) at which element t's chunk starts its
+// ring, for a level of M members.
+template <int M>
+__device__ __forceinline__ int chunk_start(uint32_t t, const __attribute__((address_space(4))) ChunkMap& c) {
+    uint32_t r;
+    return static_cast<int>((c.first + chunk_steps(t, c, r)) % static_cast<uint32_t>(M));
+}
+__device__ __forceinline__ int chunk_start(uint32_t t, const __attribute__((address_space(4))) ChunkMap& c, int M) {
+    uint32_t r;
+    return static_cast<int>((c.first + chunk_steps(t, c, r)) % static_cast<uint32_t>(M));
+}
+
+// The start member of the chunk holding tile element t0, and the first
+// launch-local element of the next chunk.
+template <int M>
+__device__ __forceinline__ int tile_chunk(uint32_t t0, const __attribute__((address_space(4))) ChunkMap& c,
+                                          uint32_t& next) {
+    uint32_t r;
+    const uint32_t q = chunk_steps(t0, c, r);
+    next = t0 + (c.d - r);
+    return static_cast<int>((c.first + q) % static_cast<uint32_t>(M));
 }
 
 // Every output rank receives the same value, so the order of the P stores
@@ -231,7 +268,7 @@ __device__ __forceinline__ void rotated_ins(KArgs a, int s, const char* (&src)[P
 template <int P, bool INB, bool OUTB, bool SGD>
 __device__ __forceinline__ void process_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    const int s = chunk_of(a->base + i, a->L, a->rcpL) % P;
+    const int s = chunk_start<P>(i, a->ring);
     float g;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -279,7 +316,7 @@ __device__ __forceinline__ u32x4 load_lane(const void* p) {
 // One tile = U rows of 256 lane vectors of V elements per rank, processed
 // by one workgroup.  FULL: the whole tile lies below n_vec.
 template <int P, bool INB, bool OUTB, bool SGD, bool FULL>
-__device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int j0) {
+__device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int s0, uint32_t next) {
 #pragma clang fp contract(off)
     constexpr int U = ring_vectors_per_lane(P, SGD);
     constexpr int V = ring_lane_elems(INB, OUTB, SGD);
@@ -291,11 +328,9 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int j0) {
     const uint32_t n_vec = a->n_vec;
 
     // Chunks are at least TILE long on this path, so the tile holds one
-    // start rank, or two with the boundary at element `split` of the launch.
+    // start rank, or two with the boundary at element `next` of the launch.
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int64_t next = static_cast<int64_t>(j0 + 1) * a->L;   // first element of chunk j0 + 1
-    const bool straddle = next <= a->base + last;
-    const int s0 = j0 % P;
+    const bool straddle = next <= last;
     const char* src[P];
     rotated_ins<P>(a, s0, src);
 
@@ -331,13 +366,12 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int j0) {
     if (straddle) {
         float acc2[U][V];
         fold<P, 1, INB, U, V>(x, acc2);
-        const uint32_t split = static_cast<uint32_t>(next - a->base);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i0 = t0 + (u * kBlock + tid) * V;
 #pragma unroll
             for (int e = 0; e < V; ++e)
-                if (i0 + e >= split) acc[u][e] = acc2[u][e];
+                if (i0 + e >= next) acc[u][e] = acc2[u][e];
         }
     }
 
@@ -399,13 +433,14 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
     const KArgs a = kernel_args();
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
-    // The tile's chunk, computed before the branch so that its argument
+    // The tile's start rank, computed before the branch so that its argument
     // loads go out together with n_vec's.
-    const int j0 = chunk_of(a->base + t0, a->L, a->rcpL);
+    uint32_t next;
+    const int s0 = tile_chunk<P>(t0, a->ring, next);
     if (t0 + TILE <= n_vec) {
-        process_tile<P, INB, OUTB, SGD, true>(a, t0, j0);
+        process_tile<P, INB, OUTB, SGD, true>(a, t0, s0, next);
     } else if (t0 < n_vec) {
-        process_tile<P, INB, OUTB, SGD, false>(a, t0, j0);
+        process_tile<P, INB, OUTB, SGD, false>(a, t0, s0, next);
     }
     if (blockIdx.x == gridDim.x - 1) {
         const uint32_t i = n_vec + threadIdx.x;
@@ -434,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_scalar_kernel(RingArgs) {
 template <int P, bool INB, bool OUTB>
 __device__ __forceinline__ void rs_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    const int s = chunk_of(a->base + i, a->L, a->rcpL) % P;
+    const int s = chunk_start<P>(i, a->ring);
     float g;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -458,7 +493,7 @@ __device__ __forceinline__ void rs_element(KArgs a, uint32_t i) {
 
 template <int P, int ES>
 __device__ __forceinline__ void ag_element(KArgs a, uint32_t i) {
-    const int s = chunk_of(a->base + i, a->L, a->rcpL) % P;
+    const int s = chunk_start<P>(i, a->ring);
     const int o = rank_at(s, P - 1, P);
     if constexpr (ES == 2) {
         const uint16_t v = static_cast<const uint16_t*>(a->out[o])[i];
@@ -485,8 +520,9 @@ __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
     const uint32_t tid = threadIdx.x;
     const uint32_t n_vec = a->n_vec;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int j0 = chunk_of(a->base + t0, a->L, a->rcpL);
-    if (static_cast<int64_t>(j0 + 1) * a->L <= a->base + last) {
+    uint32_t next;
+    const int s0 = tile_chunk<P>(t0, a->ring, next);
+    if (next <= last) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -496,7 +532,6 @@ __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
         }
         return;
     }
-    const int s0 = j0 % P;
     const char* src[P];
     rotated_ins<P>(a, s0, src);
     u32x4 x[P][U];
@@ -551,13 +586,14 @@ __device__ __forceinline__ void ag_tile(KArgs a, uint32_t t0) {
     const uint32_t n_vec = a->n_vec;
     const uint32_t i0 = t0 + tid * V;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int j0 = chunk_of(a->base + t0, a->L, a->rcpL);
+    uint32_t next;
+    const int s0 = tile_chunk<P>(t0, a->ring, next);
     if (!FULL && i0 >= n_vec) return;
-    if (static_cast<int64_t>(j0 + 1) * a->L <= a->base + last) {
+    if (next <= last) {
         for (int e = 0; e < V; ++e) ag_element<P, ES>(a, i0 + e);
         return;
     }
-    const int o = rank_at(j0 % P, P - 1, P);
+    const int o = rank_at(s0, P - 1, P);
     const u32x4 y = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a->out[o]) + i0 * ES);
     // the P-1 other ranks, starting at a rank that differs from wave to wave
     const int rot = P > 1 ? store_rotation(P - 1) : 0;
@@ -725,11 +761,10 @@ __device__ __forceinline__ void tree_fold(const u32x4 (&x)[P][U], uint64_t paren
 template <int P, bool INB, bool OUTB>
 __device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    const int64_t gi = a->base + i;
     const int G = a->groups;
     const int Lr = a->group_size;
     int rank[P];
-    level_ranks<P>(G, Lr, chunk_of(gi, a->L, a->rcpL) % Lr, chunk_of(gi, a->Lg, a->rcpLg) % G, rank);
+    level_ranks<P>(G, Lr, chunk_start(i, a->ring, Lr), chunk_start(i, a->global, G), rank);
     float part[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -770,10 +805,12 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     const uint32_t tid = threadIdx.x;
     const uint32_t n_vec = a->n_vec;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int jl = chunk_of(a->base + t0, a->L, a->rcpL);
-    const int jg = chunk_of(a->base + t0, a->Lg, a->rcpLg);
-    if (static_cast<int64_t>(jl + 1) * a->L <= a->base + last ||
-        static_cast<int64_t>(jg + 1) * a->Lg <= a->base + last) {
+    const int G = a->groups;
+    const int Lr = a->group_size;
+    uint32_t rl, rg;
+    const uint32_t ql = chunk_steps(t0, a->ring, rl);
+    const uint32_t qg = chunk_steps(t0, a->global, rg);
+    if (t0 + (a->ring.d - rl) <= last || t0 + (a->global.d - rg) <= last) {
         // a local or global chunk boundary inside the tile: element by element
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -783,10 +820,9 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
         }
         return;
     }
-    const int G = a->groups;
-    const int Lr = a->group_size;
     int rank[P];
-    level_ranks<P>(G, Lr, jl % Lr, jg % G, rank);
+    level_ranks<P>(G, Lr, static_cast<int>((a->ring.first + ql) % static_cast<uint32_t>(Lr)),
+                   static_cast<int>((a->global.first + qg) % static_cast<uint32_t>(G)), rank);
     u32x4 x[P][U];
     bool ok[U];
 #pragma unroll

@@ -191,7 +191,7 @@ int launch_ring_stepwise(const StepLaunch& l, const char** msg) {
                 if (grid < 1) grid = 1;
                 void* args[] = {&a};
                 const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(kBlock), args,
-                                                     lds_reserve(kStepWgPerCu),
+                                                     lds_reserve(wg_per_cu_for(DDP_KF_STEP, kStepWgPerCu)),
                                                      static_cast<hipStream_t>(l.stream));
                 if (e != hipSuccess) {
                     *msg = "hipLaunchKernel(ring_step)";

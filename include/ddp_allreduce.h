@@ -495,6 +495,38 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
                               float lr, float mu, void* const* out_ptrs_dev,
                               ddp_dtype out_dtype, void* stream);
 
+/* Kernel families whose launch shape ddp_set_wg_per_cu can override. */
+typedef enum ddp_kernel_family {
+    DDP_KF_RING = 0,            /* allreduce_ring_emulated */
+    DDP_KF_RING_SGD = 1,        /* allreduce_fused_sgd, zero1_sgd_step_emulated */
+    DDP_KF_TREE = 2,            /* allreduce_tree_emulated, allreduce_hierarchical_emulated */
+    DDP_KF_REDUCE_SCATTER = 3,  /* reducescatter_ring_emulated */
+    DDP_KF_ALL_GATHER = 4,      /* allgather_ring_emulated */
+    DDP_KF_MULTI = 5,           /* allreduce_multi_ring_emulated, allreduce_multi_fused_sgd */
+    DDP_KF_BUCKET_COPY = 6,     /* ddp_bucket_pack, ddp_bucket_unpack */
+    DDP_KF_STEP = 7             /* allreduce_ring_stepwise */
+} ddp_kernel_family;
+
+/*
+ * ddp_set_wg_per_cu -- host only, no device work.  A tuning knob, not part
+ * of the method: results are the same bits at every setting.
+ *
+ * Every kernel here streams HBM with little arithmetic, and the mix of
+ * reads and writes reaches its highest rate on MI355X with few resident
+ * waves per CU.  Each launch therefore caps its resident workgroups per CU
+ * (by reserving LDS it never touches) at a value chosen per kernel family,
+ * rank count and element types from measurements.  This call overrides the
+ * cap of one family for every later launch of the process (all threads):
+ *
+ *   family      the kernel family
+ *   wg_per_cu   2..64: at most that many workgroups per CU; 0: no cap (the
+ *               hardware's own occupancy); -1: the built-in choice again
+ * Errors: DDP_E_ARG (unknown family, value outside -1, 0, 2..64).
+ * Calls that race with launches on other threads are safe; which setting a
+ * concurrent launch sees is unspecified.
+ */
+int ddp_set_wg_per_cu(ddp_kernel_family family, int32_t wg_per_cu);
+
 /* Message describing the calling thread's most recent non-OK status
  * ("" if none).  The pointer stays valid until the thread's next call. */
 const char* ddp_last_error(void);

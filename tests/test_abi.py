@@ -367,3 +367,22 @@ def test_multi_plan():
                                              None) == N.DDP_E_ARG
     assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 0, tile, A, 0, A, 0,
                                              None) == N.DDP_OK
+
+
+# ------------------------------------------------------- tuning knob ----
+
+def test_wg_per_cu_knob_validation():
+    lib = N.lib()
+    for fam in N.KERNEL_FAMILIES.values():
+        for k in (-1, 0, 2, 3, 16, 64):
+            assert lib.ddp_set_wg_per_cu(fam, k) == N.DDP_OK
+        assert lib.ddp_set_wg_per_cu(fam, -1) == N.DDP_OK      # back to the built-in choice
+    for k in (-2, 1, 65, 1000):
+        assert lib.ddp_set_wg_per_cu(0, k) == N.DDP_E_ARG
+        assert "wg_per_cu" in N.last_error()
+    for fam in (-1, 8, 99):
+        assert lib.ddp_set_wg_per_cu(fam, 4) == N.DDP_E_ARG
+        assert "family" in N.last_error()
+    with pytest.raises(ValueError):
+        ddp.ddp_set_wg_per_cu("no such family", 4)
+    ddp.ddp_set_wg_per_cu("ring", -1)
