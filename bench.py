@@ -39,10 +39,18 @@ KERNEL_SOURCES = ["ring_reduce_impl.h", "ring_reduce.hip", "ring_reduce_f32_f32.
 
 
 def kernel_source_hash():
+    """SHA-256 of the dominant kernel's sources with comments and blank
+    lines removed: an edit of the comments leaves the measured kernel, and
+    so its recorded counters, valid."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gradient_all_reduce_allreduce_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gradient_all_reduce_allreduce_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()
 
 
@@ -277,6 +285,74 @@ def run_suite(steps, warmup):
     return 0
 
 
+def run_occupancy_sweep(caps=(2, 3, 4, 5, 6, 8, 10, 12, 16)):
+    """Time the fused all-reduce and the fused optimizer step at every cap on
+    resident workgroups per CU (ddp_set_wg_per_cu), for each rank count and
+    element-type pair, on four 25 MiB buckets per rank (two buffer sets);
+    one JSON line per case with the rate at every cap and the built-in
+    choice's rate.  The tables of launch.h hold the fastest cap per case."""
+    import torch
+
+    import gradient_all_reduce_allreduce_amd as ddp
+
+    dev = torch.device("cuda:0")
+
+    def timed(fn, steps=20):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def sweep(name, family, fn, nbytes):
+        rates = {}
+        for k in caps:
+            ddp.ddp_set_wg_per_cu(family, k)
+            rates[k] = round(nbytes / timed(fn) / 1e6, 1)
+        ddp.ddp_set_wg_per_cu(family, -1)
+        builtin = round(nbytes / timed(fn) / 1e6, 1)
+        best = max(rates, key=rates.get)
+        print(json.dumps({"occupancy": name, "family": family, "best_cap": best, "builtin_gbps": builtin,
+                          "gbps_by_cap": rates}), flush=True)
+
+    bucket = 25 << 20
+    nb = 4
+    names = {torch.float32: "f32", torch.bfloat16: "bf16"}
+    for P in (2, 3, 4, 5, 6, 8, 12, 16):
+        for it, ot in ((torch.float32, torch.float32), (torch.float32, torch.bfloat16),
+                       (torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16)):
+            n = bucket // (2 if it == torch.bfloat16 else 4)
+            g = torch.empty(2, P, nb * n, dtype=it, device=dev).normal_(0, 0.01)
+            o = torch.empty(2, P, nb * n, dtype=ot, device=dev)
+            views = [[([g[s_, r, k * n:(k + 1) * n] for r in range(P)],
+                       [o[s_, r, k * n:(k + 1) * n] for r in range(P)]) for k in range(nb)] for s_ in range(2)]
+            sweep(f"ring P={P} {names[it]}->{names[ot]}", "ring",
+                  lambda: [[ddp.allreduce(a, "mean", P, out=b) for a, b in st] for st in views],
+                  2 * nb * n * P * (g.element_size() + o.element_size()))
+            del g, o, views
+        for it in (torch.bfloat16, torch.float32):
+            n = bucket // (2 if it == torch.bfloat16 else 4)
+            g = torch.empty(P, nb * n, dtype=it, device=dev).normal_(0, 0.01)
+            o = torch.empty(P, nb * n, dtype=it, device=dev)
+            w = torch.zeros(nb * n, device=dev)
+            v = torch.zeros(nb * n, device=dev)
+            for with_out in (False, True):
+                sweep(f"sgd P={P} {names[it]} grads, {'with' if with_out else 'no'} gradient output", "ring_sgd",
+                      lambda: [ddp.allreduce_sgd([g[r, k * n:(k + 1) * n] for r in range(P)], w[k * n:(k + 1) * n],
+                                                 v[k * n:(k + 1) * n], 1e-3, 0.9, "mean", P,
+                                                 out=[o[r, k * n:(k + 1) * n] for r in range(P)] if with_out else None)
+                               for k in range(nb)],
+                      nb * n * (P * g.element_size() * (2 if with_out else 1) + 16))
+            del g, o, w, v
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +362,9 @@ def main():
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline line, time every entry point at the shape "
                          "of its workload (one JSON line each)")
+    ap.add_argument("--occupancy-sweep", action="store_true",
+                    help="time the fused all-reduce and optimizer step at every cap on resident "
+                         "workgroups per CU (the measurements behind the built-in caps)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (a kernel of known "
                          "traffic, to scale the memory counters of a profiler run)")
@@ -313,6 +392,8 @@ def main():
 
     if args.suite:
         return run_suite(args.steps, args.warmup)
+    if args.occupancy_sweep:
+        return run_occupancy_sweep()
 
     cfg = workloads.CONFIGS["cfg2"]
     P, C = cfg["P"], cfg["chunking"]

@@ -5,22 +5,23 @@
 //
 // The ring all-reduce of P buffers reads P streams and writes P streams; its
 // roofline is HBM bandwidth for that read/write mix, not the read-only peak.
-// This program times, with hipEvents over 40 repetitions each:
-//   read   -- 2 GiB read with 16-byte non-temporal loads (XOR-folded)
-//   write  -- 2 GiB written with 16-byte stores, plain and non-temporal
-//   copy   -- 2 GiB read + 2 GiB written, 16-byte non-temporal loads, and
-//             non-temporal or ordinary stores
-//   red8   -- the all-reduce's own pattern: 8 input streams summed into 8
-//             identical output streams (25 MiB each, 4 rotating buffer sets
-//             = 1.6 GiB, more than the last-level cache), with the 16
-//             buffers (a) separately allocated, (b) packed back to back in
-//             one allocation, (c) in one allocation with an extra 4 KiB
-//             between neighbours; each with 2 vectors per lane and a common
-//             store order, and with 1 vector per lane and the store order
-//             rotated per wave (non-temporal or ordinary stores).
-// Every kernel uses one tile of 256 lanes x U vectors per workgroup and as
-// many workgroups as tiles.  Output: one line per measurement, GB/s of bytes
-// moved (read + written).
+// Every kernel here moves one 16-byte vector per lane and stream, with
+// one-wave (64-lane) workgroups, one tile each, as many workgroups as tiles,
+// and LDS reserved so that at most `cap` workgroups share a CU (cap 0: the
+// hardware's own occupancy).  Loads are non-temporal, stores device-scope
+// buffer stores, as in the library.  Buffers hold random float bit patterns
+// (the rates on all-zero buffers come out about 1% higher).  Each line is
+// the mean over 40 launches timed with hipEvents, rotating over buffer sets
+// larger in total than the 256 MB last-level cache, in GB/s of bytes moved
+// (read + written):
+//   read8       8 input streams, 25 MiB each
+//   write8      8 output streams
+//   copy        1 input stream -> 1 output stream, 200 MiB each
+//   red8 f32    the all-reduce's own pattern: 8 input streams summed into 8
+//               identical output streams, 25 MiB each (the 16 buffers back to
+//               back in one allocation)
+//   red8 bf16->f32  8 bf16 input streams of 100 MiB, 8 float32 outputs
+//   red8 f32, separate allocations   the f32 pattern on 16 hipMallocs
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -28,6 +29,7 @@
 #include <vector>
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define CK(x)                                                                  \
     do {                                                                       \
@@ -38,201 +40,194 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         }                                                                      \
     } while (0)
 
-constexpr int kBlock = 256;
-constexpr int kU = 2;
+constexpr int kW = 64;
+constexpr unsigned kLdsPerCu = 160u * 1024u;
+constexpr unsigned kLdsGranule = 1280u;
 
-__global__ __launch_bounds__(kBlock) void read_kernel(const u32x4* a, uint32_t nvec, uint32_t* sink) {
-    const uint32_t t = blockIdx.x * (kBlock * kU);
-    u32x4 acc = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const uint32_t i = t + u * kBlock + threadIdx.x;
-        if (i < nvec) acc ^= __builtin_nontemporal_load(a + i);
-    }
-    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) sink[0] = 1u;   // keeps the loads
-}
+static unsigned lds_for(int cap) { return cap <= 0 ? 0u : kLdsPerCu / cap / kLdsGranule * kLdsGranule; }
 
-template <bool NT>
-__global__ __launch_bounds__(kBlock) void write_kernel(u32x4* a, uint32_t nvec) {
-    const uint32_t t = blockIdx.x * (kBlock * kU);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const uint32_t i = t + u * kBlock + threadIdx.x;
-        const u32x4 v = {i, i, i, i};
-        if (i < nvec) {
-            if (NT) __builtin_nontemporal_store(v, a + i); else a[i] = v;
-        }
-    }
-}
-
-template <bool NT>
-__global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* a, u32x4* b, uint32_t nvec) {
-    const uint32_t t = blockIdx.x * (kBlock * kU);
-    u32x4 x[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const uint32_t i = t + u * kBlock + threadIdx.x;
-        if (i < nvec) x[u] = __builtin_nontemporal_load(a + i);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const uint32_t i = t + u * kBlock + threadIdx.x;
-        if (i < nvec) {
-            if (NT) __builtin_nontemporal_store(x[u], b + i); else b[i] = x[u];
-        }
-    }
-}
-
-struct Streams8 {
-    const u32x4* in[8];
-    u32x4* out[8];
+struct Streams {
+    const char* in[8];
+    char* out[16];       // out[q] and out[q + 8] are the same stream (rotated store order)
+    uint32_t out_bytes;  // size of each output stream
 };
 
-// The same pattern with one 16-byte vector per lane and the order of the 8
-// output stores rotated by the wave index (each wave starts at another
-// output stream); NT selects non-temporal or ordinary stores.
-template <bool NT>
-__global__ __launch_bounds__(kBlock) void red8_rotated_kernel(Streams8 p, uint32_t nvec) {
-    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (i >= nvec) return;
-    u32x4 x[8];
+__device__ __forceinline__ void store16(char* base, uint32_t bytes, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000),
+                                           off, 0, 16);
+}
+
+// Random float bit patterns of magnitude around 2^-7 (finite, both signs).
+__global__ void fill_kernel(uint32_t* p, size_t n, uint32_t seed) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        uint32_t x = static_cast<uint32_t>(i) * 2654435761u ^ seed ^ static_cast<uint32_t>(i >> 32);
+        x ^= x >> 16;
+        x *= 0x7feb352du;
+        x ^= x >> 15;
+        x *= 0x846ca68bu;
+        x ^= x >> 16;
+        p[i] = (x & 0x807fffffu) | ((120u + ((x >> 23) & 3u)) << 23);
+    }
+}
+
+// NR input streams, NW output streams; tile = one 16-byte vector per lane
+// and stream.  With both, the outputs get the sum of the inputs (float32).
+template <int NR, int NW>
+__global__ __launch_bounds__(kW) void stream_kernel(Streams p, uint32_t* sink) {
+    const uint32_t off = (blockIdx.x * kW + threadIdx.x) * 16u;
+    u32x4 x[NR > 0 ? NR : 1];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(p.in[r] + i);
+    for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.in[r] + off));
+    u32x4 s = {off, off, off, off};
+    if constexpr (NR > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = __uint_as_float(x[0][e]);
+#pragma unroll
+            for (int r = 1; r < NR; ++r) acc = acc + __uint_as_float(x[r][e]);
+            s[e] = __float_as_uint(acc);
+        }
+    }
+    if constexpr (NW == 0) {
+        if ((s[0] ^ s[1] ^ s[2] ^ s[3]) == 0x9e3779b9u) sink[0] = 1u;   // keeps the loads
+    } else {
+        const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x % NW));
+#pragma unroll
+        for (int q = 0; q < NW; ++q) store16(p.out[rot + q], p.out_bytes, off, s);
+    }
+}
+
+// The bf16 -> float32 pattern: 8-byte bf16 loads (4 elements), 16-byte stores.
+__global__ __launch_bounds__(kW) void red8_bf16_kernel(Streams p, uint32_t* sink) {
+    const uint32_t i = blockIdx.x * kW + threadIdx.x;   // 4-element group
+    u32x2 x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[r] + i * 8u));
     u32x4 s;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float acc = __uint_as_float(x[0][k]);
+    for (int e = 0; e < 4; ++e) {
+        float acc = 0.0f;
 #pragma unroll
-        for (int r = 1; r < 8; ++r) acc = acc + __uint_as_float(x[r][k]);
-        s[k] = __float_as_uint(acc);
-    }
-    const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * (kBlock / 64) + threadIdx.x / 64) & 7));
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int want = (q + rot) & 7;
-        u32x4* o = p.out[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) o = want == j ? p.out[j] : o;
-        if (NT) __builtin_nontemporal_store(s, o + i); else o[i] = s;
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void red8_kernel(Streams8 p, uint32_t nvec) {
-    const uint32_t t = blockIdx.x * (kBlock * kU);
-    u32x4 x[8][kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const uint32_t i = t + u * kBlock + threadIdx.x;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) x[r][u] = i < nvec ? __builtin_nontemporal_load(p.in[r] + i) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const uint32_t i = t + u * kBlock + threadIdx.x;
-        if (i >= nvec) continue;
-        u32x4 s;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float acc = __uint_as_float(x[0][u][k]);
-#pragma unroll
-            for (int r = 1; r < 8; ++r) acc = acc + __uint_as_float(x[r][u][k]);
-            s[k] = __float_as_uint(acc);
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t w = x[r][e >> 1];
+            const float v = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            acc = r == 0 ? v : acc + v;
         }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) __builtin_nontemporal_store(s, p.out[r] + i);
+        s[e] = __float_as_uint(acc);
     }
+    const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x & 7));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) store16(p.out[rot + q], p.out_bytes, i * 16u, s);
 }
 
-template <typename F>
-static float time_ms(F launch, int reps = 40) {
+template <typename K>
+static double rate(K kernel, unsigned grid, int cap, const std::vector<Streams>& sets, uint32_t* sink,
+                   double bytes_per_launch, int reps = 40) {
+    const unsigned lds = lds_for(cap);
     hipEvent_t a, b;
     CK(hipEventCreate(&a));
     CK(hipEventCreate(&b));
-    launch(0);
-    launch(1);
+    for (int i = 0; i < 3; ++i) hipLaunchKernelGGL(kernel, dim3(grid), dim3(kW), lds, 0, sets[i % sets.size()], sink);
+    CK(hipGetLastError());
     CK(hipDeviceSynchronize());
     CK(hipEventRecord(a));
-    for (int i = 0; i < reps; ++i) launch(i);
+    for (int i = 0; i < reps; ++i) hipLaunchKernelGGL(kernel, dim3(grid), dim3(kW), lds, 0, sets[i % sets.size()], sink);
     CK(hipEventRecord(b));
     CK(hipEventSynchronize(b));
     float ms = 0.f;
     CK(hipEventElapsedTime(&ms, a, b));
     CK(hipEventDestroy(a));
     CK(hipEventDestroy(b));
-    return ms / reps;
+    return bytes_per_launch / (ms / reps * 1e-3) / 1e9;
 }
 
-static unsigned grid_for(uint32_t nvec) { return (nvec + kBlock * kU - 1) / (kBlock * kU); }
+static void fill(char* p, size_t bytes, uint32_t seed) {
+    hipLaunchKernelGGL(fill_kernel, dim3(4096), dim3(256), 0, 0, reinterpret_cast<uint32_t*>(p), bytes / 4, seed);
+    CK(hipGetLastError());
+}
+
+// Streams of one set: inputs at `in`, outputs at `out`, each `stride` apart.
+static Streams make_set(char* in, size_t in_stride, char* out, size_t out_stride, uint32_t out_bytes) {
+    Streams s{};
+    for (int r = 0; r < 8; ++r) s.in[r] = in + r * in_stride;
+    for (int q = 0; q < 8; ++q) s.out[q] = s.out[q + 8] = out + q * out_stride;
+    s.out_bytes = out_bytes;
+    return s;
+}
 
 int main() {
-    const size_t big = size_t(2) << 30;
-    const uint32_t nvec = static_cast<uint32_t>(big / 16);
-    char* A = nullptr;
-    char* B = nullptr;
+    const int caps[] = {0, 3, 4, 5, 6, 8};
     uint32_t* sink = nullptr;
-    CK(hipMalloc(&A, big));
-    CK(hipMalloc(&B, big));
     CK(hipMalloc(&sink, 64));
-    CK(hipMemset(A, 1, big));
-    CK(hipMemset(B, 2, big));
-    const unsigned g = grid_for(nvec);
 
-    float ms = time_ms([&](int) { read_kernel<<<g, kBlock>>>(reinterpret_cast<const u32x4*>(A), nvec, sink); });
-    std::printf("read  nt          : %7.0f GB/s\n", big / ms / 1e6);
-    ms = time_ms([&](int) { write_kernel<false><<<g, kBlock>>>(reinterpret_cast<u32x4*>(A), nvec); });
-    std::printf("write plain       : %7.0f GB/s\n", big / ms / 1e6);
-    ms = time_ms([&](int) { write_kernel<true><<<g, kBlock>>>(reinterpret_cast<u32x4*>(A), nvec); });
-    std::printf("write nt          : %7.0f GB/s\n", big / ms / 1e6);
-    ms = time_ms([&](int) {
-        copy_kernel<true><<<g, kBlock>>>(reinterpret_cast<const u32x4*>(A), reinterpret_cast<u32x4*>(B), nvec);
-    });
-    std::printf("copy  nt          : %7.0f GB/s\n", 2.0 * big / ms / 1e6);
-    ms = time_ms([&](int) {
-        copy_kernel<false><<<g, kBlock>>>(reinterpret_cast<const u32x4*>(A), reinterpret_cast<u32x4*>(B), nvec);
-    });
-    std::printf("copy  nt load, plain store: %7.0f GB/s\n", 2.0 * big / ms / 1e6);
-
-    const size_t rb = size_t(25) << 20;               // 25 MiB per stream
-    const uint32_t rv = static_cast<uint32_t>(rb / 16);
-    const int sets = 4;
-    std::vector<char*> separate;
-    for (int s = 0; s < 16 * sets; ++s) {
-        char* p = nullptr;
-        CK(hipMalloc(&p, rb));
-        CK(hipMemset(p, 0, rb));
-        separate.push_back(p);
-    }
-    const size_t max_stride = rb + 4096;
+    // 25 MiB streams: 4 sets of 16 streams back to back (1.6 GiB)
+    const size_t sb = size_t(25) << 20;
+    const int nsets = 4;
     char* arena = nullptr;
-    CK(hipMalloc(&arena, max_stride * 16 * sets));
-    CK(hipMemset(arena, 0, max_stride * 16 * sets));
-    const char* names[3] = {"separate allocations", "one allocation, stride 25 MiB",
-                            "one allocation, stride 25 MiB + 4 KiB"};
-    for (int layout = 0; layout < 3; ++layout) {
-        const size_t stride = layout == 2 ? max_stride : rb;
-        Streams8 ps[sets];
-        for (int s = 0; s < sets; ++s) {
-            for (int r = 0; r < 8; ++r) {
-                char* in = layout == 0 ? separate[s * 16 + r] : arena + (s * 16 + r) * stride;
-                char* out = layout == 0 ? separate[s * 16 + 8 + r] : arena + (s * 16 + 8 + r) * stride;
-                ps[s].in[r] = reinterpret_cast<const u32x4*>(in);
-                ps[s].out[r] = reinterpret_cast<u32x4*>(out);
-            }
-        }
-        ms = time_ms([&](int i) { red8_kernel<<<grid_for(rv), kBlock>>>(ps[i % sets], rv); });
-        std::printf("red8  %-38s: %7.0f GB/s (%.1f us per 25 MiB x 16 streams)\n", names[layout],
-                    16.0 * rb / ms / 1e6, ms * 1e3);
-        ms = time_ms([&](int i) { red8_rotated_kernel<true><<<(rv + kBlock - 1) / kBlock, kBlock>>>(ps[i % sets], rv); });
-        std::printf("red8  %-38s: %7.0f GB/s (%.1f us) one vector per lane, rotated stores\n",
-                    names[layout], 16.0 * rb / ms / 1e6, ms * 1e3);
-        ms = time_ms([&](int i) { red8_rotated_kernel<false><<<(rv + kBlock - 1) / kBlock, kBlock>>>(ps[i % sets], rv); });
-        std::printf("red8  %-38s: %7.0f GB/s (%.1f us) one vector per lane, rotated plain stores\n",
-                    names[layout], 16.0 * rb / ms / 1e6, ms * 1e3);
+    CK(hipMalloc(&arena, sb * 16 * nsets));
+    fill(arena, sb * 16 * nsets, 1u);
+    std::vector<Streams> red;
+    for (int s = 0; s < nsets; ++s)
+        red.push_back(make_set(arena + s * 16 * sb, sb, arena + (s * 16 + 8) * sb, sb, static_cast<uint32_t>(sb)));
+    const unsigned g25 = static_cast<unsigned>(sb / 16 / kW);
+
+    // copy: 200 MiB streams, 4 pairs (1.6 GiB)
+    const size_t cb = size_t(200) << 20;
+    std::vector<Streams> copy;
+    for (int s = 0; s < nsets; ++s)
+        copy.push_back(make_set(arena + 2 * s * cb, cb, arena + (2 * s + 1) * cb, cb, static_cast<uint32_t>(cb)));
+    const unsigned g200 = static_cast<unsigned>(cb / 16 / kW);
+
+    // bf16 -> f32: 100 MiB bf16 inputs, 200 MiB float32 outputs, 2 sets (4.7 GiB)
+    const size_t bin = size_t(100) << 20, bout = size_t(200) << 20;
+    char* barena = nullptr;
+    CK(hipMalloc(&barena, (bin + bout) * 8 * 2));
+    fill(barena, (bin + bout) * 8 * 2, 2u);
+    std::vector<Streams> bf;
+    for (int s = 0; s < 2; ++s) {
+        char* base = barena + s * (bin + bout) * 8;
+        bf.push_back(make_set(base, bin, base + 8 * bin, bout, static_cast<uint32_t>(bout)));
     }
-    for (char* p : separate) CK(hipFree(p));
+    const unsigned gbf = static_cast<unsigned>(bin / 8 / kW);
+
+    // separate allocations for the f32 pattern
+    std::vector<char*> sep;
+    for (int i = 0; i < 16 * nsets; ++i) {
+        char* p = nullptr;
+        CK(hipMalloc(&p, sb));
+        fill(p, sb, 3u + i);
+        sep.push_back(p);
+    }
+    std::vector<Streams> red_sep;
+    for (int s = 0; s < nsets; ++s) {
+        Streams st{};
+        for (int r = 0; r < 8; ++r) st.in[r] = sep[s * 16 + r];
+        for (int q = 0; q < 8; ++q) st.out[q] = st.out[q + 8] = sep[s * 16 + 8 + q];
+        st.out_bytes = static_cast<uint32_t>(sb);
+        red_sep.push_back(st);
+    }
+    CK(hipDeviceSynchronize());
+
+    std::printf("%-36s", "pattern \\ workgroups per CU");
+    for (int c : caps) std::printf(c ? "%8d" : "    none", c);
+    std::printf("\n");
+    auto row = [&](const char* name, auto kernel, unsigned grid, const std::vector<Streams>& sets, double bytes) {
+        std::printf("%-36s", name);
+        for (int c : caps) std::printf("%8.0f", rate(kernel, grid, c, sets, sink, bytes));
+        std::printf("   GB/s\n");
+        std::fflush(stdout);
+    };
+    row("read8 (25 MiB streams)", stream_kernel<8, 0>, g25, red, 8.0 * sb);
+    row("write8 (25 MiB streams)", stream_kernel<0, 8>, g25, red, 8.0 * sb);
+    row("copy (200 MiB)", stream_kernel<1, 1>, g200, copy, 2.0 * cb);
+    row("red8 f32 (25 MiB, one allocation)", stream_kernel<8, 8>, g25, red, 16.0 * sb);
+    row("red8 f32 (25 MiB, separate allocs)", stream_kernel<8, 8>, g25, red_sep, 16.0 * sb);
+    row("red8 bf16->f32 (100 MiB inputs)", red8_bf16_kernel, gbf, bf, 8.0 * (bin + bout));
+
+    for (char* p : sep) CK(hipFree(p));
+    CK(hipFree(barena));
     CK(hipFree(arena));
-    CK(hipFree(A));
-    CK(hipFree(B));
     CK(hipFree(sink));
     return 0;
 }

@@ -18,16 +18,17 @@
 //
 // The work is bound by HBM bandwidth: per element it reads P inputs, writes
 // P outputs and does P-1 float32 additions.  The design follows from that:
-//   * one workgroup of 256 lanes per tile and as many workgroups as tiles;
-//     the dispatcher balances tiles over the CUs and XCDs as they free up
-//     (measured faster than fixed per-workgroup shares of the buffer);
+//   * one one-wave workgroup (64 lanes) per tile and as many workgroups as
+//     tiles, with the number resident per CU capped (launch.h): this mix of
+//     reads and writes streams fastest with few waves per CU, and the
+//     dispatcher balances tiles over the CUs and XCDs as they free up;
 //   * each lane loads U vectors of V elements from each of the P ranks (P*U
 //     loads in flight) with non-temporal hints, folds them in registers and
-//     stores them non-temporally.  Every lane store is 16 bytes wide when
-//     the output or the momentum state is float32 (V = 4), so a wave writes
-//     1 KiB contiguous per instruction; bf16 -> bf16 moves 8 elements per
-//     lane.  The data is touched once, so nothing is staged in LDS and no
-//     cache lines are kept;
+//     stores the result with device-scope buffer stores.  Every lane store is
+//     16 bytes wide when the output or the momentum state is float32 (V = 4),
+//     so a wave writes 1 KiB contiguous per instruction; bf16 -> bf16 moves 8
+//     elements per lane.  The data is touched once, so nothing is staged in
+//     LDS;
 //   * addresses are a per-rank base in SGPRs plus one 32-bit lane offset
 //     shared by all ranks (the host splits buffers over 2^29 elements into
 //     several launches), which keeps VGPRs for data;
@@ -38,7 +39,8 @@
 //     tile long on this path, so a tile holds at most two start ranks; the
 //     second order is the same registers folded from k = 1, selected per
 //     element.  Chunks shorter than a tile go to a one-element-per-lane
-//     kernel;
+//     kernel.  The tile's chunk comes from 32-bit scalar arithmetic on a
+//     divisor map the host builds per launch;
 //   * bf16 inputs are widened exactly (a shift) inside the fold, float32
 //     accumulation throughout, no FMA contraction, subnormals kept.
 #pragma once
@@ -99,8 +101,8 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 // SGPRs, a 32-bit lane offset), because the buffer form carries a cache
 // policy: device scope (sc1) without the non-temporal hint measured 2-3%
 // faster than non-temporal stores for the all-reduce's 8-in/8-out pattern
-// at the occupancy the launches use (6.39 against 6.22 TB/s), and faster
-// than ordinary stores (5.86).  The hardware drops stores at or beyond
+// at the occupancy the launches use, and about 6% faster than ordinary
+// stores.  The hardware drops stores at or beyond
 // `bytes` from the base.
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit format, no swizzle
 constexpr int kStoreDeviceScope = 16;      // cache-policy operand of the store: sc1
@@ -238,6 +240,17 @@ __device__ __forceinline__ int tile_chunk(uint32_t t0, const __attribute__((addr
     return static_cast<int>((c.first + q) % static_cast<uint32_t>(M));
 }
 
+// Holds a uniform value in SGPRs from this point of the program on.  Placed
+// right after a tile's loads are issued, it makes the scalar loads of the
+// kernel arguments the stores need (output bases, sizes, flags) go out and
+// return while the tile's data is in flight; left to itself the compiler
+// sinks them to their first use, which puts their round trips between the
+// data arriving and the results leaving.
+template <typename T>
+__device__ __forceinline__ void pin_sgpr(T v) {
+    asm volatile("" ::"s"(v));
+}
+
 // Every output rank receives the same value, so the order of the P stores
 // is free.  Each wave starts at a different rank (its wave index mod P):
 // the waves in flight then write to all P output streams at once instead
@@ -313,8 +326,8 @@ __device__ __forceinline__ u32x4 load_lane(const void* p) {
     }
 }
 
-// One tile = U rows of 256 lane vectors of V elements per rank, processed
-// by one workgroup.  FULL: the whole tile lies below n_vec.
+// One tile = U rows of kBlock lane vectors of V elements per rank,
+// processed by one workgroup.  FULL: the whole tile lies below n_vec.
 template <int P, bool INB, bool OUTB, bool SGD, bool FULL>
 __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int s0, uint32_t next) {
 #pragma clang fp contract(off)
@@ -361,6 +374,26 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int s0, uint3
         }
     }
 
+    // What the stores need, fetched while the loads are in flight.
+    const uint32_t n = a->n;
+    const int32_t mean_flag = a->mean;
+    const int32_t write_out = SGD ? a->write_out : 1;
+    const float lr = SGD ? a->lr : 0.0f;
+    const float mu = SGD ? a->mu : 0.0f;
+    char* dst[P];
+    rotated_outs<P>(a, store_rotation(P), dst);
+    pin_sgpr(n);
+    pin_sgpr(mean_flag);
+    if constexpr (SGD) {
+        pin_sgpr(write_out);
+        pin_sgpr(lr);
+        pin_sgpr(mu);
+    }
+    if (!SGD || write_out) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) pin_sgpr(dst[q]);
+    }
+
     float acc[U][V];
     fold<P, 0, INB, U, V>(x, acc);
     if (straddle) {
@@ -375,9 +408,7 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int s0, uint3
         }
     }
 
-    const bool mean = a->mean != 0;
-    char* dst[P];
-    rotated_outs<P>(a, store_rotation(P), dst);
+    const bool mean = mean_flag != 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -389,14 +420,14 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int s0, uint3
             u32x4 wq, vq;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                momentum_step(g[e], ws[u][e], vs[u][e], a->lr, a->mu);
+                momentum_step(g[e], ws[u][e], vs[u][e], lr, mu);
                 wq[e] = __float_as_uint(ws[u][e]);
                 vq[e] = __float_as_uint(vs[u][e]);
             }
-            store16(a->w, a->n * 4u, i0 * 4u, wq);
-            store16(a->v, a->n * 4u, i0 * 4u, vq);
-            if (!a->write_out) continue;
-            if (a->write_out == 2) {
+            store16(a->w, n * 4u, i0 * 4u, wq);
+            store16(a->v, n * 4u, i0 * 4u, vq);
+            if (!write_out) continue;
+            if (write_out == 2) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) g[e] = ws[u][e];
             }
@@ -406,19 +437,19 @@ __device__ __forceinline__ void process_tile(KArgs a, uint32_t t0, int s0, uint3
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store8(dst[q], a->n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) store8(dst[q], n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], n * OES, i0 * OES, o);
         }
     }
 }
@@ -838,11 +869,20 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
             for (int r = 0; r < P; ++r) x[r][u] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    float acc[U][V];
-    tree_fold<P, INB, U, V>(x, a->parents, acc);
-    const bool mean = a->mean != 0;
+    // What the fold and the stores need, fetched while the loads are in flight.
+    const uint64_t parents = a->parents;
+    const uint32_t n = a->n;
+    const int32_t mean_flag = a->mean;
     char* dst[P];
     rotated_outs<P>(a, store_rotation(P), dst);
+    pin_sgpr(parents);
+    pin_sgpr(n);
+    pin_sgpr(mean_flag);
+#pragma unroll
+    for (int q = 0; q < P; ++q) pin_sgpr(dst[q]);
+    float acc[U][V];
+    tree_fold<P, INB, U, V>(x, parents, acc);
+    const bool mean = mean_flag != 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -855,19 +895,19 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store8(dst[q], a->n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) store8(dst[q], n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int q = 0; q < P; ++q) store16(dst[q], a->n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) store16(dst[q], n * OES, i0 * OES, o);
         }
     }
 }
