@@ -9,22 +9,24 @@
 //
 // A pure copy: bound by HBM bandwidth, 2 * bucket bytes per rank.  One
 // workgroup per (tile of the bucket, rank), as many workgroups as tiles, so
-// that the dispatcher keeps every CU busy.  For its tile a workgroup stages
-// the overlapping segments in LDS (one uniform binary search in the segment
-// table finds the first), so that each lane finds the segment of each of
-// its vectors with a short binary search in LDS instead of a chain of
+// that the dispatcher keeps every CU busy.  One uniform binary search in
+// the segment table finds the segment holding the tile's first element.
+// Most tiles lie inside that one segment (tensors are long against a tile):
+// every vector then maps to the tensor at a uniform offset and the tile
+// moves with no further lookup.  Otherwise the workgroup stages the
+// overlapping segments in LDS, so that each lane finds the segment of each
+// of its vectors with a short binary search in LDS instead of a chain of
 // dependent global loads.  A vector (16 bytes on the bucket side, always
 // aligned) that lies inside one segment moves as one 16-byte access on the
 // bucket side and, on the tensor side, as one 16-byte access when the
 // tensor address is aligned, else as element-size accesses; a lane issues
 // all of those loads before its first store, so kVecPerLane vectors per
 // lane are in flight.  Vectors across a segment boundary move element by
-// element afterwards.  Pack stores are ordinary (the all-reduce that reads
-// a packed bucket next finds part of it in the last-level cache), unpack
-// stores non-temporal (the tensors are not read again soon); both choices
-// measured faster than the other.  Every bucket element is written exactly
-// once (the segments tile the bucket), so no synchronisation between
-// workgroups is needed.
+// element afterwards.  Pack stores the bucket with device-scope buffer
+// stores, unpack stores the tensors non-temporally; each measured fastest
+// of the store policies tried (ordinary, non-temporal, device scope).
+// Every bucket element is written exactly once (the segments tile the
+// bucket), so no synchronisation between workgroups is needed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,6 +91,15 @@ __device__ __forceinline__ void store_elems_nt(char* p, u32x4 v, int es) {
     }
 }
 
+// Bucket-side stores of pack: a buffer store with device scope (sc1), the
+// policy of the all-reduce's result stores, over the tile (measured 2%
+// faster than ordinary stores, and faster than non-temporal ones).
+__device__ __forceinline__ void store16_tile(char* tile_base, int64_t tile_bytes, int64_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        v, __builtin_amdgcn_make_buffer_rsrc(tile_base, 0, static_cast<int>(tile_bytes), 0x00020000),
+        static_cast<uint32_t>(off), 0, 16);
+}
+
 // Largest index g in [0, count) with dst[g] <= e (dst sorted ascending,
 // dst[0] <= e).
 __device__ __forceinline__ int lds_find(const int64_t* dst, int count, int64_t e) {
@@ -126,6 +137,53 @@ __global__ __launch_bounds__(kBlock) void bucket_copy_kernel(CopyArgs a) {
             if (a.segs[mid].dst_off <= lo) l = mid; else h = mid - 1;
         }
         f = l;
+    }
+
+    // Most tiles lie inside one segment (tensors are long against a tile):
+    // then every vector maps to that tensor at a uniform offset, with no
+    // staging and no per-lane search.
+    {
+        const ddp_segment sg = a.segs[f];
+        if (sg.dst_off + sg.len >= hi) {
+            const char* ten = static_cast<const char*>(tensors[sg.tensor]) + (sg.src_off + (lo - sg.dst_off)) * es;
+            const bool aligned = (reinterpret_cast<uintptr_t>(ten) & 15u) == 0;   // uniform
+            u32x4 x[kVecPerLane];
+#pragma unroll
+            for (int u = 0; u < kVecPerLane; ++u) {
+                const int64_t d = static_cast<int64_t>(u * kBlock + tid) * ve;   // element offset in the tile
+                if (lo + d + ve > hi) continue;
+                const char* src = PACK ? ten + d * es : bucket + (lo + d) * es;
+                if (!PACK || aligned) {
+                    x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+                } else {
+                    x[u] = load_elems(src, es);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kVecPerLane; ++u) {
+                const int64_t d = static_cast<int64_t>(u * kBlock + tid) * ve;
+                if (lo + d + ve > hi) continue;
+                if (PACK) {
+                    store16_tile(bucket + lo * es, (hi - lo) * es, d * es, x[u]);
+                } else if (aligned) {
+                    __builtin_nontemporal_store(x[u], reinterpret_cast<u32x4*>(const_cast<char*>(ten) + d * es));
+                } else {
+                    store_elems_nt(const_cast<char*>(ten) + d * es, x[u], es);
+                }
+            }
+            // A partial last vector (the bucket's end): element by element.
+#pragma unroll
+            for (int u = 0; u < kVecPerLane; ++u) {
+                const int64_t d = static_cast<int64_t>(u * kBlock + tid) * ve;
+                if (lo + d >= hi || lo + d + ve <= hi) continue;
+                for (int64_t e = lo + d; e < hi; ++e) {
+                    char* pb = bucket + e * es;
+                    char* pt = const_cast<char*>(ten) + (e - lo) * es;
+                    if (PACK) copy_elem(pb, pt, es); else copy_elem(pt, pb, es);
+                }
+            }
+            return;
+        }
     }
 
     while (true) {
@@ -177,16 +235,16 @@ __global__ __launch_bounds__(kBlock) void bucket_copy_kernel(CopyArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kVecPerLane; ++u) {
-            char* bk = bucket + (lo + static_cast<int64_t>(u * kBlock + tid) * ve) * es;
+            const int64_t d = static_cast<int64_t>(u * kBlock + tid) * ve;   // element offset in the tile
             if (cls[u] == 1) {
                 if (PACK) {
-                    *reinterpret_cast<u32x4*>(bk) = x[u];
+                    store16_tile(bucket + lo * es, (hi - lo) * es, d * es, x[u]);
                 } else {
                     __builtin_nontemporal_store(x[u], reinterpret_cast<u32x4*>(tn[u]));
                 }
             } else if (cls[u] == 2) {
                 if (PACK) {
-                    *reinterpret_cast<u32x4*>(bk) = x[u];
+                    store16_tile(bucket + lo * es, (hi - lo) * es, d * es, x[u]);
                 } else {
                     store_elems_nt(tn[u], x[u], es);
                 }

@@ -182,9 +182,9 @@ def sampled_indices(n, C, extra=()):
     return np.unique(np.concatenate(parts))
 
 
-def test_more_than_one_launch_bf16_to_f32_two_passes():
-    """bf16 -> fp32 runs as a reduce-scatter pass and an all-gather pass;
-    both carry the chunk order across the split at 2^29 elements."""
+def test_more_than_one_launch_bf16_to_f32():
+    """bf16 -> fp32 (outputs twice as wide as the inputs) carries the chunk
+    order across the split at 2^29 elements."""
     P, n, C = 3, (1 << 29) + 77, 4
     ins = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
     for r, t in enumerate(ins):
@@ -200,6 +200,31 @@ def test_more_than_one_launch_bf16_to_f32_two_passes():
     got = np.stack([t[it].cpu().numpy() for t in outs])
     assert_same_bits(got, want, "split launch, bf16 -> f32")
     del ins, outs
+    torch.cuda.empty_cache()
+
+
+def test_chunks_longer_than_2_30_elements():
+    """Chunks longer than 2^30 elements: a launch of 2^29 elements then holds
+    at most one chunk boundary, which the launch's chunk map must place
+    exactly (here inside the fourth launch); in place, bf16, Mean."""
+    P, n, C = 3, 3 * (1 << 30) + 4097, 2
+    L = -(-n // C)
+    assert L > (1 << 30)
+    bufs = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    for r, t in enumerate(bufs):
+        workloads.torch_normal_(t, 1.0, seed=400 + r)
+    splits = [np.arange(max(0, k * (1 << 29) - 40), min(n, k * (1 << 29) + 40)) for k in range(1, 7)]
+    idx = sampled_indices(n, C, extra=splits)
+    it = torch.from_numpy(idx).to(DEV)
+    V = np.stack([t[it].view(torch.int16).cpu().numpy().view(np.uint16) for t in bufs])
+    ddp.allreduce(bufs, "mean", C, out=bufs)
+    torch.cuda.synchronize()
+    start = oracle.chunk_start_ranks_at(n, C, P, idx)
+    assert set(start.tolist()) == {0, 1}
+    want = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="bf16")
+    got = np.stack([t[it].view(torch.int16).cpu().numpy().view(np.uint16) for t in bufs])
+    assert_same_bits(got, want, "chunks over 2^30 elements")
+    del bufs
     torch.cuda.empty_cache()
 
 
