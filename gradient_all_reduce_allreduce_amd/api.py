@@ -399,7 +399,10 @@ class MultiAllReduce:
                                           pout, dtout, stream)
             return out
 
-        run.tables = (tin, tout)      # kept alive with the launcher
+        # The launcher holds raw device addresses: it must own every table
+        # they point into, the tile plan included, so that it stays valid
+        # after this object is dropped (``MultiAllReduce(...).bind(...)``).
+        run.tables = (self.tiles_dev, tin, tout)
         run.out = out
         return run
 
@@ -434,7 +437,7 @@ class MultiAllReduce:
                                       torch_dtype_code(self.out_dtype), stream)
             return out
 
-        run.tables = (tin, tout, tw, tv)   # kept alive with the launcher
+        run.tables = (self.tiles_dev, tin, tout, tw, tv)   # owned by the launcher, as in bind()
         return run
 
     def __call__(self, rank_lists, op="sum", chunking=None, out=None):

@@ -386,3 +386,34 @@ def test_wg_per_cu_knob_validation():
     with pytest.raises(ValueError):
         ddp.ddp_set_wg_per_cu("no such family", 4)
     ddp.ddp_set_wg_per_cu("ring", -1)
+
+
+def test_multi_launcher_owns_its_tables(monkeypatch):
+    """A launcher from MultiAllReduce.bind() keeps every device table its
+    raw addresses point into alive (the tile plan included) after the
+    MultiAllReduce object itself is dropped; built on CPU tensors, nothing
+    launched."""
+    import gc
+    import weakref
+
+    import torch
+
+    from gradient_all_reduce_allreduce_amd import api
+
+    monkeypatch.setattr(api, "current_stream", lambda device: None)
+    shapes = [(3,), (70,), (5, 4)]
+    ts = [[torch.zeros(s) for s in shapes] for _ in range(2)]
+    for bind in ("bind", "bind_sgd"):
+        m = api.MultiAllReduce(shapes, 2, torch.float32, device="cpu")
+        plan = weakref.ref(m.tiles_dev)
+        if bind == "bind":
+            run = m.bind(ts, out=[[torch.zeros(s) for s in shapes] for _ in range(2)])
+        else:
+            run = m.bind_sgd(ts, [torch.zeros(s) for s in shapes], [torch.zeros(s) for s in shapes])
+        del m
+        gc.collect()
+        assert plan() is not None, bind
+        assert any(t is plan() for t in run.tables), bind
+        del run
+        gc.collect()
+        assert plan() is None, bind
