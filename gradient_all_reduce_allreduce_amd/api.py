@@ -218,6 +218,11 @@ def current_stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _same_device(a, b, what):
+    if a[0].device != b[0].device:
+        raise ValueError(f"{what}: outputs must live on the inputs' device")
+
+
 def _rank_tensors(tensors, what):
     tensors = list(tensors)
     if not 1 <= len(tensors) <= MAX_RANKS:
@@ -247,6 +252,7 @@ def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None):
     out = _rank_tensors(out, "allreduce out")
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("allreduce: out must match the inputs")
+    _same_device(tensors, out, "allreduce")
     allreduce_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
                             torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
                             torch_dtype_code(out[0].dtype), tensors[0].numel(),
@@ -266,6 +272,7 @@ def allreduce_tree(tensors, op="sum", branching=2, out=None, out_dtype=None):
     out = _rank_tensors(out, "allreduce_tree out")
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("allreduce_tree: out must match the inputs")
+    _same_device(tensors, out, "allreduce_tree")
     allreduce_tree_emulated(op, P, branching, [t.data_ptr() for t in tensors],
                             torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
                             torch_dtype_code(out[0].dtype), tensors[0].numel(),
@@ -291,6 +298,7 @@ def allreduce_hierarchical(tensors, nodes, op="sum", local=("ring", None), globa
     out = _rank_tensors(out, "allreduce_hierarchical out")
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("allreduce_hierarchical: out must match the inputs")
+    _same_device(tensors, out, "allreduce_hierarchical")
     allreduce_hierarchical_emulated(op, nodes, P // nodes, local[0], local[1], global_[0], global_[1],
                                     [t.data_ptr() for t in tensors],
                                     torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
@@ -312,6 +320,7 @@ def reduce_scatter(tensors, op="sum", chunking=None, out=None, out_dtype=None):
     out = _rank_tensors(out, "reduce_scatter out")
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("reduce_scatter: out must match the inputs")
+    _same_device(tensors, out, "reduce_scatter")
     reducescatter_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
                                 torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
                                 torch_dtype_code(out[0].dtype), tensors[0].numel(),
@@ -380,8 +389,9 @@ class MultiAllReduce:
     def bind(self, rank_lists, out=None):
         """Validate the tensors once and upload their pointer tables; returns
         a launcher ``run(op="sum", chunking=None)`` that enqueues the whole
-        multi-tensor all-reduce with one call.  The tensors (and ``out``,
-        default: new tensors) must stay alive while the launcher is used."""
+        multi-tensor all-reduce with one call on the stream current at that
+        call.  The tensors (and ``out``, default: new tensors) must stay
+        alive while the launcher is used."""
         import torch
         if out is None:
             out = [[torch.empty(s, dtype=self.out_dtype, device=self.device) for s in self.shapes]
@@ -391,12 +401,12 @@ class MultiAllReduce:
         args = (self.P, len(self.shapes), self.tiles_dev.data_ptr(), self.total_tiles,
                 self.tile_elems, tin.data_ptr(), torch_dtype_code(self.dtype), tout.data_ptr(),
                 torch_dtype_code(self.out_dtype))
-        stream = current_stream(self.device)
+        device = self.device
 
         def run(op="sum", chunking=None):
             P, T, tiles, total, tile, pin, dtin, pout, dtout = args
             allreduce_multi_ring_emulated(op, P, chunking or P, T, tiles, total, tile, pin, dtin,
-                                          pout, dtout, stream)
+                                          pout, dtout, current_stream(device))
             return out
 
         # The launcher holds raw device addresses: it must own every table
@@ -426,7 +436,6 @@ class MultiAllReduce:
         tout = self._table(out, self.out_dtype) if out is not None else None
         tw = self._state_table(w)
         tv = self._state_table(v)
-        stream = current_stream(self.device)
         T = len(self.shapes)
 
         def run(lr, mu, op="mean", chunking=None):
@@ -434,7 +443,7 @@ class MultiAllReduce:
                                       self.total_tiles, self.tile_elems, tin.data_ptr(),
                                       torch_dtype_code(self.dtype), tw.data_ptr(), tv.data_ptr(), lr, mu,
                                       tout.data_ptr() if tout is not None else None,
-                                      torch_dtype_code(self.out_dtype), stream)
+                                      torch_dtype_code(self.out_dtype), current_stream(self.device))
             return out
 
         run.tables = (self.tiles_dev, tin, tout, tw, tv)   # owned by the launcher, as in bind()
@@ -463,6 +472,7 @@ def zero1_sgd_step(grads, w, v, lr, mu, params, op="mean", chunking=None):
                              "gradient's size on its device")
     if len(params) != len(grads) or params[0].numel() != grads[0].numel():
         raise ValueError("zero1_sgd_step: one parameter tensor per rank, of the gradient's size")
+    _same_device(grads, params, "zero1_sgd_step")
     zero1_sgd_step_emulated(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
                             torch_dtype_code(grads[0].dtype), grads[0].numel(), w.data_ptr(),
                             v.data_ptr(), lr, mu, [p.data_ptr() for p in params],
@@ -484,6 +494,9 @@ def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):
     out_ptrs, out_code = None, F32
     if out is not None:
         out = _rank_tensors(out, "allreduce_sgd out")
+        if len(out) != len(grads) or out[0].numel() != grads[0].numel():
+            raise ValueError("allreduce_sgd: out must match the gradients")
+        _same_device(grads, out, "allreduce_sgd")
         out_ptrs = [t.data_ptr() for t in out]
         out_code = torch_dtype_code(out[0].dtype)
     allreduce_fused_sgd(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],

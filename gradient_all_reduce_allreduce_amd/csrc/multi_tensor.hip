@@ -51,10 +51,10 @@ __device__ __forceinline__ KMulti multi_args() {
 }
 
 template <int P, bool INB, bool OUTB, bool SGD>
-__device__ __forceinline__ void multi_element(KMulti a, int t, uint32_t i, int64_t L) {
+__device__ __forceinline__ void multi_element(KMulti a, int t, uint32_t i, uint32_t L) {
 #pragma clang fp contract(off)
     const int T = a->T;
-    const int s = static_cast<int>((static_cast<int64_t>(i) / L) % P);
+    const int s = static_cast<int>((i / L) % P);
     float g;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -115,10 +115,12 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     const uint32_t t0 = static_cast<uint32_t>((b - a->tiles[t].first_tile) * TILE);
     if (static_cast<int64_t>(t0) >= numel) return;
     const uint32_t n = static_cast<uint32_t>(numel);
-    const int64_t L = (numel + a->chunking - 1) / a->chunking;
+    // Tensors hold at most 2^29 elements (ddp_multi_plan), so the chunk
+    // arithmetic fits 32 bits (a 64-bit division is a long sequence).
+    const uint32_t L = static_cast<uint32_t>((numel + a->chunking - 1) / a->chunking);
     const uint32_t end = t0 + TILE < n ? t0 + TILE : n;
-    const int64_t j0 = t0 / L;
-    const int64_t j1 = (end - 1) / L;
+    const uint32_t j0 = t0 / L;
+    const uint32_t j1 = (end - 1) / L;
     const uint32_t tid = threadIdx.x;
 
     const bool write_out = !SGD || a->out != nullptr;
