@@ -73,6 +73,17 @@ int check_overlaps(const std::vector<Buf>& bufs) {
     return DDP_OK;
 }
 
+// Longest buffer a call accepts, in elements: 2^40 (4 TiB of float32, far
+// beyond any device), so that byte extents and pointer ends cannot wrap.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int check_length(int64_t n, const char* what) {
+    if (n < 0) return fail(DDP_E_ARG, "%s = %lld is negative", what, static_cast<long long>(n));
+    if (n > kMaxElems)
+        return fail(DDP_E_ARG, "%s = %lld is over 2^40 elements", what, static_cast<long long>(n));
+    return DDP_OK;
+}
+
 int check_ranks(int32_t P) {
     if (P < 1 || P > DDP_MAX_RANKS) return fail(DDP_E_ARG, "P = %d outside 1..%d", P, DDP_MAX_RANKS);
     return DDP_OK;
@@ -99,7 +110,7 @@ int validate_reduce(int op, int32_t P, int32_t chunking, const void* const* in, 
     int s = check_ranks(P);
     if (s) return s;
     if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
-    if (n < 0) return fail(DDP_E_ARG, "n = %lld is negative", static_cast<long long>(n));
+    if (int e = check_length(n, "n")) return e;
     if (!valid_dtype(in_dtype)) return fail(DDP_E_ARG, "unknown input dtype %d", in_dtype);
     if (!valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown output dtype %d", out_dtype);
     if ((s = check_ptr_array(in, P, "rank_in"))) return s;
@@ -218,7 +229,7 @@ static int bucket_copy(bool pack, int32_t P, ddp_dtype dtype, const ddp_segment*
     int s = check_ranks(P);
     if (s) return s;
     if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
-    if (bucket_len < 0) return fail(DDP_E_ARG, "bucket_len is negative");
+    if (int e = check_length(bucket_len, "bucket_len")) return e;
     if (n_segs < 0) return fail(DDP_E_ARG, "n_segs is negative");
     if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
     if (bucket_len > 0 && n_segs == 0) return fail(DDP_E_PLAN, "a non-empty bucket needs segments");
@@ -409,7 +420,7 @@ int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf, 
     int s = check_ranks(P);
     if (s) return s;
     if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
-    if (n < 0) return fail(DDP_E_ARG, "n = %lld is negative", static_cast<long long>(n));
+    if (int e = check_length(n, "n")) return e;
     if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if ((s = check_ptr_array(const_cast<const void* const*>(rank_buf), P, "rank_buf"))) return s;
     std::vector<Buf> bufs;
@@ -442,7 +453,7 @@ int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void*
     int s = check_ranks(P);
     if (s) return s;
     if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
-    if (n < 0) return fail(DDP_E_ARG, "n = %lld is negative", static_cast<long long>(n));
+    if (int e = check_length(n, "n")) return e;
     if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if (dtype != DDP_F32)
         return fail(DDP_E_UNSUPPORTED, "the stepwise ring keeps partial sums in the rank buffers, "

@@ -41,6 +41,8 @@
  *     returns a ddp_status; on any error nothing has been enqueued.  The
  *     library never aborts and never prints; ddp_last_error() gives a message
  *     for the calling thread's most recent failure.
+ *   - Element counts (n, bucket_len) are 0..2^40; larger ones are rejected
+ *     with DDP_E_ARG.
  *   - Device buffers must be 16-byte aligned.  Two buffers of one call may
  *     either be disjoint or start at the same address with the same element
  *     size (exact aliasing, e.g. an in-place all-reduce); any other overlap

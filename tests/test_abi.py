@@ -124,6 +124,8 @@ def ar(op=0, P=2, C=2, ins=None, it=0, outs=None, ot=0, n=16):
 
 
 def test_allreduce_argument_errors():
+    assert ar(n=(1 << 40) + 1) == N.DDP_E_ARG and "2^40" in N.last_error()
+    assert ar(n=-1) == N.DDP_E_ARG and "negative" in N.last_error()
     assert ar(op=2) == N.DDP_E_ARG
     assert ar(P=0) == N.DDP_E_ARG
     assert ar(P=17, ins=[A + r * MB for r in range(17)],
