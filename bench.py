@@ -205,7 +205,17 @@ def run_suite(steps, warmup):
     report("cfg2 resnet50 p8 f32, unpack alone (4 buckets -> 161 tensors, all ranks)",
            _time(lambda i: [plan.unpack(table, k, bufs) for k in range(plan.n_buckets)], steps, warmup),
            copy_bytes)
-    del tensors, outs, run, table, bufs
+    # The lines above reuse one set of P bucket buffers (200 MiB) for every
+    # bucket, as a DDP step does, so the last-level cache can hold part of
+    # them; with a buffer set per bucket (800 MiB) every byte goes to HBM.
+    per_bucket = [plan.alloc_buckets(P) for _ in range(plan.n_buckets)]
+    report("cfg2 resnet50 p8 f32, pack alone, a bucket buffer set per bucket",
+           _time(lambda i: [plan.pack(table, k, per_bucket[k]) for k in range(plan.n_buckets)], steps, warmup),
+           copy_bytes)
+    report("cfg2 resnet50 p8 f32, unpack alone, a bucket buffer set per bucket",
+           _time(lambda i: [plan.unpack(table, k, per_bucket[k]) for k in range(plan.n_buckets)], steps, warmup),
+           copy_bytes)
+    del tensors, outs, run, table, bufs, per_bucket
     torch.cuda.empty_cache()
 
     # config 3: ViT-B/16 bf16 gradients, Mean, fused SGD-momentum

@@ -38,7 +38,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
-constexpr int kVecPerLane = 4;   // 16-byte vectors per lane and tile
+constexpr int kVecPerLane = 2;   // 16-byte vectors per lane and tile
 
 struct CopyArgs {
     const ddp_segment* segs;
