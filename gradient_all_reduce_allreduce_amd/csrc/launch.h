@@ -58,16 +58,15 @@ constexpr signed char kRingWg[4][17] = {
     {0, 6, 6, 16, 10, 10, 8, 6, 5, 5, 4, 4, 4, 3, 3, 3, 3},
     {0, 6, 6, 12, 10, 8, 6, 6, 5, 5, 4, 4, 4, 3, 3, 3, 3},
 };
-// The all-reduce fused with the optimizer step (two lane vectors per tile),
-// by gradient type and whether the reduced gradients (or updated
-// parameters) are written to the ranks: rows bf16 without, bf16 with, f32
-// without, f32 with.
+// The all-reduce fused with the optimizer step, by gradient type and
+// whether the reduced gradients (or updated parameters) are written to the
+// ranks: rows bf16 without, bf16 with, f32 without, f32 with.
 constexpr signed char kSgdWg[4][17] = {
     //   P: 1   2   3   4   5  6  7  8  9 10 11 12 13 14 15 16
-    {0, 6, 6, 10, 5, 6, 5, 5, 4, 4, 4, 5, 5, 4, 4, 4, 4},
-    {0, 5, 5, 8, 6, 6, 6, 5, 5, 5, 4, 4, 4, 4, 3, 3, 3},
-    {0, 8, 8, 10, 12, 10, 12, 10, 10, 10, 8, 8, 8, 8, 8, 8, 3},
-    {0, 3, 3, 6, 5, 4, 3, 3, 3, 3, 3, 2, 2, 2, 2, 2, 2},
+    {0, 6, 6, 12, 16, 10, 10, 8, 8, 8, 8, 6, 6, 6, 6, 6, 6},
+    {0, 4, 4, 10, 8, 8, 6, 6, 6, 6, 5, 4, 4, 4, 4, 4, 4},
+    {0, 8, 8, 12, 16, 10, 8, 10, 10, 8, 8, 6, 5, 5, 5, 5, 5},
+    {0, 3, 3, 6, 5, 5, 4, 4, 3, 3, 3, 3, 3, 3, 3, 2, 2},
 };
 constexpr int ring_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
     return kRingWg[(in_bf16 ? 2 : 0) + (out_bf16 ? 1 : 0)][P];
@@ -136,11 +135,11 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg);
 
 // Vectors of each rank a lane keeps in flight per tile: P * U loads.  One
 // vector per lane (a tile of 256 or 512 elements per wave) measured fastest
-// from P = 3 up; P <= 2 keeps more loads in flight with U = 4.  The fused
-// optimizer step, whose outputs are the two 16-byte state vectors instead
-// of P gradient copies, keeps two vectors per lane in flight.
-constexpr int ring_vectors_per_lane(int P, bool sgd) {
-    return P <= 2 ? 4 : (sgd ? 2 : 1);
+// from P = 3 up, with the fused optimizer step too once its occupancy cap
+// was tuned for it (3-5% over two vectors); P <= 2 keeps more loads in
+// flight with U = 4.
+constexpr int ring_vectors_per_lane(int P, bool /*sgd*/) {
+    return P <= 2 ? 4 : 1;
 }
 
 // Elements per lane vector: 8 for bf16 -> bf16 (16-byte loads and stores),
