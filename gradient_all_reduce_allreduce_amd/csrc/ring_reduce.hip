@@ -67,6 +67,8 @@ rr::ChunkMap chunk_map(int64_t base, int64_t L, int M) {
     }
     c.m = 0xffffffffu / c.d;
     c.first = static_cast<uint32_t>(first % M);
+    c.members = static_cast<uint32_t>(M);
+    c.members_m = 0xffffffffu / c.members;
     return c;
 }
 

@@ -70,6 +70,8 @@ struct ChunkMap {
     uint32_t m;          // floor((2^32 - 1) / d)
     uint32_t off;        // launch-local origin shift
     uint32_t first;      // first chunk of the launch, modulo the member count
+    uint32_t members;    // the level's member count M
+    uint32_t members_m;  // floor((2^32 - 1) / M)
 };
 
 struct RingArgs {
@@ -224,9 +226,17 @@ __device__ __forceinline__ int chunk_start(uint32_t t, const __attribute__((addr
     uint32_t r;
     return static_cast<int>((c.first + chunk_steps(t, c, r)) % static_cast<uint32_t>(M));
 }
-__device__ __forceinline__ int chunk_start(uint32_t t, const __attribute__((address_space(4))) ChunkMap& c, int M) {
+// x mod M for the level's run-time member count, by the same
+// multiply-high as chunk_steps (x < 2^31 + 16).
+__device__ __forceinline__ int mod_members(uint32_t x, const __attribute__((address_space(4))) ChunkMap& c) {
+    const uint32_t q = __umulhi(x, c.members_m);
+    uint32_t r = x - q * c.members;
+    if (r >= c.members) r -= c.members;
+    return static_cast<int>(r);
+}
+__device__ __forceinline__ int chunk_start_rt(uint32_t t, const __attribute__((address_space(4))) ChunkMap& c) {
     uint32_t r;
-    return static_cast<int>((c.first + chunk_steps(t, c, r)) % static_cast<uint32_t>(M));
+    return mod_members(c.first + chunk_steps(t, c, r), c);
 }
 
 // The start member of the chunk holding tile element t0, and the first
@@ -795,7 +805,7 @@ __device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
     const int G = a->groups;
     const int Lr = a->group_size;
     int rank[P];
-    level_ranks<P>(G, Lr, chunk_start(i, a->ring, Lr), chunk_start(i, a->global, G), rank);
+    level_ranks<P>(G, Lr, chunk_start_rt(i, a->ring), chunk_start_rt(i, a->global), rank);
     float part[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -852,8 +862,8 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
         return;
     }
     int rank[P];
-    level_ranks<P>(G, Lr, static_cast<int>((a->ring.first + ql) % static_cast<uint32_t>(Lr)),
-                   static_cast<int>((a->global.first + qg) % static_cast<uint32_t>(G)), rank);
+    level_ranks<P>(G, Lr, mod_members(a->ring.first + ql, a->ring), mod_members(a->global.first + qg, a->global),
+                   rank);
     u32x4 x[P][U];
     bool ok[U];
 #pragma unroll
@@ -869,8 +879,12 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
             for (int r = 0; r < P; ++r) x[r][u] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    // What the fold and the stores need, fetched while the loads are in flight.
-    const uint64_t parents = a->parents;
+    // What the fold and the stores need, fetched while the loads are in
+    // flight.  The parent table passes through an empty asm first, so that
+    // the fold's edge tests (P(P-1)/2 of them) are not hoisted in front of
+    // the loads.
+    uint64_t parents = a->parents;
+    asm volatile("" : "+s"(parents));
     const uint32_t n = a->n;
     const int32_t mean_flag = a->mean;
     char* dst[P];
