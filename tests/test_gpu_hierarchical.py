@@ -140,3 +140,32 @@ def test_more_than_one_launch():
         assert_same_bits(got, expect, f"split launch G={G}")
     del ins, outs
     torch.cuda.empty_cache()
+
+
+def test_two_level_across_launches():
+    """Buffers over 2^29 elements go out in several launches; both levels'
+    ring orders must carry across the splits (each launch's chunk maps).
+    Sampled elements around every chunk boundary of both levels and every
+    split, against the oracle evaluated per element."""
+    from sampled_oracle import hierarchical_sampled
+    P, G, n = 8, 2, (1 << 29) + 4099
+    local, glob = ("ring", 3), ("ring", 5)
+    bufs = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    for r, t in enumerate(bufs):
+        workloads.torch_normal_(t, 1.0, seed=600 + r)
+    outs = [torch.empty_like(t) for t in bufs]
+    ddp.allreduce_hierarchical(bufs, G, "mean", local, glob, out=outs)
+    torch.cuda.synchronize()
+    parts = [np.arange(0, 64), np.arange(n - 64, n), np.arange((1 << 29) - 40, (1 << 29) + 40),
+             np.random.default_rng(3).integers(0, n, 600)]
+    for chunks in (3, 5):
+        L = -(-n // chunks)
+        parts += [np.arange(max(0, j * L - 20), min(n, j * L + 20)) for j in range(1, chunks)]
+    idx = np.unique(np.concatenate(parts))
+    it = torch.from_numpy(idx).to(DEV)
+    V = np.stack([t[it].cpu().numpy() for t in bufs])
+    want_ = hierarchical_sampled(V, idx, n, "mean", G, local, glob)
+    got = np.stack([t[it].cpu().numpy() for t in outs])
+    assert_same_bits(got, want_, "two-level across launches")
+    del bufs, outs
+    torch.cuda.empty_cache()

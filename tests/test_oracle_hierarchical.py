@@ -201,3 +201,20 @@ def test_bf16_inputs_equal_the_widened_f32_path():
 def test_rejects_a_node_count_that_does_not_divide_the_ranks():
     with pytest.raises(ValueError):
         oracle.hierarchical_allreduce(np.zeros((6, 3), np.float32), "sum", nodes=4)
+
+
+def test_sampled_two_level_oracle_matches_the_whole_buffer():
+    """The sampled form used by the full-size GPU test gives, for every
+    element, the bits of the whole-buffer oracle."""
+    from sampled_oracle import hierarchical_sampled
+    rng = np.random.default_rng(7)
+    for P, G in ((8, 2), (8, 4), (6, 3), (12, 4)):
+        for local, glob in ((("ring", None), ("ring", None)), (("ring", 3), ("ring", 5)),
+                            (("tree", 2), ("ring", None)), (("ring", None), ("centralized", None))):
+            n = 257
+            X = (rng.standard_normal((P, n)) * np.exp2(rng.integers(-20, 21, (P, n)))).astype(np.float32)
+            for op in ("sum", "mean"):
+                whole = oracle.hierarchical_allreduce(X, op, nodes=G, local=local, global_=glob)
+                idx = np.arange(n)
+                got = hierarchical_sampled(X, idx, n, op, G, local, glob)
+                assert np.array_equal(got.view(np.uint32), whole.view(np.uint32)), (P, G, local, glob, op)
