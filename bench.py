@@ -478,6 +478,14 @@ def main():
     pair_ms = sum(map(sum, durs)) / (args.steps * len(lens))
     full = [d for row in durs for k, d in enumerate(row) if lens[k] == E]
     full_gbs = P * E * 8 / (sum(full) / len(full) * 1e-3) / 1e9 if full else None
+    per_bucket = []
+    for k, n in enumerate(lens):
+        col = sorted(row[k] for row in durs)
+        med = float(np.median(col))
+        per_bucket.append({"elements": n, "median_us": round(med * 1e3, 2),
+                           "min_us": round(col[0] * 1e3, 2),
+                           "median_gbs": round(P * n * 8 / (med * 1e-3) / 1e9, 1)})
+    per_set = sorted(map(sum, durs))
     traffic = measured_traffic()
 
     out = {
@@ -516,6 +524,12 @@ def main():
             "timing": "events around the timed steps, which hold only this kernel's launches",
             "event_pair_avg_launch_us": round(pair_ms * 1e3, 2),
             "event_pair_full_bucket_gbs": round(full_gbs, 1) if full_gbs else None,
+        },
+        "event_pairs": {
+            "per_bucket": per_bucket,
+            "per_set_median_ms": round(float(np.median(per_set)), 4),
+            "per_set_min_ms": round(per_set[0], 4),
+            "note": "an event pair around every launch (region 2); the pairs add about 2 us each",
         },
         "cpu_baseline": None,
     }

@@ -218,6 +218,19 @@ def current_stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _stream_for(tables):
+    """Handle of the stream current on the tables' device.  The tables were
+    allocated on the stream current at bind time; a launch on another stream
+    is recorded on them, so that torch's allocator does not hand their memory
+    out again before that launch has read it."""
+    import torch
+    s = torch.cuda.current_stream(tables[0].device)
+    for t in tables:
+        if t.device.type == "cuda":
+            t.record_stream(s)
+    return s.cuda_stream
+
+
 def _same_device(a, b, what):
     if a[0].device != b[0].device:
         raise ValueError(f"{what}: outputs must live on the inputs' device")
@@ -345,8 +358,9 @@ def allreduce_stepwise(tensors, op="sum", chunking=None, sent=None):
     import torch
     tensors = _rank_tensors(tensors, "allreduce_stepwise")
     if sent is not None and (sent.dtype != torch.int64 or sent.numel() != len(tensors)
-                             or not sent.is_cuda or not sent.is_contiguous()):
-        raise ValueError("allreduce_stepwise: sent must be a contiguous int64 GPU tensor of P")
+                             or sent.device != tensors[0].device or not sent.is_contiguous()):
+        raise ValueError("allreduce_stepwise: sent must be a contiguous int64 tensor of P on the "
+                         "tensors' device")
     allreduce_ring_stepwise(op, len(tensors), chunking or len(tensors),
                             [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
                             tensors[0].numel(), sent.data_ptr() if sent is not None else None,
@@ -401,18 +415,18 @@ class MultiAllReduce:
         args = (self.P, len(self.shapes), self.tiles_dev.data_ptr(), self.total_tiles,
                 self.tile_elems, tin.data_ptr(), torch_dtype_code(self.dtype), tout.data_ptr(),
                 torch_dtype_code(self.out_dtype))
-        device = self.device
+        tables = (self.tiles_dev, tin, tout)
 
         def run(op="sum", chunking=None):
             P, T, tiles, total, tile, pin, dtin, pout, dtout = args
             allreduce_multi_ring_emulated(op, P, chunking or P, T, tiles, total, tile, pin, dtin,
-                                          pout, dtout, current_stream(device))
+                                          pout, dtout, _stream_for(tables))
             return out
 
         # The launcher holds raw device addresses: it must own every table
         # they point into, the tile plan included, so that it stays valid
         # after this object is dropped (``MultiAllReduce(...).bind(...)``).
-        run.tables = (self.tiles_dev, tin, tout)
+        run.tables = tables
         run.out = out
         return run
 
@@ -438,15 +452,17 @@ class MultiAllReduce:
         tv = self._state_table(v)
         T = len(self.shapes)
 
+        tables = tuple(t for t in (self.tiles_dev, tin, tout, tw, tv) if t is not None)
+
         def run(lr, mu, op="mean", chunking=None):
             allreduce_multi_fused_sgd(op, self.P, chunking or self.P, T, self.tiles_dev.data_ptr(),
                                       self.total_tiles, self.tile_elems, tin.data_ptr(),
                                       torch_dtype_code(self.dtype), tw.data_ptr(), tv.data_ptr(), lr, mu,
                                       tout.data_ptr() if tout is not None else None,
-                                      torch_dtype_code(self.out_dtype), current_stream(self.device))
+                                      torch_dtype_code(self.out_dtype), _stream_for(tables))
             return out
 
-        run.tables = (self.tiles_dev, tin, tout, tw, tv)   # owned by the launcher, as in bind()
+        run.tables = tables   # owned by the launcher, as in bind()
         return run
 
     def __call__(self, rank_lists, op="sum", chunking=None, out=None):

@@ -104,9 +104,28 @@ class GradBucketer:
         first, count = self.segment_range(b)
         return self.segs_dev.data_ptr() + first * api.SEGMENT_DTYPE.itemsize, count
 
+    def _check_copy(self, table, b, rank_buckets):
+        """The kernels read P * T table entries and bucket_len(b) elements of
+        every bucket buffer: both are checked here, since the library cannot
+        read device tables on the host."""
+        import torch
+        if not 0 <= b < self.n_buckets:
+            raise ValueError(f"bucket {b} outside 0..{self.n_buckets - 1}")
+        P = len(rank_buckets)
+        if table.dtype != torch.int64 or table.numel() != P * len(self.shapes) \
+                or table.device != self.device or not table.is_contiguous():
+            raise ValueError("pointer table must be the int64 device table of P ranks' tensors "
+                             "(pointer_table)")
+        for r, x in enumerate(rank_buckets):
+            if x.dtype != self.dtype or x.device != self.device or not x.is_contiguous() \
+                    or x.numel() < self.bucket_len(b):
+                raise ValueError(f"rank {r}: bucket buffer must be a contiguous {self.dtype} tensor "
+                                 f"of at least {self.bucket_len(b)} elements on {self.device}")
+
     def pack(self, table, b, rank_buckets):
         """Gather bucket b of every rank (pointer table from ``pointer_table``)
         into ``rank_buckets`` on the current stream."""
+        self._check_copy(table, b, rank_buckets)
         ptr, count = self._seg_ptr(b)
         api.ddp_bucket_pack(len(rank_buckets), self.code, ptr, count, table.data_ptr(),
                             len(self.shapes), [x.data_ptr() for x in rank_buckets],
@@ -114,6 +133,7 @@ class GradBucketer:
 
     def unpack(self, table, b, rank_buckets):
         """Scatter bucket b of every rank back into its tensors."""
+        self._check_copy(table, b, rank_buckets)
         ptr, count = self._seg_ptr(b)
         api.ddp_bucket_unpack(len(rank_buckets), self.code, ptr, count, table.data_ptr(),
                               len(self.shapes), [x.data_ptr() for x in rank_buckets],

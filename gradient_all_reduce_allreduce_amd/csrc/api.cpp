@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -321,7 +322,7 @@ int fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* 
     if (master_w == nullptr || momentum == nullptr) return fail(DDP_E_ARG, "master_w or momentum is NULL");
     if ((reinterpret_cast<uintptr_t>(master_w) | reinterpret_cast<uintptr_t>(momentum)) & 15u)
         return fail(DDP_E_ALIGN, "master_w or momentum is not 16-byte aligned");
-    if (!(lr == lr) || !(mu == mu) || lr > 3.4e38f || lr < -3.4e38f || mu > 3.4e38f || mu < -3.4e38f)
+    if (!std::isfinite(lr) || !std::isfinite(mu))
         return fail(DDP_E_ARG, "lr and mu must be finite");
     std::vector<Buf> bufs;
     add_rank_bufs(bufs, rank_grad, P, n, elem_bytes(grad_dtype), "rank_grad");
@@ -654,7 +655,7 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, int
                            out_dtype);
     if (s) return s;
     if (w_ptrs_dev == nullptr || v_ptrs_dev == nullptr) return fail(DDP_E_ARG, "NULL weight or momentum table");
-    if (!(lr == lr) || !(mu == mu) || lr > 3.4e38f || lr < -3.4e38f || mu > 3.4e38f || mu < -3.4e38f)
+    if (!std::isfinite(lr) || !std::isfinite(mu))
         return fail(DDP_E_ARG, "lr and mu must be finite");
     if (total_tiles == 0) return ok();
 

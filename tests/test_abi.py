@@ -176,6 +176,8 @@ def test_fused_sgd_errors():
     assert sgd(w=A + 200 * MB + 4) == N.DDP_E_ALIGN
     assert sgd(lr=float("nan")) == N.DDP_E_ARG
     assert sgd(mu=float("inf")) == N.DDP_E_ARG
+    assert sgd(lr=float("-inf")) == N.DDP_E_ARG
+    assert sgd(lr=3.4028234e38, mu=-3.4028234e38, n=0) == N.DDP_OK   # the largest finite floats
     assert sgd(v=A + 200 * MB + 16, n=1024) == N.DDP_E_OVERLAP       # w and v overlap
     assert sgd(w=A, n=1024) == N.DDP_E_OVERLAP                       # w aliases a gradient
     assert sgd(outs=[A + 500 * MB, A + 500 * MB + 32], n=1024) == N.DDP_E_OVERLAP
@@ -268,6 +270,42 @@ def test_bucket_views_match_pack_layout():
         want = oracle.pack(host, 4, 256)
         for k in range(b.n_buckets):
             assert np.array_equal(b.bucket_view(arena[r], k).numpy(), want[k])
+
+
+def test_bucketer_rejects_tables_and_buffers_that_do_not_fit(monkeypatch):
+    """pack/unpack check what the kernels would read (P * T table entries,
+    bucket_len elements per bucket buffer) before calling the library; the
+    library itself is replaced by a recorder, so nothing is launched."""
+    import torch
+
+    from gradient_all_reduce_allreduce_amd import api
+    calls = []
+    monkeypatch.setattr(api, "ddp_bucket_pack", lambda *a: calls.append(a))
+    monkeypatch.setattr(api, "ddp_bucket_unpack", lambda *a: calls.append(a))
+    monkeypatch.setattr(api, "current_stream", lambda device: None)
+    shapes = [(3, 5), (7,), (1000,)]
+    b = ddp.GradBucketer(shapes, torch.float32, 256, device="cpu")
+    ts = [[torch.zeros(s) for s in shapes] for _ in range(2)]
+    table = b.pointer_table(ts)
+    bufs = b.alloc_buckets(2)
+    for copy in (b.pack, b.unpack):
+        with pytest.raises(ValueError):
+            copy(table[:-1], 0, bufs)                                   # P * T - 1 entries
+        with pytest.raises(ValueError):
+            copy(table, 0, bufs + [torch.zeros(b.bucket_elems)])        # table of 2 ranks, 3 buffers
+        with pytest.raises(ValueError):
+            copy(table, 0, [bufs[0], bufs[1][:b.bucket_len(0) - 1]])    # short bucket buffer
+        with pytest.raises(ValueError):
+            copy(table, 0, [bufs[0], bufs[1].double()])                 # wrong dtype
+        with pytest.raises(ValueError):
+            copy(table, b.n_buckets, bufs)                              # no such bucket
+        with pytest.raises(ValueError):
+            copy(table.int(), 0, bufs)
+        assert not calls
+        last = b.n_buckets - 1
+        copy(table, last, [x[:b.bucket_len(last)] for x in bufs])      # the tail fits exactly
+        assert len(calls) == 1
+        calls.clear()
 
 
 def test_reduce_scatter_and_all_gather_errors():

@@ -69,6 +69,29 @@ def test_multi_equals_oracle_per_tensor(pair, P, misalign):
                 assert_same_bits(got, want, f"{it}->{ot} P={P} t={t} C={C} {op}")
 
 
+def test_launcher_run_on_another_stream():
+    """A launcher bound on one stream and run on another, then dropped while
+    the launch may still be in flight: its tables are recorded on the stream
+    that reads them, so new allocations cannot take their memory early."""
+    P, C = 4, 4
+    shapes = [(7,), (4097,), (70001,)]
+    host, dev = make(P, shapes, torch.float32, seed=17)
+    run = ddp.MultiAllReduce(shapes, P, torch.float32, device=DEV).bind(dev)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        out = run("sum", C)
+    del run
+    junk = [torch.full((1 << 16,), 7.0, device=DEV) for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    for t in range(len(shapes)):
+        want = oracle_ring(np.stack([host[r][t] for r in range(P)]), "sum", C)
+        got = np.stack([bits_of(out[r][t]) for r in range(P)])
+        assert_same_bits(got, want, f"t={t}")
+    del junk
+
+
 def test_multi_in_place_equals_single_calls():
     P = 8
     shapes = workloads.resnet50_shapes()
