@@ -43,10 +43,14 @@
  *     for the calling thread's most recent failure.
  *   - Element counts (n, bucket_len) are 0..2^40; larger ones are rejected
  *     with DDP_E_ARG.
- *   - Device buffers must be 16-byte aligned.  Two buffers of one call may
- *     either be disjoint or start at the same address with the same element
- *     size (exact aliasing, e.g. an in-place all-reduce); any other overlap
- *     is rejected.
+ *   - Device buffers named in host arrays (rank buffers, bucket buffers,
+ *     master weights, momentum) must be 16-byte aligned.  Tensors reached
+ *     through device tables (pack/unpack, the multi-tensor calls) need only
+ *     their element type's alignment; the library cannot read those tables
+ *     on the host, so their contents are the caller's responsibility.
+ *   - Two buffers of one call named in host arrays may either be disjoint or
+ *     start at the same address with the same element size (exact aliasing,
+ *     e.g. an in-place all-reduce); any other overlap is rejected.
  */
 #ifndef DDP_ALLREDUCE_H
 #define DDP_ALLREDUCE_H
@@ -188,9 +192,9 @@ int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
  *             match (in-place all-reduce)
  *   out_dtype DDP_F32 or DDP_BF16
  *   n         elements per rank, >= 0 (0: nothing is launched)
- * One launch per 2^29 elements; for bf16 inputs with float32 outputs the
- * call runs as a reduce-scatter pass followed by an all-gather pass (see
- * below), which is faster for that shape and gives the same bits.
+ * One launch per 2^29 elements, for every pair of element types: each
+ * element is read from the P inputs, folded and written to the P outputs
+ * in one pass.
  * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
  */
 int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
