@@ -130,6 +130,32 @@ def test_sgd_exact_closed_form():
         assert Fraction(float(wk[i])) == ws
 
 
+def test_sgd_rounds_every_operation_once():
+    """No multiply-add contraction (each product is rounded before the add):
+    two hand-worked cases where a fused multiply-add would give another
+    value.
+
+    Momentum: mu = float32(0.9) = 15099494 * 2^-24 and v = 3.  The exact
+    product 45298482 * 2^-24 = 11324620.5 * 2^-22 (a float32 in [2, 4) is a
+    multiple of 2^-22) lies halfway between two floats; ties-to-even gives
+    11324620 * 2^-22.  With g = -11324620 * 2^-22 the new momentum is 0
+    exactly (fused: 2^-23), and the weight is unchanged.
+
+    Weights: lr = float32(0.1) = 13421773 * 2^-27, v_new = 3 (from v = 0,
+    g = 3).  The exact product 40265319 * 2^-27 = 10066329.75 * 2^-25 (a
+    float32 in [1/4, 1/2) is a multiple of 2^-25) rounds to 10066330 * 2^-25.
+    With w = 10066330 * 2^-25 the new weight is 0 exactly (fused: 2^-27)."""
+    mu32, lr32 = np.float32(0.9), np.float32(0.1)
+    assert int(mu32.view(np.uint32)) == 0x3F000000 | (15099494 - (1 << 23))
+    assert int(lr32.view(np.uint32)) == (123 << 23) | (13421773 - (1 << 23))
+    g = np.array([-11324620 * 2.0 ** -22, 3.0], np.float32)
+    w = np.array([0.5, 10066330 * 2.0 ** -25], np.float32)
+    v = np.array([3.0, 0.0], np.float32)
+    w1, v1 = oracle.sgd_momentum(g, w, v, 0.1, 0.9)
+    assert v1[0] == 0.0 and w1[0] == 0.5
+    assert v1[1] == 3.0 and w1[1] == 0.0
+
+
 def test_sgd_constant_gradient_geometric_series():
     g = np.full(10, 0.25, np.float32)
     w = np.zeros(10, np.float32)
