@@ -149,6 +149,45 @@ def run_suite(steps, warmup):
                          for k in range(plan.n_buckets)])
         return sets
 
+    # config 1: 4 ranks x 65,536 fp32, Sum, 4 chunks, out of place.  2 MB
+    # per call sits in the last-level cache, so the call is bound by launch
+    # and host overhead: a parity case, not a bandwidth one.
+    x1 = [torch.empty(65536, device=dev).normal_() for _ in range(4)]
+    o1 = [torch.empty_like(t) for t in x1]
+    ms1 = _time(lambda i: ddp.allreduce(x1, "sum", 4, out=o1), steps, warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ddp.allreduce(x1, "sum", 4, out=o1)
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    torch.cuda.synchronize()
+    report("cfg1 p4 f32 sum n=65,536 (2 MB per call, cache resident: launch-bound)", ms1, 4 * 65536 * 8,
+           host_us_per_call=round(host_us, 2),
+           note="time per call on the stream; host_us_per_call is the Python call alone")
+    # The same call through the C ABI with its arguments prepared once (what
+    # a C caller or a bound launcher pays per call).
+    from gradient_all_reduce_allreduce_amd import _native
+    lib = _native.lib()
+    pin = _native.pointer_array([t.data_ptr() for t in x1])
+    pout = _native.pointer_array([t.data_ptr() for t in o1])
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def c_call(i):
+        if lib.allreduce_ring_emulated(_native.DDP_SUM, 4, 4, pin, _native.DDP_F32, pout,
+                                       _native.DDP_F32, 65536, sh) != 0:
+            raise RuntimeError(_native.last_error())
+    ms1c = _time(c_call, steps, warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        c_call(i)
+    host_c_us = (time.perf_counter() - t0) / steps * 1e6
+    torch.cuda.synchronize()
+    report("cfg1 p4 f32 sum n=65,536, C ABI call with prepared arguments", ms1c, 4 * 65536 * 8,
+           host_us_per_call=round(host_c_us, 2),
+           note="time per call on the stream; host_us_per_call is the ctypes call alone")
+    del x1, o1
+
     # config 2, bucket views (the headline step), the multi-tensor launch
     # over the 161 separate per-parameter tensors, and pack/unpack
     P = 8

@@ -302,3 +302,47 @@ def test_fused_sgd_sum_and_zero_momentum():
     assert_same_bits(w.cpu().numpy(), ow, "w")
     assert_same_bits(v.cpu().numpy(), ov, "v")
     assert np.array_equal(v.cpu().numpy(), g)
+
+
+def test_fused_steps_round_every_operation_once():
+    """The two hand-worked cases where a fused multiply-add would differ
+    (mu * v a tie that rounds to even and is then cancelled by g; lr * v
+    rounded up and then cancelled by w), repeated over several tiles and a
+    ragged tail, through every fused optimizer entry point: P = 2 ranks,
+    Sum, rank 1 all zeros, so the reduced gradient is rank 0's exactly."""
+    n = 3 * 4096 + 5
+    case = np.arange(n) % 2
+    g = np.where(case == 0, -11324620 * 2.0 ** -22, 3.0).astype(np.float32)
+    w0 = np.where(case == 0, 0.5, 10066330 * 2.0 ** -25).astype(np.float32)
+    v0 = np.where(case == 0, 3.0, 0.0).astype(np.float32)
+    want_w = np.where(case == 0, 0.5, 0.0).astype(np.float32)
+    want_v = np.where(case == 0, 0.0, 3.0).astype(np.float32)
+    X = np.stack([g, np.zeros(n, np.float32)])
+    ow, ov = oracle.sgd_momentum(g, w0, v0, 0.1, 0.9)
+    assert np.array_equal(ow, want_w) and np.array_equal(ov, want_v)
+
+    w = torch.from_numpy(w0.copy()).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    ddp.allreduce_sgd(to_device(X, "f32"), w, v, 0.1, 0.9, "sum", 2)
+    torch.cuda.synchronize()
+    assert_same_bits(w.cpu().numpy(), want_w, "allreduce_sgd w")
+    assert_same_bits(v.cpu().numpy(), want_v, "allreduce_sgd v")
+
+    w = torch.from_numpy(w0.copy()).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    params = [torch.empty(n, device=DEV) for _ in range(2)]
+    ddp.zero1_sgd_step(to_device(X, "f32"), w, v, 0.1, 0.9, params, "sum", 2)
+    torch.cuda.synchronize()
+    assert_same_bits(w.cpu().numpy(), want_w, "zero1 w")
+    assert_same_bits(v.cpu().numpy(), want_v, "zero1 v")
+    assert_same_bits(to_host(params), np.stack([want_w, want_w]), "zero1 params")
+
+    m = ddp.MultiAllReduce([(n,)], 2, torch.float32, device=DEV)
+    grads = [[t] for t in to_device(X, "f32")]
+    w = torch.from_numpy(w0.copy()).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    run = m.bind_sgd(grads, [w], [v])
+    run(0.1, 0.9, "sum", 2)
+    torch.cuda.synchronize()
+    assert_same_bits(w.cpu().numpy(), want_w, "multi w")
+    assert_same_bits(v.cpu().numpy(), want_v, "multi v")
