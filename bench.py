@@ -7,7 +7,10 @@ emulated ranks, each holding a ResNet-50-shaped gradient set of 161 fp32
 tensors (25,557,032 parameters) drawn from N(0, 0.01), laid out as views of
 25 MiB buckets filled in reverse parameter order (3 full buckets and a
 partial tail).  One step all-reduces every bucket with Mean in the chunked
-ring order (8 chunks), every rank receiving its own copy of the result.
+ring order (8 chunks), every rank receiving its own copy of the result, in
+one bucketed call (each bucket its own ring; the 3 full buckets go out as
+one launch, the tail as another).  The same buckets with one call each are
+timed beside it.
 
 Metric: effective HBM GB/s = algorithmic bytes / time, where the algorithmic
 bytes of one all-reduce of n elements over P ranks are P*n*(s_in + s_out)
@@ -17,9 +20,10 @@ more than the 256 MB last-level cache, and two buffer sets alternate.
 
 Prints one JSON line with the step throughput, the dominant kernel's
 roofline (its launches timed with HIP events on the stream they run on: the
-timed steps consist of nothing but its launches; an event pair around every
-launch is reported beside it as a cross-check) and the CPU oracle timed on a
-bounded sample of the same workload.
+timed steps consist of nothing but its launches), the one-call-per-bucket
+step (with each bucket's median and minimum launch time from an event pair
+around every launch) and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 import argparse
@@ -54,10 +58,21 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
+def bucketed_launches(lens, E, C, P, max_launch=1 << 29):
+    """Launches of one allreduce_ring_buckets call over these buckets, by
+    the rule its declaration states: consecutive full buckets as one ring
+    when C is a multiple of P and E of C, otherwise one launch per bucket;
+    a launch per 2^29 elements."""
+    full = sum(1 for n in lens if n == E)
+    parts = [full * E] if full > 1 and C % P == 0 and E % C == 0 else [E] * full
+    parts += [n for n in lens if n != E]
+    return sum(-(-n // max_launch) for n in parts)
+
+
+def measured_traffic(alg_bytes_per_launch):
     """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source;
-    otherwise None."""
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    and on launches of the current shape; otherwise None."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     fields = {}
@@ -67,6 +82,8 @@ def measured_traffic():
                 k, v = line.split(":", 1)
                 fields[k.strip().lstrip("- ").strip()] = v.strip()
     if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    if fields.get("algorithmic_bytes_per_launch") != str(alg_bytes_per_launch):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -137,7 +154,10 @@ def run_suite(steps, warmup):
         print(json.dumps(line), flush=True)
 
     def arena_sets(plan, P, n_sets=2, std=0.01, out_dtype=None):
-        sets = []
+        """Buffer sets of bucket views into per-rank arenas: per set, the
+        (inputs, outputs) of every bucket, and the P input and output rows
+        that hold the buckets end to end."""
+        sets, rows = [], []
         for s_ in range(n_sets):
             g = plan.alloc_arena(P)
             for r in range(P):
@@ -147,7 +167,8 @@ def run_suite(steps, warmup):
             sets.append([([plan.bucket_view(g[r], k) for r in range(P)],
                           [o[r, k * E:k * E + plan.bucket_len(k)] for r in range(P)])
                          for k in range(plan.n_buckets)])
-        return sets
+            rows.append(([g[r, :plan.total] for r in range(P)], [o[r, :plan.total] for r in range(P)]))
+        return sets, rows
 
     # config 1: 4 ranks x 65,536 fp32, Sum, 4 chunks, out of place.  2 MB
     # per call sits in the last-level cache, so the call is bound by launch
@@ -194,10 +215,14 @@ def run_suite(steps, warmup):
     shapes = workloads.model_shapes("resnet50")
     plan = ddp.GradBucketer(shapes, torch.float32, 25 << 20, device=dev)
     nbytes = P * plan.total * 8
-    sets = arena_sets(plan, P)
+    sets, rows = arena_sets(plan, P)
     report("cfg2 resnet50 p8 f32 mean, bucket views",
            _time(lambda i: [ddp.allreduce(a, "mean", P, out=o) for a, o in sets[i % 2]], steps, warmup),
            nbytes)
+    report("cfg2 resnet50 p8 f32 mean, bucket views, all buckets in one bucketed call",
+           _time(lambda i: ddp.allreduce(rows[i % 2][0], "mean", P, out=rows[i % 2][1],
+                                         bucket_elems=plan.bucket_elems), steps, warmup),
+           nbytes, note="every bucket its own ring, the same bits; 2 launches per step")
     report("cfg2 resnet50 p8 f32 mean, tree b=2 on bucket views",
            _time(lambda i: [ddp.allreduce_tree(a, "mean", 2, out=o) for a, o in sets[i % 2]], steps, warmup),
            nbytes)
@@ -212,7 +237,7 @@ def run_suite(steps, warmup):
     report("cfg2 resnet50 p8 f32 mean, stepwise ring (2(P-1) launches per bucket, in place)",
            _time(lambda i: [ddp.allreduce_stepwise(o, "mean", P) for _, o in sets[i % 2]],
                  max(2, steps // 10), 2), nbytes, note="moves 35n floats per bucket against 16n")
-    del sets
+    del sets, rows
     tensors = [[torch.empty(s_, device=dev).normal_(0, 0.01) for s_ in shapes] for _ in range(P)]
     outs = [[torch.empty(s_, device=dev) for s_ in shapes] for _ in range(P)]
     run = ddp.MultiAllReduce(shapes, P, torch.float32, device=dev).bind(tensors, outs)
@@ -259,7 +284,7 @@ def run_suite(steps, warmup):
 
     # config 3: ViT-B/16 bf16 gradients, Mean, fused SGD-momentum
     plan = ddp.GradBucketer(workloads.model_shapes("vit_b16"), torch.bfloat16, 25 << 20, device=dev)
-    sets = arena_sets(plan, P, std=1e-3)
+    sets, rows = arena_sets(plan, P, std=1e-3)
     w = torch.empty(plan.total, device=dev).normal_(0, 0.02)
     v = torch.zeros(plan.total, device=dev)
     E = plan.bucket_elems
@@ -273,6 +298,15 @@ def run_suite(steps, warmup):
            _time(lambda i: sgd_step(i, False), steps, warmup), P * plan.total * 2 + 16 * plan.total)
     report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum, gradients also written (bf16)",
            _time(lambda i: sgd_step(i, True), steps, warmup), P * plan.total * 4 + 16 * plan.total)
+    for with_out in (False, True):
+        report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum, " +
+               ("gradients also written (bf16), " if with_out else "no gradient output, ") +
+               "all buckets in one bucketed call",
+               _time(lambda i: ddp.allreduce_sgd(rows[i % 2][0], w, v, 1e-3, 0.9, "mean", P,
+                                                 out=rows[i % 2][1] if with_out else None,
+                                                 bucket_elems=E), steps, warmup),
+               P * plan.total * (4 if with_out else 2) + 16 * plan.total,
+               note="every bucket its own ring, the same bits; 2 launches per step")
 
     def zero1_step(i):
         for k, (a, o) in enumerate(sets[i % 2]):
@@ -280,7 +314,7 @@ def run_suite(steps, warmup):
             ddp.zero1_sgd_step(a, w[lo:lo + n], v[lo:lo + n], 1e-3, 0.9, o, "mean", P)
     report("cfg3 vitb16 p8 bf16 mean, ZeRO stage 1 step (owner sgd-momentum, bf16 parameters to every rank)",
            _time(zero1_step, steps, warmup), P * plan.total * 4 + 16 * plan.total)
-    del sets, w, v
+    del sets, rows, w, v
     torch.cuda.empty_cache()
 
     # config 4: 2,000 ragged fp32 tensors, P=4, Sum, 25 MiB buckets
@@ -310,6 +344,23 @@ def run_suite(steps, warmup):
     report(f"cfg4 ragged {len(sizes)} tensors p4 f32, unpack alone ({plan.n_buckets} buckets, all ranks)",
            _time(lambda i: [plan.unpack(table, k, bufs) for k in range(plan.n_buckets)], max(2, steps // 20), 1),
            P4 * plan.total * 8)
+    arena = plan.alloc_arena(P4)
+    E4 = plan.bucket_elems
+    slots = [[arena[r, k * E4:k * E4 + plan.bucket_len(k)] for r in range(P4)] for k in range(plan.n_buckets)]
+    flat = [arena[r, :plan.total] for r in range(P4)]
+
+    def ragged_bucketed(i):
+        for k in range(plan.n_buckets):
+            plan.pack(table, k, slots[k])
+        ddp.allreduce(flat, "sum", P4, out=flat, bucket_elems=E4)
+        for k in range(plan.n_buckets):
+            plan.unpack(table, k, slots[k])
+    ms = _time(ragged_bucketed, max(2, steps // 20), 1)
+    report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, pack every bucket -> one bucketed "
+           f"all-reduce -> unpack", ms, nbytes4,
+           with_copies_gbps=round(3 * nbytes4 / (ms * 1e-3) / 1e9, 1),
+           note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
+    del arena, slots, flat
     run = ddp.MultiAllReduce(shapes4, P4, torch.float32, device=dev).bind(tensors, tensors)
     report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, one multi-tensor launch, in place",
            _time(lambda i: run("sum"), max(2, steps // 20), 1), nbytes4)
@@ -329,6 +380,11 @@ def run_suite(steps, warmup):
     report(f"cfg5 transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets)",
            _time(lambda i: [ddp.allreduce(a, "mean", P, out=b) for a, b in views], 3, 1),
            P * plan.total * 6)
+    report(f"cfg5 transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets), one bucketed call",
+           _time(lambda i: ddp.allreduce([g[r, :plan.total] for r in range(P)], "mean", P,
+                                         out=[o[r, :plan.total] for r in range(P)],
+                                         bucket_elems=E), 3, 1),
+           P * plan.total * 6, note="every bucket its own ring, the same bits")
     del g, o, views
     torch.cuda.empty_cache()
     return 0
@@ -402,6 +458,43 @@ def run_occupancy_sweep(caps=(2, 3, 4, 5, 6, 8, 10, 12, 16)):
     return 0
 
 
+def one_call_per_bucket(timed, bucket_calls, lens, P, bytes_step, steps):
+    """Timed region 2: the step's buckets with one single-bucket call (one
+    launch) each; region 3: the same with an event pair around every launch
+    (on the stream it runs on; the pairs add about 2 us each) for each
+    bucket's median and minimum."""
+    import numpy as np
+    import torch
+    ms_calls = timed(bucket_calls)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in lens] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        bucket_calls(i, ev[i])
+    torch.cuda.synchronize()
+    durs = [[ev[i][k][0].elapsed_time(ev[i][k][1]) for k in range(len(lens))] for i in range(steps)]
+    per_bucket = []
+    for k, n in enumerate(lens):
+        col = sorted(row[k] for row in durs)
+        med = float(np.median(col))
+        per_bucket.append({"elements": n, "median_us": round(med * 1e3, 2),
+                           "min_us": round(col[0] * 1e3, 2),
+                           "median_gbs": round(P * n * 8 / (med * 1e-3) / 1e9, 1)})
+    per_set = sorted(map(sum, durs))
+    gbs = bytes_step / (ms_calls * 1e-3) / 1e9
+    return {
+        "ms_per_step": round(ms_calls, 4),
+        "value": round(gbs, 1),
+        "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "avg_launch_us": round(ms_calls / len(lens) * 1e3, 2),
+        "per_bucket": per_bucket,
+        "per_set_median_ms": round(float(np.median(per_set)), 4),
+        "per_set_min_ms": round(per_set[0], 4),
+        "note": "the same buckets, one allreduce_ring_emulated call (one launch) each; per_bucket "
+                "from an event pair around every launch, which adds about 2 us",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +507,9 @@ def main():
     ap.add_argument("--occupancy-sweep", action="store_true",
                     help="time the fused all-reduce and optimizer step at every cap on resident "
                          "workgroups per CU (the measurements behind the built-in caps)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step (the bucketed call), without the one-call-per-bucket "
+                         "regions: under a profiler every launch of the kernel is then a step launch")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (a kernel of known "
                          "traffic, to scale the memory counters of a profiler run)")
@@ -467,10 +563,19 @@ def main():
         views.append([([plan.bucket_view(g[r], k) for r in range(P)],
                        [plan.bucket_view(o[r], k) for r in range(P)], n)
                       for k, n in enumerate(lens)])
+    rows = [([g[r, :plan.total] for r in range(P)], [o[r, :plan.total] for r in range(P)])
+            for g, o in sets]
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, events=None):
+    def step(i):
+        """The step: every bucket in one bucketed call, each bucket its own
+        ring (bit for bit the one-call-per-bucket result)."""
+        ins, outs = rows[i % 2]
+        ddp.allreduce(ins, "mean", C, out=outs, bucket_elems=E)
+
+    def bucket_calls(i, events=None):
+        """The same buckets, one single-bucket call each."""
         for k, (ins, outs, n) in enumerate(views[i % 2]):
             if events is not None:
                 events[k][0].record(stream)
@@ -480,52 +585,38 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+        if not args.step_only:
+            bucket_calls(i)
     torch.cuda.synchronize()
 
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
     # Timed region 1: the step throughput, K steps bracketed by events.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = timed(step)
     bytes_step = sum(P * n * (4 + 4) for n in lens)
     value = bytes_step / (ms_step * 1e-3) / 1e9
 
     # The step is nothing but launches of the dominant kernel, back to back
     # on one stream, so region 1 also gives that kernel's average launch
     # duration: step time / launches per step.
-    launches_per_step = len(lens)
+    launches_per_step = bucketed_launches(lens, E, C, P)
     avg_ms = ms_step / launches_per_step
     avg_bytes = bytes_step / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
 
-    # Timed region 2 (cross-check and per-bucket split): the same K steps
-    # with an event pair around every launch, on the stream it runs on; the
-    # pairs themselves add about 2 us per launch.
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in lens] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    durs = [[ev[i][k][0].elapsed_time(ev[i][k][1]) for k in range(len(lens))]
-            for i in range(args.steps)]
-    pair_ms = sum(map(sum, durs)) / (args.steps * len(lens))
-    full = [d for row in durs for k, d in enumerate(row) if lens[k] == E]
-    full_gbs = P * E * 8 / (sum(full) / len(full) * 1e-3) / 1e9 if full else None
-    per_bucket = []
-    for k, n in enumerate(lens):
-        col = sorted(row[k] for row in durs)
-        med = float(np.median(col))
-        per_bucket.append({"elements": n, "median_us": round(med * 1e3, 2),
-                           "min_us": round(col[0] * 1e3, 2),
-                           "median_gbs": round(P * n * 8 / (med * 1e-3) / 1e9, 1)})
-    per_set = sorted(map(sum, durs))
-    traffic = measured_traffic()
+    traffic = measured_traffic(int(avg_bytes))
+    one_call = None
+    if not args.step_only:
+        one_call = one_call_per_bucket(timed, bucket_calls, lens, P, bytes_step, args.steps)
 
     out = {
         "metric": METRIC,
@@ -544,7 +635,9 @@ def main():
             "workload": "resnet50-gradient-set all-reduce: P=8 ranks x 161 fp32 tensors "
                         "(25,557,032 params) N(0,0.01), 25 MiB buckets (3 full + tail of "
                         "5,896,232), grads as bucket views of a per-rank arena padded to "
-                        "whole buckets, Mean, 8 ring chunks",
+                        "whole buckets, Mean, 8 ring chunks; one bucketed call per step "
+                        "(every bucket its own ring; the 3 full buckets in one launch, the "
+                        "tail in another)",
             "P": P, "chunking": C, "op": "mean", "bucket_bytes": cfg["bucket_bytes"],
             "buckets": len(lens), "elements_per_rank": plan.total,
             "bytes_per_step": bytes_step,
@@ -559,23 +652,17 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(avg_ms * 1e3, 2),
+            "launches_per_step": launches_per_step,
             "algorithmic_bytes_per_launch": int(avg_bytes),
             "timing": "events around the timed steps, which hold only this kernel's launches",
-            "event_pair_avg_launch_us": round(pair_ms * 1e3, 2),
-            "event_pair_full_bucket_gbs": round(full_gbs, 1) if full_gbs else None,
         },
-        "event_pairs": {
-            "per_bucket": per_bucket,
-            "per_set_median_ms": round(float(np.median(per_set)), 4),
-            "per_set_min_ms": round(per_set[0], 4),
-            "note": "an event pair around every launch (region 2); the pairs add about 2 us each",
-        },
+        "one_call_per_bucket": one_call,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         g = sets[0][0]
         host = [np.ascontiguousarray(g[:, k * E:k * E + n].cpu().numpy()) for k, n in enumerate(lens)]
-        del sets, views
+        del sets, views, rows
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(host, lens, P, C)
     print(json.dumps(out), flush=True)

@@ -14,7 +14,8 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
                   allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
                   allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step,
-                  allreduce_multi_fused_sgd, ddp_set_wg_per_cu, KERNEL_FAMILIES)
+                  allreduce_multi_fused_sgd, ddp_set_wg_per_cu, KERNEL_FAMILIES,
+                  allreduce_ring_buckets, allreduce_fused_sgd_buckets)
 from .bucketer import GradBucketer
 
 __all__ = [
@@ -27,4 +28,5 @@ __all__ = [
     "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",
     "allreduce_hierarchical", "zero1_sgd_step_emulated", "zero1_sgd_step",
     "allreduce_multi_fused_sgd", "ddp_set_wg_per_cu", "KERNEL_FAMILIES",
+    "allreduce_ring_buckets", "allreduce_fused_sgd_buckets",
 ]

@@ -68,6 +68,13 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,
         ctypes.c_int, ctypes.c_void_p]),
+    "allreduce_ring_buckets": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "allreduce_fused_sgd_buckets": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,
+        ctypes.c_int, ctypes.c_void_p]),
     "zero1_sgd_step_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,

@@ -5,7 +5,8 @@ here for device memory, pointers and the current stream.
 Raw entry points (same names and argument order as the C header, pointers as
 Python ints, stream as an int handle or None):
     ddp_bucket_plan, ddp_bucket_pack, ddp_bucket_unpack,
-    allreduce_ring_emulated, allreduce_fused_sgd, zero1_sgd_step_emulated,
+    allreduce_ring_emulated, allreduce_fused_sgd, allreduce_ring_buckets,
+    allreduce_fused_sgd_buckets, zero1_sgd_step_emulated,
     reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
     allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
@@ -103,6 +104,20 @@ def allreduce_fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, mom
     _check(N.lib().allreduce_fused_sgd(_op(op), P, chunking, N.pointer_array(rank_grad),
                                        grad_dtype, n, master_w, momentum, lr, mu, out,
                                        out_dtype, stream))
+
+
+def allreduce_ring_buckets(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, bucket_elems,
+                           stream=None):
+    _check(N.lib().allreduce_ring_buckets(_op(op), P, chunking, N.pointer_array(rank_in), in_dtype,
+                                          N.pointer_array(rank_out), out_dtype, n, bucket_elems, stream))
+
+
+def allreduce_fused_sgd_buckets(op, P, chunking, rank_grad, grad_dtype, n, bucket_elems, master_w,
+                                momentum, lr, mu, rank_grad_out, out_dtype, stream=None):
+    out = N.pointer_array(rank_grad_out) if rank_grad_out is not None else None
+    _check(N.lib().allreduce_fused_sgd_buckets(_op(op), P, chunking, N.pointer_array(rank_grad),
+                                               grad_dtype, n, bucket_elems, master_w, momentum, lr, mu,
+                                               out, out_dtype, stream))
 
 
 def zero1_sgd_step_emulated(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu,
@@ -251,11 +266,14 @@ def _rank_tensors(tensors, what):
     return tensors
 
 
-def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None):
+def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None, bucket_elems=None):
     """All-reduce a list of P equal-size GPU tensors (one per rank) in the
     chunked ring order.  ``out``: list of P output tensors ("in place" when
     they are the inputs); default: new tensors of ``out_dtype`` (default the
-    input dtype).  Enqueued on the current stream; returns the outputs."""
+    input dtype).  ``bucket_elems``: the tensors are flat gradient buffers
+    of consecutive buckets of that many elements, each bucket all-reduced as
+    its own ring (one call for all of them); None: one bucket.  Enqueued on
+    the current stream; returns the outputs."""
     import torch
     tensors = _rank_tensors(tensors, "allreduce")
     P = len(tensors)
@@ -266,6 +284,12 @@ def allreduce(tensors, op="sum", chunking=None, out=None, out_dtype=None):
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("allreduce: out must match the inputs")
     _same_device(tensors, out, "allreduce")
+    if bucket_elems is not None:
+        allreduce_ring_buckets(op, P, chunking or P, [t.data_ptr() for t in tensors],
+                               torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
+                               torch_dtype_code(out[0].dtype), tensors[0].numel(), bucket_elems,
+                               current_stream(tensors[0].device))
+        return out
     allreduce_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
                             torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
                             torch_dtype_code(out[0].dtype), tensors[0].numel(),
@@ -496,10 +520,11 @@ def zero1_sgd_step(grads, w, v, lr, mu, params, op="mean", chunking=None):
     return params
 
 
-def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):
+def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None, bucket_elems=None):
     """All-reduce the rank gradients, then one SGD-momentum step on the
     float32 master weights ``w`` and momentum ``v`` (updated in place).
-    ``out``: optional list of P tensors receiving the reduced gradient."""
+    ``out``: optional list of P tensors receiving the reduced gradient.
+    ``bucket_elems``: as for ``allreduce`` (w and v in the same layout)."""
     import torch
     grads = _rank_tensors(grads, "allreduce_sgd")
     for t in (w, v):
@@ -515,6 +540,12 @@ def allreduce_sgd(grads, w, v, lr, mu, op="mean", chunking=None, out=None):
         _same_device(grads, out, "allreduce_sgd")
         out_ptrs = [t.data_ptr() for t in out]
         out_code = torch_dtype_code(out[0].dtype)
+    if bucket_elems is not None:
+        allreduce_fused_sgd_buckets(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
+                                    torch_dtype_code(grads[0].dtype), grads[0].numel(), bucket_elems,
+                                    w.data_ptr(), v.data_ptr(), lr, mu, out_ptrs, out_code,
+                                    current_stream(grads[0].device))
+        return out
     allreduce_fused_sgd(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
                         torch_dtype_code(grads[0].dtype), grads[0].numel(), w.data_ptr(),
                         v.data_ptr(), lr, mu, out_ptrs, out_code, current_stream(grads[0].device))

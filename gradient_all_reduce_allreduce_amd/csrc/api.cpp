@@ -138,6 +138,49 @@ uint64_t fnv1a(uint64_t h, const void* data, size_t len) {
     return h;
 }
 
+// Buckets of E elements laid end to end in every rank buffer (the last one
+// may be shorter), each all-reduced as its own ring.  Consecutive full
+// buckets go out as one ring over all of them when that ring adds in the
+// same order: with C a multiple of P and E = C * L, chunk k * C + j of the
+// joint ring covers the elements of bucket k's chunk j and starts at rank
+// (k * C + j) mod P = j mod P, where bucket k's chunk j starts.  Otherwise,
+// and for the last, partial bucket, one call per bucket.
+int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
+    const int ies = l.in_bf16 ? 2 : 4;
+    const int oes = l.out_bf16 ? 2 : 4;
+    auto part = [&](int64_t first, int64_t count, int chunking) {
+        ddp::RingLaunch b = l;
+        for (int r = 0; r < l.P; ++r) {
+            b.in[r] = static_cast<const char*>(l.in[r]) + first * ies;
+            b.out[r] = l.out[r] ? static_cast<char*>(l.out[r]) + first * oes : nullptr;
+        }
+        if (l.w) b.w = l.w + first;
+        if (l.v) b.v = l.v + first;
+        b.n = count;
+        b.chunking = chunking;
+        return ddp::launch_ring_reduce(b, msg);
+    };
+    const int64_t full = l.n / E;
+    const int64_t tail = l.n - full * E;
+    int e = 0;
+    if (full > 1 && l.chunking % l.P == 0 && E % l.chunking == 0 && full * l.chunking <= INT32_MAX) {
+        e = part(0, full * E, static_cast<int>(full * l.chunking));
+    } else {
+        for (int64_t k = 0; k < full && e == 0; ++k) e = part(k * E, E, l.chunking);
+    }
+    if (e == 0 && tail > 0) e = part(full * E, tail, l.chunking);
+    return e;
+}
+
+int check_bucket_elems(int64_t E, int in_dtype, int out_dtype) {
+    if (E < 1) return fail(DDP_E_ARG, "bucket_elems = %lld, must be >= 1", static_cast<long long>(E));
+    if (E > kMaxElems) return fail(DDP_E_ARG, "bucket_elems is over 2^40");
+    if ((E * elem_bytes(in_dtype)) % 16 != 0 || (E * elem_bytes(out_dtype)) % 16 != 0)
+        return fail(DDP_E_ALIGN, "bucket_elems = %lld does not keep every bucket 16-byte aligned",
+                    static_cast<long long>(E));
+    return DDP_OK;
+}
+
 }  // namespace
 
 namespace ddp {
@@ -310,15 +353,50 @@ int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const
     return ok();
 }
 
+int allreduce_ring_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
+                           ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                           int64_t bucket_elems, void* stream) {
+    int s = validate_reduce(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, true);
+    if (s) return s;
+    if ((s = check_bucket_elems(bucket_elems, in_dtype, out_dtype))) return s;
+    std::vector<Buf> bufs;
+    add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
+    add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
+    if ((s = check_overlaps(bufs))) return s;
+    if (n == 0) return ok();
+
+    ddp::RingLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.sgd = 0;
+    l.write_out = 1;
+    for (int r = 0; r < P; ++r) {
+        l.in[r] = rank_in[r];
+        l.out[r] = rank_out[r];
+    }
+    l.n = n;
+    l.stream = stream;
+    const char* msg = nullptr;
+    const int e = launch_buckets(l, bucket_elems, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
 namespace {
 
 // The fused optimizer step; write_out: 0 nothing, 1 the reduced gradient,
-// 2 the updated weights, into rank_out.
+// 2 the updated weights, into rank_out.  bucket_elems = 0: the buffers are
+// one bucket.
 int fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
               ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr, float mu,
-              void* const* rank_grad_out, ddp_dtype out_dtype, int write_out, void* stream) {
+              void* const* rank_grad_out, ddp_dtype out_dtype, int write_out, void* stream,
+              int64_t bucket_elems = 0) {
     int s = validate_reduce(op, P, chunking, rank_grad, grad_dtype, rank_grad_out, out_dtype, n, false);
     if (s) return s;
+    if (bucket_elems != 0 && (s = check_bucket_elems(bucket_elems, grad_dtype, out_dtype))) return s;
     if (master_w == nullptr || momentum == nullptr) return fail(DDP_E_ARG, "master_w or momentum is NULL");
     if ((reinterpret_cast<uintptr_t>(master_w) | reinterpret_cast<uintptr_t>(momentum)) & 15u)
         return fail(DDP_E_ALIGN, "master_w or momentum is not 16-byte aligned");
@@ -364,12 +442,21 @@ int fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* 
     l.n = n;
     l.stream = stream;
     const char* msg = nullptr;
-    const int e = ddp::launch_ring_reduce(l, &msg);
+    const int e = bucket_elems != 0 ? launch_buckets(l, bucket_elems, &msg) : ddp::launch_ring_reduce(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
 }
 
 }  // namespace
+
+int allreduce_fused_sgd_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
+                                ddp_dtype grad_dtype, int64_t n, int64_t bucket_elems, float* master_w,
+                                float* momentum, float lr, float mu, void* const* rank_grad_out,
+                                ddp_dtype out_dtype, void* stream) {
+    if (bucket_elems == 0) return fail(DDP_E_ARG, "bucket_elems = 0, must be >= 1");
+    return fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu, rank_grad_out,
+                     out_dtype, 1, stream, bucket_elems);
+}
 
 int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
                         ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr,

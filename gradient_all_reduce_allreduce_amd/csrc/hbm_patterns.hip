@@ -20,6 +20,9 @@
 //   red8 f32    the all-reduce's own pattern: 8 input streams summed into 8
 //               identical output streams, 25 MiB each (the 16 buffers back to
 //               back in one allocation)
+//   red8 f32, 100 MiB streams   the same pattern, four times as much per
+//               launch: the fixed cost of starting and draining a launch
+//               weighs a quarter as much
 //   red8 bf16->f32  8 bf16 input streams of 100 MiB, 8 float32 outputs
 //   red8 f32, separate allocations   the f32 pattern on 16 hipMallocs
 #include <hip/hip_runtime.h>
@@ -161,12 +164,18 @@ int main() {
     uint32_t* sink = nullptr;
     CK(hipMalloc(&sink, 64));
 
-    // 25 MiB streams: 4 sets of 16 streams back to back (1.6 GiB)
+    // 25 MiB streams: 4 sets of 16 streams back to back (1.6 GiB); the
+    // arena holds twice that for 2 sets of 100 MiB streams
     const size_t sb = size_t(25) << 20;
     const int nsets = 4;
     char* arena = nullptr;
-    CK(hipMalloc(&arena, sb * 16 * nsets));
-    fill(arena, sb * 16 * nsets, 1u);
+    CK(hipMalloc(&arena, sb * 16 * nsets * 2));
+    fill(arena, sb * 16 * nsets * 2, 1u);
+    const size_t lb = 4 * sb;
+    std::vector<Streams> red_long;
+    for (int s = 0; s < 2; ++s)
+        red_long.push_back(make_set(arena + s * 16 * lb, lb, arena + (s * 16 + 8) * lb, lb, static_cast<uint32_t>(lb)));
+    const unsigned g100 = static_cast<unsigned>(lb / 16 / kW);
     std::vector<Streams> red;
     for (int s = 0; s < nsets; ++s)
         red.push_back(make_set(arena + s * 16 * sb, sb, arena + (s * 16 + 8) * sb, sb, static_cast<uint32_t>(sb)));
@@ -223,6 +232,7 @@ int main() {
     row("copy (200 MiB)", stream_kernel<1, 1>, g200, copy, 2.0 * cb);
     row("red8 f32 (25 MiB, one allocation)", stream_kernel<8, 8>, g25, red, 16.0 * sb);
     row("red8 f32 (25 MiB, separate allocs)", stream_kernel<8, 8>, g25, red_sep, 16.0 * sb);
+    row("red8 f32 (100 MiB streams)", stream_kernel<8, 8>, g100, red_long, 16.0 * lb);
     row("red8 bf16->f32 (100 MiB inputs)", red8_bf16_kernel, gbf, bf, 8.0 * (bin + bout));
 
     for (char* p : sep) CK(hipFree(p));

@@ -233,6 +233,44 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
                         ddp_dtype out_dtype, void* stream);
 
 /*
+ * allreduce_ring_buckets / allreduce_fused_sgd_buckets -- every bucket of
+ * a flat gradient buffer in one call.
+ *
+ * DDP cuts the gradients into fixed-size buckets and every rank reduces
+ * them in the same order ("Distributed Training", "Data parallelism and
+ * all-reduce"); with the gradients kept as views of one flat buffer per
+ * rank, bucket k is elements [k * E, min((k + 1) * E, n)) of it.  These
+ * calls all-reduce every bucket of such buffers, each bucket exactly as
+ * allreduce_ring_emulated (or allreduce_fused_sgd) reduces it on its own:
+ * its own C chunks of ceil(len_k / C) elements, its own start ranks, the
+ * same bits.  Fewer, longer launches use the memory system better than one
+ * short launch per bucket (the same page, "Communication costs", on larger
+ * messages): when C is a multiple of P and E a multiple of C, consecutive
+ * full buckets are one ring with the same order of additions and go out as
+ * one launch; otherwise each bucket is its own launch.
+ *
+ *   bucket_elems  E >= 1, with E * element size a multiple of 16 bytes for
+ *                 both element types (every bucket stays 16-byte aligned)
+ *   n             elements per rank buffer (all its buckets), >= 0
+ *   other arguments, layout, ownership and errors as for
+ *   allreduce_ring_emulated and allreduce_fused_sgd; master_w and momentum
+ *   hold n floats in the same bucket layout.
+ * Errors: those of the single-bucket calls; DDP_E_ARG for bucket_elems < 1,
+ * DDP_E_ALIGN for a bucket size that misaligns the buckets.
+ */
+int allreduce_ring_buckets(ddp_reduce_op op, int32_t P, int32_t chunking,
+                           const void* const* rank_in, ddp_dtype in_dtype,
+                           void* const* rank_out, ddp_dtype out_dtype,
+                           int64_t n, int64_t bucket_elems, void* stream);
+
+int allreduce_fused_sgd_buckets(ddp_reduce_op op, int32_t P, int32_t chunking,
+                                const void* const* rank_grad, ddp_dtype grad_dtype,
+                                int64_t n, int64_t bucket_elems, float* master_w,
+                                float* momentum, float lr, float mu,
+                                void* const* rank_grad_out, ddp_dtype out_dtype,
+                                void* stream);
+
+/*
  * zero1_sgd_step_emulated -- one ZeRO stage 1 step: the optimizer state is
  * sharded over the ranks and the updated parameters go to every rank.
  *

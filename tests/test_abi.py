@@ -184,6 +184,35 @@ def test_fused_sgd_errors():
     assert sgd(n=0) == N.DDP_OK
 
 
+def test_bucketed_calls_errors():
+    """allreduce_ring_buckets and allreduce_fused_sgd_buckets validate as the
+    single-bucket calls do, plus the bucket size: at least one element, and
+    a multiple of 16 bytes for both element types."""
+    lib = N.lib()
+    ins = N.pointer_array([A, A + MB])
+    outs = N.pointer_array([A + 64 * MB, A + 65 * MB])
+
+    def b(E, it=0, ot=0, n=1024, o=outs, P=2, C=2):
+        return lib.allreduce_ring_buckets(1, P, C, ins, it, o, ot, n, E, None)
+
+    def bs(E, gt=0, n=1024, w=A + 200 * MB, v=A + 300 * MB):
+        return lib.allreduce_fused_sgd_buckets(1, 2, 2, ins, gt, n, E, w, v, 1e-3, 0.9, None, 0, None)
+
+    assert b(0) == N.DDP_E_ARG and "bucket_elems" in N.last_error()
+    assert b(-4) == N.DDP_E_ARG
+    assert b((1 << 40) + 4) == N.DDP_E_ARG
+    assert b(6) == N.DDP_E_ALIGN                      # 24 bytes of float32
+    assert b(4, it=1) == N.DDP_E_ALIGN                # 8 bytes of bf16 input
+    assert b(4, o=N.pointer_array([A + 16, A + 65 * MB])) == N.DDP_E_OVERLAP
+    assert b(4, C=0) == N.DDP_E_ARG
+    assert b(4, n=0) == N.DDP_OK                      # nothing to do, nothing launched
+    assert bs(0) == N.DDP_E_ARG
+    assert bs(6) == N.DDP_E_ALIGN
+    assert bs(4, w=A) == N.DDP_E_OVERLAP              # master weights over a gradient
+    assert bs(4, gt=1) == N.DDP_E_ALIGN
+    assert bs(4, n=0) == N.DDP_OK
+
+
 def zero1(P=2, C=2, grads=None, gt=1, n=16, w=A + 200 * MB, v=A + 300 * MB, lr=1e-3, mu=0.9,
           params="default", pt=1, op=1):
     grads = grads if grads is not None else [A + r * MB for r in range(P)]

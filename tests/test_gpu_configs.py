@@ -59,7 +59,8 @@ def fill_arena(P, total, dtype, std, seed_base):
 def test_config2_resnet50_buckets():
     """P=8, ResNet-50 gradient set (161 tensors, 25,557,032 fp32), 25 MiB
     buckets, Mean, gradients laid out as bucket views of one [P, total]
-    arena."""
+    arena, all buckets in one bucketed call (the benchmark's step); then the
+    same buckets one call each, which must give the same bits."""
     cfg = workloads.CONFIGS["cfg2"]
     P, C = cfg["P"], cfg["chunking"]
     shapes = workloads.model_shapes("resnet50")
@@ -73,15 +74,15 @@ def test_config2_resnet50_buckets():
         lo, n = k * b.bucket_elems, b.bucket_len(k)
         idx = sample_indices(n, C, rng)
         checks.append((lo, n, idx, host_values([grads[r, lo:lo + n] for r in range(P)], idx)))
-        ddp.allreduce([grads[r, lo:lo + n] for r in range(P)], "mean", C,
-                      out=[out[r, lo:lo + n] for r in range(P)])
+    ddp.allreduce([grads[r] for r in range(P)], "mean", C, out=[out[r] for r in range(P)],
+                  bucket_elems=b.bucket_elems)
     torch.cuda.synchronize()
     assert all_ranks_equal([out[r] for r in range(P)])
     for lo, n, idx, V in checks:
         want = oracle.ring_allreduce_sampled(V, oracle.chunk_start_ranks_at(n, C, P, idx), "mean")
         got = host_values([out[r, lo:lo + n] for r in range(P)], idx)
         assert_same_bits(got, want, f"bucket at {lo}")
-    # second run: identical bits
+    # second run, one call per bucket: identical bits
     out2 = torch.empty_like(grads)
     for k in range(b.n_buckets):
         lo, n = k * b.bucket_elems, b.bucket_len(k)
@@ -129,6 +130,17 @@ def test_config3_vit_bf16_fused_sgd():
         gb = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="bf16")
         assert_same_bits(host_values([gout[r, lo:lo + n] for r in range(P)], idx), gb,
                          f"grads bucket at {lo}")
+    # the same step as one bucketed call, from the same state: identical bits
+    w_after, v_after = w.clone(), v.clone()
+    workloads.torch_normal_(w, sg["w_std"], seed=31)
+    workloads.torch_normal_(v, sg["v_std"], seed=32)
+    gout2 = torch.empty_like(grads)
+    ddp.allreduce_sgd([grads[r] for r in range(P)], w, v, sg["lr"], sg["mu"], "mean", C,
+                      out=[gout2[r] for r in range(P)], bucket_elems=b.bucket_elems)
+    torch.cuda.synchronize()
+    assert torch.equal(w.view(torch.int32), w_after.view(torch.int32))
+    assert torch.equal(v.view(torch.int32), v_after.view(torch.int32))
+    assert torch.equal(gout2.view(torch.int16), gout.view(torch.int16))
 
 
 def test_config4_ragged_pack_allreduce_unpack():
@@ -215,5 +227,11 @@ def test_config5_transformer_bf16_to_f32_100MiB():
                                              in_dtype="bf16", out_dtype="f32")
         got = host_values([out[r, lo:lo + n] for r in range(P)], idx)
         assert_same_bits(got, want, f"bucket at {lo}")
-    del grads, out
+    # all 39 buckets as one bucketed call: identical bits
+    out2 = torch.empty_like(out)
+    ddp.allreduce([grads[r] for r in range(P)], "mean", C, out=[out2[r] for r in range(P)],
+                  bucket_elems=b.bucket_elems)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    del grads, out, out2
     torch.cuda.empty_cache()
