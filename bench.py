@@ -162,7 +162,7 @@ def run_suite(steps, warmup):
             g = plan.alloc_arena(P)
             for r in range(P):
                 workloads.torch_normal_(g[r], std, seed=77 * s_ + r)
-            o = torch.empty(g.shape, dtype=out_dtype or g.dtype, device=dev)
+            o = plan.alloc_arena(P, out_dtype)
             E = plan.bucket_elems
             sets.append([([plan.bucket_view(g[r], k) for r in range(P)],
                           [o[r, k * E:k * E + plan.bucket_len(k)] for r in range(P)])
@@ -373,7 +373,7 @@ def run_suite(steps, warmup):
     g = plan.alloc_arena(P)
     for r in range(P):
         workloads.torch_normal_(g[r], 1e-4, seed=500 + r)
-    o = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    o = plan.alloc_arena(P, torch.float32)
     E = plan.bucket_elems
     views = [([plan.bucket_view(g[r], k) for r in range(P)],
               [o[r, k * E:k * E + plan.bucket_len(k)] for r in range(P)]) for k in range(plan.n_buckets)]
@@ -635,7 +635,7 @@ def main():
             "workload": "resnet50-gradient-set all-reduce: P=8 ranks x 161 fp32 tensors "
                         "(25,557,032 params) N(0,0.01), 25 MiB buckets (3 full + tail of "
                         "5,896,232), grads as bucket views of a per-rank arena padded to "
-                        "whole buckets, Mean, 8 ring chunks; one bucketed call per step "
+                        "whole buckets + 4 KiB, Mean, 8 ring chunks; one bucketed call per step "
                         "(every bucket its own ring; the 3 full buckets in one launch, the "
                         "tail in another)",
             "P": P, "chunking": C, "op": "mean", "bucket_bytes": cfg["bucket_bytes"],
