@@ -143,8 +143,10 @@ uint64_t fnv1a(uint64_t h, const void* data, size_t len) {
 // buckets go out as one ring over all of them when that ring adds in the
 // same order: with C a multiple of P and E = C * L, chunk k * C + j of the
 // joint ring covers the elements of bucket k's chunk j and starts at rank
-// (k * C + j) mod P = j mod P, where bucket k's chunk j starts.  Otherwise,
-// and for the last, partial bucket, one call per bucket.
+// (k * C + j) mod P = j mod P, where bucket k's chunk j starts.  The
+// partial last bucket rides in the same launch as a second segment with its
+// own chunks when the whole fits one launch; otherwise it, and every bucket
+// when the full ones do not form one ring, gets a call of its own.
 int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
     const int ies = l.in_bf16 ? 2 : 4;
     const int oes = l.out_bf16 ? 2 : 4;
@@ -162,8 +164,20 @@ int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
     };
     const int64_t full = l.n / E;
     const int64_t tail = l.n - full * E;
+    const bool joint = full > 1 && l.chunking % l.P == 0 && E % l.chunking == 0 && full * l.chunking <= INT32_MAX;
+    // The joint ring and the partial last bucket in one launch, each with its
+    // own chunks, when both take the vector path and no tile straddles them.
+    const int64_t tile = ddp::ring_tile_elems(l);
+    if (joint && tail > 0 && l.n <= ddp::kMaxLaunchElems && (full * E) % tile == 0 && E / l.chunking >= tile &&
+        (tail + l.chunking - 1) / l.chunking >= tile) {
+        ddp::RingLaunch b = l;
+        b.chunking = static_cast<int>(full * l.chunking);
+        b.seg2 = full * E;
+        b.seg2_chunking = l.chunking;
+        return ddp::launch_ring_reduce(b, msg);
+    }
     int e = 0;
-    if (full > 1 && l.chunking % l.P == 0 && E % l.chunking == 0 && full * l.chunking <= INT32_MAX) {
+    if (joint) {
         e = part(0, full * E, static_cast<int>(full * l.chunking));
     } else {
         for (int64_t k = 0; k < full && e == 0; ++k) e = part(k * E, E, l.chunking);

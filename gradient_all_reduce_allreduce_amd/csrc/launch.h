@@ -128,10 +128,21 @@ struct RingLaunch {
     int global_chunking;  // kTree: chunk count of a ring over the nodes, 0 = fixed order
     int64_t n;
     void* stream;
+    // kAllReduce: elements [seg2, n) are a second ring of their own with
+    // seg2_chunking chunks (0: none).  Only for a single launch (n <= 2^29)
+    // with seg2 a multiple of ring_tile_elems and whole chunks before it.
+    int64_t seg2;
+    int seg2_chunking;
 };
 
 // Returns 0 on success, else a HIP error code; *msg names the failing call.
 int launch_ring_reduce(const RingLaunch& l, const char** msg);
+
+// Elements per workgroup tile of the vector ring kernel for this launch.
+int64_t ring_tile_elems(const RingLaunch& l);
+
+// Elements per launch; longer buffers go out in several launches.
+constexpr int64_t kMaxLaunchElems = int64_t(1) << 29;
 
 // Vectors of each rank a lane keeps in flight per tile: P * U loads.  One
 // vector per lane (a tile of 256 or 512 elements per wave) measured fastest

@@ -10,11 +10,6 @@
 namespace ddp {
 namespace {
 
-// Buffers longer than this go out in several launches so that lane offsets
-// stay 32-bit; a multiple of every lane-vector width, so each launch's first
-// element stays 16-byte aligned.
-constexpr int64_t kMaxLaunchElems = int64_t(1) << 29;
-
 const void* select_kernel(const RingLaunch& l, int scalar) {
     const int P = l.P;
     switch (l.mode) {
@@ -88,11 +83,25 @@ int wg_per_cu(const RingLaunch& l) {
 
 }  // namespace
 
+int64_t ring_tile_elems(const RingLaunch& l) {
+    int64_t V = 4, tile = 0;
+    tile_shape(l, &V, &tile);
+    return tile;
+}
+
+// Buffers longer than kMaxLaunchElems go out in several launches so that
+// lane offsets stay 32-bit; it is a multiple of every lane-vector width, so
+// each launch's first element stays 16-byte aligned.
 int launch_ring_reduce(const RingLaunch& l, const char** msg) {
     if (l.n <= 0) return 0;
     if (l.mode == kAllGather && l.P == 1) return 0;   // one rank already holds everything
     int64_t V = 4, tile = 0;
     tile_shape(l, &V, &tile);
+    const bool two = l.seg2 > 0 && l.seg2 < l.n;
+    if (two && (l.mode != kAllReduce || l.n > kMaxLaunchElems || l.seg2 % tile != 0)) {
+        *msg = "second segment not supported for this launch";
+        return static_cast<int>(hipErrorInvalidValue);
+    }
     // Chunk lengths: the ring's; for the tree strategies those of a ring
     // within the nodes (L) and over the nodes (Lg), or a length beyond any
     // index where a level's order is fixed.
@@ -102,6 +111,9 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
     if (l.mode == kTree) {
         L = l.local_chunking > 0 ? (l.n + l.local_chunking - 1) / l.local_chunking : kFixed;
         Lg = l.global_chunking > 0 ? (l.n + l.global_chunking - 1) / l.global_chunking : kFixed;
+    } else if (two) {
+        L = (l.seg2 + l.chunking - 1) / l.chunking;
+        Lg = (l.n - l.seg2 + l.seg2_chunking - 1) / l.seg2_chunking;
     } else {
         L = (l.n + l.chunking - 1) / l.chunking;
     }
@@ -135,9 +147,10 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
         a.mean = l.op == DDP_MEAN;
         a.write_out = l.write_out;
         a.parents = l.parents;
-        a.global = chunk_map(base, Lg, groups);
+        a.global = two ? chunk_map(0, Lg, l.P) : chunk_map(base, Lg, groups);
         a.groups = groups;
         a.group_size = l.P / groups;
+        a.seg2 = two ? static_cast<uint32_t>(l.seg2) : 0xffffffffu;
 
         int64_t grid;
         if (scalar) {

@@ -90,9 +90,12 @@ struct RingArgs {
     int32_t mean;
     int32_t write_out;   // with SGD: 0 nothing, 1 the reduced gradient, 2 the updated weights
     uint64_t parents;    // tree strategies: 4 bits per fold register c >= 1, its parent register
-    ChunkMap global;     // two-level strategies: the chunks of the ring over the nodes
+    ChunkMap global;     // two-level strategies: the chunks of the ring over the nodes;
+                         // ring all-reduce with a second segment: that segment's chunks
     int32_t groups;      // two-level strategies: G nodes of group_size ranks, node-major
     int32_t group_size;
+    uint32_t seg2;       // ring all-reduce: the first element of a second segment -- a ring of
+                         // its own, chunked by `global` from there -- or 2^32 - 1 for none
 };
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
@@ -288,10 +291,18 @@ __device__ __forceinline__ void rotated_ins(KArgs a, int s, const char* (&src)[P
 
 // ---- one element per lane: tails and chunks shorter than a tile ----------
 
+// The start rank of element i of a ring all-reduce launch: its chunk in
+// the first segment, or in the second one (a ring of its own from seg2).
+template <int P>
+__device__ __forceinline__ int ring_start_rank(KArgs a, uint32_t i) {
+    const uint32_t seg2 = a->seg2;
+    return i < seg2 ? chunk_start<P>(i, a->ring) : chunk_start<P>(i - seg2, a->global);
+}
+
 template <int P, bool INB, bool OUTB, bool SGD>
 __device__ __forceinline__ void process_element(KArgs a, uint32_t i) {
 #pragma clang fp contract(off)
-    const int s = chunk_start<P>(i, a->ring);
+    const int s = ring_start_rank<P>(a, i);
     float g;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -475,9 +486,18 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
     // The tile's start rank, computed before the branch so that its argument
-    // loads go out together with n_vec's.
+    // loads go out together with n_vec's.  A tile of a second segment (the
+    // host keeps tiles from straddling its start) takes that segment's
+    // chunks, counted from its start.
+    const uint32_t seg2 = a->seg2;
     uint32_t next;
-    const int s0 = tile_chunk<P>(t0, a->ring, next);
+    int s0;
+    if (t0 < seg2) {
+        s0 = tile_chunk<P>(t0, a->ring, next);
+    } else {
+        s0 = tile_chunk<P>(t0 - seg2, a->global, next);
+        next += seg2;
+    }
     if (t0 + TILE <= n_vec) {
         process_tile<P, INB, OUTB, SGD, true>(a, t0, s0, next);
     } else if (t0 < n_vec) {

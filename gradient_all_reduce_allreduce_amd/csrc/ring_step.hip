@@ -160,8 +160,6 @@ const void* step_kernel(int P, bool scalar) {
     }
 }
 
-constexpr int64_t kMaxLaunchElems = int64_t(1) << 29;
-
 }  // namespace
 
 int launch_ring_stepwise(const StepLaunch& l, const char** msg) {

@@ -247,7 +247,10 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
  * short launch per bucket (the same page, "Communication costs", on larger
  * messages): when C is a multiple of P and E a multiple of C, consecutive
  * full buckets are one ring with the same order of additions and go out as
- * one launch; otherwise each bucket is its own launch.
+ * one launch, which also carries the partial last bucket (with its own
+ * chunks) when all n elements fit one launch (2^29), the full buckets end
+ * on a whole workgroup tile and every chunk is at least a tile long;
+ * otherwise each bucket is its own launch.
  *
  *   bucket_elems  E >= 1, with E * element size a multiple of 16 bytes for
  *                 both element types (every bucket stays 16-byte aligned)

@@ -30,9 +30,14 @@ def per_bucket_oracle(X, op, C, E, it, ot):
     return np.concatenate(parts, axis=1)
 
 
-# (P, C, E, n): joint path with a tail, joint without a tail, C not a
+# (P, C, E, n): joint full buckets and the tail in one launch (two
+# segments: tails of whole tiles and chunks at least a tile long, with a
+# ragged end), joint path with a short tail, joint without a tail, C not a
 # multiple of P, E not a multiple of C, one bucket, a tail only
 CASES = [
+    (4, 4, 16384, 3 * 16384 + 5001),
+    (8, 8, 32768, 2 * 32768 + 12347),
+    (3, 6, 12288, 4 * 12288 + 9001),
     (8, 8, 16384, 3 * 16384 + 1001),
     (4, 4, 10000, 4 * 10000),
     (3, 6, 6000, 5 * 6000 + 13),
@@ -62,7 +67,7 @@ def test_buckets_equal_oracle_and_single_calls(case, pair):
     assert_same_bits(to_host(single), to_host(out), "single-bucket calls")
 
 
-@pytest.mark.parametrize("case", CASES[:4])
+@pytest.mark.parametrize("case", CASES[:6])
 def test_buckets_in_place_and_sum(case):
     P, C, E, n = case
     X = draw(P, n, "f32", seed=7 + n)
