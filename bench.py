@@ -232,6 +232,9 @@ def run_suite(steps, warmup):
     report("cfg2 resnet50 p8 f32 mean, tree b=2 on bucket views",
            _time(lambda i: [ddp.allreduce_tree(a, "mean", 2, out=o) for a, o in sets[i % 2]], steps, warmup),
            nbytes)
+    report("cfg2 resnet50 p8 f32 mean, tree b=2 over the flat buffer (every bucket's tree, one launch)",
+           _time(lambda i: ddp.allreduce_tree(rows[i % 2][0], "mean", 2, out=rows[i % 2][1]), steps, warmup),
+           nbytes, note="the tree's order is the same for every element: the same bits as one tree per bucket")
     report("cfg2 resnet50 p8 f32 mean, two-level 2 nodes x 4: ring in the nodes, ring over them",
            _time(lambda i: [ddp.allreduce_hierarchical(a, 2, "mean", ("ring", None), ("ring", None), out=o)
                             for a, o in sets[i % 2]], steps, warmup),
@@ -320,6 +323,10 @@ def run_suite(steps, warmup):
             ddp.zero1_sgd_step(a, w[lo:lo + n], v[lo:lo + n], 1e-3, 0.9, o, "mean", P)
     report("cfg3 vitb16 p8 bf16 mean, ZeRO stage 1 step (owner sgd-momentum, bf16 parameters to every rank)",
            _time(zero1_step, steps, warmup), P * plan.total * 4 + 16 * plan.total)
+    report("cfg3 vitb16 p8 bf16 mean, ZeRO stage 1 step, all buckets in one bucketed call",
+           _time(lambda i: ddp.zero1_sgd_step(rows[i % 2][0], w, v, 1e-3, 0.9, rows[i % 2][1], "mean", P,
+                                              bucket_elems=E), steps, warmup),
+           P * plan.total * 4 + 16 * plan.total, note="every bucket its own ring, the same bits; 1 launch per step")
     del sets, rows, w, v
     torch.cuda.empty_cache()
 

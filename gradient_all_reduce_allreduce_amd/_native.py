@@ -75,6 +75,10 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,
         ctypes.c_int, ctypes.c_void_p]),
+    "zero1_sgd_step_buckets": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,
+        ctypes.c_int, ctypes.c_void_p]),
     "zero1_sgd_step_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,

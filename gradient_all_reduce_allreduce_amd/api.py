@@ -6,7 +6,7 @@ Raw entry points (same names and argument order as the C header, pointers as
 Python ints, stream as an int handle or None):
     ddp_bucket_plan, ddp_bucket_pack, ddp_bucket_unpack,
     allreduce_ring_emulated, allreduce_fused_sgd, allreduce_ring_buckets,
-    allreduce_fused_sgd_buckets, zero1_sgd_step_emulated,
+    allreduce_fused_sgd_buckets, zero1_sgd_step_emulated, zero1_sgd_step_buckets,
     reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
     allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
@@ -125,6 +125,13 @@ def zero1_sgd_step_emulated(op, P, chunking, rank_grad, grad_dtype, n, master_w,
     _check(N.lib().zero1_sgd_step_emulated(_op(op), P, chunking, N.pointer_array(rank_grad), grad_dtype,
                                            n, master_w, momentum, lr, mu,
                                            N.pointer_array(rank_param_out), param_dtype, stream))
+
+
+def zero1_sgd_step_buckets(op, P, chunking, rank_grad, grad_dtype, n, bucket_elems, master_w, momentum,
+                           lr, mu, rank_param_out, param_dtype, stream=None):
+    _check(N.lib().zero1_sgd_step_buckets(_op(op), P, chunking, N.pointer_array(rank_grad), grad_dtype,
+                                          n, bucket_elems, master_w, momentum, lr, mu,
+                                          N.pointer_array(rank_param_out), param_dtype, stream))
 
 
 def reducescatter_ring_emulated(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n,
@@ -496,12 +503,13 @@ class MultiAllReduce:
         return run(op, chunking)
 
 
-def zero1_sgd_step(grads, w, v, lr, mu, params, op="mean", chunking=None):
+def zero1_sgd_step(grads, w, v, lr, mu, params, op="mean", chunking=None, bucket_elems=None):
     """ZeRO stage 1 step: reduce-scatter the rank gradients, the momentum
     step on the float32 master weights ``w`` and momentum ``v`` (updated in
     place; element i is its chunk owner's shard), and all-gather of the
     updated weights into every rank's ``params`` tensor (float32 or
-    bfloat16; may be the gradient tensors themselves).  Returns ``params``."""
+    bfloat16; may be the gradient tensors themselves).  ``bucket_elems``: as
+    for ``allreduce``.  Returns ``params``."""
     import torch
     grads = _rank_tensors(grads, "zero1_sgd_step")
     params = _rank_tensors(params, "zero1_sgd_step params")
@@ -513,6 +521,12 @@ def zero1_sgd_step(grads, w, v, lr, mu, params, op="mean", chunking=None):
     if len(params) != len(grads) or params[0].numel() != grads[0].numel():
         raise ValueError("zero1_sgd_step: one parameter tensor per rank, of the gradient's size")
     _same_device(grads, params, "zero1_sgd_step")
+    if bucket_elems is not None:
+        zero1_sgd_step_buckets(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
+                               torch_dtype_code(grads[0].dtype), grads[0].numel(), bucket_elems,
+                               w.data_ptr(), v.data_ptr(), lr, mu, [p.data_ptr() for p in params],
+                               torch_dtype_code(params[0].dtype), current_stream(grads[0].device))
+        return params
     zero1_sgd_step_emulated(op, len(grads), chunking or len(grads), [g.data_ptr() for g in grads],
                             torch_dtype_code(grads[0].dtype), grads[0].numel(), w.data_ptr(),
                             v.data_ptr(), lr, mu, [p.data_ptr() for p in params],

@@ -472,6 +472,16 @@ int allreduce_fused_sgd_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, c
                      out_dtype, 1, stream, bucket_elems);
 }
 
+int zero1_sgd_step_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
+                           ddp_dtype grad_dtype, int64_t n, int64_t bucket_elems, float* master_w,
+                           float* momentum, float lr, float mu, void* const* rank_param_out,
+                           ddp_dtype param_dtype, void* stream) {
+    if (rank_param_out == nullptr) return fail(DDP_E_ARG, "rank_param_out is NULL");
+    if (bucket_elems == 0) return fail(DDP_E_ARG, "bucket_elems = 0, must be >= 1");
+    return fused_sgd(op, P, chunking, rank_grad, grad_dtype, n, master_w, momentum, lr, mu, rank_param_out,
+                     param_dtype, 2, stream, bucket_elems);
+}
+
 int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_grad,
                         ddp_dtype grad_dtype, int64_t n, float* master_w, float* momentum, float lr,
                         float mu, void* const* rank_grad_out, ddp_dtype out_dtype, void* stream) {

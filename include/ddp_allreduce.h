@@ -312,6 +312,25 @@ int zero1_sgd_step_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
                             ddp_dtype param_dtype, void* stream);
 
 /*
+ * zero1_sgd_step_buckets -- zero1_sgd_step_emulated over every bucket of a
+ * flat gradient buffer in one call, each bucket exactly as
+ * zero1_sgd_step_emulated steps it on its own (its own ring, chunks and
+ * owners), launched as allreduce_ring_buckets launches its buckets.  ZeRO
+ * flattens the parameters of a partition into one buffer ("Distributed
+ * Training", "Sharded data parallelism: ZeRO and FSDP").
+ *
+ *   bucket_elems  as for allreduce_ring_buckets
+ *   other arguments, layout, ownership and errors as for
+ *   zero1_sgd_step_emulated and allreduce_ring_buckets.
+ */
+int zero1_sgd_step_buckets(ddp_reduce_op op, int32_t P, int32_t chunking,
+                           const void* const* rank_grad, ddp_dtype grad_dtype,
+                           int64_t n, int64_t bucket_elems, float* master_w,
+                           float* momentum, float lr, float mu,
+                           void* const* rank_param_out, ddp_dtype param_dtype,
+                           void* stream);
+
+/*
  * reducescatter_ring_emulated -- the first half of the ring on its own.
  *
  * Every rank ends holding the finished reduction of the chunks it owns

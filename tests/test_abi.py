@@ -212,6 +212,14 @@ def test_bucketed_calls_errors():
     assert bs(4, gt=1) == N.DDP_E_ALIGN
     assert bs(4, n=0) == N.DDP_OK
 
+    def bz(E, params=outs, n=1024):
+        return lib.zero1_sgd_step_buckets(1, 2, 2, ins, 0, n, E, A + 200 * MB, A + 300 * MB, 1e-3, 0.9,
+                                          params, 0, None)
+    assert bz(0) == N.DDP_E_ARG
+    assert bz(4, params=None) == N.DDP_E_ARG
+    assert bz(6) == N.DDP_E_ALIGN
+    assert bz(4, n=0) == N.DDP_OK
+
 
 def zero1(P=2, C=2, grads=None, gt=1, n=16, w=A + 200 * MB, v=A + 300 * MB, lr=1e-3, mu=0.9,
           params="default", pt=1, op=1):

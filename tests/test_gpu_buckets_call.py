@@ -128,3 +128,47 @@ def test_buckets_across_launch_splits():
         start[sel] = oracle.chunk_start_ranks_at(min(E, n - k * E), C, P, idx[sel] - k * E)
     want = oracle.ring_allreduce_sampled(V, start, "mean", in_dtype="bf16", out_dtype="bf16")
     assert_same_bits(got, want, "sampled")
+
+
+@pytest.mark.parametrize("case", CASES[:5])
+@pytest.mark.parametrize("gt,pt", [("bf16", "bf16"), ("f32", "f32")])
+def test_zero1_buckets_equal_oracle(case, gt, pt):
+    """zero1_sgd_step_buckets: every bucket's ZeRO stage 1 step as the
+    oracle's phase-by-phase simulation of that bucket alone."""
+    P, C, E, n = case
+    X = draw(P, n, gt, seed=3 * P + C + n)
+    w0 = workloads.rank_buffers(1, n, "normal", 0.02, seed=10)[0]
+    v0 = workloads.rank_buffers(1, n, "normal", 1e-3, seed=11)[0]
+    g = to_device(X, gt)
+    w = torch.from_numpy(w0.copy()).to(DEV)
+    v = torch.from_numpy(v0.copy()).to(DEV)
+    params = [torch.empty(n, dtype=torch_dtype(pt), device=DEV) for _ in range(P)]
+    ddp.zero1_sgd_step(g, w, v, 1e-3, 0.9, params, "mean", C, bucket_elems=E)
+    torch.cuda.synchronize()
+    got_p, got_w, got_v = to_host(params), w.cpu().numpy(), v.cpu().numpy()
+    for lo in range(0, n, E):
+        hi = min(n, lo + E)
+        want_p, want_w, want_v, _ = oracle.zero1_sgd_step(X[:, lo:hi], w0[lo:hi], v0[lo:hi], 1e-3, 0.9, "mean",
+                                                          C, gt, pt)
+        what = f"{gt}->{pt} P={P} C={C} E={E} n={n} bucket at {lo}"
+        assert_same_bits(got_w[None, lo:hi], want_w[None], what + " w")
+        assert_same_bits(got_v[None, lo:hi], want_v[None], what + " v")
+        assert_same_bits(got_p[:, lo:hi], want_p, what + " params")
+
+
+def test_tree_over_the_flat_buffer_equals_per_bucket_calls():
+    """The tree's order of additions is the same for every element, so one
+    tree all-reduce over the flat buffer gives every bucket's own tree
+    all-reduce, bit for bit (no bucketed variant is needed)."""
+    P, E, n = 8, 16384, 3 * 16384 + 5001
+    X = draw(P, n, "f32", seed=12)
+    flat = ddp.allreduce_tree(to_device(X, "f32"), "mean", 2)
+    ins = to_device(X, "f32")
+    per = [torch.empty(n, device=DEV) for _ in range(P)]
+    for lo in range(0, n, E):
+        hi = min(n, lo + E)
+        ddp.allreduce_tree([t[lo:hi] for t in ins], "mean", 2, out=[t[lo:hi] for t in per])
+    torch.cuda.synchronize()
+    assert_same_bits(to_host(flat), to_host(per), "flat tree vs per-bucket trees")
+    want, _ = oracle.tree_allreduce(X, "mean", 2)
+    assert_same_bits(to_host(flat), want, "flat tree vs oracle")
