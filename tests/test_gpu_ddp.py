@@ -94,10 +94,12 @@ def test_synchronized_batchnorm_statistics():
     assert torch.allclose(var, ref_var, rtol=1e-4, atol=1e-5)
 
 
-def test_graph_capture_and_replay_of_a_bucket_step():
-    """The launches of a bucket step captured in a HIP graph and replayed
-    several times, with eager work and synchronizations between replays,
-    give the eager result every time."""
+@pytest.mark.parametrize("bucketed", [False, True])
+def test_graph_capture_and_replay_of_a_bucket_step(bucketed):
+    """The launches of a bucket step (one call per bucket, or one bucketed
+    call) captured in a HIP graph and replayed several times, with eager
+    work and synchronizations between replays, give the eager result every
+    time."""
     P = 8
     plan = ddp.GradBucketer(workloads.model_shapes("resnet50"), torch.float32, 25 << 20,
                             device=DEV)
@@ -105,8 +107,12 @@ def test_graph_capture_and_replay_of_a_bucket_step():
     o = plan.alloc_arena(P)
     views = [([plan.bucket_view(g[r], k) for r in range(P)],
               [plan.bucket_view(o[r], k) for r in range(P)]) for k in range(plan.n_buckets)]
+    rows = ([g[r, :plan.total] for r in range(P)], [o[r, :plan.total] for r in range(P)])
 
     def step():
+        if bucketed:
+            ddp.allreduce(rows[0], "mean", P, out=rows[1], bucket_elems=plan.bucket_elems)
+            return
         for a, b in views:
             ddp.allreduce(a, "mean", P, out=b)
 
