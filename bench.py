@@ -243,6 +243,12 @@ def run_suite(steps, warmup):
            _time(lambda i: [ddp.allreduce_hierarchical(a, 4, "mean", ("tree", 2), ("ring", None), out=o)
                             for a, o in sets[i % 2]], steps, warmup),
            nbytes)
+    report("cfg2 resnet50 p8 f32 mean, reduce-scatter alone (owner-only writes), one call per bucket",
+           _time(lambda i: [ddp.reduce_scatter(a, "mean", P, out=o) for a, o in sets[i % 2]], steps, warmup),
+           P * plan.total * 4 + plan.total * 4, note="reads P*n, writes n (each element to its owner)")
+    report("cfg2 resnet50 p8 f32, all-gather alone (owner to every other rank), one call per bucket",
+           _time(lambda i: [ddp.all_gather(o, P) for _, o in sets[i % 2]], steps, warmup),
+           plan.total * 4 + (P - 1) * plan.total * 4, note="reads n, writes (P-1)*n")
     report("cfg2 resnet50 p8 f32 mean, stepwise ring (2(P-1) launches per bucket, in place)",
            _time(lambda i: [ddp.allreduce_stepwise(o, "mean", P) for _, o in sets[i % 2]],
                  max(2, steps // 10), 2), nbytes, note="moves 35n floats per bucket against 16n")
