@@ -176,7 +176,7 @@ def run_suite(steps, warmup):
             rows.append(([g[r, :plan.total] for r in range(P)], [o[r, :plan.total] for r in range(P)]))
         return sets, rows
 
-    # config 1: 4 ranks x 65,536 fp32, Sum, 4 chunks, out of place.  2 MB
+    # 4 ranks x 65,536 fp32, Sum, 4 chunks, out of place.  2 MB
     # per call sits in the last-level cache, so the call is bound by launch
     # and host overhead: a parity case, not a bandwidth one.
     x1 = [torch.empty(65536, device=dev).normal_() for _ in range(4)]
@@ -188,7 +188,7 @@ def run_suite(steps, warmup):
         ddp.allreduce(x1, "sum", 4, out=o1)
     host_us = (time.perf_counter() - t0) / steps * 1e6
     torch.cuda.synchronize()
-    report("cfg1 p4 f32 sum n=65,536 (2 MB per call, cache resident: launch-bound)", ms1, 4 * 65536 * 8,
+    report("p4 f32 sum n=65,536 (2 MB per call, cache resident: launch-bound)", ms1, 4 * 65536 * 8,
            host_us_per_call=round(host_us, 2),
            note="time per call on the stream; host_us_per_call is the Python call alone")
     # The same call through the C ABI with its arguments prepared once (what
@@ -210,58 +210,58 @@ def run_suite(steps, warmup):
         c_call(i)
     host_c_us = (time.perf_counter() - t0) / steps * 1e6
     torch.cuda.synchronize()
-    report("cfg1 p4 f32 sum n=65,536, C ABI call with prepared arguments", ms1c, 4 * 65536 * 8,
+    report("p4 f32 sum n=65,536, C ABI call with prepared arguments", ms1c, 4 * 65536 * 8,
            host_us_per_call=round(host_c_us, 2),
            note="time per call on the stream; host_us_per_call is the ctypes call alone")
     del x1, o1
 
-    # config 2, bucket views (the headline step), the multi-tensor launch
+    # ResNet-50 gradient set, P=8: bucket views (the headline step), the multi-tensor launch
     # over the 161 separate per-parameter tensors, and pack/unpack
     P = 8
     shapes = workloads.model_shapes("resnet50")
     plan = ddp.GradBucketer(shapes, torch.float32, 25 << 20, device=dev)
     nbytes = P * plan.total * 8
     sets, rows = arena_sets(plan, P)
-    report("cfg2 resnet50 p8 f32 mean, bucket views",
+    report("resnet50 p8 f32 mean, bucket views",
            _time(lambda i: [ddp.allreduce(a, "mean", P, out=o) for a, o in sets[i % 2]], steps, warmup),
            nbytes)
-    report("cfg2 resnet50 p8 f32 mean, bucket views, all buckets in one bucketed call",
+    report("resnet50 p8 f32 mean, bucket views, all buckets in one bucketed call",
            _time(lambda i: ddp.allreduce(rows[i % 2][0], "mean", P, out=rows[i % 2][1],
                                          bucket_elems=plan.bucket_elems), steps, warmup),
            nbytes, note="every bucket its own ring, the same bits; 1 launch per step")
-    report("cfg2 resnet50 p8 f32 mean, tree b=2 on bucket views",
+    report("resnet50 p8 f32 mean, tree b=2 on bucket views",
            _time(lambda i: [ddp.allreduce_tree(a, "mean", 2, out=o) for a, o in sets[i % 2]], steps, warmup),
            nbytes)
-    report("cfg2 resnet50 p8 f32 mean, tree b=2 over the flat buffer (every bucket's tree, one launch)",
+    report("resnet50 p8 f32 mean, tree b=2 over the flat buffer (every bucket's tree, one launch)",
            _time(lambda i: ddp.allreduce_tree(rows[i % 2][0], "mean", 2, out=rows[i % 2][1]), steps, warmup),
            nbytes, note="the tree's order is the same for every element: the same bits as one tree per bucket")
-    report("cfg2 resnet50 p8 f32 mean, two-level 2 nodes x 4: ring in the nodes, ring over them",
+    report("resnet50 p8 f32 mean, two-level 2 nodes x 4: ring in the nodes, ring over them",
            _time(lambda i: [ddp.allreduce_hierarchical(a, 2, "mean", ("ring", None), ("ring", None), out=o)
                             for a, o in sets[i % 2]], steps, warmup),
            nbytes)
-    report("cfg2 resnet50 p8 f32 mean, two-level 4 nodes x 2: tree in the nodes, ring over them",
+    report("resnet50 p8 f32 mean, two-level 4 nodes x 2: tree in the nodes, ring over them",
            _time(lambda i: [ddp.allreduce_hierarchical(a, 4, "mean", ("tree", 2), ("ring", None), out=o)
                             for a, o in sets[i % 2]], steps, warmup),
            nbytes)
-    report("cfg2 resnet50 p8 f32 mean, reduce-scatter alone (owner-only writes), one call per bucket",
+    report("resnet50 p8 f32 mean, reduce-scatter alone (owner-only writes), one call per bucket",
            _time(lambda i: [ddp.reduce_scatter(a, "mean", P, out=o) for a, o in sets[i % 2]], steps, warmup),
            P * plan.total * 4 + plan.total * 4, note="reads P*n, writes n (each element to its owner)")
-    report("cfg2 resnet50 p8 f32, all-gather alone (owner to every other rank), one call per bucket",
+    report("resnet50 p8 f32, all-gather alone (owner to every other rank), one call per bucket",
            _time(lambda i: [ddp.all_gather(o, P) for _, o in sets[i % 2]], steps, warmup),
            plan.total * 4 + (P - 1) * plan.total * 4, note="reads n, writes (P-1)*n")
-    report("cfg2 resnet50 p8 f32 mean, stepwise ring (2(P-1) launches per bucket, in place)",
+    report("resnet50 p8 f32 mean, stepwise ring (2(P-1) launches per bucket, in place)",
            _time(lambda i: [ddp.allreduce_stepwise(o, "mean", P) for _, o in sets[i % 2]],
                  max(2, steps // 10), 2), nbytes, note="moves 35n floats per bucket against 16n")
     del sets, rows
     tensors = [[torch.empty(s_, device=dev).normal_(0, 0.01) for s_ in shapes] for _ in range(P)]
     outs = [[torch.empty(s_, device=dev) for s_ in shapes] for _ in range(P)]
     run = ddp.MultiAllReduce(shapes, P, torch.float32, device=dev).bind(tensors, outs)
-    report("cfg2 resnet50 p8 f32 mean, 161 separate tensors, one multi-tensor launch",
+    report("resnet50 p8 f32 mean, 161 separate tensors, one multi-tensor launch",
            _time(lambda i: run("mean"), steps, warmup), nbytes)
     mw = [torch.empty(s_, device=dev).normal_(0, 0.02) for s_ in shapes]
     mv = [torch.zeros(s_, device=dev) for s_ in shapes]
     run_sgd = ddp.MultiAllReduce(shapes, P, torch.float32, device=dev).bind_sgd(tensors, mw, mv)
-    report("cfg2 resnet50 p8 f32 mean, 161 separate tensors, one launch with fused sgd-momentum per tensor",
+    report("resnet50 p8 f32 mean, 161 separate tensors, one launch with fused sgd-momentum per tensor",
            _time(lambda i: run_sgd(1e-3, 0.9, "mean"), steps, warmup), P * plan.total * 4 + 16 * plan.total)
     del mw, mv, run_sgd
     table = plan.pointer_table(tensors)
@@ -274,30 +274,30 @@ def run_suite(steps, warmup):
             ddp.allreduce([x[:n] for x in bufs], "mean", P, out=[x[:n] for x in bufs])
             plan.unpack(table, k, bufs)
     ms = _time(packed_step, steps, warmup)
-    report("cfg2 resnet50 p8 f32 mean, pack -> all-reduce -> unpack", ms, nbytes,
+    report("resnet50 p8 f32 mean, pack -> all-reduce -> unpack", ms, nbytes,
            with_copies_gbps=round(3 * nbytes / (ms * 1e-3) / 1e9, 1),
            note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
     copy_bytes = P * plan.total * 4 * 2     # every rank's gradients read once and written once
-    report("cfg2 resnet50 p8 f32, pack alone (161 tensors -> 4 buckets, all ranks)",
+    report("resnet50 p8 f32, pack alone (161 tensors -> 4 buckets, all ranks)",
            _time(lambda i: [plan.pack(table, k, bufs) for k in range(plan.n_buckets)], steps, warmup),
            copy_bytes)
-    report("cfg2 resnet50 p8 f32, unpack alone (4 buckets -> 161 tensors, all ranks)",
+    report("resnet50 p8 f32, unpack alone (4 buckets -> 161 tensors, all ranks)",
            _time(lambda i: [plan.unpack(table, k, bufs) for k in range(plan.n_buckets)], steps, warmup),
            copy_bytes)
     # The lines above reuse one set of P bucket buffers (200 MiB) for every
     # bucket, as a DDP step does, so the last-level cache can hold part of
     # them; with a buffer set per bucket (800 MiB) every byte goes to HBM.
     per_bucket = [plan.alloc_buckets(P) for _ in range(plan.n_buckets)]
-    report("cfg2 resnet50 p8 f32, pack alone, a bucket buffer set per bucket",
+    report("resnet50 p8 f32, pack alone, a bucket buffer set per bucket",
            _time(lambda i: [plan.pack(table, k, per_bucket[k]) for k in range(plan.n_buckets)], steps, warmup),
            copy_bytes)
-    report("cfg2 resnet50 p8 f32, unpack alone, a bucket buffer set per bucket",
+    report("resnet50 p8 f32, unpack alone, a bucket buffer set per bucket",
            _time(lambda i: [plan.unpack(table, k, per_bucket[k]) for k in range(plan.n_buckets)], steps, warmup),
            copy_bytes)
     del tensors, outs, run, table, bufs, per_bucket
     torch.cuda.empty_cache()
 
-    # config 3: ViT-B/16 bf16 gradients, Mean, fused SGD-momentum
+    # ViT-B/16 bf16 gradients, P=8, Mean, fused SGD-momentum
     plan = ddp.GradBucketer(workloads.model_shapes("vit_b16"), torch.bfloat16, 25 << 20, device=dev)
     sets, rows = arena_sets(plan, P, std=1e-3)
     w = torch.empty(plan.total, device=dev).normal_(0, 0.02)
@@ -309,12 +309,12 @@ def run_suite(steps, warmup):
             lo, n = k * E, plan.bucket_len(k)
             ddp.allreduce_sgd(a, w[lo:lo + n], v[lo:lo + n], 1e-3, 0.9, "mean", P,
                               out=o if with_out else None)
-    report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum (w, v fp32), no gradient output",
+    report("vitb16 p8 bf16 mean + fused sgd-momentum (w, v fp32), no gradient output",
            _time(lambda i: sgd_step(i, False), steps, warmup), P * plan.total * 2 + 16 * plan.total)
-    report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum, gradients also written (bf16)",
+    report("vitb16 p8 bf16 mean + fused sgd-momentum, gradients also written (bf16)",
            _time(lambda i: sgd_step(i, True), steps, warmup), P * plan.total * 4 + 16 * plan.total)
     for with_out in (False, True):
-        report("cfg3 vitb16 p8 bf16 mean + fused sgd-momentum, " +
+        report("vitb16 p8 bf16 mean + fused sgd-momentum, " +
                ("gradients also written (bf16), " if with_out else "no gradient output, ") +
                "all buckets in one bucketed call",
                _time(lambda i: ddp.allreduce_sgd(rows[i % 2][0], w, v, 1e-3, 0.9, "mean", P,
@@ -327,16 +327,16 @@ def run_suite(steps, warmup):
         for k, (a, o) in enumerate(sets[i % 2]):
             lo, n = k * E, plan.bucket_len(k)
             ddp.zero1_sgd_step(a, w[lo:lo + n], v[lo:lo + n], 1e-3, 0.9, o, "mean", P)
-    report("cfg3 vitb16 p8 bf16 mean, ZeRO stage 1 step (owner sgd-momentum, bf16 parameters to every rank)",
+    report("vitb16 p8 bf16 mean, ZeRO stage 1 step (owner sgd-momentum, bf16 parameters to every rank)",
            _time(zero1_step, steps, warmup), P * plan.total * 4 + 16 * plan.total)
-    report("cfg3 vitb16 p8 bf16 mean, ZeRO stage 1 step, all buckets in one bucketed call",
+    report("vitb16 p8 bf16 mean, ZeRO stage 1 step, all buckets in one bucketed call",
            _time(lambda i: ddp.zero1_sgd_step(rows[i % 2][0], w, v, 1e-3, 0.9, rows[i % 2][1], "mean", P,
                                               bucket_elems=E), steps, warmup),
            P * plan.total * 4 + 16 * plan.total, note="every bucket its own ring, the same bits; 1 launch per step")
     del sets, rows, w, v
     torch.cuda.empty_cache()
 
-    # config 4: 2,000 ragged fp32 tensors, P=4, Sum, 25 MiB buckets
+    # 2,000 ragged fp32 tensors, P=4, Sum, 25 MiB buckets
     P4 = 4
     sizes = workloads.ragged_sizes()
     shapes4 = [(n,) for n in sizes]
@@ -353,14 +353,14 @@ def run_suite(steps, warmup):
             ddp.allreduce([x[:n] for x in bufs], "sum", P4, out=[x[:n] for x in bufs])
             plan.unpack(table, k, bufs)
     ms = _time(ragged_step, max(2, steps // 20), 1)
-    report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, pack -> all-reduce -> unpack "
+    report(f"ragged {len(sizes)} tensors p4 f32 sum, pack -> all-reduce -> unpack "
            f"({plan.n_buckets} buckets)", ms, nbytes4,
            with_copies_gbps=round(3 * nbytes4 / (ms * 1e-3) / 1e9, 1),
            note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
-    report(f"cfg4 ragged {len(sizes)} tensors p4 f32, pack alone ({plan.n_buckets} buckets, all ranks)",
+    report(f"ragged {len(sizes)} tensors p4 f32, pack alone ({plan.n_buckets} buckets, all ranks)",
            _time(lambda i: [plan.pack(table, k, bufs) for k in range(plan.n_buckets)], max(2, steps // 20), 1),
            P4 * plan.total * 8)
-    report(f"cfg4 ragged {len(sizes)} tensors p4 f32, unpack alone ({plan.n_buckets} buckets, all ranks)",
+    report(f"ragged {len(sizes)} tensors p4 f32, unpack alone ({plan.n_buckets} buckets, all ranks)",
            _time(lambda i: [plan.unpack(table, k, bufs) for k in range(plan.n_buckets)], max(2, steps // 20), 1),
            P4 * plan.total * 8)
     arena = plan.alloc_arena(P4)
@@ -375,18 +375,18 @@ def run_suite(steps, warmup):
         for k in range(plan.n_buckets):
             plan.unpack(table, k, slots[k])
     ms = _time(ragged_bucketed, max(2, steps // 20), 1)
-    report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, pack every bucket -> one bucketed "
+    report(f"ragged {len(sizes)} tensors p4 f32 sum, pack every bucket -> one bucketed "
            f"all-reduce -> unpack", ms, nbytes4,
            with_copies_gbps=round(3 * nbytes4 / (ms * 1e-3) / 1e9, 1),
            note="gbps counts the all-reduce bytes; with_copies_gbps adds pack and unpack traffic")
     del arena, slots, flat
     run = ddp.MultiAllReduce(shapes4, P4, torch.float32, device=dev).bind(tensors, tensors)
-    report(f"cfg4 ragged {len(sizes)} tensors p4 f32 sum, one multi-tensor launch, in place",
+    report(f"ragged {len(sizes)} tensors p4 f32 sum, one multi-tensor launch, in place",
            _time(lambda i: run("sum"), max(2, steps // 20), 1), nbytes4)
     del tensors, table, bufs, run
     torch.cuda.empty_cache()
 
-    # config 5: 2B-parameter transformer, bf16 in, fp32 out, 100 MiB buckets
+    # 2B-parameter transformer, P=8, bf16 in, fp32 out, 100 MiB buckets
     plan = ddp.GradBucketer(workloads.model_shapes("transformer_2b"), torch.bfloat16, 100 << 20,
                             device=dev)
     g = plan.alloc_arena(P)
@@ -396,10 +396,10 @@ def run_suite(steps, warmup):
     E = plan.bucket_elems
     views = [([plan.bucket_view(g[r], k) for r in range(P)],
               [o[r, k * E:k * E + plan.bucket_len(k)] for r in range(P)]) for k in range(plan.n_buckets)]
-    report(f"cfg5 transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets)",
+    report(f"transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets)",
            _time(lambda i: [ddp.allreduce(a, "mean", P, out=b) for a, b in views], 3, 1),
            P * plan.total * 6)
-    report(f"cfg5 transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets), one bucketed call",
+    report(f"transformer-2b p8 bf16 -> f32 mean ({plan.n_buckets} x 100 MiB buckets), one bucketed call",
            _time(lambda i: ddp.allreduce([g[r, :plan.total] for r in range(P)], "mean", P,
                                          out=[o[r, :plan.total] for r in range(P)],
                                          bucket_elems=E), 3, 1),
@@ -559,7 +559,7 @@ def main():
     if args.occupancy_sweep:
         return run_occupancy_sweep()
 
-    cfg = workloads.CONFIGS["cfg2"]
+    cfg = workloads.CONFIGS["p8-resnet50-f32-mean-25MiB"]
     P, C = cfg["P"], cfg["chunking"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -31,11 +31,11 @@ def draw(P, n, dtype, seed, dist="wide"):
     return workloads.to_bf16_bits(X) if dtype == "bf16" else X
 
 
-def test_config1_exact():
+def test_p4_65536_f32_sum():
     """P = 4 ranks, 65,536 fp32 gradients N(0,1) per rank, 4 chunks, Sum."""
     X = workloads.rank_buffers(4, 65536, "normal", 1.0, seed=0)
     Y = gpu_ring(X, "sum", 4)
-    assert_same_bits(Y, oracle_ring(X, "sum", 4), "config 1")
+    assert_same_bits(Y, oracle_ring(X, "sum", 4), "P=4, 65,536 fp32, Sum, 4 chunks")
     for r in range(1, 4):
         assert np.array_equal(Y[r].view(np.uint32), Y[0].view(np.uint32))
 

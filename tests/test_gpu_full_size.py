@@ -56,12 +56,12 @@ def fill_arena(P, total, dtype, std, seed_base):
     return arena
 
 
-def test_config2_resnet50_buckets():
+def test_resnet50_p8_f32_full_size():
     """P=8, ResNet-50 gradient set (161 tensors, 25,557,032 fp32), 25 MiB
     buckets, Mean, gradients laid out as bucket views of one [P, total]
     arena, all buckets in one bucketed call (the benchmark's step); then the
     same buckets one call each, which must give the same bits."""
-    cfg = workloads.CONFIGS["cfg2"]
+    cfg = workloads.CONFIGS["p8-resnet50-f32-mean-25MiB"]
     P, C = cfg["P"], cfg["chunking"]
     shapes = workloads.model_shapes("resnet50")
     b = ddp.GradBucketer(shapes, torch.float32, cfg["bucket_bytes"], device=DEV)
@@ -92,11 +92,11 @@ def test_config2_resnet50_buckets():
     assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
 
 
-def test_config3_vit_bf16_fused_sgd():
+def test_vitb16_p8_bf16_fused_sgd_full_size():
     """P=8, ViT-B/16 gradient set (152 tensors, 86,567,656 bf16), Mean with
     fp32 accumulation, fused SGD-momentum (0.9, lr 1e-3) on fp32 master
     weights, 25 MiB buckets."""
-    cfg = workloads.CONFIGS["cfg3"]
+    cfg = workloads.CONFIGS["p8-vitb16-bf16-mean-sgd-25MiB"]
     P, C, sg = cfg["P"], cfg["chunking"], cfg["sgd"]
     b = ddp.GradBucketer(workloads.model_shapes("vit_b16"), torch.bfloat16, cfg["bucket_bytes"],
                          device=DEV)
@@ -143,11 +143,11 @@ def test_config3_vit_bf16_fused_sgd():
     assert torch.equal(gout2.view(torch.int16), gout.view(torch.int16))
 
 
-def test_config4_ragged_pack_allreduce_unpack():
+def test_ragged2000_p4_pack_allreduce_unpack_full_size():
     """P=4, 2,000 separately allocated fp32 tensors per rank with log-uniform
     sizes in [1e3, 4e6], U[-1, 1], Sum, 25 MiB buckets with a partial tail:
     pack -> all-reduce -> unpack for every bucket, in place."""
-    cfg = workloads.CONFIGS["cfg4"]
+    cfg = workloads.CONFIGS["p4-ragged2000-f32-sum-25MiB"]
     P, C = cfg["P"], cfg["chunking"]
     sizes = workloads.ragged_sizes()
     shapes = [(s,) for s in sizes]
@@ -197,11 +197,11 @@ def test_config4_ragged_pack_allreduce_unpack():
             assert torch.equal(tensors[r][t].view(torch.int32), tensors[0][t].view(torch.int32))
 
 
-def test_config5_transformer_bf16_to_f32_100MiB():
+def test_transformer2b_p8_bf16_to_f32_100MiB_full_size():
     """P=8, 2,017,529,856-parameter dense transformer gradient set in bf16
     (32.3 GB of rank inputs), N(0, 1e-4), Mean, fp32 outputs (64.6 GB),
     100 MiB buckets."""
-    cfg = workloads.CONFIGS["cfg5"]
+    cfg = workloads.CONFIGS["p8-transformer2b-bf16-mean-f32out-100MiB"]
     P, C = cfg["P"], cfg["chunking"]
     b = ddp.GradBucketer(workloads.model_shapes("transformer_2b"), torch.bfloat16,
                          cfg["bucket_bytes"], device=DEV)

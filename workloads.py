@@ -145,22 +145,22 @@ def torch_uniform_(t, lo, hi, seed):
 # --------------------------------------------------------------------------
 
 CONFIGS = {
-    "cfg1": dict(name="p4-65536-f32-sum", P=4, shapes=[(65536,)], dtype="f32",
+    "p4-65536-f32-sum": dict(name="p4-65536-f32-sum", P=4, shapes=[(65536,)], dtype="f32",
                  out_dtype="f32", op="sum", chunking=4, bucket_bytes=None,
                  dist=("normal", 1.0), sgd=None),
-    "cfg2": dict(name="p8-resnet50-f32-mean-25MiB", P=8, shapes=None,
+    "p8-resnet50-f32-mean-25MiB": dict(name="p8-resnet50-f32-mean-25MiB", P=8, shapes=None,
                  model="resnet50", dtype="f32", out_dtype="f32", op="mean",
                  chunking=8, bucket_bytes=25 * MiB, dist=("normal", 0.01),
                  sgd=None),
-    "cfg3": dict(name="p8-vitb16-bf16-mean-sgd-25MiB", P=8, shapes=None,
+    "p8-vitb16-bf16-mean-sgd-25MiB": dict(name="p8-vitb16-bf16-mean-sgd-25MiB", P=8, shapes=None,
                  model="vit_b16", dtype="bf16", out_dtype="bf16", op="mean",
                  chunking=8, bucket_bytes=25 * MiB, dist=("normal", 1e-3),
                  sgd=dict(lr=1e-3, mu=0.9, w_std=0.02, v_std=1e-3)),
-    "cfg4": dict(name="p4-ragged2000-f32-sum-25MiB", P=4, shapes=None,
+    "p4-ragged2000-f32-sum-25MiB": dict(name="p4-ragged2000-f32-sum-25MiB", P=4, shapes=None,
                  model="ragged", dtype="f32", out_dtype="f32", op="sum",
                  chunking=4, bucket_bytes=25 * MiB, dist=("uniform", 1.0),
                  sgd=None),
-    "cfg5": dict(name="p8-transformer2b-bf16-mean-f32out-100MiB", P=8,
+    "p8-transformer2b-bf16-mean-f32out-100MiB": dict(name="p8-transformer2b-bf16-mean-f32out-100MiB", P=8,
                  shapes=None, model="transformer_2b", dtype="bf16",
                  out_dtype="f32", op="mean", chunking=8,
                  bucket_bytes=100 * MiB, dist=("normal", 1e-4), sgd=None),
