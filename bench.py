@@ -58,23 +58,6 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def bucketed_launches(lens, E, C, P, tile, max_launch=1 << 29):
-    """Launches of one allreduce_ring_buckets call over these buckets, by
-    the rule its declaration states: consecutive full buckets as one ring
-    when C is a multiple of P and E of C, the partial last bucket in the
-    same launch when everything fits one launch, the full buckets end on a
-    whole tile and every chunk is at least a tile long; otherwise one launch
-    per bucket; a launch per 2^29 elements."""
-    full = sum(1 for n in lens if n == E)
-    tail = [n for n in lens if n != E]
-    joint = full > 1 and C % P == 0 and E % C == 0
-    if (joint and tail and sum(lens) <= max_launch and (full * E) % tile == 0 and E // C >= tile
-            and -(-tail[0] // C) >= tile):
-        return 1
-    parts = ([full * E] if joint else [E] * full) + tail
-    return sum(-(-n // max_launch) for n in parts)
-
-
 def measured_traffic(alg_bytes_per_launch):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source
@@ -627,7 +610,7 @@ def main():
     # The step is nothing but launches of the dominant kernel, back to back
     # on one stream, so region 1 also gives that kernel's average launch
     # duration: step time / launches per step.
-    launches_per_step = bucketed_launches(lens, E, C, P, tile=256)   # 64 lanes x 4 floats
+    launches_per_step = ddp.ddp_buckets_launch_count(P, C, ddp.F32, ddp.F32, False, plan.total, E)
     avg_ms = ms_step / launches_per_step
     avg_bytes = bytes_step / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9

@@ -75,6 +75,9 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,
         ctypes.c_int, ctypes.c_void_p]),
+    "ddp_buckets_launch_count": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
+        ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "zero1_sgd_step_buckets": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, _c_void_pp,

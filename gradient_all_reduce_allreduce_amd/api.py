@@ -7,6 +7,7 @@ Python ints, stream as an int handle or None):
     ddp_bucket_plan, ddp_bucket_pack, ddp_bucket_unpack,
     allreduce_ring_emulated, allreduce_fused_sgd, allreduce_ring_buckets,
     allreduce_fused_sgd_buckets, zero1_sgd_step_emulated, zero1_sgd_step_buckets,
+    ddp_buckets_launch_count,
     reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
     allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
@@ -125,6 +126,14 @@ def zero1_sgd_step_emulated(op, P, chunking, rank_grad, grad_dtype, n, master_w,
     _check(N.lib().zero1_sgd_step_emulated(_op(op), P, chunking, N.pointer_array(rank_grad), grad_dtype,
                                            n, master_w, momentum, lr, mu,
                                            N.pointer_array(rank_param_out), param_dtype, stream))
+
+
+def ddp_buckets_launch_count(P, chunking, in_dtype, out_dtype, sgd, n, bucket_elems):
+    """Kernel launches one bucketed call makes for these arguments (host only)."""
+    out = ctypes.c_int64(0)
+    _check(N.lib().ddp_buckets_launch_count(P, chunking, in_dtype, out_dtype, 1 if sgd else 0, n,
+                                            bucket_elems, ctypes.byref(out)))
+    return out.value
 
 
 def zero1_sgd_step_buckets(op, P, chunking, rank_grad, grad_dtype, n, bucket_elems, master_w, momentum,

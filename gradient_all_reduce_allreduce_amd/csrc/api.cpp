@@ -147,21 +147,18 @@ uint64_t fnv1a(uint64_t h, const void* data, size_t len) {
 // partial last bucket rides in the same launch as a second segment with its
 // own chunks when the whole fits one launch; otherwise it, and every bucket
 // when the full ones do not form one ring, gets a call of its own.
-int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
-    const int ies = l.in_bf16 ? 2 : 4;
-    const int oes = l.out_bf16 ? 2 : 4;
-    auto part = [&](int64_t first, int64_t count, int chunking) {
-        ddp::RingLaunch b = l;
-        for (int r = 0; r < l.P; ++r) {
-            b.in[r] = static_cast<const char*>(l.in[r]) + first * ies;
-            b.out[r] = l.out[r] ? static_cast<char*>(l.out[r]) + first * oes : nullptr;
-        }
-        if (l.w) b.w = l.w + first;
-        if (l.v) b.v = l.v + first;
-        b.n = count;
-        b.chunking = chunking;
-        return ddp::launch_ring_reduce(b, msg);
-    };
+// One ring call of a bucketed all-reduce: elements [first, first + count)
+// with `chunking` chunks, and optionally a second segment from `seg2` on.
+struct BucketPart {
+    int64_t first;
+    int64_t count;
+    int chunking;
+    int64_t seg2;
+    int seg2_chunking;
+};
+
+std::vector<BucketPart> bucket_parts(const ddp::RingLaunch& l, int64_t E) {
+    std::vector<BucketPart> parts;
     const int64_t full = l.n / E;
     const int64_t tail = l.n - full * E;
     const bool joint = full > 1 && l.chunking % l.P == 0 && E % l.chunking == 0 && full * l.chunking <= INT32_MAX;
@@ -170,20 +167,36 @@ int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
     const int64_t tile = ddp::ring_tile_elems(l);
     if (joint && tail > 0 && l.n <= ddp::kMaxLaunchElems && (full * E) % tile == 0 && E / l.chunking >= tile &&
         (tail + l.chunking - 1) / l.chunking >= tile) {
-        ddp::RingLaunch b = l;
-        b.chunking = static_cast<int>(full * l.chunking);
-        b.seg2 = full * E;
-        b.seg2_chunking = l.chunking;
-        return ddp::launch_ring_reduce(b, msg);
+        parts.push_back({0, l.n, static_cast<int>(full * l.chunking), full * E, l.chunking});
+        return parts;
     }
-    int e = 0;
     if (joint) {
-        e = part(0, full * E, static_cast<int>(full * l.chunking));
+        parts.push_back({0, full * E, static_cast<int>(full * l.chunking), 0, 0});
     } else {
-        for (int64_t k = 0; k < full && e == 0; ++k) e = part(k * E, E, l.chunking);
+        for (int64_t k = 0; k < full; ++k) parts.push_back({k * E, E, l.chunking, 0, 0});
     }
-    if (e == 0 && tail > 0) e = part(full * E, tail, l.chunking);
-    return e;
+    if (tail > 0) parts.push_back({full * E, tail, l.chunking, 0, 0});
+    return parts;
+}
+
+int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
+    const int ies = l.in_bf16 ? 2 : 4;
+    const int oes = l.out_bf16 ? 2 : 4;
+    for (const BucketPart& p : bucket_parts(l, E)) {
+        ddp::RingLaunch b = l;
+        for (int r = 0; r < l.P; ++r) {
+            b.in[r] = static_cast<const char*>(l.in[r]) + p.first * ies;
+            b.out[r] = l.out[r] ? static_cast<char*>(l.out[r]) + p.first * oes : nullptr;
+        }
+        if (l.w) b.w = l.w + p.first;
+        if (l.v) b.v = l.v + p.first;
+        b.n = p.count;
+        b.chunking = p.chunking;
+        b.seg2 = p.seg2;
+        b.seg2_chunking = p.seg2_chunking;
+        if (const int e = ddp::launch_ring_reduce(b, msg)) return e;
+    }
+    return 0;
 }
 
 int check_bucket_elems(int64_t E, int in_dtype, int out_dtype) {
@@ -396,6 +409,30 @@ int allreduce_ring_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, const 
     const char* msg = nullptr;
     const int e = launch_buckets(l, bucket_elems, &msg);
     if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+int ddp_buckets_launch_count(int32_t P, int32_t chunking, ddp_dtype in_dtype, ddp_dtype out_dtype,
+                             int32_t sgd, int64_t n, int64_t bucket_elems, int64_t* launches) {
+    int s = check_ranks(P);
+    if (s) return s;
+    if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
+    if ((s = check_length(n, "n"))) return s;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown dtype");
+    if ((s = check_bucket_elems(bucket_elems, in_dtype, out_dtype))) return s;
+    if (launches == nullptr) return fail(DDP_E_ARG, "launches is NULL");
+    ddp::RingLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.sgd = sgd != 0;
+    l.n = n;
+    int64_t count = 0;
+    if (n > 0)
+        for (const BucketPart& p : bucket_parts(l, bucket_elems))
+            count += (p.count + ddp::kMaxLaunchElems - 1) / ddp::kMaxLaunchElems;
+    *launches = count;
     return ok();
 }
 

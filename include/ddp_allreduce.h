@@ -312,6 +312,23 @@ int zero1_sgd_step_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
                             ddp_dtype param_dtype, void* stream);
 
 /*
+ * ddp_buckets_launch_count -- host only, no device work: how many kernel
+ * launches one of the bucketed calls above (or zero1_sgd_step_buckets)
+ * enqueues for these arguments, by the rule stated above.  For callers
+ * that size launch-time budgets or time the kernel per launch.
+ *
+ *   P, chunking, in_dtype, out_dtype, n, bucket_elems   as for the call
+ *                (out_dtype: the output or parameter type, or the gradient
+ *                type when nothing is written)
+ *   sgd          nonzero for the fused optimizer calls
+ *   launches     out: the number of launches (0 for n = 0)
+ * Errors: DDP_E_ARG, DDP_E_ALIGN, as for the calls.
+ */
+int ddp_buckets_launch_count(int32_t P, int32_t chunking, ddp_dtype in_dtype,
+                             ddp_dtype out_dtype, int32_t sgd, int64_t n,
+                             int64_t bucket_elems, int64_t* launches);
+
+/*
  * zero1_sgd_step_buckets -- zero1_sgd_step_emulated over every bucket of a
  * flat gradient buffer in one call, each bucket exactly as
  * zero1_sgd_step_emulated steps it on its own (its own ring, chunks and

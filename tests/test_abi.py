@@ -221,6 +221,30 @@ def test_bucketed_calls_errors():
     assert bz(4, n=0) == N.DDP_OK
 
 
+def test_buckets_launch_count():
+    """The launch count the bucketed calls report, by the rule of their
+    declaration: one launch when the full buckets form one ring and the
+    tail fits with them, more otherwise."""
+    f = ddp.ddp_buckets_launch_count
+    F32, BF16 = ddp.F32, ddp.BF16
+    E = 6_553_600
+    assert f(8, 8, F32, F32, False, 3 * E + 5_896_232, E) == 1        # ResNet-50 set: one launch
+    assert f(8, 17, F32, F32, False, 3 * E + 5_896_232, E) == 4       # C not a multiple of P: per bucket
+    assert f(8, 8, F32, F32, False, 3 * E + 1000, E) == 2             # tail chunks shorter than a tile
+    assert f(8, 8, F32, F32, False, 3 * E, E) == 1                    # no tail
+    assert f(8, 8, F32, F32, False, E, E) == 1
+    assert f(8, 8, F32, F32, False, 100, E) == 1                      # one partial bucket
+    assert f(8, 8, F32, F32, False, 0, E) == 0
+    assert f(8, 8, BF16, F32, False, 38 * 52_428_800 + 25_235_456, 52_428_800) == 5   # 4 x 2^29 + tail
+    assert f(8, 8, BF16, BF16, True, 6 * 13_107_200 + 7_924_456, 13_107_200) == 1     # ViT set, fused step
+    assert f(3, 6, F32, F32, False, 5 * 6000 + 13, 6000) == 2
+    assert f(5, 5, F32, F32, False, 4 * 4104 + 3, 4104) == 5           # E not a multiple of C
+    with pytest.raises(ddp.DdpError):
+        f(8, 8, F32, F32, False, 100, 6)                               # misaligned buckets
+    with pytest.raises(ddp.DdpError):
+        f(0, 8, F32, F32, False, 100, 64)
+
+
 def zero1(P=2, C=2, grads=None, gt=1, n=16, w=A + 200 * MB, v=A + 300 * MB, lr=1e-3, mu=0.9,
           params="default", pt=1, op=1):
     grads = grads if grads is not None else [A + r * MB for r in range(P)]
