@@ -24,6 +24,9 @@
 //               launch: the fixed cost of starting and draining a launch
 //               weighs a quarter as much
 //   red8 bf16->f32  8 bf16 input streams of 100 MiB, 8 float32 outputs
+//   sgd step    the fused optimizer step: 8 bf16 gradient streams of 25 MiB
+//               summed, float32 w and v read and written, and with output
+//               the bf16 sum to 8 streams
 //   red8 f32, separate allocations   the f32 pattern on 16 hipMallocs
 #include <hip/hip_runtime.h>
 
@@ -124,8 +127,64 @@ __global__ __launch_bounds__(kW) void red8_bf16_kernel(Streams p, uint32_t* sink
     for (int q = 0; q < 8; ++q) store16(p.out[rot + q], p.out_bytes, i * 16u, s);
 }
 
-template <typename K>
-static double rate(K kernel, unsigned grid, int cap, const std::vector<Streams>& sets, uint32_t* sink,
+// The fused optimizer step's pattern: 8 bf16 input streams (8-byte loads,
+// 4 elements per lane) summed, one momentum step on float32 w and v (read
+// and written, 16 bytes per lane each), and with WOUT the sum rounded to
+// bf16 into 8 output streams (8-byte stores).  (The bf16 rounding here is
+// a truncation: only the traffic matters.)
+struct SgdStreams {
+    const char* in[8];
+    char* out[16];
+    char* w;
+    char* v;
+    uint32_t out_bytes;
+    uint32_t wv_bytes;
+};
+
+__device__ __forceinline__ void store8(char* base, uint32_t bytes, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000),
+                                          off, 0, 16);
+}
+
+template <bool WOUT>
+__global__ __launch_bounds__(kW) void sgd_kernel(SgdStreams p, uint32_t* sink) {
+    const uint32_t i = blockIdx.x * kW + threadIdx.x;   // 4-element group
+    u32x2 x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[r] + i * 8u));
+    const u32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.w + i * 16u));
+    const u32x4 vq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v + i * 16u));
+    u32x4 wn, vn;
+    u32x2 o;
+    float g[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t w = x[r][e >> 1];
+            const float val = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            acc = r == 0 ? val : acc + val;
+        }
+        g[e] = acc * 0.125f;
+        const float v1 = 0.9f * __uint_as_float(vq[e]) + g[e];
+        vn[e] = __float_as_uint(v1);
+        wn[e] = __float_as_uint(__uint_as_float(wq[e]) - 1e-3f * v1);
+    }
+    for (int k = 0; k < 2; ++k) o[k] = (__float_as_uint(g[2 * k]) >> 16) | (__float_as_uint(g[2 * k + 1]) & 0xffff0000u);
+    store16(p.w, p.wv_bytes, i * 16u, wn);
+    store16(p.v, p.wv_bytes, i * 16u, vn);
+    if constexpr (WOUT) {
+        const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x & 7));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) store8(p.out[rot + q], p.out_bytes, i * 8u, o);
+    } else {
+        if ((o[0] ^ o[1]) == 0x9e3779b9u) sink[0] = 1u;
+    }
+}
+
+template <typename K, typename S>
+static double rate(K kernel, unsigned grid, int cap, const std::vector<S>& sets, uint32_t* sink,
                    double bytes_per_launch, int reps = 40) {
     const unsigned lds = lds_for(cap);
     hipEvent_t a, b;
@@ -200,6 +259,24 @@ int main() {
     }
     const unsigned gbf = static_cast<unsigned>(bin / 8 / kW);
 
+    // the fused optimizer step: bf16 gradients of 25 MiB per rank, w and v
+    // float32 (50 MiB each), outputs bf16; 4 sets, carved from the bf16 arena
+    const size_t gb = sb;                 // 25 MiB of bf16 per stream
+    const size_t wvb = 2 * sb;            // 50 MiB of float32
+    std::vector<SgdStreams> sgd;
+    for (int s = 0; s < 4; ++s) {
+        char* base = barena + s * (16 * gb + 2 * wvb);
+        SgdStreams st{};
+        for (int r = 0; r < 8; ++r) st.in[r] = base + r * gb;
+        for (int q = 0; q < 8; ++q) st.out[q] = st.out[q + 8] = base + (8 + q) * gb;
+        st.w = base + 16 * gb;
+        st.v = base + 16 * gb + wvb;
+        st.out_bytes = static_cast<uint32_t>(gb);
+        st.wv_bytes = static_cast<uint32_t>(wvb);
+        sgd.push_back(st);
+    }
+    const unsigned gsgd = static_cast<unsigned>(gb / 8 / kW);
+
     // separate allocations for the f32 pattern
     std::vector<char*> sep;
     for (int i = 0; i < 16 * nsets; ++i) {
@@ -221,7 +298,7 @@ int main() {
     std::printf("%-36s", "pattern \\ workgroups per CU");
     for (int c : caps) std::printf(c ? "%8d" : "    none", c);
     std::printf("\n");
-    auto row = [&](const char* name, auto kernel, unsigned grid, const std::vector<Streams>& sets, double bytes) {
+    auto row = [&](const char* name, auto kernel, unsigned grid, const auto& sets, double bytes) {
         std::printf("%-36s", name);
         for (int c : caps) std::printf("%8.0f", rate(kernel, grid, c, sets, sink, bytes));
         std::printf("   GB/s\n");
@@ -234,6 +311,8 @@ int main() {
     row("red8 f32 (25 MiB, separate allocs)", stream_kernel<8, 8>, g25, red_sep, 16.0 * sb);
     row("red8 f32 (100 MiB streams)", stream_kernel<8, 8>, g100, red_long, 16.0 * lb);
     row("red8 bf16->f32 (100 MiB inputs)", red8_bf16_kernel, gbf, bf, 8.0 * (bin + bout));
+    row("sgd step, bf16 in, no output", sgd_kernel<false>, gsgd, sgd, 8.0 * gb + 4.0 * wvb);
+    row("sgd step, bf16 in, bf16 out", sgd_kernel<true>, gsgd, sgd, 16.0 * gb + 4.0 * wvb);
 
     for (char* p : sep) CK(hipFree(p));
     CK(hipFree(barena));
