@@ -33,7 +33,8 @@ def per_bucket_oracle(X, op, C, E, it, ot):
 # (P, C, E, n): joint full buckets and the tail in one launch (two
 # segments: tails of whole tiles and chunks at least a tile long, with a
 # ragged end), joint path with a short tail, joint without a tail, C not a
-# multiple of P, E not a multiple of C, one bucket, a tail only
+# multiple of P, E not a multiple of C, one bucket, a tail only, one full
+# bucket and a tail, 16 ranks
 CASES = [
     (4, 4, 16384, 3 * 16384 + 5001),
     (8, 8, 32768, 2 * 32768 + 12347),
@@ -45,6 +46,8 @@ CASES = [
     (5, 5, 4104, 4 * 4104 + 3),
     (2, 2, 8192, 8192),
     (4, 8, 65536, 4097),
+    (4, 4, 8192, 8192 + 3001),
+    (16, 16, 16384, 2 * 16384 + 7777),
 ]
 
 
