@@ -40,7 +40,9 @@
 //     second order is the same registers folded from k = 1, selected per
 //     element.  Chunks shorter than a tile go to a one-element-per-lane
 //     kernel.  The tile's chunk comes from 32-bit scalar arithmetic on a
-//     divisor map the host builds per launch;
+//     divisor map the host builds per launch; a launch of several buckets
+//     may end in a second segment (the last, partial bucket) with a map of
+//     its own, chosen per tile by one comparison;
 //   * bf16 inputs are widened exactly (a shift) inside the fold, float32
 //     accumulation throughout, no FMA contraction, subnormals kept.
 #pragma once
