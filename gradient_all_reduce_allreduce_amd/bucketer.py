@@ -78,8 +78,10 @@ class GradBucketer:
         the 4 KiB stagger keeps the P copies the all-reduce reads at the
         same offset from lining up in memory (measured about 1% faster than
         rows exactly a whole number of buckets apart, and about 19% faster
-        than rows that are not 128-byte aligned).  ``dtype``: the element
-        type (default the plan's), e.g. float32 outputs of bf16 gradients."""
+        than rows that are not 128-byte aligned).  Each row is contiguous;
+        the [P, n_buckets * E] view as a whole is not (row stride n_buckets *
+        E + 4096 bytes' worth of elements).  ``dtype``: the element type
+        (default the plan's), e.g. float32 outputs of bf16 gradients."""
         import torch
         dtype = dtype or self.dtype
         cols = max(1, self.n_buckets) * self.bucket_elems
