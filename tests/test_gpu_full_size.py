@@ -141,6 +141,27 @@ def test_vitb16_p8_bf16_fused_sgd_full_size():
     assert torch.equal(w.view(torch.int32), w_after.view(torch.int32))
     assert torch.equal(v.view(torch.int32), v_after.view(torch.int32))
     assert torch.equal(gout2.view(torch.int16), gout.view(torch.int16))
+    # the ZeRO stage 1 step from the same state, bucket by bucket and as one
+    # bucketed call: the same master weights, momentum and bf16 parameters as
+    # the replicated step (stage 1 only partitions the state)
+    for bucketed in (False, True):
+        workloads.torch_normal_(w, sg["w_std"], seed=31)
+        workloads.torch_normal_(v, sg["v_std"], seed=32)
+        params = torch.empty_like(grads)
+        if bucketed:
+            ddp.zero1_sgd_step([grads[r] for r in range(P)], w, v, sg["lr"], sg["mu"],
+                               [params[r] for r in range(P)], "mean", C, bucket_elems=b.bucket_elems)
+        else:
+            for k in range(b.n_buckets):
+                lo, n = k * b.bucket_elems, b.bucket_len(k)
+                ddp.zero1_sgd_step([grads[r, lo:lo + n] for r in range(P)], w[lo:lo + n], v[lo:lo + n],
+                                   sg["lr"], sg["mu"], [params[r, lo:lo + n] for r in range(P)], "mean", C)
+        torch.cuda.synchronize()
+        assert torch.equal(w.view(torch.int32), w_after.view(torch.int32)), bucketed
+        assert torch.equal(v.view(torch.int32), v_after.view(torch.int32)), bucketed
+        wb = w_after.to(torch.bfloat16).view(torch.int16)
+        for r in range(P):
+            assert torch.equal(params[r].view(torch.int16), wb), (bucketed, r)
 
 
 def test_ragged2000_p4_pack_allreduce_unpack_full_size():
