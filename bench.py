@@ -1,6 +1,6 @@
 """Benchmark: the data-parallel gradient all-reduce on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--per-bucket]
 
 Workload (the configuration the headline metric is quoted on): P = 8
 emulated ranks, each holding a ResNet-50-shaped gradient set of 161 fp32
@@ -9,8 +9,8 @@ tensors (25,557,032 parameters) drawn from N(0, 0.01), laid out as views of
 partial tail).  One step all-reduces every bucket with Mean in the chunked
 ring order (8 chunks), every rank receiving its own copy of the result, in
 one bucketed call (each bucket its own ring; one launch holds the 3 full
-buckets as one ring and the tail bucket as a second segment).  The same buckets with one call each are
-timed beside it.
+buckets as one ring and the tail bucket as a second segment).  The same
+buckets with one call each are timed beside it with --per-bucket.
 
 Metric: effective HBM GB/s = algorithmic bytes / time, where the algorithmic
 bytes of one all-reduce of n elements over P ranks are P*n*(s_in + s_out)
@@ -20,10 +20,11 @@ more than the 256 MB last-level cache, and two buffer sets alternate.
 
 Prints one JSON line with the step throughput, the dominant kernel's
 roofline (its launches timed with HIP events on the stream they run on: the
-timed steps consist of nothing but its launches), the one-call-per-bucket
-step (with each bucket's median and minimum launch time from an event pair
-around every launch) and the CPU oracle timed on a bounded sample of the
-same workload.
+timed steps consist of nothing but its launches, so a profiler's average
+over the run is that launch's duration) and the CPU oracle timed on a
+bounded sample of the same workload.  --per-bucket adds the same buckets
+with one call each (with each bucket's median and minimum launch time from
+an event pair around every launch).
 """
 
 import argparse
@@ -509,9 +510,10 @@ def main():
     ap.add_argument("--occupancy-sweep", action="store_true",
                     help="time the fused all-reduce and optimizer step at every cap on resident "
                          "workgroups per CU (the measurements behind the built-in caps)")
-    ap.add_argument("--step-only", action="store_true",
-                    help="time only the step (the bucketed call), without the one-call-per-bucket "
-                         "regions: under a profiler every launch of the kernel is then a step launch")
+    ap.add_argument("--per-bucket", action="store_true",
+                    help="also time the same buckets with one single-bucket call each (adds the "
+                         "one_call_per_bucket object; its launches have another shape, so a "
+                         "profiler's average over the run no longer describes the step's launch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (a kernel of known "
                          "traffic, to scale the memory counters of a profiler run)")
@@ -587,7 +589,7 @@ def main():
 
     for i in range(args.warmup):
         step(i)
-        if not args.step_only:
+        if args.per_bucket:
             bucket_calls(i)
     torch.cuda.synchronize()
 
@@ -617,7 +619,7 @@ def main():
 
     traffic = measured_traffic(int(avg_bytes))
     one_call = None
-    if not args.step_only:
+    if args.per_bucket:
         one_call = one_call_per_bucket(timed, bucket_calls, lens, P, bytes_step, args.steps)
 
     out = {
