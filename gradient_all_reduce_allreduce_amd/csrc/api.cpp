@@ -162,12 +162,14 @@ std::vector<BucketPart> bucket_parts(const ddp::RingLaunch& l, int64_t E) {
     const int64_t full = l.n / E;
     const int64_t tail = l.n - full * E;
     const bool joint = full > 1 && l.chunking % l.P == 0 && E % l.chunking == 0 && full * l.chunking <= INT32_MAX;
-    // The joint ring and the partial last bucket in one launch, each with its
-    // own chunks, when both take the vector path and no tile straddles them.
+    // The joint ring (or a single full bucket) and the partial last bucket in
+    // one launch, each with its own chunks, when both take the vector path
+    // and no tile straddles them.
     const int64_t tile = ddp::ring_tile_elems(l);
-    if (joint && tail > 0 && l.n <= ddp::kMaxLaunchElems && (full * E) % tile == 0 && E / l.chunking >= tile &&
-        (tail + l.chunking - 1) / l.chunking >= tile) {
-        parts.push_back({0, l.n, static_cast<int>(full * l.chunking), full * E, l.chunking});
+    const int64_t first_chunks = joint ? full * l.chunking : l.chunking;
+    if ((joint || full == 1) && tail > 0 && l.n <= ddp::kMaxLaunchElems && (full * E) % tile == 0 &&
+        (E + l.chunking - 1) / l.chunking >= tile && (tail + l.chunking - 1) / l.chunking >= tile) {
+        parts.push_back({0, l.n, static_cast<int>(first_chunks), full * E, l.chunking});
         return parts;
     }
     if (joint) {

@@ -249,8 +249,9 @@ int allreduce_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
  * full buckets are one ring with the same order of additions and go out as
  * one launch, which also carries the partial last bucket (with its own
  * chunks) when all n elements fit one launch (2^29), the full buckets end
- * on a whole workgroup tile and every chunk is at least a tile long;
- * otherwise each bucket is its own launch.
+ * on a whole workgroup tile and every chunk is at least a tile long; a
+ * single full bucket shares a launch with the partial one on the same
+ * size conditions, for any C; otherwise each bucket is its own launch.
  *
  *   bucket_elems  E >= 1, with E * element size a multiple of 16 bytes for
  *                 both element types (every bucket stays 16-byte aligned)

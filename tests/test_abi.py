@@ -239,6 +239,9 @@ def test_buckets_launch_count():
     assert f(8, 8, BF16, BF16, True, 6 * 13_107_200 + 7_924_456, 13_107_200) == 1     # ViT set, fused step
     assert f(3, 6, F32, F32, False, 5 * 6000 + 13, 6000) == 2
     assert f(5, 5, F32, F32, False, 4 * 4104 + 3, 4104) == 5           # E not a multiple of C
+    assert f(4, 4, F32, F32, False, 8192 + 3001, 8192) == 1            # one full bucket and the tail
+    assert f(8, 17, F32, F32, False, 65536 + 9000, 65536) == 1         # ... for any C
+    assert f(4, 4, F32, F32, False, 8192 + 100, 8192) == 2             # tail chunks shorter than a tile
     with pytest.raises(ddp.DdpError):
         f(8, 8, F32, F32, False, 100, 6)                               # misaligned buckets
     with pytest.raises(ddp.DdpError):

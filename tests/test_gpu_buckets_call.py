@@ -47,6 +47,7 @@ CASES = [
     (2, 2, 8192, 8192),
     (4, 8, 65536, 4097),
     (4, 4, 8192, 8192 + 3001),
+    (8, 17, 65536, 65536 + 9000),
     (16, 16, 16384, 2 * 16384 + 7777),
 ]
 
