@@ -68,6 +68,48 @@ def test_ddp_step_with_bucket_views_and_fused_sgd():
         assert torch.allclose(v, want, rtol=0, atol=1e-6), float((v - want).abs().max())
 
 
+def test_no_sync_accumulation_then_one_bucketed_all_reduce():
+    """Gradient accumulation without synchronization ("Distributed
+    Training", DDP's no_sync): every rank runs backward on two micro-batches
+    into the same bucket views, with no all-reduce in between, and the
+    accumulated gradients then go through one bucketed all-reduce with
+    Mean.  Bit for bit the oracle's ring over the accumulated gradients of
+    every bucket, and within float32 rounding of the full-batch gradient of
+    the mean micro-batch loss."""
+    W, B, M = 4, 64, 2
+    torch.manual_seed(5)
+    net = torch.nn.Sequential(torch.nn.Linear(32, 128), torch.nn.Tanh(), torch.nn.Linear(128, 10)).to(DEV)
+    params = list(net.parameters())
+    g = torch.Generator(device=DEV).manual_seed(6)
+    X = torch.randn(M, B, 32, device=DEV, generator=g)
+    y = torch.randint(0, 10, (M, B), device=DEV, generator=g)
+    plan = ddp.GradBucketer([tuple(p.shape) for p in params], torch.float32, 8 << 10, device=DEV)
+    assert plan.n_buckets > 2
+    arena = plan.alloc_arena(W)
+    arena.zero_()
+    for r in range(W):
+        views = plan.tensor_views(arena[r])
+        for p, v in zip(params, views):
+            p.grad = v
+        for mb in range(M):                 # no all-reduce between micro-batches
+            (F.cross_entropy(net(X[mb, r::W]), y[mb, r::W]) / M).backward()
+    rows = [arena[r, :plan.total] for r in range(W)]
+    before = np.stack([x.cpu().numpy() for x in rows])
+    ddp.allreduce(rows, "mean", W, out=rows, bucket_elems=plan.bucket_elems)
+    torch.cuda.synchronize()
+    got = np.stack([x.cpu().numpy() for x in rows])
+    E = plan.bucket_elems
+    for k in range(plan.n_buckets):
+        lo, n = k * E, plan.bucket_len(k)
+        want, _ = oracle.ring_allreduce(before[:, lo:lo + n], "mean", W)
+        assert_same_bits(got[:, lo:lo + n], want, f"bucket {k}")
+    net.zero_grad(set_to_none=True)
+    for mb in range(M):
+        (F.cross_entropy(net(X[mb]), y[mb]) / M).backward()
+    for p, v in zip(params, plan.tensor_views(rows[0])):
+        assert torch.allclose(v, p.grad, rtol=0, atol=1e-6), float((v - p.grad).abs().max())
+
+
 def test_synchronized_batchnorm_statistics():
     """Per-channel sums and sums of squares of W shards, all-reduced as two
     small tensors in one launch, give the whole batch's statistics."""
