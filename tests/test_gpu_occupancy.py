@@ -41,6 +41,21 @@ def test_ring_same_bits_at_every_cap(pair):
         assert_same_bits(to_host(out), want, f"{it}->{ot} cap={cap}")
 
 
+def test_bucketed_call_same_bits_at_every_cap():
+    """The bucketed call (the full buckets as one ring and the partial one
+    as a second segment, one launch) at every cap."""
+    P, C, E = 8, 8, 32768
+    n = 3 * E + 12347
+    X = draw(P, n, "f32", seed=47)
+    want = np.concatenate([oracle_ring(X[:, lo:lo + E], "mean", C) for lo in range(0, n, E)], axis=1)
+    assert ddp.ddp_buckets_launch_count(P, C, ddp.F32, ddp.F32, False, n, E) == 1
+    for cap in CAPS:
+        ddp.ddp_set_wg_per_cu("ring", cap)
+        out = ddp.allreduce(to_device(X, "f32"), "mean", C, bucket_elems=E)
+        torch.cuda.synchronize()
+        assert_same_bits(to_host(out), want, f"cap={cap}")
+
+
 def test_fused_sgd_same_bits_at_every_cap():
     P, n, C = 8, 200_003, 8
     G = draw(P, n, "bf16", seed=42)
