@@ -617,6 +617,18 @@ def main():
     avg_bytes = bytes_step / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
 
+    # Per-step spread: the same K steps again with an event pair around
+    # each (the pairs add about 2 us per step); the same launches only.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+
     traffic = measured_traffic(int(avg_bytes))
     one_call = None
     if args.per_bucket:
@@ -659,6 +671,12 @@ def main():
             "launches_per_step": launches_per_step,
             "algorithmic_bytes_per_launch": int(avg_bytes),
             "timing": "events around the timed steps, which hold only this kernel's launches",
+        },
+        "per_step": {
+            "median_ms": round(float(np.median(step_ms)), 4),
+            "min_ms": round(step_ms[0], 4),
+            "max_ms": round(step_ms[-1], 4),
+            "note": "an event pair around every step (about 2 us each), a second pass of K steps",
         },
         "one_call_per_bucket": one_call,
         "cpu_baseline": None,
