@@ -444,8 +444,8 @@ class MultiAllReduce:
         """Validate the tensors once and upload their pointer tables; returns
         a launcher ``run(op="sum", chunking=None)`` that enqueues the whole
         multi-tensor all-reduce with one call on the stream current at that
-        call.  The tensors (and ``out``, default: new tensors) must stay
-        alive while the launcher is used."""
+        call.  The launcher keeps the bound tensors (and ``out``, default:
+        new tensors) alive; it always reduces those same tensors."""
         import torch
         if out is None:
             out = [[torch.empty(s, dtype=self.out_dtype, device=self.device) for s in self.shapes]
@@ -465,8 +465,14 @@ class MultiAllReduce:
 
         # The launcher holds raw device addresses: it must own every table
         # they point into, the tile plan included, so that it stays valid
-        # after this object is dropped (``MultiAllReduce(...).bind(...)``).
+        # after this object is dropped (``MultiAllReduce(...).bind(...)``),
+        # and every tensor whose address a table holds, so that a tensor
+        # the caller drops (e.g. a gradient replaced by zero_grad(set_to_none=
+        # True)) is never freed and reused while the launcher can still
+        # write it.  The launcher reduces exactly the tensors it was bound
+        # to; new gradient tensors need a new bind().
         run.tables = tables
+        run.tensors = (rank_lists, out)
         run.out = out
         return run
 
@@ -502,7 +508,8 @@ class MultiAllReduce:
                                       torch_dtype_code(self.out_dtype), _stream_for(tables))
             return out
 
-        run.tables = tables   # owned by the launcher, as in bind()
+        run.tables = tables                    # owned by the launcher, as in bind()
+        run.tensors = (rank_grads, w, v, out)  # every tensor the tables point to
         return run
 
     def __call__(self, rank_lists, op="sum", chunking=None, out=None):

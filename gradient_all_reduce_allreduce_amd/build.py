@@ -1,6 +1,11 @@
 """Compile the HIP library ``libddp_allreduce.so`` in-tree for gfx950.
 
-    python -m gradient_all_reduce_allreduce_amd.build
+    python -m gradient_all_reduce_allreduce_amd.build              # the library
+    python -m gradient_all_reduce_allreduce_amd.build --patterns   # hbm_patterns only
+
+The HBM access-pattern benchmark (``csrc/hbm_patterns.hip``, a standalone
+measurement program, not part of the library) has its own command, so that
+the library build never depends on it.
 
 Every source is compiled by hipcc for gfx950 only, with
   -ffp-contract=off      no fused multiply-add anywhere (results are defined
@@ -45,22 +50,24 @@ def _compile(src):
     return obj
 
 
-def _compile_patterns():
+def build_patterns(verbose=False):
+    """Compile the HBM access-pattern benchmark to ``hbm_patterns``."""
     cmd = [HIPCC, *COMMON, *DEVICE, os.path.join(CSRC, "hbm_patterns.hip"), "-o",
            PATTERNS + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(PATTERNS + ".tmp", PATTERNS)
+    if verbose:
+        print(f"built {PATTERNS}")
+    return PATTERNS
 
 
 def build(verbose=False):
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        patterns = ex.submit(_compile_patterns)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
-        patterns.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,5 +80,8 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--patterns" in sys.argv[1:]:
+        build_patterns(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -521,3 +521,39 @@ def test_multi_launcher_owns_its_tables(monkeypatch):
         del run
         gc.collect()
         assert plan() is None, bind
+
+
+def test_multi_launcher_keeps_bound_tensors_alive(monkeypatch):
+    """The launcher's device tables hold the raw addresses of the bound
+    gradients, outputs and optimizer state: the launcher must keep every one
+    of those tensors alive, so that dropping the caller's references (as
+    zero_grad(set_to_none=True) does for gradients) cannot free memory the
+    next launch would read or write."""
+    import gc
+    import weakref
+
+    import torch
+
+    from gradient_all_reduce_allreduce_amd import api
+
+    monkeypatch.setattr(api, "current_stream", lambda device: None)
+    shapes = [(3,), (70,), (5, 4)]
+    for bind in ("bind", "bind_sgd"):
+        m = api.MultiAllReduce(shapes, 2, torch.float32, device="cpu")
+        ts = [[torch.zeros(s) for s in shapes] for _ in range(2)]
+        out = [[torch.zeros(s) for s in shapes] for _ in range(2)]
+        w = [torch.zeros(s) for s in shapes]
+        v = [torch.zeros(s) for s in shapes]
+        bound = [x for lst in ts + out for x in lst]
+        if bind == "bind":
+            run = m.bind(ts, out=out)
+        else:
+            run = m.bind_sgd(ts, w, v, out=out)
+            bound += w + v
+        refs = [weakref.ref(x) for x in bound]
+        del ts, out, w, v, bound, m
+        gc.collect()
+        assert all(r() is not None for r in refs), bind
+        del run
+        gc.collect()
+        assert all(r() is None for r in refs), bind

@@ -19,7 +19,6 @@ import os
 import numpy as np
 import torch
 import torch.nn.functional as F
-from torch.utils.data import DistributedSampler
 
 import oracle
 
@@ -43,20 +42,20 @@ def data(dtype):
     return X, y
 
 
-def flat_grad(net):
-    return torch.cat([p.grad.reshape(-1) for p in net.parameters()]).clone()
+def loss_gradient(net, X, y):
+    """Gradient of the mean cross-entropy over (X, y) with respect to every
+    parameter, concatenated in parameter order (torch.autograd.grad, so no
+    .grad state is kept between calls)."""
+    params = list(net.parameters())
+    loss = F.cross_entropy(net(X), y)
+    return torch.cat([g.reshape(-1) for g in torch.autograd.grad(loss, params)]).detach()
 
 
-def grad(net, X, y):
-    net.zero_grad()
-    F.cross_entropy(net(X), y).backward()
-    return flat_grad(net)
-
-
-def shards():
-    ds = list(range(B))
-    return [list(DistributedSampler(ds, num_replicas=W, rank=r, shuffle=False))
-            for r in range(W)]
+def shard_gradients(net, X, y):
+    """(W, n) gradients of the W equal shards.  Rank r takes samples r,
+    r + W, r + 2W, ... -- the split an unshuffled distributed sampler gives
+    when W divides the batch."""
+    return np.stack([loss_gradient(net, X[r::W], y[r::W]).numpy() for r in range(W)])
 
 
 def rel(a, b):
@@ -74,8 +73,8 @@ def test_ring_mean_of_shards_is_full_batch_gradient_float64(golden_dir):
     printed = _printed(golden_dir)
     net = make_mlp(torch.float64)
     X, y = data(torch.float64)
-    g_full = grad(net, X, y).numpy()
-    G = np.stack([grad(net, X[i], y[i]).numpy() for i in shards()])
+    g_full = loss_gradient(net, X, y).numpy()
+    G = shard_gradients(net, X, y)
     Y, _ = oracle.ring_allreduce(G, "mean", W, in_dtype="f64")
     for r in range(W):
         d = rel(Y[r], g_full)
@@ -88,8 +87,8 @@ def test_ring_mean_of_shards_is_full_batch_gradient_float32(golden_dir):
     printed = _printed(golden_dir)
     net = make_mlp(torch.float32)
     X, y = data(torch.float32)
-    g_full = grad(net, X, y).numpy()
-    G = np.stack([grad(net, X[i], y[i]).numpy() for i in shards()])
+    g_full = loss_gradient(net, X, y).numpy()
+    G = shard_gradients(net, X, y)
     Y, _ = oracle.ring_allreduce(G, "mean", W)
     d = rel(Y[0], g_full)
     assert d < 100 * printed["rel_diff_float32"], d
@@ -100,8 +99,8 @@ def test_sum_without_division_is_exactly_W_times(golden_dir):
     printed = _printed(golden_dir)
     net = make_mlp(torch.float64)
     X, y = data(torch.float64)
-    g_full = grad(net, X, y).numpy()
-    G = np.stack([grad(net, X[i], y[i]).numpy() for i in shards()])
+    g_full = loss_gradient(net, X, y).numpy()
+    G = shard_gradients(net, X, y)
     Y, _ = oracle.ring_allreduce(G, "sum", W, in_dtype="f64")
     ratio = np.linalg.norm(Y[0]) / np.linalg.norm(g_full)
     assert f"{ratio:.12f}" == printed["accumulation_without_division_norm_ratio"]
@@ -112,7 +111,7 @@ def test_replicas_stay_identical_after_local_momentum_step():
     rank steps its own optimizer and the weights stay in sync."""
     net = make_mlp(torch.float32)
     X, y = data(torch.float32)
-    G = np.stack([grad(net, X[i], y[i]).numpy() for i in shards()])
+    G = shard_gradients(net, X, y)
     w0 = torch.cat([p.detach().reshape(-1) for p in net.parameters()]).numpy()
     Y, _ = oracle.ring_allreduce(G, "mean", W)
     states = [oracle.sgd_momentum(Y[r], w0, np.zeros_like(w0), 1e-3, 0.9)
