@@ -57,10 +57,10 @@ _SIGNATURES = {
         ctypes.POINTER(ctypes.c_uint64)]),
     "ddp_bucket_pack": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-        ctypes.c_int32, _c_void_pp, ctypes.c_int64, ctypes.c_void_p]),
+        ctypes.c_int32, _c_void_pp, _c_void_pp, ctypes.c_int64, ctypes.c_void_p]),
     "ddp_bucket_unpack": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-        ctypes.c_int32, _c_void_pp, ctypes.c_int64, ctypes.c_void_p]),
+        ctypes.c_int32, _c_void_pp, _c_void_pp, ctypes.c_int64, ctypes.c_void_p]),
     "allreduce_ring_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
         ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),

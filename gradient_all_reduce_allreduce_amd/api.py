@@ -80,15 +80,40 @@ def ddp_bucket_plan(numels, dtype, bucket_bytes):
     return segs, n_buckets.value, total.value, fp.value
 
 
-def ddp_bucket_pack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors, rank_bucket,
-                    bucket_len, stream=None):
-    _check(N.lib().ddp_bucket_pack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors,
+def _host_addr(x, dtype=None):
+    """Address of a host array: a numpy array (converted to ``dtype`` if
+    given), a ctypes object or an int address; None stays NULL."""
+    if x is None or isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        if dtype is not None and x.dtype != dtype:
+            raise TypeError(f"expected a {dtype} array, got {x.dtype}")
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("host arrays must be contiguous")
+        return x.ctypes.data
+    return ctypes.addressof(x)
+
+
+def _ptr_array(ptrs):
+    if isinstance(ptrs, ctypes.Array):
+        return ptrs
+    return N.pointer_array(ptrs)
+
+
+def ddp_bucket_pack(P, dtype, segs, n_segs, numels, n_tensors, tensor_ptrs, rank_bucket, bucket_len,
+                    stream=None):
+    """segs: the bucket's segments (a SEGMENT_DTYPE numpy array or a host
+    address); numels: int64 numpy array (or address); tensor_ptrs: P *
+    n_tensors device addresses, rank-major (a list or a ctypes array)."""
+    _check(N.lib().ddp_bucket_pack(P, dtype, _host_addr(segs, SEGMENT_DTYPE), n_segs,
+                                   _host_addr(numels, np.int64), n_tensors, _ptr_array(tensor_ptrs),
                                    N.pointer_array(rank_bucket), bucket_len, stream))
 
 
-def ddp_bucket_unpack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors, rank_bucket,
-                      bucket_len, stream=None):
-    _check(N.lib().ddp_bucket_unpack(P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors,
+def ddp_bucket_unpack(P, dtype, segs, n_segs, numels, n_tensors, tensor_ptrs, rank_bucket, bucket_len,
+                      stream=None):
+    _check(N.lib().ddp_bucket_unpack(P, dtype, _host_addr(segs, SEGMENT_DTYPE), n_segs,
+                                     _host_addr(numels, np.int64), n_tensors, _ptr_array(tensor_ptrs),
                                      N.pointer_array(rank_bucket), bucket_len, stream))
 
 

@@ -4,9 +4,9 @@ DDP packs gradients into buckets (25 MB by default), filled in the reverse
 order of the parameters, and every rank reduces the buckets in the same
 order ("Distributed Training", "Data parallelism and all-reduce").  The plan
 comes from the library's ``ddp_bucket_plan``; pack and unpack run as HIP
-kernels for all P ranks in one launch each.  This class only owns the
-torch-allocated tables the kernels read (the device copy of the segment
-table and the per-rank tensor pointer tables).
+kernels for all P ranks per launch.  The library checks each bucket's
+segments and the tensors' addresses on the host before launching; this
+class only holds the plan and the tensor address tables it passes.
 """
 
 import math
@@ -35,10 +35,8 @@ class GradBucketer:
                                for b in range(nb)]
         first = np.searchsorted(segs["bucket"], np.arange(nb + 1), side="left")
         self._seg_first = [int(x) for x in first]
+        self._numels = np.ascontiguousarray(self.numels, dtype=np.int64)
         self.device = torch.device(device)
-        self.segs_dev = None
-        if segs.size:
-            self.segs_dev = torch.from_numpy(segs.view(np.uint8).copy()).to(self.device)
 
     def bucket_len(self, b):
         return self.bucket_lengths[b]
@@ -59,11 +57,11 @@ class GradBucketer:
                     raise ValueError(f"rank {r} tensor {t} does not match the plan")
 
     def pointer_table(self, rank_tensors):
-        """Device table [P * T] of the tensors' addresses, rank-major."""
-        import torch
+        """Host table [P * T] of the tensors' device addresses, rank-major,
+        checked against the plan once.  The table keeps the tensors alive;
+        pack and unpack always copy to and from these same tensors."""
         self.check_rank_tensors(rank_tensors)
-        ptrs = [x.data_ptr() for ts in rank_tensors for x in ts]
-        return torch.tensor(ptrs, dtype=torch.int64).to(self.device)
+        return TensorTable(rank_tensors, self.device)
 
     # Extra distance between consecutive rank rows of an arena, in bytes.
     ROW_STAGGER = 4096
@@ -112,41 +110,47 @@ class GradBucketer:
         return [torch.empty(self.bucket_elems, dtype=self.dtype, device=self.device)
                 for _ in range(P)]
 
-    def _seg_ptr(self, b):
-        first, count = self.segment_range(b)
-        return self.segs_dev.data_ptr() + first * api.SEGMENT_DTYPE.itemsize, count
-
     def _check_copy(self, table, b, rank_buckets):
-        """The kernels read P * T table entries and bucket_len(b) elements of
-        every bucket buffer: both are checked here, since the library cannot
-        read device tables on the host."""
-        import torch
+        """The table must be this plan's, for as many ranks as buckets given;
+        every bucket buffer a contiguous tensor of at least bucket_len(b)
+        elements.  (The library checks the segments and addresses.)"""
         if not 0 <= b < self.n_buckets:
             raise ValueError(f"bucket {b} outside 0..{self.n_buckets - 1}")
         P = len(rank_buckets)
-        if table.dtype != torch.int64 or table.numel() != P * len(self.shapes) \
-                or table.device != self.device or not table.is_contiguous():
-            raise ValueError("pointer table must be the int64 device table of P ranks' tensors "
-                             "(pointer_table)")
+        if not isinstance(table, TensorTable) or table.P != P or table.T != len(self.shapes) \
+                or table.device != self.device:
+            raise ValueError("pointer table must come from pointer_table() for these P ranks")
         for r, x in enumerate(rank_buckets):
             if x.dtype != self.dtype or x.device != self.device or not x.is_contiguous() \
                     or x.numel() < self.bucket_len(b):
                 raise ValueError(f"rank {r}: bucket buffer must be a contiguous {self.dtype} tensor "
                                  f"of at least {self.bucket_len(b)} elements on {self.device}")
 
-    def pack(self, table, b, rank_buckets):
-        """Gather bucket b of every rank (pointer table from ``pointer_table``)
-        into ``rank_buckets`` on the current stream."""
+    def _copy(self, fn, table, b, rank_buckets):
         self._check_copy(table, b, rank_buckets)
-        ptr, count = self._seg_ptr(b)
-        api.ddp_bucket_pack(len(rank_buckets), self.code, ptr, count, table.data_ptr(),
-                            len(self.shapes), [x.data_ptr() for x in rank_buckets],
-                            self.bucket_len(b), api.current_stream(self.device))
+        first, count = self.segment_range(b)
+        fn(len(rank_buckets), self.code, self.segments[first:first + count], count, self._numels,
+           len(self.shapes), table.ptrs, [x.data_ptr() for x in rank_buckets], self.bucket_len(b),
+           api.current_stream(self.device))
+
+    def pack(self, table, b, rank_buckets):
+        """Gather bucket b of every rank (tensors of ``pointer_table``) into
+        ``rank_buckets`` on the current stream."""
+        self._copy(api.ddp_bucket_pack, table, b, rank_buckets)
 
     def unpack(self, table, b, rank_buckets):
         """Scatter bucket b of every rank back into its tensors."""
-        self._check_copy(table, b, rank_buckets)
-        ptr, count = self._seg_ptr(b)
-        api.ddp_bucket_unpack(len(rank_buckets), self.code, ptr, count, table.data_ptr(),
-                              len(self.shapes), [x.data_ptr() for x in rank_buckets],
-                              self.bucket_len(b), api.current_stream(self.device))
+        self._copy(api.ddp_bucket_unpack, table, b, rank_buckets)
+
+
+class TensorTable:
+    """The device addresses of P ranks' T tensors as one host array
+    (rank-major), with the tensors it points to kept alive."""
+
+    def __init__(self, rank_tensors, device):
+        import ctypes
+        self.P = len(rank_tensors)
+        self.T = len(rank_tensors[0]) if rank_tensors else 0
+        self.device = device
+        self.tensors = [list(ts) for ts in rank_tensors]
+        self.ptrs = (ctypes.c_void_p * (self.P * self.T))(*[x.data_ptr() for ts in rank_tensors for x in ts])

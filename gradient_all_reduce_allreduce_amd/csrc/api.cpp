@@ -6,6 +6,7 @@
 // succeeds, so every error path can be exercised on a machine without a GPU.
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -14,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "launch.h"
@@ -296,8 +298,11 @@ int ddp_bucket_plan(const int64_t* numels, int32_t n_tensors, ddp_dtype dtype, i
     return ok();
 }
 
-static int bucket_copy(bool pack, int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
-                       int64_t n_segs, const void* const* tensor_ptrs_dev, int32_t n_tensors,
+// Pack and unpack: every argument is checked on the host before anything
+// is launched, the segment table included, and the kernels read nothing but
+// what was checked (the table travels in the kernel arguments).
+static int bucket_copy(bool pack, int32_t P, ddp_dtype dtype, const ddp_segment* segs, int64_t n_segs,
+                       const int64_t* numels, int32_t n_tensors, const void* const* tensor_ptrs,
                        const void* const* rank_bucket, int64_t bucket_len, void* stream) {
     int s = check_ranks(P);
     if (s) return s;
@@ -305,12 +310,60 @@ static int bucket_copy(bool pack, int32_t P, ddp_dtype dtype, const ddp_segment*
     if (int e = check_length(bucket_len, "bucket_len")) return e;
     if (n_segs < 0) return fail(DDP_E_ARG, "n_segs is negative");
     if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
-    if (bucket_len > 0 && n_segs == 0) return fail(DDP_E_PLAN, "a non-empty bucket needs segments");
-    if (n_segs > bucket_len) return fail(DDP_E_PLAN, "more segments than bucket elements");
-    if (bucket_len > 0 && (segs_dev == nullptr || tensor_ptrs_dev == nullptr))
-        return fail(DDP_E_ARG, "segment table or tensor pointer table is NULL");
+    if (numels == nullptr) return fail(DDP_E_ARG, "numels is NULL");
+    for (int32_t t = 0; t < n_tensors; ++t)
+        if (numels[t] < 0 || numels[t] > kMaxElems) return fail(DDP_E_ARG, "numels[%d] outside 0..2^40", t);
     if ((s = check_ptr_array(rank_bucket, P, "rank_bucket"))) return s;
     const int es = elem_bytes(dtype);
+
+    // The segments must tile [0, bucket_len) in order, all with one bucket
+    // index, each a non-empty piece inside its tensor.
+    if (n_segs > 0 && segs == nullptr) return fail(DDP_E_ARG, "segs is NULL");
+    if (bucket_len > 0 && n_segs == 0) return fail(DDP_E_PLAN, "a non-empty bucket needs segments");
+    int64_t pos = 0;
+    for (int64_t k = 0; k < n_segs; ++k) {
+        const ddp_segment& g = segs[k];
+        if (g.bucket != segs[0].bucket)
+            return fail(DDP_E_PLAN, "segment %lld belongs to bucket %d, segment 0 to bucket %d",
+                        static_cast<long long>(k), g.bucket, segs[0].bucket);
+        if (g.tensor < 0 || g.tensor >= n_tensors)
+            return fail(DDP_E_PLAN, "segment %lld names tensor %d of %d", static_cast<long long>(k), g.tensor,
+                        n_tensors);
+        if (g.len < 1) return fail(DDP_E_PLAN, "segment %lld is empty", static_cast<long long>(k));
+        if (g.dst_off != pos)
+            return fail(DDP_E_PLAN, "segment %lld starts at %lld, the previous one ends at %lld",
+                        static_cast<long long>(k), static_cast<long long>(g.dst_off), static_cast<long long>(pos));
+        if (g.src_off < 0 || g.len > numels[g.tensor] || g.src_off > numels[g.tensor] - g.len)
+            return fail(DDP_E_PLAN, "segment %lld reads [%lld, %lld) of tensor %d, which holds %lld elements",
+                        static_cast<long long>(k), static_cast<long long>(g.src_off),
+                        static_cast<long long>(g.src_off + g.len), g.tensor,
+                        static_cast<long long>(numels[g.tensor]));
+        if (g.len > bucket_len - pos)
+            return fail(DDP_E_PLAN, "segment %lld ends past the bucket's %lld elements", static_cast<long long>(k),
+                        static_cast<long long>(bucket_len));
+        pos += g.len;
+    }
+    if (pos != bucket_len)
+        return fail(DDP_E_PLAN, "the segments cover %lld of the bucket's %lld elements", static_cast<long long>(pos),
+                    static_cast<long long>(bucket_len));
+    if (bucket_len == 0) return ok();
+
+    // The tensors the segments touch: non-null, aligned to the element size.
+    if (tensor_ptrs == nullptr) return fail(DDP_E_ARG, "tensor_ptrs is NULL");
+    for (int64_t k = 0; k < n_segs; ++k) {
+        for (int r = 0; r < P; ++r) {
+            const void* t = tensor_ptrs[static_cast<int64_t>(r) * n_tensors + segs[k].tensor];
+            if (t == nullptr) return fail(DDP_E_ARG, "tensor_ptrs[rank %d, tensor %d] is NULL", r, segs[k].tensor);
+            if (reinterpret_cast<uintptr_t>(t) % es)
+                return fail(DDP_E_ALIGN, "tensor_ptrs[rank %d, tensor %d] is not aligned to its element size", r,
+                            segs[k].tensor);
+        }
+    }
+
+    // What the copy writes must overlap nothing it reads or writes
+    // elsewhere: the buckets are pairwise disjoint, no tensor piece
+    // overlaps a bucket, and unpack's pieces (its destinations) are
+    // pairwise disjoint.
     std::vector<Buf> bufs;
     add_rank_bufs(bufs, rank_bucket, P, bucket_len, es, "rank_bucket");
     for (size_t i = 0; i < bufs.size(); ++i)
@@ -318,37 +371,86 @@ static int bucket_copy(bool pack, int32_t P, ddp_dtype dtype, const ddp_segment*
             if (bufs[i].lo < bufs[j].hi && bufs[j].lo < bufs[i].hi)
                 return fail(DDP_E_OVERLAP, "rank_bucket[%d] and rank_bucket[%d] overlap", bufs[i].index,
                             bufs[j].index);
-    if (bucket_len == 0) return ok();
+    std::vector<std::pair<uintptr_t, uintptr_t>> pieces;
+    pieces.reserve(static_cast<size_t>(n_segs) * P);
+    for (int64_t k = 0; k < n_segs; ++k) {
+        for (int r = 0; r < P; ++r) {
+            const uintptr_t t =
+                reinterpret_cast<uintptr_t>(tensor_ptrs[static_cast<int64_t>(r) * n_tensors + segs[k].tensor]);
+            const uintptr_t lo = t + static_cast<uintptr_t>(segs[k].src_off) * es;
+            const uintptr_t hi = lo + static_cast<uintptr_t>(segs[k].len) * es;
+            for (const Buf& b : bufs)
+                if (lo < b.hi && b.lo < hi)
+                    return fail(DDP_E_OVERLAP, "rank %d's piece of tensor %d overlaps rank_bucket[%d]", r,
+                                segs[k].tensor, b.index);
+            pieces.push_back({lo, hi});
+        }
+    }
+    if (!pack) {
+        std::sort(pieces.begin(), pieces.end());
+        for (size_t i = 1; i < pieces.size(); ++i)
+            if (pieces[i].first < pieces[i - 1].second)
+                return fail(DDP_E_OVERLAP, "two tensor pieces that unpack writes overlap");
+    }
 
-    ddp::CopyLaunch l{};
-    l.P = P;
-    l.elem_bytes = es;
-    l.pack = pack ? 1 : 0;
-    l.segs = segs_dev;
-    l.n_segs = n_segs;
-    l.tensors = tensor_ptrs_dev;
-    l.n_tensors = n_tensors;
-    for (int r = 0; r < P; ++r) l.bucket[r] = const_cast<void*>(rank_bucket[r]);
-    l.bucket_len = bucket_len;
-    l.stream = stream;
-    const char* msg = nullptr;
-    const int e = ddp::launch_bucket_copy(l, &msg);
-    if (e != 0) return hip_fail(e, msg);
+    // Launches over consecutive ranges [A, B) of the bucket, each holding at
+    // most copy_segments_per_launch(P) segments.  Every range but the last
+    // ends on a 16-byte boundary of the bucket; the first segment of a
+    // range may have begun in the previous one.
+    const int per_launch = ddp::copy_segments_per_launch(P);
+    const int64_t ve = 16 / es;
+    int64_t A = 0;
+    int64_t f = 0;   // the segment holding element A
+    while (A < bucket_len) {
+        int64_t B = bucket_len;
+        if (n_segs - f > per_launch || bucket_len - A > ddp::kCopyMaxLaunchElems) {
+            int64_t lim = A + ddp::kCopyMaxLaunchElems;
+            if (f + per_launch < n_segs && segs[f + per_launch].dst_off < lim) lim = segs[f + per_launch].dst_off;
+            // lim >= A + per_launch (segments are non-empty) and per_launch
+            // > ve, so the vector boundary below lies past A.
+            B = lim / ve * ve;
+            if (B <= A) return fail(DDP_E_PLAN, "internal: empty copy range");
+        }
+        ddp::CopyLaunch l{};
+        l.P = P;
+        l.elem_bytes = es;
+        l.pack = pack ? 1 : 0;
+        l.len = static_cast<int32_t>(B - A);
+        for (int r = 0; r < P; ++r) l.bucket[r] = static_cast<char*>(const_cast<void*>(rank_bucket[r])) + A * es;
+        int n = 0;
+        for (int64_t k = f; k < n_segs && segs[k].dst_off < B; ++k, ++n) {
+            const int64_t first = segs[k].dst_off > A ? segs[k].dst_off : A;
+            l.start[n] = static_cast<int32_t>(first - A);
+            const int64_t src = segs[k].src_off + (first - segs[k].dst_off);
+            for (int r = 0; r < P; ++r)
+                l.piece[n * P + r] = static_cast<char*>(const_cast<void*>(
+                                         tensor_ptrs[static_cast<int64_t>(r) * n_tensors + segs[k].tensor])) +
+                                     src * es;
+        }
+        if (n < 1 || n > per_launch) return fail(DDP_E_PLAN, "internal: %d segments in one copy launch", n);
+        l.n_segs = n;
+        l.stream = stream;
+        const char* msg = nullptr;
+        const int e = ddp::launch_bucket_copy(l, &msg);
+        if (e != 0) return hip_fail(e, msg);
+        A = B;
+        while (f < n_segs && segs[f].dst_off + segs[f].len <= A) ++f;
+    }
     return ok();
 }
 
-int ddp_bucket_pack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev, int64_t n_segs,
-                    const void* const* tensor_ptrs_dev, int32_t n_tensors, void* const* rank_bucket,
+int ddp_bucket_pack(int32_t P, ddp_dtype dtype, const ddp_segment* segs, int64_t n_segs, const int64_t* numels,
+                    int32_t n_tensors, const void* const* tensor_ptrs, void* const* rank_bucket,
                     int64_t bucket_len, void* stream) {
-    return bucket_copy(true, P, dtype, segs_dev, n_segs, tensor_ptrs_dev, n_tensors,
+    return bucket_copy(true, P, dtype, segs, n_segs, numels, n_tensors, tensor_ptrs,
                        const_cast<const void* const*>(rank_bucket), bucket_len, stream);
 }
 
-int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev, int64_t n_segs,
-                      void* const* tensor_ptrs_dev, int32_t n_tensors, const void* const* rank_bucket,
+int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs, int64_t n_segs, const int64_t* numels,
+                      int32_t n_tensors, void* const* tensor_ptrs, const void* const* rank_bucket,
                       int64_t bucket_len, void* stream) {
-    return bucket_copy(false, P, dtype, segs_dev, n_segs, const_cast<const void* const*>(tensor_ptrs_dev),
-                       n_tensors, rank_bucket, bucket_len, stream);
+    return bucket_copy(false, P, dtype, segs, n_segs, numels, n_tensors, const_cast<const void* const*>(tensor_ptrs),
+                       rank_bucket, bucket_len, stream);
 }
 
 int allreduce_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,

@@ -17,6 +17,13 @@
 //   read8       8 input streams, 25 MiB each
 //   write8      8 output streams
 //   copy        1 input stream -> 1 output stream, 200 MiB each
+//   bcast 1 -> 7  the all-gather's pattern: 1 input stream, each tile
+//               stored to 7 of the 8 output streams (25 MiB each)
+//   LDS-staged  the all-reduce's pattern with the inputs brought into LDS
+//               by direct global -> LDS loads, 1, 2 or 4 tiles per
+//               workgroup (the next tile's loads in flight while one is
+//               folded), float32 and bf16 -> float32; checked bit for bit
+//               against the register kernels
 //   red8 f32    the all-reduce's own pattern: 8 input streams summed into 8
 //               identical output streams, 25 MiB each (the 16 buffers back to
 //               back in one allocation)
@@ -183,10 +190,77 @@ __global__ __launch_bounds__(kW) void sgd_kernel(SgdStreams p, uint32_t* sink) {
     }
 }
 
+// The all-reduce's pattern with the input tiles staged in LDS by direct
+// global -> LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at
+// the wave's LDS base + 16 i), then read back to registers, folded and
+// stored as above.  T tiles per workgroup: the loads of tile t + 1 are
+// issued (into the other LDS buffer) before tile t is folded and stored.
+// The compiler does not order reads of LDS after these loads on its own,
+// so every read waits explicitly for the vector memory counter to drain
+// (loads and stores share that counter on this chip and may complete out
+// of order with each other, so only vmcnt(0) is safe); the empty asm
+// also keeps the LDS reads below the wait.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* gbl_ptr;
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ES_IN 4: float32 inputs, a 64-lane tile of 4 elements per lane; ES_IN 2:
+// bf16 inputs, 8 elements per lane (the direct loads move 16 bytes per
+// lane), float32 outputs in two 16-byte stores per lane and stream.
+template <int T, int ES_IN>
+__global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink) {
+    constexpr int VE = 16 / ES_IN;                  // elements per lane and tile
+    __shared__ u32x4 buf[T > 1 ? 2 : 1][8][kW];
+    const uint32_t lane = threadIdx.x;
+    const uint32_t tile0 = blockIdx.x * T;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        __builtin_amdgcn_global_load_lds((gbl_ptr)(p.in[r] + (tile0 * kW + lane) * 16u), (lds_ptr)&buf[0][r][0], 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        wait_vm_all();
+        u32x4 x[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[r] = buf[t & 1][r][lane];
+        if (t + 1 < T) {
+            // the LDS reads above complete before the next loads overwrite
+            // the other buffer's previous contents (read two tiles ago)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                __builtin_amdgcn_global_load_lds((gbl_ptr)(p.in[r] + ((tile0 + t + 1) * kW + lane) * 16u),
+                                                 (lds_ptr)&buf[(t + 1) & 1][r][0], 16, 0, 0);
+        }
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t w = ES_IN == 4 ? x[r][e] : x[r][e >> 1];
+                const float v = ES_IN == 4 ? __uint_as_float(w) : __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+                acc[e] = r == 0 ? v : acc[e] + v;
+            }
+        }
+        const uint32_t off = ((tile0 + t) * kW + lane) * (VE * 4u);
+        const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>((tile0 + t) & 7));
+#pragma unroll
+        for (int h = 0; h < VE / 4; ++h) {
+            u32x4 s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] = __float_as_uint(acc[4 * h + e]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) store16(p.out[rot + q], p.out_bytes, off + 16u * h, s);
+        }
+    }
+}
+
 template <typename K, typename S>
 static double rate(K kernel, unsigned grid, int cap, const std::vector<S>& sets, uint32_t* sink,
                    double bytes_per_launch, int reps = 40) {
-    const unsigned lds = lds_for(cap);
+    hipFuncAttributes at{};
+    CK(hipFuncGetAttributes(&at, reinterpret_cast<const void*>(kernel)));
+    const unsigned want = lds_for(cap);
+    const unsigned lds = want > at.sharedSizeBytes ? want - static_cast<unsigned>(at.sharedSizeBytes) : 0u;
     hipEvent_t a, b;
     CK(hipEventCreate(&a));
     CK(hipEventCreate(&b));
@@ -219,7 +293,7 @@ static Streams make_set(char* in, size_t in_stride, char* out, size_t out_stride
 }
 
 int main() {
-    const int caps[] = {0, 3, 4, 5, 6, 8};
+    const int caps[] = {0, 3, 4, 5, 6, 8, 12, 16};
     uint32_t* sink = nullptr;
     CK(hipMalloc(&sink, 64));
 
@@ -307,12 +381,44 @@ int main() {
     row("read8 (25 MiB streams)", stream_kernel<8, 0>, g25, red, 8.0 * sb);
     row("write8 (25 MiB streams)", stream_kernel<0, 8>, g25, red, 8.0 * sb);
     row("copy (200 MiB)", stream_kernel<1, 1>, g200, copy, 2.0 * cb);
+    row("bcast 1 -> 7 (25 MiB streams)", stream_kernel<1, 7>, g25, red, 8.0 * sb);
     row("red8 f32 (25 MiB, one allocation)", stream_kernel<8, 8>, g25, red, 16.0 * sb);
     row("red8 f32 (25 MiB, separate allocs)", stream_kernel<8, 8>, g25, red_sep, 16.0 * sb);
     row("red8 f32 (100 MiB streams)", stream_kernel<8, 8>, g100, red_long, 16.0 * lb);
     row("red8 bf16->f32 (100 MiB inputs)", red8_bf16_kernel, gbf, bf, 8.0 * (bin + bout));
     row("sgd step, bf16 in, no output", sgd_kernel<false>, gsgd, sgd, 8.0 * gb + 4.0 * wvb);
     row("sgd step, bf16 in, bf16 out", sgd_kernel<true>, gsgd, sgd, 16.0 * gb + 4.0 * wvb);
+    row("red8 f32 LDS-staged, 1 tile/wg", red8_lds_kernel<1, 4>, g25, red, 16.0 * sb);
+    row("red8 f32 LDS-staged, 2 tiles/wg", red8_lds_kernel<2, 4>, g25 / 2, red, 16.0 * sb);
+    row("red8 f32 LDS-staged, 4 tiles/wg", red8_lds_kernel<4, 4>, g25 / 4, red, 16.0 * sb);
+    row("red8 f32 LDS-staged, 1 tile, 100 MiB", red8_lds_kernel<1, 4>, g100, red_long, 16.0 * lb);
+    row("red8 bf16->f32 LDS-staged, 1 tile/wg", red8_lds_kernel<1, 2>, gbf / 2, bf, 8.0 * (bin + bout));
+    row("red8 bf16->f32 LDS-staged, 2 tiles/wg", red8_lds_kernel<2, 2>, gbf / 4, bf, 8.0 * (bin + bout));
+
+    // The staged kernels compute what the register kernels compute: the
+    // same sums in the same order, compared bit for bit on one set.
+    {
+        std::vector<uint32_t> a(sb / 4), b(sb / 4);
+        auto run_cmp = [&](const char* name, auto k1, unsigned g1, auto k2, unsigned g2, const Streams& st,
+                           size_t bytes) {
+            hipLaunchKernelGGL(k1, dim3(g1), dim3(kW), 0, 0, st, sink);
+            CK(hipGetLastError());
+            CK(hipMemcpy(a.data(), st.out[3], bytes, hipMemcpyDeviceToHost));
+            CK(hipMemset(st.out[3], 0, bytes));
+            hipLaunchKernelGGL(k2, dim3(g2), dim3(kW), 0, 0, st, sink);
+            CK(hipGetLastError());
+            CK(hipMemcpy(b.data(), st.out[3], bytes, hipMemcpyDeviceToHost));
+            size_t bad = 0;
+            for (size_t i = 0; i < bytes / 4; ++i) bad += a[i] != b[i];
+            std::printf("check %-44s %zu of %zu words differ\n", name, bad, bytes / 4);
+        };
+        run_cmp("red8 f32: registers vs LDS-staged (1 tile)", stream_kernel<8, 8>, g25, red8_lds_kernel<1, 4>, g25,
+                red[0], sb);
+        run_cmp("red8 f32: registers vs LDS-staged (4 tiles)", stream_kernel<8, 8>, g25, red8_lds_kernel<4, 4>,
+                g25 / 4, red[1], sb);
+        run_cmp("red8 bf16->f32: registers vs LDS-staged (2 tiles)", red8_bf16_kernel, gbf, red8_lds_kernel<2, 2>,
+                gbf / 4, bf[0], sb);
+    }
 
     for (char* p : sep) CK(hipFree(p));
     CK(hipFree(barena));

