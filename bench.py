@@ -415,6 +415,28 @@ def _w_multi(ctx):
                 lambda i: run("mean"), 8 * plan.total * 8, "multi_ring_kernel<8, false, false, false>", 1)
 
 
+@work("multi-resnet50-views", "resnet")
+def _w_multi_views(ctx):
+    """The multi-tensor launch over the same 161 tensors laid out as views of
+    the per-rank arena rows the bucketed call reads (gradients as bucket
+    views): the kernel on the bucketed call's memory layout."""
+    import torch
+
+    import gradient_all_reduce_allreduce_amd as ddp
+    import workloads
+    plan, _, rows = _resnet(ctx)
+    shapes = workloads.model_shapes("resnet50")
+    runs = []
+    for ins, outs in rows:
+        tin = [plan.tensor_views(x) for x in ins]
+        tout = [plan.tensor_views(x) for x in outs]
+        runs.append(ddp.MultiAllReduce(shapes, 8, torch.float32, device=_dev()).bind(tin, tout))
+    return Work("resnet50 p8 f32 mean, 161 tensors as views of the bucketed call's arena rows, one "
+                "multi-tensor launch", lambda i: runs[i % 2]("mean"), 8 * plan.total * 8,
+                "multi_ring_kernel<8, false, false, false>", 1,
+                note="the same memory layout as the bucketed call: separates the kernel from the layout")
+
+
 @work("multi-sgd-resnet50", "resnet_tensors")
 def _w_multi_sgd(ctx):
     import torch

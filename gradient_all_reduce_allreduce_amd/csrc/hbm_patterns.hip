@@ -18,7 +18,9 @@
 //   write8      8 output streams
 //   copy        1 input stream -> 1 output stream, 200 MiB each
 //   bcast 1 -> 7  the all-gather's pattern: 1 input stream, each tile
-//               stored to 7 of the 8 output streams (25 MiB each)
+//               stored to 7 of the 8 output streams (25 MiB each); and the
+//               same with one output stream per workgroup, the 7 workgroups
+//               that read one tile on one XCD (reads mostly from its L2)
 //   LDS-staged  the all-reduce's pattern with the inputs brought into LDS
 //               by direct global -> LDS loads, 1, 2 or 4 tiles per
 //               workgroup (the next tile's loads in flight while one is
@@ -108,6 +110,31 @@ __global__ __launch_bounds__(kW) void stream_kernel(Streams p, uint32_t* sink) {
         const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x % NW));
 #pragma unroll
         for (int q = 0; q < NW; ++q) store16(p.out[rot + q], p.out_bytes, off, s);
+    }
+}
+
+// The all-gather's pattern with one output stream per workgroup: the
+// workgroups that copy one input tile to the 7 outputs sit on one XCD
+// (workgroups are dispatched to the 8 XCDs round robin, so workgroup b runs
+// on XCD b mod 8), so that the first read of a tile fills that XCD's L2 and
+// the other six hit it.  Workgroup b: tile (b / 64) * 8 + b mod 8, output
+// slot (b / 8) mod 8, slot 7 idle.  U vectors per lane.
+template <int U>
+__global__ __launch_bounds__(kW) void bcast_xcd_kernel(Streams p, uint32_t* sink) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t slot = (b >> 3) & 7u;
+    if (slot == 7u) return;
+    const uint32_t tile = (b >> 6) * 8u + (b & 7u);
+    u32x4 y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t off = ((tile * U + u) * kW + threadIdx.x) * 16u;
+        y[u] = *reinterpret_cast<const u32x4*>(p.in[0] + off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t off = ((tile * U + u) * kW + threadIdx.x) * 16u;
+        store16(p.out[slot], p.out_bytes, off, y[u]);
     }
 }
 
@@ -206,12 +233,15 @@ typedef __attribute__((address_space(1))) void* gbl_ptr;
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ES_IN 4: float32 inputs, a 64-lane tile of 4 elements per lane; ES_IN 2:
-// bf16 inputs, 8 elements per lane (the direct loads move 16 bytes per
-// lane), float32 outputs in two 16-byte stores per lane and stream.
+// bf16 inputs, a tile of 512 elements (the direct loads move 16 bytes per
+// lane), read back transposed: lane i takes elements 4i..4i+3 and
+// 256+4i..256+4i+3, so that each of its two 16-byte float32 stores per
+// stream belongs to one contiguous 1 KB store of the wave.
 template <int T, int ES_IN>
 __global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink) {
     constexpr int VE = 16 / ES_IN;                  // elements per lane and tile
     __shared__ u32x4 buf[T > 1 ? 2 : 1][8][kW];
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
     const uint32_t lane = threadIdx.x;
     const uint32_t tile0 = blockIdx.x * T;
 #pragma unroll
@@ -222,7 +252,16 @@ __global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink)
         wait_vm_all();
         u32x4 x[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) x[r] = buf[t & 1][r][lane];
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (ES_IN == 4) {
+                x[r] = buf[t & 1][r][lane];
+            } else {
+                const u32x2v* row = reinterpret_cast<const u32x2v*>(&buf[t & 1][r][0]);
+                const u32x2v lo2 = row[lane];        // elements 4 lane .. 4 lane + 3
+                const u32x2v hi2 = row[kW + lane];   // elements 256 + 4 lane ..
+                x[r] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+            }
+        }
         if (t + 1 < T) {
             // the LDS reads above complete before the next loads overwrite
             // the other buffer's previous contents (read two tiles ago)
@@ -241,7 +280,9 @@ __global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink)
                 acc[e] = r == 0 ? v : acc[e] + v;
             }
         }
-        const uint32_t off = ((tile0 + t) * kW + lane) * (VE * 4u);
+        // float32 output offset of lane's first element; the second half
+        // of a bf16 tile is 256 elements (1 KB) further
+        const uint32_t off = ((tile0 + t) * kW * VE + 4u * lane) * 4u;
         const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>((tile0 + t) & 7));
 #pragma unroll
         for (int h = 0; h < VE / 4; ++h) {
@@ -249,7 +290,7 @@ __global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[e] = __float_as_uint(acc[4 * h + e]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) store16(p.out[rot + q], p.out_bytes, off + 16u * h, s);
+            for (int q = 0; q < 8; ++q) store16(p.out[rot + q], p.out_bytes, off + 1024u * h, s);
         }
     }
 }
@@ -382,6 +423,8 @@ int main() {
     row("write8 (25 MiB streams)", stream_kernel<0, 8>, g25, red, 8.0 * sb);
     row("copy (200 MiB)", stream_kernel<1, 1>, g200, copy, 2.0 * cb);
     row("bcast 1 -> 7 (25 MiB streams)", stream_kernel<1, 7>, g25, red, 8.0 * sb);
+    row("bcast 1 -> 7, a stream per wg, XCD", bcast_xcd_kernel<1>, g25 * 8, red, 8.0 * sb);
+    row("bcast 1 -> 7, the same, 2 vec/lane", bcast_xcd_kernel<2>, g25 * 4, red, 8.0 * sb);
     row("red8 f32 (25 MiB, one allocation)", stream_kernel<8, 8>, g25, red, 16.0 * sb);
     row("red8 f32 (25 MiB, separate allocs)", stream_kernel<8, 8>, g25, red_sep, 16.0 * sb);
     row("red8 f32 (100 MiB streams)", stream_kernel<8, 8>, g100, red_long, 16.0 * lb);

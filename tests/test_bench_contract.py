@@ -32,6 +32,25 @@ def test_traffic_is_reported_only_for_the_measured_kernel_and_step(tmp_path, mon
     assert bench.measured_traffic(3900, 39) is None
 
 
+def test_committed_traffic_profile_matches_the_headline_kernel():
+    """The committed counter summary of the headline kernel was taken on the
+    current kernel source and on the headline step: bytes per step are P * n
+    * (2 + 4) over the transformer gradient set, one launch per bucket."""
+    import math
+
+    import workloads
+    fields = bench.profile_fields(bench.TRAFFIC_PROFILE)
+    assert fields["source_sha256"] == bench.kernel_source_hash()
+    total = sum(math.prod(s) for s in workloads.model_shapes("transformer_2b"))
+    alg = 8 * total * 6
+    assert int(fields["algorithmic_bytes_per_step"]) == alg
+    assert int(fields["launches_per_step"]) == -(-total // (100 * 2**20 // 2))
+    traffic = bench.measured_traffic(alg, int(fields["launches_per_step"]))
+    assert traffic is not None
+    # within 1% of the algorithmic bytes: no re-reads, no write amplification
+    assert abs(traffic * int(fields["launches_per_step"]) / alg - 1) < 0.01
+
+
 def test_every_suite_workload_names_its_kernel():
     """Each workload of the suite states the kernel a profiler attributes its
     time and counters to (or None for multi-kernel steps)."""
