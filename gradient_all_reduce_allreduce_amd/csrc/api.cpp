@@ -19,6 +19,9 @@
 #include <vector>
 
 #include "launch.h"
+#include "launch_copy.h"
+#include "launch_multi.h"
+#include "launch_step.h"
 
 namespace {
 

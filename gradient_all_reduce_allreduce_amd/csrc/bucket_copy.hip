@@ -39,7 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "launch.h"
+#include "launch_copy.h"
 
 namespace ddp {
 namespace {

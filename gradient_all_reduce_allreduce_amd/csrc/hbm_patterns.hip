@@ -18,7 +18,8 @@
 //   write8      8 output streams
 //   copy        1 input stream -> 1 output stream, 200 MiB each
 //   bcast 1 -> 7  the all-gather's pattern: 1 input stream, each tile
-//               stored to 7 of the 8 output streams (25 MiB each); and the
+//               stored to 7 of the 8 output streams (25 MiB each), with
+//               each store cache policy and load kind; and the
 //               same with one output stream per workgroup, the 7 workgroups
 //               that read one tile on one XCD (reads mostly from its L2)
 //   LDS-staged  the all-reduce's pattern with the inputs brought into LDS
@@ -113,6 +114,23 @@ __global__ __launch_bounds__(kW) void stream_kernel(Streams p, uint32_t* sink) {
     }
 }
 
+// The all-gather's pattern (one input stream, each tile stored to 7 of the
+// 8 output streams) with the stores' cache policy as a parameter: 0 the
+// default, 2 non-temporal, 16 device scope (sc1, the library's choice for
+// the all-reduce), 18 both; and ordinary or non-temporal loads.
+template <int POL, bool NT_LOAD>
+__global__ __launch_bounds__(kW) void bcast_policy_kernel(Streams p, uint32_t* sink) {
+    const uint32_t off = (blockIdx.x * kW + threadIdx.x) * 16u;
+    const u32x4 y = NT_LOAD ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.in[0] + off))
+                            : *reinterpret_cast<const u32x4*>(p.in[0] + off);
+    const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x % 7));
+#pragma unroll
+    for (int q = 0; q < 7; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            y, __builtin_amdgcn_make_buffer_rsrc(p.out[rot + q], 0, static_cast<int>(p.out_bytes), 0x00020000), off, 0,
+            POL);
+}
+
 // The all-gather's pattern with one output stream per workgroup: the
 // workgroups that copy one input tile to the 7 outputs sit on one XCD
 // (workgroups are dispatched to the 8 XCDs round robin, so workgroup b runs
@@ -136,6 +154,59 @@ __global__ __launch_bounds__(kW) void bcast_xcd_kernel(Streams p, uint32_t* sink
         const uint32_t off = ((tile * U + u) * kW + threadIdx.x) * 16u;
         store16(p.out[slot], p.out_bytes, off, y[u]);
     }
+}
+
+// stream_kernel with the stores' cache policy as a parameter (the values of
+// bcast_policy_kernel).
+template <int NR, int NW, int POL>
+__global__ __launch_bounds__(kW) void stream_policy_kernel(Streams p, uint32_t* sink) {
+    const uint32_t off = (blockIdx.x * kW + threadIdx.x) * 16u;
+    u32x4 x[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.in[r] + off));
+    u32x4 s = {off, off, off, off};
+    if constexpr (NR > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = __uint_as_float(x[0][e]);
+#pragma unroll
+            for (int r = 1; r < NR; ++r) acc = acc + __uint_as_float(x[r][e]);
+            s[e] = __float_as_uint(acc);
+        }
+    }
+    const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x % NW));
+#pragma unroll
+    for (int q = 0; q < NW; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            s, __builtin_amdgcn_make_buffer_rsrc(p.out[rot + q], 0, static_cast<int>(p.out_bytes), 0x00020000), off, 0,
+            POL);
+}
+
+// The bf16 -> float32 pattern with the stores' cache policy as a parameter.
+template <int POL>
+__global__ __launch_bounds__(kW) void red8_bf16_policy_kernel(Streams p, uint32_t* sink) {
+    const uint32_t i = blockIdx.x * kW + threadIdx.x;   // 4-element group
+    u32x2 x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.in[r] + i * 8u));
+    u32x4 s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t w = x[r][e >> 1];
+            const float v = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            acc = r == 0 ? v : acc + v;
+        }
+        s[e] = __float_as_uint(acc);
+    }
+    const int rot = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x & 7));
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            s, __builtin_amdgcn_make_buffer_rsrc(p.out[rot + q], 0, static_cast<int>(p.out_bytes), 0x00020000),
+            i * 16u, 0, POL);
 }
 
 // The bf16 -> float32 pattern: 8-byte bf16 loads (4 elements), 16-byte stores.
@@ -423,6 +494,22 @@ int main() {
     row("write8 (25 MiB streams)", stream_kernel<0, 8>, g25, red, 8.0 * sb);
     row("copy (200 MiB)", stream_kernel<1, 1>, g200, copy, 2.0 * cb);
     row("bcast 1 -> 7 (25 MiB streams)", stream_kernel<1, 7>, g25, red, 8.0 * sb);
+    row("write8, stores nt", stream_policy_kernel<0, 8, 2>, g25, red, 8.0 * sb);
+    row("write8, stores sc1 nt", stream_policy_kernel<0, 8, 18>, g25, red, 8.0 * sb);
+    row("red8 f32 25 MiB, stores nt", stream_policy_kernel<8, 8, 2>, g25, red, 16.0 * sb);
+    row("red8 f32 25 MiB, stores sc1 nt", stream_policy_kernel<8, 8, 18>, g25, red, 16.0 * sb);
+    row("red8 f32 25 MiB, stores sc1", stream_policy_kernel<8, 8, 16>, g25, red, 16.0 * sb);
+    row("red8 f32 100 MiB, stores nt", stream_policy_kernel<8, 8, 2>, g100, red_long, 16.0 * lb);
+    row("red8 f32 100 MiB, stores sc1 nt", stream_policy_kernel<8, 8, 18>, g100, red_long, 16.0 * lb);
+    row("red8 bf16->f32, stores nt", red8_bf16_policy_kernel<2>, gbf, bf, 8.0 * (bin + bout));
+    row("red8 bf16->f32, stores sc1 nt", red8_bf16_policy_kernel<18>, gbf, bf, 8.0 * (bin + bout));
+    row("red8 bf16->f32, stores sc1", red8_bf16_policy_kernel<16>, gbf, bf, 8.0 * (bin + bout));
+    row("bcast 1 -> 7, stores default", bcast_policy_kernel<0, false>, g25, red, 8.0 * sb);
+    row("bcast 1 -> 7, stores nt", bcast_policy_kernel<2, false>, g25, red, 8.0 * sb);
+    row("bcast 1 -> 7, stores sc1", bcast_policy_kernel<16, false>, g25, red, 8.0 * sb);
+    row("bcast 1 -> 7, stores sc1 nt", bcast_policy_kernel<18, false>, g25, red, 8.0 * sb);
+    row("bcast 1 -> 7, nt loads, stores sc1", bcast_policy_kernel<16, true>, g25, red, 8.0 * sb);
+    row("bcast 1 -> 7, nt loads, stores nt", bcast_policy_kernel<2, true>, g25, red, 8.0 * sb);
     row("bcast 1 -> 7, a stream per wg, XCD", bcast_xcd_kernel<1>, g25 * 8, red, 8.0 * sb);
     row("bcast 1 -> 7, the same, 2 vec/lane", bcast_xcd_kernel<2>, g25 * 4, red, 8.0 * sb);
     row("red8 f32 (25 MiB, one allocation)", stream_kernel<8, 8>, g25, red, 16.0 * sb);

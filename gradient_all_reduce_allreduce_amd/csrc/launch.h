@@ -79,17 +79,11 @@ constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
 constexpr int tree_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
     return ring_wg_per_cu(P, in_bf16, out_bf16) + 1;
 }
-// Measured at P = 8, f32, ResNet-50 buckets; the multi-tensor kernel
-// searches its tile plan first and wants many more waves (16 at P = 8, 20
-// at P = 4, 20 with the optimizer step).  Bucket pack and unpack (256-lane
-// workgroups, 32 waves per CU at a cap of 8) measured best at 8 with
-// 2 vectors per lane, on the ResNet-50 set and on 2,000 ragged tensors.
+// The ring's halves, measured at P = 8, f32, ResNet-50 buckets.  (The
+// multi-tensor, stepwise and bucket-copy kernels keep their caps in their
+// own headers: launch_multi.h, launch_step.h, launch_copy.h.)
 constexpr int kRsWgPerCu = 10;      // reduce-scatter half
 constexpr int kAgWgPerCu = 12;      // all-gather half
-constexpr int multi_wg_per_cu(int P, bool sgd) { return sgd ? 20 : (P >= 6 ? 16 : 20); }
-constexpr int kStepWgPerCu = 0;     // one ring step per launch
-constexpr int kPackWgPerCu = 8;     // bucket pack (256-lane workgroups)
-constexpr int kUnpackWgPerCu = 8;   // bucket unpack (256-lane workgroups)
 
 // The cap ddp_set_wg_per_cu set for a family (ddp_kernel_family): -1 if
 // none (use the built-in choice), else the cap (0: no cap).  api.cpp.
@@ -176,74 +170,5 @@ const void* tree_kernel_bf16_f32(int P, int scalar);
 const void* tree_kernel_bf16_bf16(int P, int scalar);
 // All-gather kernels by element size (2 or 4 bytes); ring_allgather.hip.
 const void* ring_ag_kernel(int elem_bytes, int P, int scalar);
-
-// The ring one step per launch (ring_step.hip): fp32 rank buffers, in place.
-struct StepLaunch {
-    int P;
-    int chunking;
-    int op;
-    float* buf[kMaxRanks];
-    uint64_t* sent;    // device [P] counters of elements sent, or null
-    int64_t n;
-    void* stream;
-};
-
-int launch_ring_stepwise(const StepLaunch& l, const char** msg);
-
-// Many tensors in one launch (multi_tensor.hip).
-struct MultiLaunch {
-    int P;
-    int chunking;
-    int op;
-    int in_bf16;
-    int out_bf16;
-    int32_t T;
-    const ddp_tensor_tiles* tiles;
-    const void* const* in;
-    void* const* out;           // may be null with sgd: no gradient output
-    float* const* w;            // sgd: [T] device table of master weights
-    float* const* v;            // sgd: [T] device table of momentum buffers
-    float lr;
-    float mu;
-    int sgd;
-    int64_t total_tiles;
-    void* stream;
-};
-
-int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16);
-int launch_multi_ring(const MultiLaunch& l, const char** msg);
-
-// Bucket pack and unpack (bucket_copy.hip).  One launch covers a range of
-// one bucket for all P ranks; its segment table travels in the kernel
-// arguments (7.7 KB: kernel arguments of 8,000 bytes measured to arrive
-// whole on this stack), so a launch holds at most
-// copy_segments_per_launch(P) segments (110 at P = 8, enough for every
-// bucket of the ResNet-50, ViT-B/16, transformer and 2,000-tensor sets) and
-// a bucket with more goes out as several launches over consecutive ranges
-// (api.cpp).
-constexpr int kCopyMaxSegs = 128;     // segments per launch
-constexpr int kCopyMaxPieces = 880;   // (segment, rank) tensor addresses per launch
-constexpr int copy_segments_per_launch(int P) {
-    return kCopyMaxPieces / P < kCopyMaxSegs ? kCopyMaxPieces / P : kCopyMaxSegs;
-}
-// Longest range of a bucket one launch covers, in elements (offsets inside
-// a launch are 32-bit).
-constexpr int64_t kCopyMaxLaunchElems = int64_t(1) << 30;
-
-struct CopyLaunch {
-    int P;
-    int elem_bytes;    // 2 or 4
-    int pack;          // 1: tensors -> bucket, 0: bucket -> tensors
-    int32_t n_segs;    // segments of this launch, 1 .. copy_segments_per_launch(P)
-    int32_t len;       // elements of the range, 1 .. kCopyMaxLaunchElems
-    void* bucket[kMaxRanks];          // rank r's bucket at the range's first element (16-byte aligned)
-    int32_t start[kCopyMaxSegs];      // segment k's first element in the range; start[0] = 0, increasing
-    void* piece[kCopyMaxPieces];      // [k * P + r]: rank r's tensor address of segment k's first element
-    void* stream;
-};
-
-// Elements per workgroup tile of the copy.
-int64_t copy_tile_elems(int elem_bytes);
-int launch_bucket_copy(const CopyLaunch& l, const char** msg);
 
 }  // namespace ddp

@@ -1,0 +1,39 @@
+// Launch interface of the multi-tensor kernel (multi_tensor.hip) between
+// api.cpp and the kernel.  Internal, like launch.h.
+#pragma once
+
+#include "launch.h"
+
+namespace ddp {
+
+// Resident one-wave workgroups per CU.  The multi-tensor kernel searches
+// its tile plan and reads its pointers from device tables before its first
+// load, and wants a few more waves than the ring: 6 at P = 8 (161 ResNet-50
+// tensors, 152 ViT-B/16 tensors in bf16), 8 with the optimizer step, 10 at
+// P = 4 (2,000 ragged tensors), each measured best of 3..20.
+constexpr int multi_wg_per_cu(int P, bool sgd) { return P >= 6 ? (sgd ? 8 : 6) : 10; }
+
+// Many tensors in one launch (multi_tensor.hip).
+struct MultiLaunch {
+    int P;
+    int chunking;
+    int op;
+    int in_bf16;
+    int out_bf16;
+    int32_t T;
+    const ddp_tensor_tiles* tiles;
+    const void* const* in;
+    void* const* out;           // may be null with sgd: no gradient output
+    float* const* w;            // sgd: [T] device table of master weights
+    float* const* v;            // sgd: [T] device table of momentum buffers
+    float lr;
+    float mu;
+    int sgd;
+    int64_t total_tiles;
+    void* stream;
+};
+
+int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16);
+int launch_multi_ring(const MultiLaunch& l, const char** msg);
+
+}  // namespace ddp

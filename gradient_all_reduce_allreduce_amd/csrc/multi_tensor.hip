@@ -11,7 +11,15 @@
 // allreduce_ring_emulated.  The host plan gives every tensor a run of tiles;
 // a workgroup finds its tensor by a binary search over the plan (uniform,
 // scalar loads) and then works like the single-tensor kernel: rotated rank
-// pointers, one fixed fold, P output stores.  Optionally every tensor then
+// pointers, one fixed fold, P output stores.  Between the search and the
+// tile's first data load there is one more round trip: the tensor's entry,
+// then every rank pointer in fold and store order, read with independent
+// scalar loads issued together, with the chunk arithmetic in 32 bits.
+// (Reading the pointers one pair at a time for an alignment test and again
+// for the loads, with a 64-bit division for the chunk length, made a tile
+// take about twice as long before its first load: on one 25.5M-element
+// tensor the kernel ran at 3.2 TB/s with 4 workgroups per CU against the
+// ring kernel's 6.5.)  Optionally every tensor then
 // takes one SGD-momentum step on its float32 master weights and momentum,
 // as each replica's optimizer.step() does after the per-parameter
 // all-reduces (same lecture section), with or without writing the reduced
@@ -21,7 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "launch.h"
+#include "launch_multi.h"
 #include "ring_reduce_impl.h"
 
 namespace ddp {
@@ -45,6 +53,24 @@ struct MultiArgs {
 };
 
 typedef const __attribute__((address_space(4))) MultiArgs* KMulti;
+
+// Non-temporal loads through global-address-space pointers.  The tensors'
+// addresses come from device tables, so the compiler cannot tell that they
+// point to global memory and would issue flat loads, which also count
+// against the scalar-load counter: the next wait for a scalar load would
+// then drain the tile's data loads as well.
+typedef const __attribute__((address_space(1))) u32x4* GlobalVec4;
+typedef const __attribute__((address_space(1))) u32x2* GlobalVec2;
+
+template <int W>
+__device__ __forceinline__ u32x4 load_global(const char* p) {
+    if constexpr (W == 4) {
+        return __builtin_nontemporal_load((GlobalVec4)(p));
+    } else {
+        const u32x2 h = __builtin_nontemporal_load((GlobalVec2)(p));
+        return u32x4{h[0], h[1], 0u, 0u};
+    }
+}
 
 __device__ __forceinline__ KMulti multi_args() {
     return (KMulti)(__builtin_amdgcn_kernarg_segment_ptr());
@@ -103,7 +129,9 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     const int64_t b = blockIdx.x;
 
     // The tensor whose tile run holds this workgroup: largest t with
-    // first_tile <= b.
+    // first_tile <= b (a binary search over the plan: 8 dependent scalar
+    // loads for 161 tensors; a 16-way search that reads 16 entries per
+    // level in one round trip measured 7-20% slower).
     int lo = 0;
     int hi = T - 1;
     while (lo < hi) {
@@ -111,35 +139,58 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
         if (a->tiles[mid].first_tile <= b) lo = mid; else hi = mid - 1;
     }
     const int t = lo;
-    const int64_t numel = a->tiles[t].numel;
-    const uint32_t t0 = static_cast<uint32_t>((b - a->tiles[t].first_tile) * TILE);
-    if (static_cast<int64_t>(t0) >= numel) return;
-    const uint32_t n = static_cast<uint32_t>(numel);
-    // Tensors hold at most 2^29 elements (ddp_multi_plan), so the chunk
-    // arithmetic fits 32 bits (a 64-bit division is a long sequence).
-    const uint32_t L = static_cast<uint32_t>((numel + a->chunking - 1) / a->chunking);
+    const ddp_tensor_tiles tt = a->tiles[t];
+    const uint32_t t0 = static_cast<uint32_t>((b - tt.first_tile) * TILE);
+    if (static_cast<int64_t>(t0) >= tt.numel) return;
+    // Tensors hold at most 2^29 elements (ddp_multi_plan) and the chunk
+    // count is below 2^31, so the chunk arithmetic fits 32 bits: three
+    // 32-bit divisions by uniform values instead of 64-bit ones.
+    const uint32_t n = static_cast<uint32_t>(tt.numel);
+    const uint32_t C = static_cast<uint32_t>(a->chunking);
+    const uint32_t L = n / C + (n % C != 0u);
     const uint32_t end = t0 + TILE < n ? t0 + TILE : n;
     const uint32_t j0 = t0 / L;
     const uint32_t j1 = (end - 1) / L;
     const uint32_t tid = threadIdx.x;
+    const int s0 = static_cast<int>(j0 % P);
+    const int rot = rr::store_rotation(P);
 
+    // Every pointer the tile needs, read once, in fold and store order
+    // (rank (s0 + k) mod P, rank (rot + q) mod P): independent scalar loads
+    // issued together, one round trip.  The alignment test below reads the
+    // same registers.
     const bool write_out = !SGD || a->out != nullptr;
-    bool vector_path = j0 == j1 && end - t0 == TILE;
+    const char* src[P];
+    char* dst[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k)
+        src[k] = static_cast<const char*>(a->in[static_cast<int64_t>(rr::rank_at(s0, k, P)) * T + t]);
+    if (write_out) {
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+            dst[q] = static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]);
+    }
+    char* wp = nullptr;
+    char* vp = nullptr;
+    if constexpr (SGD) {
+        wp = reinterpret_cast<char*>(a->w[t]);
+        vp = reinterpret_cast<char*>(a->v[t]);
+    }
+
     uintptr_t align = 0;
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-        align |= reinterpret_cast<uintptr_t>(a->in[static_cast<int64_t>(r) * T + t]);
-        if (write_out) align |= reinterpret_cast<uintptr_t>(a->out[static_cast<int64_t>(r) * T + t]);
+    for (int k = 0; k < P; ++k) {
+        align |= reinterpret_cast<uintptr_t>(src[k]);
+        if (write_out) align |= reinterpret_cast<uintptr_t>(dst[k]);
     }
-    if constexpr (SGD) align |= reinterpret_cast<uintptr_t>(a->w[t]) | reinterpret_cast<uintptr_t>(a->v[t]);
-    vector_path = vector_path && (align & 15u) == 0;
+    if constexpr (SGD) align |= reinterpret_cast<uintptr_t>(wp) | reinterpret_cast<uintptr_t>(vp);
+    const bool vector_path = j0 == j1 && end - t0 == TILE && (align & 15u) == 0;
 
     if (!vector_path) {
         for (uint32_t i = t0 + tid; i < end; i += kBlock) multi_element<P, INB, OUTB, SGD>(a, t, i, L);
         return;
     }
 
-    const int s0 = static_cast<int>(j0 % P);
     u32x4 x[P][U];
     constexpr int WV = SGD ? V / 4 : 1;   // 16-byte state vectors per lane vector
     u32x4 wq[U][WV];
@@ -148,22 +199,18 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     for (int u = 0; u < U; ++u) {
         const uint32_t i0 = t0 + (u * kBlock + tid) * V;
 #pragma unroll
-        for (int k = 0; k < P; ++k) {
-            const char* p = static_cast<const char*>(a->in[static_cast<int64_t>(rr::rank_at(s0, k, P)) * T + t]);
-            x[k][u] = rr::load_lane<WIN>(p + i0 * IES);
-        }
+        for (int k = 0; k < P; ++k) x[k][u] = load_global<WIN>(src[k] + i0 * IES);
         if constexpr (SGD) {
 #pragma unroll
             for (int q = 0; q < WV; ++q) {
-                wq[u][q] = rr::load16(reinterpret_cast<const char*>(a->w[t]) + (i0 + 4 * q) * 4u);
-                vq[u][q] = rr::load16(reinterpret_cast<const char*>(a->v[t]) + (i0 + 4 * q) * 4u);
+                wq[u][q] = load_global<4>(wp + (i0 + 4 * q) * 4u);
+                vq[u][q] = load_global<4>(vp + (i0 + 4 * q) * 4u);
             }
         }
     }
     float acc[U][V];
     rr::fold<P, 0, INB, U, V>(x, acc);
     const bool mean = a->mean != 0;
-    const int rot = rr::store_rotation(P);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t i0 = t0 + (u * kBlock + tid) * V;
@@ -182,8 +229,8 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
                     wn[e] = __float_as_uint(w);
                     vn[e] = __float_as_uint(v);
                 }
-                rr::store16(a->w[t], n * 4u, (i0 + 4 * q) * 4u, wn);
-                rr::store16(a->v[t], n * 4u, (i0 + 4 * q) * 4u, vn);
+                rr::store16(wp, n * 4u, (i0 + 4 * q) * 4u, wn);
+                rr::store16(vp, n * 4u, (i0 + 4 * q) * 4u, vn);
             }
             if (!write_out) continue;
         }
@@ -192,22 +239,19 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = rr::bf16_bits(g[2 * k]) | (rr::bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q)
-                rr::store16(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t], n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) rr::store16(dst[q], n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = rr::bf16_bits(g[2 * k]) | (rr::bf16_bits(g[2 * k + 1]) << 16);
 #pragma unroll
-            for (int q = 0; q < P; ++q)
-                rr::store8(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t], n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) rr::store8(dst[q], n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
 #pragma unroll
-            for (int q = 0; q < P; ++q)
-                rr::store16(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t], n * OES, i0 * OES, o);
+            for (int q = 0; q < P; ++q) rr::store16(dst[q], n * OES, i0 * OES, o);
         }
     }
 }

@@ -25,7 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "launch.h"
+#include "launch_step.h"
 #include "ring_reduce_impl.h"
 
 namespace ddp {
