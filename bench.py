@@ -942,7 +942,11 @@ def headline(args):
                 "min_us": round(float(d[0]) * 1e3, 2), "max_us": round(float(d[-1]) * 1e3, 2),
                 "median_gbs": round(P * n * 6 / (med * 1e-3) / 1e9, 1)}
 
-    bucketed = None
+    bucketed = {"value": None,
+                "note": "not timed by default: one bucketed call puts consecutive full buckets in launches of up "
+                        "to 2^29 elements, another length of the same kernel, which would change a profiler's "
+                        "average over this run; `bench.py --bucketed` adds it (the same bits as one call per "
+                        "bucket)"}
     if args.bucketed:
         ins = [g[r, :plan.total] for r in range(P)]
         outs = [o[r, :plan.total] for r in range(P)]

@@ -182,6 +182,31 @@ __global__ __launch_bounds__(kW) void stream_policy_kernel(Streams p, uint32_t* 
             POL);
 }
 
+// stream_kernel with BS-lane workgroups: every wave still moves its own
+// 64-lane tile, so only the number of workgroups to dispatch changes (a
+// quarter of them with 256 lanes).
+template <int NR, int NW, int BS>
+__global__ __launch_bounds__(BS) void stream_bs_kernel(Streams p, uint32_t* sink) {
+    const uint32_t off = (blockIdx.x * BS + threadIdx.x) * 16u;
+    u32x4 x[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.in[r] + off));
+    u32x4 s = {off, off, off, off};
+    if constexpr (NR > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = __uint_as_float(x[0][e]);
+#pragma unroll
+            for (int r = 1; r < NR; ++r) acc = acc + __uint_as_float(x[r][e]);
+            s[e] = __float_as_uint(acc);
+        }
+    }
+    const int wave = static_cast<int>(blockIdx.x * (BS / 64) + threadIdx.x / 64);
+    const int rot = __builtin_amdgcn_readfirstlane(wave % NW);
+#pragma unroll
+    for (int q = 0; q < NW; ++q) store16(p.out[rot + q], p.out_bytes, off, s);
+}
+
 // The bf16 -> float32 pattern with the stores' cache policy as a parameter.
 template <int POL>
 __global__ __launch_bounds__(kW) void red8_bf16_policy_kernel(Streams p, uint32_t* sink) {
@@ -368,7 +393,7 @@ __global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink)
 
 template <typename K, typename S>
 static double rate(K kernel, unsigned grid, int cap, const std::vector<S>& sets, uint32_t* sink,
-                   double bytes_per_launch, int reps = 40) {
+                   double bytes_per_launch, int reps = 40, unsigned block = kW) {
     hipFuncAttributes at{};
     CK(hipFuncGetAttributes(&at, reinterpret_cast<const void*>(kernel)));
     const unsigned want = lds_for(cap);
@@ -376,11 +401,11 @@ static double rate(K kernel, unsigned grid, int cap, const std::vector<S>& sets,
     hipEvent_t a, b;
     CK(hipEventCreate(&a));
     CK(hipEventCreate(&b));
-    for (int i = 0; i < 3; ++i) hipLaunchKernelGGL(kernel, dim3(grid), dim3(kW), lds, 0, sets[i % sets.size()], sink);
+    for (int i = 0; i < 3; ++i) hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), lds, 0, sets[i % sets.size()], sink);
     CK(hipGetLastError());
     CK(hipDeviceSynchronize());
     CK(hipEventRecord(a));
-    for (int i = 0; i < reps; ++i) hipLaunchKernelGGL(kernel, dim3(grid), dim3(kW), lds, 0, sets[i % sets.size()], sink);
+    for (int i = 0; i < reps; ++i) hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), lds, 0, sets[i % sets.size()], sink);
     CK(hipEventRecord(b));
     CK(hipEventSynchronize(b));
     float ms = 0.f;
@@ -494,6 +519,24 @@ int main() {
     row("write8 (25 MiB streams)", stream_kernel<0, 8>, g25, red, 8.0 * sb);
     row("copy (200 MiB)", stream_kernel<1, 1>, g200, copy, 2.0 * cb);
     row("bcast 1 -> 7 (25 MiB streams)", stream_kernel<1, 7>, g25, red, 8.0 * sb);
+    {
+        // 128- and 256-lane workgroups: the caps are workgroups per CU, so
+        // waves per CU = cap * 2 or cap * 4 (at least 2 workgroups per CU)
+        auto row_bs = [&](const char* name, auto kernel, unsigned grid, const auto& sets, double bytes, unsigned bs) {
+            std::printf("%-36s", name);
+            for (int c : caps) {
+                if (c != 0 && c < 2) { std::printf("%8s", "-"); continue; }
+                std::printf("%8.0f", rate(kernel, grid, c, sets, sink, bytes, 40, bs));
+            }
+            std::printf("   GB/s\n");
+            std::fflush(stdout);
+        };
+        row_bs("red8 f32 25 MiB, 128-lane wg", stream_bs_kernel<8, 8, 128>, g25 / 2, red, 16.0 * sb, 128);
+        row_bs("red8 f32 25 MiB, 256-lane wg", stream_bs_kernel<8, 8, 256>, g25 / 4, red, 16.0 * sb, 256);
+        row_bs("red8 f32 100 MiB, 128-lane wg", stream_bs_kernel<8, 8, 128>, g100 / 2, red_long, 16.0 * lb, 128);
+        row_bs("red8 f32 100 MiB, 256-lane wg", stream_bs_kernel<8, 8, 256>, g100 / 4, red_long, 16.0 * lb, 256);
+        row_bs("write8, 256-lane wg", stream_bs_kernel<0, 8, 256>, g25 / 4, red, 8.0 * sb, 256);
+    }
     row("write8, stores nt", stream_policy_kernel<0, 8, 2>, g25, red, 8.0 * sb);
     row("write8, stores sc1 nt", stream_policy_kernel<0, 8, 18>, g25, red, 8.0 * sb);
     row("red8 f32 25 MiB, stores nt", stream_policy_kernel<8, 8, 2>, g25, red, 16.0 * sb);
