@@ -10,7 +10,8 @@ include/ddp_allreduce.h); this package is its Python binding.
 from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, ddp_bucket_pack,
                   ddp_bucket_unpack, allreduce_ring_emulated, allreduce_fused_sgd,
                   reducescatter_ring_emulated, allgather_ring_emulated, allreduce_ring_stepwise,
-                  allreduce_tree_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
+                  allreduce_tree_emulated, ddp_multi_plan, ddp_multi_block_map,
+                  allreduce_multi_ring_emulated,
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
                   allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
                   allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step,
@@ -23,7 +24,8 @@ __all__ = [
     "SUM", "MEAN", "F32", "BF16", "MAX_RANKS", "DdpError", "ddp_bucket_plan", "ddp_bucket_pack",
     "ddp_bucket_unpack", "allreduce_ring_emulated", "allreduce_fused_sgd",
     "reducescatter_ring_emulated", "allgather_ring_emulated", "allreduce_ring_stepwise",
-    "allreduce_tree_emulated", "ddp_multi_plan", "allreduce_multi_ring_emulated", "allreduce",
+    "allreduce_tree_emulated", "ddp_multi_plan", "ddp_multi_block_map", "allreduce_multi_ring_emulated",
+    "allreduce",
     "allreduce_stepwise", "allreduce_tree", "MultiAllReduce",
     "allreduce_sgd",
     "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",

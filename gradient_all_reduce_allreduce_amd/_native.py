@@ -105,15 +105,18 @@ _SIGNATURES = {
         ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
         ctypes.POINTER(TensorTiles), ctypes.POINTER(ctypes.c_int64),
         ctypes.POINTER(ctypes.c_int64)]),
+    "ddp_multi_block_map": (ctypes.c_int, [
+        ctypes.POINTER(TensorTiles), ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
+        ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "allreduce_multi_ring_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
-        ctypes.c_int, ctypes.c_void_p]),
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "allreduce_multi_fused_sgd": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
-        ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
-        ctypes.c_void_p]),
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_void_p]),
     "ddp_set_wg_per_cu": (ctypes.c_int, [ctypes.c_int, ctypes.c_int32]),
     "ddp_last_error": (ctypes.c_char_p, []),
 }

@@ -10,7 +10,7 @@ Python ints, stream as an int handle or None):
     ddp_buckets_launch_count,
     reducescatter_ring_emulated,
     allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
-    allreduce_hierarchical_emulated, ddp_multi_plan, allreduce_multi_ring_emulated,
+    allreduce_hierarchical_emulated, ddp_multi_plan, ddp_multi_block_map, allreduce_multi_ring_emulated,
     allreduce_multi_fused_sgd, ddp_set_wg_per_cu
 Tensor-level helpers:
     allreduce(tensors, op, chunking, out)            -> list of outputs
@@ -229,19 +229,36 @@ def ddp_multi_plan(numels, P, in_dtype, out_dtype):
     return tiles, total.value, tile.value
 
 
+def ddp_multi_block_map(tiles, total_tiles):
+    """Block map of a multi-tensor plan (host only): entry k is the tensor
+    holding tile 64 k.  Returns an int32 numpy array."""
+    tiles = np.ascontiguousarray(tiles, dtype=TILES_DTYPE)
+    n_blocks = ctypes.c_int64(0)
+    c_tiles = tiles.ctypes.data_as(ctypes.POINTER(N.TensorTiles))
+    lib = N.lib()
+    _check(lib.ddp_multi_block_map(c_tiles, tiles.size, total_tiles, None, 0, ctypes.byref(n_blocks)))
+    out = np.zeros(n_blocks.value, dtype=np.int32)
+    _check(lib.ddp_multi_block_map(c_tiles, tiles.size, total_tiles,
+                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), out.size,
+                                   ctypes.byref(n_blocks)))
+    return out
+
+
 def allreduce_multi_ring_emulated(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems,
-                                  in_ptrs_dev, in_dtype, out_ptrs_dev, out_dtype, stream=None):
+                                  block_first_dev, in_ptrs_dev, in_dtype, out_ptrs_dev, out_dtype,
+                                  stream=None):
     _check(N.lib().allreduce_multi_ring_emulated(_op(op), P, chunking, n_tensors, tiles_dev,
-                                                 total_tiles, tile_elems, in_ptrs_dev, in_dtype,
-                                                 out_ptrs_dev, out_dtype, stream))
+                                                 total_tiles, tile_elems, block_first_dev, in_ptrs_dev,
+                                                 in_dtype, out_ptrs_dev, out_dtype, stream))
 
 
 def allreduce_multi_fused_sgd(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems,
-                              in_ptrs_dev, grad_dtype, w_ptrs_dev, v_ptrs_dev, lr, mu, out_ptrs_dev,
-                              out_dtype, stream=None):
+                              block_first_dev, in_ptrs_dev, grad_dtype, w_ptrs_dev, v_ptrs_dev, lr, mu,
+                              out_ptrs_dev, out_dtype, stream=None):
     _check(N.lib().allreduce_multi_fused_sgd(_op(op), P, chunking, n_tensors, tiles_dev, total_tiles,
-                                             tile_elems, in_ptrs_dev, grad_dtype, w_ptrs_dev,
-                                             v_ptrs_dev, lr, mu, out_ptrs_dev, out_dtype, stream))
+                                             tile_elems, block_first_dev, in_ptrs_dev, grad_dtype,
+                                             w_ptrs_dev, v_ptrs_dev, lr, mu, out_ptrs_dev, out_dtype,
+                                             stream))
 
 
 def ddp_set_wg_per_cu(family, wg_per_cu):
@@ -438,7 +455,7 @@ class MultiAllReduce:
     small-message path).  Plans once for a list of shapes; ``__call__`` takes
     P lists of T tensors (rank-major) and optional P output lists."""
 
-    def __init__(self, shapes, P, dtype, out_dtype=None, device="cuda"):
+    def __init__(self, shapes, P, dtype, out_dtype=None, device="cuda", block_map=True):
         import torch
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         self.P = P
@@ -449,6 +466,15 @@ class MultiAllReduce:
         self.tiles, self.total_tiles, self.tile_elems = ddp_multi_plan(
             numels, P, torch_dtype_code(dtype), torch_dtype_code(self.out_dtype))
         self.tiles_dev = torch.from_numpy(self.tiles.view(np.uint8).copy()).to(self.device)
+        # The block map lets each workgroup find its tensor with one table
+        # read and a short search instead of a search over the whole plan
+        # (block_map=False: the whole-plan search; same results).
+        self.block_map = ddp_multi_block_map(self.tiles, self.total_tiles) if block_map else None
+        self.block_map_dev = (torch.from_numpy(self.block_map.copy()).to(self.device)
+                              if block_map else None)
+
+    def _block_map_ptr(self):
+        return self.block_map_dev.data_ptr() if self.block_map_dev is not None else None
 
     def _table(self, lists, dtype):
         import torch
@@ -478,13 +504,13 @@ class MultiAllReduce:
         tin = self._table(rank_lists, self.dtype)
         tout = self._table(out, self.out_dtype)
         args = (self.P, len(self.shapes), self.tiles_dev.data_ptr(), self.total_tiles,
-                self.tile_elems, tin.data_ptr(), torch_dtype_code(self.dtype), tout.data_ptr(),
-                torch_dtype_code(self.out_dtype))
-        tables = (self.tiles_dev, tin, tout)
+                self.tile_elems, self._block_map_ptr(), tin.data_ptr(),
+                torch_dtype_code(self.dtype), tout.data_ptr(), torch_dtype_code(self.out_dtype))
+        tables = tuple(t for t in (self.tiles_dev, self.block_map_dev, tin, tout) if t is not None)
 
         def run(op="sum", chunking=None):
-            P, T, tiles, total, tile, pin, dtin, pout, dtout = args
-            allreduce_multi_ring_emulated(op, P, chunking or P, T, tiles, total, tile, pin, dtin,
+            P, T, tiles, total, tile, bmap, pin, dtin, pout, dtout = args
+            allreduce_multi_ring_emulated(op, P, chunking or P, T, tiles, total, tile, bmap, pin, dtin,
                                           pout, dtout, _stream_for(tables))
             return out
 
@@ -523,11 +549,12 @@ class MultiAllReduce:
         tv = self._state_table(v)
         T = len(self.shapes)
 
-        tables = tuple(t for t in (self.tiles_dev, tin, tout, tw, tv) if t is not None)
+        tables = tuple(t for t in (self.tiles_dev, self.block_map_dev, tin, tout, tw, tv) if t is not None)
 
         def run(lr, mu, op="mean", chunking=None):
             allreduce_multi_fused_sgd(op, self.P, chunking or self.P, T, self.tiles_dev.data_ptr(),
-                                      self.total_tiles, self.tile_elems, tin.data_ptr(),
+                                      self.total_tiles, self.tile_elems, self._block_map_ptr(),
+                                      tin.data_ptr(),
                                       torch_dtype_code(self.dtype), tw.data_ptr(), tv.data_ptr(), lr, mu,
                                       tout.data_ptr() if tout is not None else None,
                                       torch_dtype_code(self.out_dtype), _stream_for(tables))

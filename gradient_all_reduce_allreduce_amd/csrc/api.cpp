@@ -881,6 +881,32 @@ int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtyp
     return ok();
 }
 
+int ddp_multi_block_map(const ddp_tensor_tiles* tiles, int32_t n_tensors, int64_t total_tiles,
+                        int32_t* block_first, int64_t cap, int64_t* n_blocks) {
+    if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
+    if (tiles == nullptr || n_blocks == nullptr) return fail(DDP_E_ARG, "NULL pointer argument");
+    if (total_tiles < 0 || total_tiles > INT32_MAX) return fail(DDP_E_ARG, "total_tiles out of range");
+    if (tiles[0].first_tile != 0) return fail(DDP_E_PLAN, "the plan does not start at tile 0");
+    for (int32_t t = 1; t < n_tensors; ++t)
+        if (tiles[t].first_tile < tiles[t - 1].first_tile || tiles[t].first_tile > total_tiles)
+            return fail(DDP_E_PLAN, "first_tile of tensor %d out of order", t);
+    const int64_t nb = (total_tiles + ddp::kMultiBlockTiles - 1) / ddp::kMultiBlockTiles;
+    *n_blocks = nb;
+    if (block_first == nullptr) return ok();
+    if (cap < nb)
+        return fail(DDP_E_PLAN, "block map capacity %lld < %lld needed", static_cast<long long>(cap),
+                    static_cast<long long>(nb));
+    // Entry k: the largest t with first_tile <= k * kMultiBlockTiles (the
+    // tensor holding that tile; tensors without tiles give way to the next).
+    int32_t t = 0;
+    for (int64_t k = 0; k < nb; ++k) {
+        const int64_t tile = k * ddp::kMultiBlockTiles;
+        while (t + 1 < n_tensors && tiles[t + 1].first_tile <= tile) ++t;
+        block_first[k] = t;
+    }
+    return ok();
+}
+
 namespace {
 
 int validate_multi(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
@@ -903,7 +929,7 @@ int validate_multi(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tens
 
 int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
                               const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
-                              const void* const* in_ptrs_dev, ddp_dtype grad_dtype, float* const* w_ptrs_dev,
+                              const int32_t* block_first_dev, const void* const* in_ptrs_dev, ddp_dtype grad_dtype, float* const* w_ptrs_dev,
                               float* const* v_ptrs_dev, float lr, float mu, void* const* out_ptrs_dev,
                               ddp_dtype out_dtype, void* stream) {
     int s = validate_multi(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems, in_ptrs_dev, grad_dtype,
@@ -922,6 +948,7 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, int
     l.out_bf16 = out_dtype == DDP_BF16;
     l.T = n_tensors;
     l.tiles = tiles_dev;
+    l.block_first = block_first_dev;
     l.in = in_ptrs_dev;
     l.out = out_ptrs_dev;
     l.w = w_ptrs_dev;
@@ -939,7 +966,7 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking, int
 
 int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
                                   const ddp_tensor_tiles* tiles_dev, int64_t total_tiles, int64_t tile_elems,
-                                  const void* const* in_ptrs_dev, ddp_dtype in_dtype, void* const* out_ptrs_dev,
+                                  const int32_t* block_first_dev, const void* const* in_ptrs_dev, ddp_dtype in_dtype, void* const* out_ptrs_dev,
                                   ddp_dtype out_dtype, void* stream) {
     int s = validate_multi(op, P, chunking, n_tensors, tiles_dev, total_tiles, tile_elems, in_ptrs_dev, in_dtype,
                            out_dtype);
@@ -955,6 +982,7 @@ int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
     l.out_bf16 = out_dtype == DDP_BF16;
     l.T = n_tensors;
     l.tiles = tiles_dev;
+    l.block_first = block_first_dev;
     l.in = in_ptrs_dev;
     l.out = out_ptrs_dev;
     l.total_tiles = total_tiles;

@@ -13,6 +13,10 @@ namespace ddp {
 // P = 4 (2,000 ragged tensors), each measured best of 3..20.
 constexpr int multi_wg_per_cu(int P, bool sgd) { return P >= 6 ? (sgd ? 8 : 6) : 10; }
 
+// Tiles per entry of the block map (ddp_multi_block_map): entry k is the
+// tensor holding tile k * kMultiBlockTiles.
+constexpr int kMultiBlockTiles = 64;
+
 // Many tensors in one launch (multi_tensor.hip).
 struct MultiLaunch {
     int P;
@@ -22,6 +26,7 @@ struct MultiLaunch {
     int out_bf16;
     int32_t T;
     const ddp_tensor_tiles* tiles;
+    const int32_t* block_first;   // device [ceil(total_tiles / kMultiBlockTiles)], or null
     const void* const* in;
     void* const* out;           // may be null with sgd: no gradient output
     float* const* w;            // sgd: [T] device table of master weights

@@ -41,6 +41,7 @@ using rr::u32x4;
 
 struct MultiArgs {
     const ddp_tensor_tiles* tiles;   // [T], device
+    const int32_t* block_first;      // [ceil(tiles / kMultiBlockTiles)], device, or null
     const void* const* in;           // [P * T] device, rank-major
     void* const* out;                // [P * T] device, rank-major; null: no output
     float* const* w;                 // SGD: [T] device, master weights
@@ -129,11 +130,22 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     const int64_t b = blockIdx.x;
 
     // The tensor whose tile run holds this workgroup: largest t with
-    // first_tile <= b (a binary search over the plan: 8 dependent scalar
+    // first_tile <= b, by a binary search over the plan.  With the block
+    // map the search starts between the tensors holding tiles 64 k and
+    // 64 (k + 1), where 64 k <= b < 64 (k + 1) (usually one tensor: no
+    // step at all); without it, over the whole plan (8 dependent scalar
     // loads for 161 tensors; a 16-way search that reads 16 entries per
     // level in one round trip measured 7-20% slower).
     int lo = 0;
     int hi = T - 1;
+    if (a->block_first != nullptr) {
+        const uint32_t k = static_cast<uint32_t>(b) / kMultiBlockTiles;
+        const int f = a->block_first[k];
+        const int g = (k + 1) * kMultiBlockTiles < gridDim.x ? a->block_first[k + 1] : T - 1;
+        // Clamped, so that a map of another plan reads only entries of this one.
+        lo = f < 0 ? 0 : (f > T - 1 ? T - 1 : f);
+        hi = g < lo ? lo : (g > T - 1 ? T - 1 : g);
+    }
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (a->tiles[mid].first_tile <= b) lo = mid; else hi = mid - 1;
@@ -296,6 +308,7 @@ int launch_multi_ring(const MultiLaunch& l, const char** msg) {
     }
     MultiArgs a{};
     a.tiles = l.tiles;
+    a.block_first = l.block_first;
     a.in = l.in;
     a.out = l.out;
     a.w = l.w;

@@ -276,13 +276,13 @@ def test_zero1_errors():
 def test_multi_fused_sgd_errors():
     _, _, tile = ddp.ddp_multi_plan([1], 8, ddp.F32, ddp.F32)
     f = N.lib().allreduce_multi_fused_sgd
-    assert f(1, 8, 8, 1, A, 1, tile, A, 0, None, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
-    assert f(1, 8, 8, 1, A, 1, tile, A, 0, A, None, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
-    assert f(1, 8, 8, 1, A, 1, tile, A, 0, A, A, float("nan"), 0.9, None, 0, None) == N.DDP_E_ARG
-    assert f(1, 8, 8, 1, A, 1, tile + 4, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_PLAN
-    assert f(1, 8, 8, 1, None, 1, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
-    assert f(5, 8, 8, 1, A, 1, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
-    assert f(1, 8, 8, 1, A, 0, tile, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_OK
+    assert f(1, 8, 8, 1, A, 1, tile, None, A, 0, None, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 1, tile, None, A, 0, A, None, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 1, tile, None, A, 0, A, A, float("nan"), 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 1, tile + 4, None, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_PLAN
+    assert f(1, 8, 8, 1, None, 1, tile, None, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(5, 8, 8, 1, A, 1, tile, None, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_E_ARG
+    assert f(1, 8, 8, 1, A, 0, tile, None, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_OK
 
 
 def _pack_case(numels, bucket_bytes, P=2, es=4):
@@ -566,12 +566,48 @@ def test_multi_plan():
     with pytest.raises(DdpError):
         ddp.ddp_multi_plan([-1], 4, ddp.F32, ddp.F32)
     # a tile size from another plan is rejected before any launch
-    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 1, tile + 4, A, 0, A, 0,
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 1, tile + 4, None, A, 0, A, 0,
                                              None) == N.DDP_E_PLAN
-    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, None, 1, tile, A, 0, A, 0,
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, None, 1, tile, None, A, 0, A, 0,
                                              None) == N.DDP_E_ARG
-    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 0, tile, A, 0, A, 0,
+    assert lib.allreduce_multi_ring_emulated(0, 8, 8, 1, A, 0, tile, A, A, 0, A, 0,
                                              None) == N.DDP_OK
+
+
+def test_multi_block_map_is_the_tensor_of_every_64th_tile():
+    """Entry k of the block map is the largest t with first_tile <= 64 k
+    (the tensor holding tile 64 k; tensors without tiles give way to the
+    next), checked against a direct search on random plans with empty and
+    one-tile tensors."""
+    rng = np.random.default_rng(3)
+    for trial in range(60):
+        T = int(rng.integers(1, 400))
+        numels = rng.choice([0, 1, 256, 1000, 70_000, 1_000_000], size=T).astype(np.int64)
+        tiles, total, _ = ddp.ddp_multi_plan(numels, 8, ddp.F32, ddp.F32)
+        bmap = ddp.ddp_multi_block_map(tiles, total)
+        assert bmap.size == -(-total // 64)
+        ft = tiles["first_tile"]
+        for k in range(bmap.size):
+            want = int(np.searchsorted(ft, 64 * k, side="right")) - 1
+            assert bmap[k] == want, (trial, k)
+            assert ft[want] <= 64 * k < ft[want] + max(1, -(-int(tiles["numel"][want]) // 256)) or \
+                int(tiles["numel"][want]) == 0
+    lib = N.lib()
+    nb = ctypes.c_int64(0)
+    bad = tiles.copy()
+    bad["first_tile"][0] = 1
+    assert lib.ddp_multi_block_map(bad.ctypes.data_as(ctypes.POINTER(N.TensorTiles)), bad.size, total,
+                                   None, 0, ctypes.byref(nb)) == N.DDP_E_PLAN
+    if tiles.size > 2 and total > 0:
+        bad = tiles.copy()
+        bad["first_tile"][1], bad["first_tile"][2] = bad["first_tile"][2] + 1, bad["first_tile"][1]
+        if bad["first_tile"][2] < bad["first_tile"][1]:
+            assert lib.ddp_multi_block_map(bad.ctypes.data_as(ctypes.POINTER(N.TensorTiles)), bad.size,
+                                           total, None, 0, ctypes.byref(nb)) == N.DDP_E_PLAN
+    small = (ctypes.c_int32 * 1)()
+    tiles, total, _ = ddp.ddp_multi_plan([100_000] * 3, 8, ddp.F32, ddp.F32)
+    assert lib.ddp_multi_block_map(tiles.ctypes.data_as(ctypes.POINTER(N.TensorTiles)), 3, total, small, 1,
+                                   ctypes.byref(nb)) == N.DDP_E_PLAN and nb.value == -(-total // 64)
 
 
 # ------------------------------------------------------- tuning knob ----

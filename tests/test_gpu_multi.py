@@ -259,3 +259,56 @@ def test_per_parameter_ddp_training_steps_on_a_tiny_mlp():
         d = (np.linalg.norm(wd.cpu().numpy() - p.detach().numpy()) /
              np.linalg.norm(p.detach().numpy()))
         assert d < 1e-5, d
+
+
+def _many_block_shapes(seed, T=600):
+    """Tensors of sizes around the tile and chunk edges (and empty ones), so
+    that the plan's tiles span many 64-tile blocks whose first tile lies
+    inside a tensor, at a tensor's start, or on an empty tensor."""
+    rng = np.random.default_rng(seed)
+    sizes = rng.choice([0, 1, 7, 255, 256, 257, 2047, 2048, 2049, 16384, 70001], size=T)
+    return [(int(n),) for n in sizes]
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "f32")])
+def test_block_map_search_equals_whole_plan_search_and_oracle(pair):
+    """With the block map each workgroup starts its search in its block's
+    tensor; the results are bit for bit those of the whole-plan search, and
+    every tensor is the oracle's ring on that tensor alone."""
+    it, ot = pair
+    tdt = torch.bfloat16 if it == "bf16" else torch.float32
+    odt = torch.bfloat16 if ot == "bf16" else torch.float32
+    P, C = 8, 8
+    shapes = _many_block_shapes(21)
+    host, dev = make(P, shapes, tdt, seed=22)
+    fast = ddp.MultiAllReduce(shapes, P, tdt, odt, device=DEV)
+    plain = ddp.MultiAllReduce(shapes, P, tdt, odt, device=DEV, block_map=False)
+    assert fast.total_tiles > 64 * 20 and fast.block_map.size == -(-fast.total_tiles // 64)
+    a = fast(dev, "mean", C)
+    b = plain(dev, "mean", C)
+    torch.cuda.synchronize()
+    for t, s in enumerate(shapes):
+        for r in range(P):
+            assert np.array_equal(bits_of(a[r][t]), bits_of(b[r][t])), (t, r)
+        X = np.stack([host[r][t] for r in range(P)])
+        if X.shape[1] == 0:
+            continue
+        want = oracle_ring(X, "mean", C, in_dtype=it, out_dtype=ot)
+        got = np.stack([bits_of(a[r][t]) for r in range(P)])
+        assert_same_bits(got, want, f"{it}->{ot} t={t} n={s[0]}")
+
+
+def test_block_map_fused_sgd_equals_whole_plan_search():
+    P = 8
+    shapes = _many_block_shapes(23, T=400)
+    _, dev = make(P, shapes, torch.float32, seed=24)
+    _, sd1 = sgd_state(shapes, seed=25)
+    _, sd2 = sgd_state(shapes, seed=25)
+    ddp.MultiAllReduce(shapes, P, torch.float32, device=DEV).bind_sgd(
+        dev, [p[0] for p in sd1], [p[1] for p in sd1])(1e-3, 0.9, "mean", P)
+    ddp.MultiAllReduce(shapes, P, torch.float32, device=DEV, block_map=False).bind_sgd(
+        dev, [p[0] for p in sd2], [p[1] for p in sd2])(1e-3, 0.9, "mean", P)
+    torch.cuda.synchronize()
+    for t in range(len(shapes)):
+        assert torch.equal(sd1[t][0].view(torch.int32), sd2[t][0].view(torch.int32)), t
+        assert torch.equal(sd1[t][1].view(torch.int32), sd2[t][1].view(torch.int32)), t
