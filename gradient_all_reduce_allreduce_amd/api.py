@@ -463,8 +463,17 @@ class MultiAllReduce:
         self.out_dtype = out_dtype or dtype
         self.device = torch.device(device)
         numels = [int(np.prod(s, dtype=np.int64)) for s in self.shapes]
+        # The plan (and every table bound to it) lists the tensors smallest
+        # first: the few-tile tensors, whose tiles do the least work per
+        # prologue, then run while the launch fills the chip rather than in
+        # its tail (measured 1.6-2% faster on the 161 ResNet-50 tensors,
+        # level on the ViT-B/16 and ragged sets).  Each tensor's result does
+        # not depend on the order.  plan_order[i] is the caller's index of
+        # the i-th planned tensor.
+        self.plan_order = sorted(range(len(numels)), key=lambda t: numels[t])
         self.tiles, self.total_tiles, self.tile_elems = ddp_multi_plan(
-            numels, P, torch_dtype_code(dtype), torch_dtype_code(self.out_dtype))
+            [numels[t] for t in self.plan_order], P, torch_dtype_code(dtype),
+            torch_dtype_code(self.out_dtype))
         self.tiles_dev = torch.from_numpy(self.tiles.view(np.uint8).copy()).to(self.device)
         # The block map lets each workgroup find its tensor with one table
         # read and a short search instead of a search over the whole plan
@@ -488,7 +497,7 @@ class MultiAllReduce:
                 if tuple(x.shape) != s or x.dtype != dtype or not x.is_contiguous() \
                         or x.device != self.device:
                     raise ValueError("tensor does not match the plan")
-                ptrs.append(x.data_ptr())
+            ptrs.extend(ts[t].data_ptr() for t in self.plan_order)
         return torch.tensor(ptrs, dtype=torch.int64).to(self.device)
 
     def bind(self, rank_lists, out=None):
@@ -535,7 +544,7 @@ class MultiAllReduce:
             if tuple(x.shape) != s or x.dtype != torch.float32 or not x.is_contiguous() \
                     or x.device != self.device:
                 raise ValueError("optimizer state must be contiguous float32 tensors of the planned shapes")
-        return torch.tensor([x.data_ptr() for x in ts], dtype=torch.int64).to(self.device)
+        return torch.tensor([ts[t].data_ptr() for t in self.plan_order], dtype=torch.int64).to(self.device)
 
     def bind_sgd(self, rank_grads, w, v, out=None):
         """Like bind(), for the all-reduce fused with one SGD-momentum step

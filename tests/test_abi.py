@@ -694,3 +694,37 @@ def test_multi_launcher_keeps_bound_tensors_alive(monkeypatch):
         del run
         gc.collect()
         assert all(r() is None for r in refs), bind
+
+
+def test_multi_tables_follow_the_plan_order(monkeypatch):
+    """MultiAllReduce plans the tensors smallest first (stable for equal
+    sizes) and writes every pointer table in that order, so that plan entry
+    i, its input and output pointers and its optimizer state all name the
+    same caller tensor; built on CPU tensors, nothing launched."""
+    import torch
+
+    from gradient_all_reduce_allreduce_amd import api
+
+    monkeypatch.setattr(api, "current_stream", lambda device: None)
+    shapes = [(70,), (3,), (5, 4), (3,), (1000,), (0,)]
+    P = 2
+    m = api.MultiAllReduce(shapes, P, torch.float32, device="cpu")
+    assert m.plan_order == [5, 1, 3, 2, 0, 4]
+    numels = [int(np.prod(s)) for s in shapes]
+    assert list(m.tiles["numel"]) == [numels[t] for t in m.plan_order]
+    ts = [[torch.zeros(s) for s in shapes] for _ in range(P)]
+    out = [[torch.zeros(s) for s in shapes] for _ in range(P)]
+    w = [torch.zeros(s) for s in shapes]
+    v = [torch.zeros(s) for s in shapes]
+    run = m.bind(ts, out=out)
+    tiles, bmap, tin, tout = run.tables
+    T = len(shapes)
+    for r in range(P):
+        for i, t in enumerate(m.plan_order):
+            assert int(tin[r * T + i]) == ts[r][t].data_ptr()
+            assert int(tout[r * T + i]) == out[r][t].data_ptr()
+    run = m.bind_sgd(ts, w, v)
+    tiles, bmap, tin, tw, tv = run.tables
+    for i, t in enumerate(m.plan_order):
+        assert int(tw[i]) == w[t].data_ptr() and int(tv[i]) == v[t].data_ptr()
+        assert int(tin[i]) == ts[0][t].data_ptr()
