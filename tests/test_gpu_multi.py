@@ -312,3 +312,33 @@ def test_block_map_fused_sgd_equals_whole_plan_search():
     for t in range(len(shapes)):
         assert torch.equal(sd1[t][0].view(torch.int32), sd2[t][0].view(torch.int32)), t
         assert torch.equal(sd1[t][1].view(torch.int32), sd2[t][1].view(torch.int32)), t
+
+
+def test_multi_fused_sgd_on_vit_bf16_equals_single_tensor_fused_sgd():
+    """The per-parameter fused step on the 152 ViT-B/16 bf16 gradient tensors
+    (P = 8, Mean, bf16 gradients written back too) gives, tensor by tensor,
+    the bits of the single-tensor fused step: weights, momentum and the
+    reduced bf16 gradients."""
+    P = 8
+    shapes = workloads.vit_b16_shapes()
+    g = torch.Generator(device=DEV).manual_seed(31)
+    dev = [[torch.empty(s, device=DEV).normal_(0, 1e-3, generator=g).to(torch.bfloat16) for s in shapes]
+           for _ in range(P)]
+    sd = [(torch.empty(s, device=DEV).normal_(0, 0.02, generator=g),
+           torch.empty(s, device=DEV).normal_(0, 1e-3, generator=g)) for s in shapes]
+    ref = [(p[0].clone(), p[1].clone()) for p in sd]
+    out = [[torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes] for _ in range(P)]
+    m = ddp.MultiAllReduce(shapes, P, torch.bfloat16, device=DEV)
+    m.bind_sgd(dev, [p[0] for p in sd], [p[1] for p in sd], out=out)(1e-3, 0.9, "mean", P)
+    ref_out = []
+    for t in range(len(shapes)):
+        o = [torch.empty(shapes[t], dtype=torch.bfloat16, device=DEV).reshape(-1) for _ in range(P)]
+        ddp.allreduce_sgd([dev[r][t].reshape(-1) for r in range(P)], ref[t][0].reshape(-1),
+                          ref[t][1].reshape(-1), 1e-3, 0.9, "mean", P, out=o)
+        ref_out.append(o)
+    torch.cuda.synchronize()
+    for t in range(len(shapes)):
+        assert torch.equal(sd[t][0].view(torch.int32), ref[t][0].view(torch.int32)), t
+        assert torch.equal(sd[t][1].view(torch.int32), ref[t][1].view(torch.int32)), t
+        for r in range(P):
+            assert torch.equal(out[r][t].reshape(-1).view(torch.int16), ref_out[t][r].view(torch.int16)), (t, r)
