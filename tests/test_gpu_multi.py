@@ -270,20 +270,22 @@ def _many_block_shapes(seed, T=600):
     return [(int(n),) for n in sizes]
 
 
-@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "f32")])
-def test_block_map_search_equals_whole_plan_search_and_oracle(pair):
+@pytest.mark.parametrize("pair,P", [(("f32", "f32"), 8), (("bf16", "f32"), 8), (("f32", "f32"), 5),
+                                    (("bf16", "bf16"), 7), (("f32", "bf16"), 2)])
+def test_block_map_search_equals_whole_plan_search_and_oracle(pair, P):
     """With the block map each workgroup starts its search in its block's
-    tensor; the results are bit for bit those of the whole-plan search, and
+    tensor (and, up to P = 8, reads ahead the tables of the tensor 768 tiles
+    on); the results are bit for bit those of the whole-plan search, and
     every tensor is the oracle's ring on that tensor alone."""
     it, ot = pair
     tdt = torch.bfloat16 if it == "bf16" else torch.float32
     odt = torch.bfloat16 if ot == "bf16" else torch.float32
-    P, C = 8, 8
+    C = P
     shapes = _many_block_shapes(21)
     host, dev = make(P, shapes, tdt, seed=22)
     fast = ddp.MultiAllReduce(shapes, P, tdt, odt, device=DEV)
     plain = ddp.MultiAllReduce(shapes, P, tdt, odt, device=DEV, block_map=False)
-    assert fast.total_tiles > 64 * 20 and fast.block_map.size == -(-fast.total_tiles // 64)
+    assert fast.total_tiles > 768 + 64 * 20 and fast.block_map.size == -(-fast.total_tiles // 64)
     a = fast(dev, "mean", C)
     b = plain(dev, "mean", C)
     torch.cuda.synchronize()
