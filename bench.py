@@ -654,6 +654,58 @@ def _w_ragged_multi(ctx):
                 lambda i: run("sum"), 4 * plan.total * 8, "multi_ring_kernel<4, false, false, false>", 1, steps=10)
 
 
+def _split_rows(ctx):
+    """Two buffer sets of P = 8 contiguous rank rows (inputs and outputs) of
+    25,559,040 floats (99,840 tiles of the multi-tensor kernel), rows 4 KiB
+    apart: the same memory handed to the multi-tensor kernel as one tensor
+    per rank or as 160 equal ones."""
+    if "split" not in ctx:
+        import torch
+
+        import workloads
+        n = 99840 * 256
+        stride = n + 1024
+        sets = []
+        for s_ in range(2):
+            g = torch.empty(8 * stride, device=_dev())
+            workloads.torch_normal_(g, 0.01, seed=700 + s_)
+            o = torch.empty(8 * stride, device=_dev())
+            sets.append(([g[r * stride:r * stride + n] for r in range(8)],
+                         [o[r * stride:r * stride + n] for r in range(8)]))
+        ctx["split"] = (n, sets)
+    return ctx["split"]
+
+
+def _split_work(ctx, T):
+    import torch
+
+    import gradient_all_reduce_allreduce_amd as ddp
+    n, sets = _split_rows(ctx)
+    each = n // T
+    m = ddp.MultiAllReduce([(each,)] * T, 8, torch.float32, device=_dev())
+    runs = [m.bind([[x[t * each:(t + 1) * each] for t in range(T)] for x in ins],
+                   [[y[t * each:(t + 1) * each] for t in range(T)] for y in outs]) for ins, outs in sets]
+    return runs, 8 * n * 8
+
+
+@work("multi-split1", "split")
+def _w_split1(ctx):
+    runs, nbytes = _split_work(ctx, 1)
+    return Work("p8 f32 mean, contiguous rank rows of 25,559,040 floats as one tensor per rank, one "
+                "multi-tensor launch", lambda i: runs[i % 2]("mean"), nbytes,
+                "multi_ring_kernel<8, false, false, false>", 1,
+                note="with multi-split160: the multi-tensor kernel's cost per tensor on the same memory")
+
+
+@work("multi-split160", "split")
+def _w_split160(ctx):
+    runs, nbytes = _split_work(ctx, 160)
+    return Work("p8 f32 mean, the same rows as 160 equal tensors per rank (624 tiles each), one "
+                "multi-tensor launch", lambda i: runs[i % 2]("mean"), nbytes,
+                "multi_ring_kernel<8, false, false, false>", 1,
+                note="no partial tile and no tile across a chunk boundary: only the tensor count differs")
+
+
 @work("ring-transformer2b", "tf2b")
 def _w_tf2b(ctx):
     import gradient_all_reduce_allreduce_amd as ddp
