@@ -44,8 +44,9 @@ class Segment(ctypes.Structure):
 
 
 class TensorTiles(ctypes.Structure):
-    """ddp_tensor_tiles: a tensor's element count and first tile."""
-    _fields_ = [("numel", ctypes.c_int64), ("first_tile", ctypes.c_int64)]
+    """ddp_tensor_tiles: a tensor's element count, first tile and lead (the
+    length of a short first tile, 0 for none)."""
+    _fields_ = [("numel", ctypes.c_int64), ("first_tile", ctypes.c_int32), ("lead", ctypes.c_int32)]
 
 
 _c_void_pp = ctypes.POINTER(ctypes.c_void_p)
@@ -103,7 +104,7 @@ _SIGNATURES = {
         ctypes.c_void_p]),
     "ddp_multi_plan": (ctypes.c_int, [
         ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
-        ctypes.POINTER(TensorTiles), ctypes.POINTER(ctypes.c_int64),
+        _c_void_pp, ctypes.POINTER(TensorTiles), ctypes.POINTER(ctypes.c_int64),
         ctypes.POINTER(ctypes.c_int64)]),
     "ddp_multi_block_map": (ctypes.c_int, [
         ctypes.POINTER(TensorTiles), ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),

@@ -211,19 +211,21 @@ def allreduce_hierarchical_emulated(op, nodes, local_ranks, local_strategy, loca
         N.pointer_array(rank_out), out_dtype, n, stream))
 
 
-TILES_DTYPE = np.dtype([("numel", "<i8"), ("first_tile", "<i8")])
+TILES_DTYPE = np.dtype([("numel", "<i8"), ("first_tile", "<i4"), ("lead", "<i4")])
 
 
-def ddp_multi_plan(numels, P, in_dtype, out_dtype):
+def ddp_multi_plan(numels, P, in_dtype, out_dtype, align_to=None):
     """Tile plan of a multi-tensor all-reduce (host only).  Returns (tiles,
     total_tiles, tile_elems); tiles is a numpy structured array in the C
-    layout."""
+    layout.  ``align_to``: one address per tensor (e.g. rank 0's inputs) to
+    put the tiles on 128-byte lines of, or None."""
     numels = np.ascontiguousarray(numels, dtype=np.int64)
     tiles = np.zeros(numels.size, dtype=TILES_DTYPE)
     total = ctypes.c_int64(0)
     tile = ctypes.c_int64(0)
     _check(N.lib().ddp_multi_plan(numels.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                   numels.size, P, in_dtype, out_dtype,
+                                  None if align_to is None else N.pointer_array(align_to),
                                   tiles.ctypes.data_as(ctypes.POINTER(N.TensorTiles)),
                                   ctypes.byref(total), ctypes.byref(tile)))
     return tiles, total.value, tile.value
@@ -471,19 +473,33 @@ class MultiAllReduce:
         # not depend on the order.  plan_order[i] is the caller's index of
         # the i-th planned tensor.
         self.plan_order = sorted(range(len(numels)), key=lambda t: numels[t])
-        self.tiles, self.total_tiles, self.tile_elems = ddp_multi_plan(
-            [numels[t] for t in self.plan_order], P, torch_dtype_code(dtype),
-            torch_dtype_code(self.out_dtype))
-        self.tiles_dev = torch.from_numpy(self.tiles.view(np.uint8).copy()).to(self.device)
+        self._planned_numels = [numels[t] for t in self.plan_order]
         # The block map lets each workgroup find its tensor with one table
         # read and a short search instead of a search over the whole plan
         # (block_map=False: the whole-plan search; same results).
-        self.block_map = ddp_multi_block_map(self.tiles, self.total_tiles) if block_map else None
-        self.block_map_dev = (torch.from_numpy(self.block_map.copy()).to(self.device)
-                              if block_map else None)
+        self._use_block_map = block_map
+        self.tiles, self.total_tiles, self.tile_elems = ddp_multi_plan(
+            self._planned_numels, P, torch_dtype_code(dtype), torch_dtype_code(self.out_dtype))
+        self.tiles_dev, self.block_map, self.block_map_dev = self._upload(self.tiles, self.total_tiles)
 
-    def _block_map_ptr(self):
-        return self.block_map_dev.data_ptr() if self.block_map_dev is not None else None
+    def _upload(self, tiles, total):
+        import torch
+        tiles_dev = torch.from_numpy(tiles.view(np.uint8).copy()).to(self.device)
+        bmap = ddp_multi_block_map(tiles, total) if self._use_block_map else None
+        bmap_dev = torch.from_numpy(bmap.copy()).to(self.device) if bmap is not None else None
+        return tiles_dev, bmap, bmap_dev
+
+    def _plan_for(self, rank_lists):
+        """(tiles_dev, total_tiles, block_map_dev) for these tensors: the
+        shared plan, or, when some tensor starts off a 128-byte line (a view
+        into a larger buffer), a plan whose tiles follow rank 0's lines."""
+        addrs = [rank_lists[0][t].data_ptr() for t in self.plan_order]
+        tiles, total, _ = ddp_multi_plan(self._planned_numels, self.P, torch_dtype_code(self.dtype),
+                                         torch_dtype_code(self.out_dtype), align_to=addrs)
+        if not np.any(tiles["lead"]):
+            return self.tiles_dev, self.total_tiles, self.block_map_dev
+        tiles_dev, _, bmap_dev = self._upload(tiles, total)
+        return tiles_dev, total, bmap_dev
 
     def _table(self, lists, dtype):
         import torch
@@ -512,10 +528,11 @@ class MultiAllReduce:
                    for _ in range(self.P)]
         tin = self._table(rank_lists, self.dtype)
         tout = self._table(out, self.out_dtype)
-        args = (self.P, len(self.shapes), self.tiles_dev.data_ptr(), self.total_tiles,
-                self.tile_elems, self._block_map_ptr(), tin.data_ptr(),
+        tiles_dev, total, bmap_dev = self._plan_for(rank_lists)
+        args = (self.P, len(self.shapes), tiles_dev.data_ptr(), total, self.tile_elems,
+                bmap_dev.data_ptr() if bmap_dev is not None else None, tin.data_ptr(),
                 torch_dtype_code(self.dtype), tout.data_ptr(), torch_dtype_code(self.out_dtype))
-        tables = tuple(t for t in (self.tiles_dev, self.block_map_dev, tin, tout) if t is not None)
+        tables = tuple(t for t in (tiles_dev, bmap_dev, tin, tout) if t is not None)
 
         def run(op="sum", chunking=None):
             P, T, tiles, total, tile, bmap, pin, dtin, pout, dtout = args
@@ -557,12 +574,13 @@ class MultiAllReduce:
         tw = self._state_table(w)
         tv = self._state_table(v)
         T = len(self.shapes)
+        tiles_dev, total, bmap_dev = self._plan_for(rank_grads)
 
-        tables = tuple(t for t in (self.tiles_dev, self.block_map_dev, tin, tout, tw, tv) if t is not None)
+        tables = tuple(t for t in (tiles_dev, bmap_dev, tin, tout, tw, tv) if t is not None)
 
         def run(lr, mu, op="mean", chunking=None):
-            allreduce_multi_fused_sgd(op, self.P, chunking or self.P, T, self.tiles_dev.data_ptr(),
-                                      self.total_tiles, self.tile_elems, self._block_map_ptr(),
+            allreduce_multi_fused_sgd(op, self.P, chunking or self.P, T, tiles_dev.data_ptr(), total,
+                                      self.tile_elems, bmap_dev.data_ptr() if bmap_dev is not None else None,
                                       tin.data_ptr(),
                                       torch_dtype_code(self.dtype), tw.data_ptr(), tv.data_ptr(), lr, mu,
                                       tout.data_ptr() if tout is not None else None,

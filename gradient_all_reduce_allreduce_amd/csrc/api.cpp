@@ -858,7 +858,8 @@ int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t loc
 }
 
 int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtype in_dtype,
-                   ddp_dtype out_dtype, ddp_tensor_tiles* tiles, int64_t* total_tiles, int64_t* tile_elems) {
+                   ddp_dtype out_dtype, const void* const* align_to, ddp_tensor_tiles* tiles,
+                   int64_t* total_tiles, int64_t* tile_elems) {
     int s = check_ranks(P);
     if (s) return s;
     if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
@@ -866,15 +867,30 @@ int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtyp
         return fail(DDP_E_ARG, "NULL pointer argument");
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown dtype");
     const int64_t tile = ddp::multi_tile_elems(P, in_dtype == DDP_BF16, out_dtype == DDP_BF16);
+    const int ies = elem_bytes(in_dtype);
+    const int small = ies < elem_bytes(out_dtype) ? ies : elem_bytes(out_dtype);
+    // A lead must move every stream by whole 16-byte vectors: inputs,
+    // outputs and float32 optimizer state.
+    const int64_t lead_step = 16 / small > 4 ? 16 / small : 4;
     int64_t next = 0;
     for (int32_t t = 0; t < n_tensors; ++t) {
         if (numels[t] < 0) return fail(DDP_E_ARG, "numels[%d] is negative", t);
         if (numels[t] > (int64_t(1) << 29))
             return fail(DDP_E_UNSUPPORTED, "numels[%d] = %lld is over 2^29 elements", t,
                         static_cast<long long>(numels[t]));
+        int64_t lead = 0;
+        if (align_to != nullptr && numels[t] > 0) {
+            const uintptr_t a = reinterpret_cast<uintptr_t>(align_to[t]);
+            if (a % 16 == 0 && a % 128 != 0) {
+                const int64_t l = static_cast<int64_t>((128 - a % 128) / ies);
+                if (l % lead_step == 0) lead = l < numels[t] ? l : numels[t];
+            }
+        }
         tiles[t].numel = numels[t];
-        tiles[t].first_tile = next;
-        next += (numels[t] + tile - 1) / tile;
+        tiles[t].first_tile = static_cast<int32_t>(next);
+        tiles[t].lead = static_cast<int32_t>(lead);
+        next += lead > 0 ? 1 + (numels[t] - lead + tile - 1) / tile : (numels[t] + tile - 1) / tile;
+        if (next > INT32_MAX) return fail(DDP_E_UNSUPPORTED, "the plan needs over 2^31 - 1 tiles");
     }
     *total_tiles = next;
     *tile_elems = tile;

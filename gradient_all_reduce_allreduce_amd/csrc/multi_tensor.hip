@@ -152,15 +152,22 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     }
     const int t = lo;
     const ddp_tensor_tiles tt = a->tiles[t];
-    const uint32_t t0 = static_cast<uint32_t>((b - tt.first_tile) * TILE);
-    if (static_cast<int64_t>(t0) >= tt.numel) return;
+    // Tile k of the tensor: with a lead, [0, lead) and then whole tiles
+    // from `lead` on (each on a 128-byte line of the address the plan was
+    // aligned to); without, whole tiles from element 0.
+    const int64_t k = b - tt.first_tile;
+    const int64_t lead = tt.lead;
+    const int64_t start = lead == 0 ? k * TILE : (k == 0 ? 0 : lead + (k - 1) * TILE);
+    if (k < 0 || start >= tt.numel) return;
     // Tensors hold at most 2^29 elements (ddp_multi_plan) and the chunk
     // count is below 2^31, so the chunk arithmetic fits 32 bits: three
     // 32-bit divisions by uniform values instead of 64-bit ones.
+    const uint32_t t0 = static_cast<uint32_t>(start);
     const uint32_t n = static_cast<uint32_t>(tt.numel);
     const uint32_t C = static_cast<uint32_t>(a->chunking);
     const uint32_t L = n / C + (n % C != 0u);
-    const uint32_t end = t0 + TILE < n ? t0 + TILE : n;
+    const uint32_t stop = lead != 0 && k == 0 ? static_cast<uint32_t>(lead) : t0 + TILE;
+    const uint32_t end = stop < n ? stop : n;
     const uint32_t j0 = t0 / L;
     const uint32_t j1 = (end - 1) / L;
     const uint32_t tid = threadIdx.x;
@@ -196,6 +203,9 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
         if (write_out) align |= reinterpret_cast<uintptr_t>(dst[k]);
     }
     if constexpr (SGD) align |= reinterpret_cast<uintptr_t>(wp) | reinterpret_cast<uintptr_t>(vp);
+    // The tile's byte offsets in each stream (whole tiles past a lead start
+    // off a multiple of the tile size).
+    align |= (t0 * IES) | (t0 * OES) | (SGD ? t0 * 4u : 0u);
     const bool vector_path = j0 == j1 && end - t0 == TILE && (align & 15u) == 0;
 
     if (!vector_path) {

@@ -95,11 +95,14 @@ typedef struct ddp_segment {
     int64_t len;
 } ddp_segment;
 
-/* One tensor of a multi-tensor all-reduce: its element count and the index
- * of its first tile in the launch (from ddp_multi_plan). */
+/* One tensor of a multi-tensor all-reduce (from ddp_multi_plan): its
+ * element count, the index of its first tile in the launch, and `lead`:
+ * 0, or the length of a short first tile [0, lead) after which every tile
+ * starts on a 128-byte boundary of the address the plan was aligned to. */
 typedef struct ddp_tensor_tiles {
     int64_t numel;
-    int64_t first_tile;
+    int32_t first_tile;
+    int32_t lead;
 } ddp_tensor_tiles;
 
 /*
@@ -528,17 +531,34 @@ int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t loc
  * of the launch rather than in its tail (measured 1.6-2% faster on the
  * 161 ResNet-50 gradient tensors).
  *
+ *
+ * Tiles of a tensor start at its first element, so a tensor that starts
+ * off a 128-byte line (a view into a larger buffer) has every wave access
+ * straddle one line more than it covers, and its stores leave lines partly
+ * written (measured 25% slower on the 161 ResNet-50 tensors as views of
+ * arena rows).  With `align_to`, the address of each tensor (say rank 0's
+ * input), a tensor whose address is 16-byte aligned but not on a line gets
+ * a short first tile up to the next line (`lead` elements) when that keeps
+ * every later tile's offsets 16-byte aligned for both element types and for
+ * float32 optimizer state; the other ranks' copies should then sit at the
+ * same offset within a line, as rows of one arena do.  The plan is then
+ * specific to those addresses.
+ *
  *   numels       host array [n_tensors], each 0 .. 2^29 elements
  *   P, in_dtype, out_dtype   as for the all-reduce (they set the tile size)
+ *   align_to     host array [n_tensors] of addresses, or NULL (no short
+ *                first tiles: the plan depends on the numels only)
  *   tiles        host array [n_tensors] to receive the plan
- *   total_tiles  out: tiles of all tensors (the launch's workgroups)
+ *   total_tiles  out: tiles of all tensors (the launch's workgroups), at
+ *                most 2^31 - 1
  *   tile_elems   out: elements per tile (pass it back to the all-reduce)
  * Errors: DDP_E_ARG (bad counts, pointers, P or dtypes), DDP_E_UNSUPPORTED
- * (a tensor over 2^29 elements: use the single-tensor call).
+ * (a tensor over 2^29 elements: use the single-tensor call; over 2^31 - 1
+ * tiles in all).
  */
 int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P,
-                   ddp_dtype in_dtype, ddp_dtype out_dtype, ddp_tensor_tiles* tiles,
-                   int64_t* total_tiles, int64_t* tile_elems);
+                   ddp_dtype in_dtype, ddp_dtype out_dtype, const void* const* align_to,
+                   ddp_tensor_tiles* tiles, int64_t* total_tiles, int64_t* tile_elems);
 
 /*
  * ddp_multi_block_map -- host only: an index into a multi-tensor plan, so

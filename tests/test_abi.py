@@ -574,6 +574,47 @@ def test_multi_plan():
                                              None) == N.DDP_OK
 
 
+def _plan_reference(numels, tile, ies, oes, addrs):
+    """The plan's rule restated: a tensor whose address is 16-byte aligned
+    but off a 128-byte line gets a short first tile up to the next line when
+    that moves every stream (inputs, outputs, float32 state) by whole
+    16-byte vectors."""
+    step = max(4, 16 // min(ies, oes))
+    out, nxt = [], 0
+    for n, a in zip(numels, addrs):
+        lead = 0
+        if a is not None and n > 0 and a % 16 == 0 and a % 128 != 0:
+            l = (128 - a % 128) // ies
+            if l % step == 0:
+                lead = min(l, n)
+        out.append((n, nxt, lead))
+        nxt += 1 + -(-(n - lead) // tile) if lead else -(-n // tile)
+    return out, nxt
+
+
+def test_multi_plan_leads_put_whole_tiles_on_lines():
+    """With addresses, tensors off a 128-byte line get a short first tile
+    (every later tile starts on a line, at a whole 16-byte vector of every
+    stream); aligned, misaligned (not 16-byte) and tiny tensors get none or
+    the whole tensor; every dtype pair."""
+    rng = np.random.default_rng(11)
+    F32, BF16 = N.DDP_F32, N.DDP_BF16
+    for ins, outs in ((F32, F32), (BF16, F32), (F32, BF16), (BF16, BF16)):
+        ies, oes = (2 if ins == BF16 else 4), (2 if outs == BF16 else 4)
+        for P in (2, 8):
+            numels = rng.choice([0, 1, 5, 31, 64, 1000, 70_001], size=50).astype(np.int64)
+            addrs = [int(rng.integers(1, 1 << 20)) * 4 + (1 << 40) for _ in numels]
+            tiles, total, tile = ddp.ddp_multi_plan(numels, P, ins, outs, align_to=addrs)
+            want, want_total = _plan_reference([int(n) for n in numels], tile, ies, oes, addrs)
+            assert total == want_total
+            for t, (n, first, lead) in enumerate(want):
+                assert (tiles["numel"][t], tiles["first_tile"][t], tiles["lead"][t]) == (n, first, lead), t
+                if lead and lead < n:
+                    assert (addrs[t] + lead * ies) % 128 == 0 and (lead * oes) % 16 == 0 and (lead * 4) % 16 == 0
+            plain, plain_total, _ = ddp.ddp_multi_plan(numels, P, ins, outs)
+            assert not plain["lead"].any() and plain_total <= total
+
+
 def test_multi_block_map_is_the_tensor_of_every_64th_tile():
     """Entry k of the block map is the largest t with first_tile <= 64 k
     (the tensor holding tile 64 k; tensors without tiles give way to the
@@ -646,18 +687,21 @@ def test_multi_launcher_owns_its_tables(monkeypatch):
     ts = [[torch.zeros(s) for s in shapes] for _ in range(2)]
     for bind in ("bind", "bind_sgd"):
         m = api.MultiAllReduce(shapes, 2, torch.float32, device="cpu")
-        plan = weakref.ref(m.tiles_dev)
         if bind == "bind":
             run = m.bind(ts, out=[[torch.zeros(s) for s in shapes] for _ in range(2)])
         else:
             run = m.bind_sgd(ts, [torch.zeros(s) for s in shapes], [torch.zeros(s) for s in shapes])
+        # The plan the launcher uses: the shared one, or its own when some
+        # tensor starts off a 128-byte line.
+        assert run.tables[0].numel() == len(shapes) * api.TILES_DTYPE.itemsize, bind
+        plan = weakref.ref(run.tables[0])
+        bmap = weakref.ref(run.tables[1])
         del m
         gc.collect()
-        assert plan() is not None, bind
-        assert any(t is plan() for t in run.tables), bind
+        assert plan() is not None and bmap() is not None, bind
         del run
         gc.collect()
-        assert plan() is None, bind
+        assert plan() is None and bmap() is None, bind
 
 
 def test_multi_launcher_keeps_bound_tensors_alive(monkeypatch):

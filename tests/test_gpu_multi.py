@@ -344,3 +344,61 @@ def test_multi_fused_sgd_on_vit_bf16_equals_single_tensor_fused_sgd():
         assert torch.equal(sd[t][1].view(torch.int32), ref[t][1].view(torch.int32)), t
         for r in range(P):
             assert torch.equal(out[r][t].reshape(-1).view(torch.int16), ref_out[t][r].view(torch.int16)), (t, r)
+
+
+@pytest.mark.parametrize("pair,sgd", [(("f32", "f32"), False), (("bf16", "f32"), False), (("f32", "f32"), True),
+                                      (("bf16", "bf16"), False)])
+def test_tensors_as_views_off_lines_equal_oracle(pair, sgd):
+    """Tensors that are views of one buffer per rank, at 16-byte but mostly
+    not 128-byte boundaries (rows of equal stride, as gradients as bucket
+    views lie): the plan gives them short first tiles so that whole tiles
+    sit on lines.  Every tensor is still the oracle's ring on that tensor
+    alone (with its momentum step when fused), bit for bit."""
+    it, ot = pair
+    tdt = torch.bfloat16 if it == "bf16" else torch.float32
+    odt = torch.bfloat16 if ot == "bf16" else torch.float32
+    P = 8
+    rng = np.random.default_rng(41)
+    numels = [int(n) * 8 for n in rng.choice([1, 3, 40, 129, 1000, 8191], size=120)]
+    offs, o = [], 8
+    for n in numels:
+        offs.append(o)
+        o += n
+    stride = -(-o // 64) * 64 + 1024
+    shapes = [(n,) for n in numels]
+    host = []
+    base_in = torch.empty(P * stride, dtype=tdt, device=DEV)
+    base_out = torch.empty(P * stride, dtype=odt, device=DEV)
+    views_in, views_out = [], []
+    for r in range(P):
+        x = (rng.standard_normal(o) * np.exp2(rng.integers(-10, 11, o))).astype(np.float32)
+        if tdt == torch.bfloat16:
+            x = workloads.to_bf16_bits(x)
+            base_in[r * stride:r * stride + o].copy_(torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16))
+        else:
+            base_in[r * stride:r * stride + o].copy_(torch.from_numpy(x).to(DEV))
+        host.append(x)
+        views_in.append([base_in[r * stride + a:r * stride + a + n] for a, n in zip(offs, numels)])
+        views_out.append([base_out[r * stride + a:r * stride + a + n] for a, n in zip(offs, numels)])
+    m = ddp.MultiAllReduce(shapes, P, tdt, odt, device=DEV)
+    addrs = [views_in[0][t].data_ptr() for t in m.plan_order]
+    tiles, total, _ = ddp.ddp_multi_plan([numels[t] for t in m.plan_order], P, ddp.api.torch_dtype_code(tdt),
+                                         ddp.api.torch_dtype_code(odt), align_to=addrs)
+    assert (tiles["lead"] > 0).sum() > 60 and total > m.total_tiles
+    C = P
+    if not sgd:
+        m.bind(views_in, views_out)("mean", C)
+    else:
+        sh, sd = sgd_state(shapes, seed=42)
+        m.bind_sgd(views_in, [p[0] for p in sd], [p[1] for p in sd], out=views_out)(1e-3, 0.9, "mean", C)
+    torch.cuda.synchronize()
+    for t, (a, n) in enumerate(zip(offs, numels)):
+        X = np.stack([host[r][a:a + n] for r in range(P)])
+        want = oracle_ring(X, "mean", C, in_dtype=it, out_dtype=ot)
+        got = np.stack([bits_of(views_out[r][t]) for r in range(P)])
+        assert_same_bits(got, want, f"{it}->{ot} t={t} n={n} off={a}")
+        if sgd:
+            g = oracle_ring(X, "mean", C, in_dtype=it, out_dtype="f32")[0]
+            w1, v1 = oracle.sgd_momentum(g, sh[t][0], sh[t][1], 1e-3, 0.9)
+            assert_same_bits(sd[t][0].cpu().numpy().reshape(1, -1), w1[None], f"t={t} w")
+            assert_same_bits(sd[t][1].cpu().numpy().reshape(1, -1), v1[None], f"t={t} v")
