@@ -218,6 +218,41 @@ def test_ragged2000_p4_pack_allreduce_unpack_full_size():
             assert torch.equal(tensors[r][t].view(torch.int32), tensors[0][t].view(torch.int32))
 
 
+def test_ragged2000_p4_multi_tensor_full_size():
+    """The same 2,000 tensors per rank (P = 4, Sum, in place) through the
+    multi-tensor launch the benchmark times: each tensor its own ring with
+    chunk length ceil(n_t / C); sampled elements of 300 tensors checked
+    against the oracle's ring one element at a time."""
+    cfg = workloads.CONFIGS["p4-ragged2000-f32-sum-25MiB"]
+    P, C = cfg["P"], cfg["chunking"]
+    sizes = workloads.ragged_sizes()
+    tensors = []
+    for r in range(P):
+        ts = []
+        for t, s in enumerate(sizes):
+            x = torch.empty(s, dtype=torch.float32, device=DEV)
+            workloads.torch_uniform_(x, -1.0, 1.0, seed=40_000 * (r + 1) + t)
+            ts.append(x)
+        tensors.append(ts)
+    rng = np.random.default_rng(5)
+    picks = []
+    for t in sorted(set(rng.integers(0, len(sizes), 300).tolist()) | {0, len(sizes) - 1}):
+        L = -(-sizes[t] // C)
+        for off in {0, sizes[t] - 1, int(rng.integers(0, sizes[t])), min(sizes[t] - 1, L), max(0, L - 1)}:
+            picks.append((t, off))
+    V = np.array([[tensors[r][t][off].item() for (t, off) in picks] for r in range(P)], np.float32)
+    run = ddp.MultiAllReduce([(s,) for s in sizes], P, torch.float32, device=DEV).bind(tensors, tensors)
+    run("sum", C)
+    torch.cuda.synchronize()
+    start = np.array([oracle.chunk_start_ranks_at(sizes[t], C, P, [off])[0] for (t, off) in picks])
+    want = oracle.ring_allreduce_sampled(V, start, "sum")
+    got = np.array([[tensors[r][t][off].item() for (t, off) in picks] for r in range(P)], np.float32)
+    assert_same_bits(got, want, "multi-tensor ragged samples")
+    for t in (0, len(sizes) // 2, len(sizes) - 1):
+        for r in range(1, P):
+            assert torch.equal(tensors[r][t].view(torch.int32), tensors[0][t].view(torch.int32))
+
+
 def test_transformer2b_p8_bf16_to_f32_100MiB_full_size():
     """P=8, 2,017,529,856-parameter dense transformer gradient set in bf16
     (32.3 GB of rank inputs), N(0, 1e-4), Mean, fp32 outputs (64.6 GB),
