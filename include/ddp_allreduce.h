@@ -587,8 +587,11 @@ int ddp_multi_block_map(const ddp_tensor_tiles* tiles, int32_t n_tensors,
  * ceil(numel_t / C)).
  *
  *   tiles_dev    DEVICE array [n_tensors]: the plan of ddp_multi_plan for
- *                these tensors, P and dtypes (the library does not read it
- *                on the host; any other table is undefined behaviour)
+ *                these tensors, P and dtypes (made with or without align_to;
+ *                with, the tiles sit on lines of the addresses it was given,
+ *                and the results are the same bits either way; the library
+ *                does not read it on the host; any other table is undefined
+ *                behaviour)
  *   total_tiles, tile_elems   the values ddp_multi_plan returned
  *                (tile_elems is checked against this call's tile size)
  *   block_first_dev  DEVICE array: the block map of ddp_multi_block_map for
