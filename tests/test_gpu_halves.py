@@ -89,3 +89,38 @@ def test_reduce_scatter_then_all_gather_is_the_all_reduce(pair, P):
             ddp.all_gather(ins, C)
             torch.cuda.synchronize()
             assert_same_bits(to_host(ins), to_host(fused), "in place")
+
+
+@pytest.mark.parametrize("P,C", [(8, 8), (4, 8), (2, 6)])
+def test_full_buckets_as_one_call_equal_one_call_per_bucket(P, C):
+    """With C a multiple of P and the bucket length a multiple of C,
+    consecutive full buckets form one ring with chunking (buckets x C): the
+    reduce-scatter and the all-gather over three full buckets in one call
+    give the bits of one call per bucket (what the flat-buffer measurement
+    of the halves relies on)."""
+    E, nb = 8192 * C, 3
+    n = nb * E
+    X = draw(P, n, "f32", seed=60 + P)
+    ins = to_device(X, "f32")
+    per_rs, _ = sentinel_tensors(P, n, "f32")
+    one_rs, _ = sentinel_tensors(P, n, "f32")
+    for k in range(nb):
+        ddp.reduce_scatter([x[k * E:(k + 1) * E] for x in ins], "mean", C,
+                           out=[y[k * E:(k + 1) * E] for y in per_rs])
+    ddp.reduce_scatter(ins, "mean", nb * C, out=one_rs)
+    torch.cuda.synchronize()
+    for r in range(P):
+        assert torch.equal(per_rs[r].view(torch.int32), one_rs[r].view(torch.int32)), r
+    per_ag = [x.clone() for x in per_rs]
+    one_ag = [x.clone() for x in per_rs]
+    for k in range(nb):
+        ddp.all_gather([x[k * E:(k + 1) * E] for x in per_ag], C)
+    ddp.all_gather(one_ag, nb * C)
+    torch.cuda.synchronize()
+    for r in range(P):
+        assert torch.equal(per_ag[r].view(torch.int32), one_ag[r].view(torch.int32)), r
+    # and the pair is the oracle's all-reduce of each bucket
+    for k in range(nb):
+        want, _ = oracle.ring_allreduce(X[:, k * E:(k + 1) * E], "mean", C)
+        got = to_host([t[k * E:(k + 1) * E] for t in one_ag])
+        assert_same_bits(got, want, f"bucket {k}")
