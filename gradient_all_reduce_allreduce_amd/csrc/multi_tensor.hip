@@ -8,10 +8,15 @@
 // and all-reduce", "Communication costs").  Here T tensors of P ranks are
 // all-reduced by one launch: tensor t is its own ring all-reduce, with its
 // own chunk length ceil(numel_t / C), exactly as if it were passed alone to
-// allreduce_ring_emulated.  The host plan gives every tensor a run of tiles;
-// a workgroup finds its tensor by a binary search over the plan (uniform,
-// scalar loads) and then works like the single-tensor kernel: rotated rank
-// pointers, one fixed fold, P output stores.  Between the search and the
+// allreduce_ring_emulated.  The host plan gives every tensor a run of tiles
+// (with a short first tile when the tensor starts off a 128-byte line, so
+// that the others cover whole lines); a workgroup finds its tensor by a
+// binary search over the plan (uniform, scalar loads), narrowed by a map of
+// every 64th tile's tensor, and then works like the single-tensor kernel:
+// rotated rank pointers, one fixed fold, P output stores.  While its data
+// is in flight it also reads the plan entry and rank pointers of the tensor
+// a few rounds of tiles ahead, so that later tiles on the same CU find them
+// in the scalar cache.  Between the search and the
 // tile's first data load there is one more round trip: the tensor's entry,
 // then every rank pointer in fold and store order, read with independent
 // scalar loads issued together, with the chunk arithmetic in 32 bits.
@@ -23,9 +28,9 @@
 // takes one SGD-momentum step on its float32 master weights and momentum,
 // as each replica's optimizer.step() does after the per-parameter
 // all-reduces (same lecture section), with or without writing the reduced
-// gradients.  Tiles of small tensors, tiles
-// across a chunk boundary and tensors (or optimizer state) not 16-byte
-// aligned take a per-element path whose rank pointers are read per lane.
+// gradients.  Tiles of small tensors, short first tiles, tiles across a
+// chunk boundary and tensors (or optimizer state) not 16-byte aligned take
+// a per-element path whose rank pointers are read per lane.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -155,10 +160,10 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     // Tile k of the tensor: with a lead, [0, lead) and then whole tiles
     // from `lead` on (each on a 128-byte line of the address the plan was
     // aligned to); without, whole tiles from element 0.
-    const int64_t k = b - tt.first_tile;
+    const int64_t kt = b - tt.first_tile;
     const int64_t lead = tt.lead;
-    const int64_t start = lead == 0 ? k * TILE : (k == 0 ? 0 : lead + (k - 1) * TILE);
-    if (k < 0 || start >= tt.numel) return;
+    const int64_t start = lead == 0 ? kt * TILE : (kt == 0 ? 0 : lead + (kt - 1) * TILE);
+    if (kt < 0 || start >= tt.numel) return;
     // Tensors hold at most 2^29 elements (ddp_multi_plan) and the chunk
     // count is below 2^31, so the chunk arithmetic fits 32 bits: three
     // 32-bit divisions by uniform values instead of 64-bit ones.
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     const uint32_t n = static_cast<uint32_t>(tt.numel);
     const uint32_t C = static_cast<uint32_t>(a->chunking);
     const uint32_t L = n / C + (n % C != 0u);
-    const uint32_t stop = lead != 0 && k == 0 ? static_cast<uint32_t>(lead) : t0 + TILE;
+    const uint32_t stop = lead != 0 && kt == 0 ? static_cast<uint32_t>(lead) : t0 + TILE;
     const uint32_t end = stop < n ? stop : n;
     const uint32_t j0 = t0 / L;
     const uint32_t j1 = (end - 1) / L;
