@@ -626,17 +626,17 @@ __device__ __forceinline__ void rs_tile(KArgs a, uint32_t t0) {
             u32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
-            *reinterpret_cast<u32x4*>(owner + i0 * OES) = o;
+            store16(owner, a->n * OES, i0 * OES, o);
         } else if constexpr (OUTB) {
             u32x2 o;
 #pragma unroll
             for (int k = 0; k < 2; ++k) o[k] = bf16_bits(g[2 * k]) | (bf16_bits(g[2 * k + 1]) << 16);
-            *reinterpret_cast<u32x2*>(owner + i0 * OES) = o;
+            store8(owner, a->n * OES, i0 * OES, o);
         } else {
             u32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(g[e]);
-            *reinterpret_cast<u32x4*>(owner + i0 * OES) = o;
+            store16(owner, a->n * OES, i0 * OES, o);
         }
     }
 }
