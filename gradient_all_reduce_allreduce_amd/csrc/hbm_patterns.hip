@@ -38,7 +38,17 @@
 //               summed, float32 w and v read and written, and with output
 //               the bf16 sum to 8 streams
 //   red8 f32, separate allocations   the f32 pattern on 16 hipMallocs
+//
+//   gradient_all_reduce_allreduce_amd/hbm_patterns --launch-cost
+//
+// prints instead what a launch costs the GPU itself: empty one-wave kernels
+// of 1 and of 25,600 workgroups (one 25 MiB float32 bucket's tiles), back to
+// back on one stream behind about 1.5 ms of copying, so that the host has
+// queued every measured launch before the GPU reaches them and the events
+// around them time the GPU's side alone.
 #include <hip/hip_runtime.h>
+
+#include <cstring>
 
 #include <cstdio>
 #include <cstdlib>
@@ -391,6 +401,43 @@ __global__ __launch_bounds__(kW) void red8_lds_kernel(Streams p, uint32_t* sink)
     }
 }
 
+// Does nothing (the store is never taken: no stream is that long); the
+// arguments are as large as the pattern kernels'.
+__global__ __launch_bounds__(kW) void empty_kernel(Streams p, uint32_t* sink) {
+    if (p.out_bytes == 0xffffffffu && threadIdx.x == 0) sink[0] = blockIdx.x;
+}
+
+// GPU-side microseconds per launch of `grid` empty workgroups at `cap`
+// workgroups per CU (best of 3 batches of `iters`), behind `ahead` copy
+// launches over `copy` sets of `copy_grid` workgroups.
+static double launch_us(unsigned grid, int cap, const Streams& st, uint32_t* sink,
+                        const std::vector<Streams>& copy, unsigned copy_grid, int ahead, int iters) {
+    hipFuncAttributes at{};
+    CK(hipFuncGetAttributes(&at, reinterpret_cast<const void*>(empty_kernel)));
+    const unsigned want = lds_for(cap);
+    const unsigned lds = want > at.sharedSizeBytes ? want - static_cast<unsigned>(at.sharedSizeBytes) : 0u;
+    hipEvent_t a, b;
+    CK(hipEventCreate(&a));
+    CK(hipEventCreate(&b));
+    double best = 1e30;
+    for (int rep = 0; rep < 3; ++rep) {
+        CK(hipDeviceSynchronize());
+        for (int i = 0; i < ahead; ++i)
+            hipLaunchKernelGGL((stream_kernel<1, 1>), dim3(copy_grid), dim3(kW), 0, 0, copy[i % copy.size()], sink);
+        CK(hipEventRecord(a));
+        for (int i = 0; i < iters; ++i) hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(kW), lds, 0, st, sink);
+        CK(hipEventRecord(b));
+        CK(hipGetLastError());
+        CK(hipEventSynchronize(b));
+        float ms = 0.f;
+        CK(hipEventElapsedTime(&ms, a, b));
+        if (ms * 1e3 / iters < best) best = ms * 1e3 / iters;
+    }
+    CK(hipEventDestroy(a));
+    CK(hipEventDestroy(b));
+    return best;
+}
+
 template <typename K, typename S>
 static double rate(K kernel, unsigned grid, int cap, const std::vector<S>& sets, uint32_t* sink,
                    double bytes_per_launch, int reps = 40, unsigned block = kW) {
@@ -429,10 +476,43 @@ static Streams make_set(char* in, size_t in_stride, char* out, size_t out_stride
     return s;
 }
 
-int main() {
+static int launch_cost(uint32_t* sink) {
+    const size_t cb = size_t(200) << 20;
+    char* arena = nullptr;
+    CK(hipMalloc(&arena, cb * 4));
+    fill(arena, cb * 4, 4u);
+    std::vector<Streams> copy;
+    for (int s = 0; s < 2; ++s) copy.push_back(make_set(arena + 2 * s * cb, cb, arena + (2 * s + 1) * cb, cb,
+                                                        static_cast<uint32_t>(cb)));
+    const unsigned g200 = static_cast<unsigned>(cb / 16 / kW);
+    CK(hipDeviceSynchronize());
+    const Streams st = copy[0];
+    std::printf("GPU-side cost of one launch (empty one-wave workgroups, back to back on one stream)\n");
+    std::printf("%-44s %8s %8s\n", "launch", "cap", "us");
+    const struct { const char* name; unsigned grid; int cap; int iters; } rows[] = {
+        {"1 workgroup", 1, 0, 200},
+        {"1 workgroup, LDS for 5 per CU", 1, 5, 200},
+        {"25,600 workgroups", 25600, 0, 150},
+        {"25,600 workgroups, LDS for 5 per CU", 25600, 5, 150},
+        {"102,400 workgroups, LDS for 5 per CU", 102400, 5, 60},
+    };
+    for (const auto& r : rows) {
+        std::printf("%-44s %8d %8.2f\n", r.name, r.cap, launch_us(r.grid, r.cap, st, sink, copy, g200, 24, r.iters));
+        std::fflush(stdout);
+    }
+    CK(hipFree(arena));
+    return 0;
+}
+
+int main(int argc, char** argv) {
     const int caps[] = {0, 3, 4, 5, 6, 8, 12, 16};
     uint32_t* sink = nullptr;
     CK(hipMalloc(&sink, 64));
+    if (argc > 1 && std::strcmp(argv[1], "--launch-cost") == 0) {
+        const int rc = launch_cost(sink);
+        CK(hipFree(sink));
+        return rc;
+    }
 
     // 25 MiB streams: 4 sets of 16 streams back to back (1.6 GiB); the
     // arena holds twice that for 2 sets of 100 MiB streams
