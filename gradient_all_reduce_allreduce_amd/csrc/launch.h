@@ -74,8 +74,8 @@ constexpr int ring_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
 constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
     return kSgdWg[(grad_bf16 ? 0 : 2) + (writes_ranks ? 1 : 0)][P];
 }
-// The tree strategies walk a parent table before their first load and
-// measured best one workgroup above the ring (5 at P = 8, f32).
+// The tree strategies measured best one workgroup above the ring (5 at
+// P = 8, f32; 4 and 6 were slower, also with the order table).
 constexpr int tree_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
     return ring_wg_per_cu(P, in_bf16, out_bf16) + 1;
 }

@@ -159,7 +159,20 @@ int launch_ring_reduce(const RingLaunch& l, const char** msg) {
             grid = (a.n_vec + tile - 1) / tile;   // one tile per workgroup
             if (grid < 1) grid = 1;               // the tail still needs a workgroup
         }
+        rr::TreeArgs ta{};
         void* args[] = {&a};
+        if (l.mode == kTree) {
+            // Row s_g * Lr + s_l: rank k of the fold is node (s_g + k / Lr) mod G,
+            // peer (s_l + k) mod Lr, as the kernels' level_ranks walks it.
+            const int Lr = a.group_size;
+            ta.ring = a;
+            for (int sg = 0; sg < groups; ++sg)
+                for (int sl = 0; sl < Lr; ++sl)
+                    for (int k = 0; k < l.P; ++k)
+                        ta.order_in[(sg * Lr + sl) * l.P + k] =
+                            a.in[((sg + k / Lr) % groups) * Lr + (sl + k) % Lr];
+            args[0] = &ta;
+        }
         const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(rr::kBlock), args,
                                              lds_reserve(wg_per_cu(l)), static_cast<hipStream_t>(l.stream));
         if (e != hipSuccess) {

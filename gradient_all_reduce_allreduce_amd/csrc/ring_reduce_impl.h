@@ -174,6 +174,19 @@ __device__ __forceinline__ void momentum_step(float g, float& w, float& v, float
 // scalar load, with no private copy of the argument block.
 typedef const __attribute__((address_space(4))) RingArgs* KArgs;
 
+// The tree strategies' arguments: the ring's, then the input pointers in
+// fold order for every pair of level start ranks.  Row s_g * group_size +
+// s_l holds the P ranks that the fold registers take when the local order
+// starts at peer s_l and the global order at node s_g (level_ranks), so
+// that a tile reads its P pointers with one scalar load, as the ring's
+// tiles do, instead of deriving the order first.  The host fills the P
+// rows of the launch (G * group_size = P).
+struct TreeArgs {
+    RingArgs ring;
+    const void* order_in[kMaxRanks * kMaxRanks];
+};
+typedef const __attribute__((address_space(4))) TreeArgs* KTree;
+
 __device__ __forceinline__ KArgs kernel_args() {
     return (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
 }
@@ -856,8 +869,28 @@ __device__ __forceinline__ void tree_element(KArgs a, uint32_t i) {
     }
 }
 
+// Where a tree tile's chunks end at both levels, and its row of the order
+// table.
+struct TreeTileStart {
+    uint32_t next_local;    // first element of the next local chunk
+    uint32_t next_global;   // first element of the next global chunk
+    int row;                // s_g * group_size + s_l
+};
+
+__device__ __forceinline__ TreeTileStart tree_tile_start(KArgs a, uint32_t t0) {
+    uint32_t rl, rg;
+    const uint32_t ql = chunk_steps(t0, a->ring, rl);
+    const uint32_t qg = chunk_steps(t0, a->global, rg);
+    TreeTileStart st;
+    st.next_local = t0 + (a->ring.d - rl);
+    st.next_global = t0 + (a->global.d - rg);
+    st.row = mod_members(a->global.first + qg, a->global) * a->group_size + mod_members(a->ring.first + ql, a->ring);
+    return st;
+}
+
 template <int P, bool INB, bool OUTB, bool FULL>
-__device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
+__device__ __forceinline__ void tree_tile(KArgs a, const void* const __attribute__((address_space(4)))* order,
+                                          uint32_t t0, const TreeTileStart& st) {
 #pragma clang fp contract(off)
     constexpr int U = ring_vectors_per_lane(P, false);
     constexpr int V = ring_lane_elems(INB, OUTB, false);
@@ -868,12 +901,7 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
     const uint32_t tid = threadIdx.x;
     const uint32_t n_vec = a->n_vec;
     const uint32_t last = FULL ? t0 + TILE - 1 : n_vec - 1;
-    const int G = a->groups;
-    const int Lr = a->group_size;
-    uint32_t rl, rg;
-    const uint32_t ql = chunk_steps(t0, a->ring, rl);
-    const uint32_t qg = chunk_steps(t0, a->global, rg);
-    if (t0 + (a->ring.d - rl) <= last || t0 + (a->global.d - rg) <= last) {
+    if (st.next_local <= last || st.next_global <= last) {
         // a local or global chunk boundary inside the tile: element by element
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -883,9 +911,9 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
         }
         return;
     }
-    int rank[P];
-    level_ranks<P>(G, Lr, mod_members(a->ring.first + ql, a->ring), mod_members(a->global.first + qg, a->global),
-                   rank);
+    const char* src[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) src[k] = static_cast<const char*>(order[st.row * P + k]);
     u32x4 x[P][U];
     bool ok[U];
 #pragma unroll
@@ -895,7 +923,7 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
         if (ok[u]) {
 #pragma unroll
             for (int k = 0; k < P; ++k)
-                x[k][u] = load_lane<WIN>(static_cast<const char*>(a->in[rank[k]]) + i0 * IES);
+                x[k][u] = load_lane<WIN>(src[k] + i0 * IES);
         } else {
 #pragma unroll
             for (int r = 0; r < P; ++r) x[r][u] = u32x4{0u, 0u, 0u, 0u};
@@ -949,16 +977,23 @@ __device__ __forceinline__ void tree_tile(KArgs a, uint32_t t0) {
 }
 
 template <int P, bool INB, bool OUTB>
-__global__ __launch_bounds__(kBlock) void tree_reduce_kernel(RingArgs) {
+__global__ __launch_bounds__(kBlock) void tree_reduce_kernel(TreeArgs) {
     constexpr uint32_t TILE =
         static_cast<uint32_t>(kBlock) * ring_vectors_per_lane(P, false) * ring_lane_elems(INB, OUTB, false);
-    const KArgs a = kernel_args();
+    const KTree ta = (KTree)(__builtin_amdgcn_kernarg_segment_ptr());
+    const KArgs a = &ta->ring;
     const uint32_t t0 = blockIdx.x * TILE;
     const uint32_t n_vec = a->n_vec;
+    // The tile's chunk ends and order row, computed before the branch so
+    // that every argument they need goes out together with n_vec.
+    const TreeTileStart st = tree_tile_start(a, t0);
+    pin_sgpr(st.next_local);
+    pin_sgpr(st.next_global);
+    pin_sgpr(st.row);
     if (t0 + TILE <= n_vec) {
-        tree_tile<P, INB, OUTB, true>(a, t0);
+        tree_tile<P, INB, OUTB, true>(a, ta->order_in, t0, st);
     } else if (t0 < n_vec) {
-        tree_tile<P, INB, OUTB, false>(a, t0);
+        tree_tile<P, INB, OUTB, false>(a, ta->order_in, t0, st);
     }
     if (blockIdx.x == gridDim.x - 1) {
         const uint32_t i = n_vec + threadIdx.x;
@@ -968,8 +1003,8 @@ __global__ __launch_bounds__(kBlock) void tree_reduce_kernel(RingArgs) {
 
 // Local or global chunks shorter than a tile: one element per lane.
 template <int P, bool INB, bool OUTB>
-__global__ __launch_bounds__(kBlock) void tree_reduce_scalar_kernel(RingArgs) {
-    const KArgs a = kernel_args();
+__global__ __launch_bounds__(kBlock) void tree_reduce_scalar_kernel(TreeArgs) {
+    const KArgs a = &((KTree)(__builtin_amdgcn_kernarg_segment_ptr()))->ring;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i < a->n) tree_element<P, INB, OUTB>(a, i);
 }
