@@ -507,11 +507,35 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
     const uint32_t seg2 = a->seg2;
     uint32_t next;
     int s0;
-    if (t0 < seg2) {
-        s0 = tile_chunk<P>(t0, a->ring, next);
+    if constexpr (INB && !OUTB && !SGD) {
+        // bf16 -> float32: seg2 first, then the segment's chunk map.  On
+        // 100 MiB buckets this measured 0.9% faster than the one batch
+        // below, which is 0.2-0.7% faster for every other instantiation
+        // measured (float32, and bf16 with the optimizer step).
+        if (t0 < seg2) {
+            s0 = tile_chunk<P>(t0, a->ring, next);
+        } else {
+            s0 = tile_chunk<P>(t0 - seg2, a->global, next);
+            next += seg2;
+        }
     } else {
-        s0 = tile_chunk<P>(t0 - seg2, a->global, next);
-        next += seg2;
+        // Both segments' chunk maps are read in the same batch as seg2 and
+        // n_vec, and the tile selects one: no round trip waits for seg2.
+        const uint32_t rd = a->ring.d, rm = a->ring.m, roff = a->ring.off, rfirst = a->ring.first;
+        const uint32_t gd = a->global.d, gm = a->global.m, goff = a->global.off, gfirst = a->global.first;
+        asm volatile("" ::"s"(seg2), "s"(n_vec), "s"(rd), "s"(rm), "s"(roff), "s"(rfirst), "s"(gd), "s"(gm),
+                     "s"(goff), "s"(gfirst));
+        const bool second = t0 >= seg2;
+        const uint32_t d = second ? gd : rd;
+        const uint32_t x = (second ? t0 - seg2 : t0) + (second ? goff : roff);
+        uint32_t q = __umulhi(x, second ? gm : rm);
+        uint32_t r = x - q * d;
+        if (r >= d) {
+            ++q;
+            r -= d;
+        }
+        next = t0 + (d - r);
+        s0 = static_cast<int>(((second ? gfirst : rfirst) + q) % static_cast<uint32_t>(P));
     }
     if (t0 + TILE <= n_vec) {
         process_tile<P, INB, OUTB, SGD, true>(a, t0, s0, next);
