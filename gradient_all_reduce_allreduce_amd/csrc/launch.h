@@ -74,6 +74,18 @@ constexpr int ring_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
 constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
     return kSgdWg[(grad_bf16 ? 0 : 2) + (writes_ranks ? 1 : 0)][P];
 }
+// A pause at the start of every workgroup of the fused all-reduce, in
+// units of 64 clocks (s_sleep): 0 except where measured faster.  It acts as
+// a fraction of a workgroup below the cap: a new workgroup issues its loads
+// a little after the one it replaces finished.  bf16 -> f32 at P = 8 and 5
+// workgroups per CU, on 100 MiB buckets: 6,389 GB/s with no pause, 6,505-6,512
+// with 3, 4 or 5, 6,451 with 8; at 6 per CU a pause of 12 came to 6,477.
+// The same pause for the other type pairs and the optimizer step was level
+// or slower at their caps.
+constexpr int ring_start_sleep(int P, bool in_bf16, bool out_bf16, bool sgd) {
+    return (P == 8 && in_bf16 && !out_bf16 && !sgd) ? 4 : 0;
+}
+
 // The tree strategies measured best one workgroup above the ring (5 at
 // P = 8, f32; 4 and 6 were slower, also with the order table).
 constexpr int tree_wg_per_cu(int P, bool in_bf16, bool out_bf16) {
