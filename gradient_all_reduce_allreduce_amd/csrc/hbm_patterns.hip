@@ -48,10 +48,9 @@
 // around them time the GPU's side alone.
 #include <hip/hip_runtime.h>
 
-#include <cstring>
-
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

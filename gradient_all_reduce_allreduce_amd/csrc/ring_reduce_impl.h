@@ -510,9 +510,10 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_kernel(RingArgs) {
     if constexpr (INB && !OUTB && !SGD) {
         constexpr int kSleep = ring_start_sleep(P, INB, OUTB, SGD);
         if constexpr (kSleep > 0) __builtin_amdgcn_s_sleep(kSleep);
-        // bf16 -> float32: seg2 first, then the segment's chunk map.  On
-        // 100 MiB buckets this measured 0.9% faster than the one batch
-        // below, which is 0.2-0.7% faster for every other instantiation
+        // bf16 -> float32: the start pause (launch.h), then seg2, then the
+        // segment's chunk map.  Without the pause this order measured 0.9%
+        // faster on 100 MiB buckets than the one batch below, and level with
+        // it; the one batch is 0.2-0.7% faster for every other instantiation
         // measured (float32, and bf16 with the optimizer step).
         if (t0 < seg2) {
             s0 = tile_chunk<P>(t0, a->ring, next);
