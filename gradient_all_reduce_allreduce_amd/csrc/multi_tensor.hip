@@ -59,6 +59,16 @@ struct MultiArgs {
 };
 
 typedef const __attribute__((address_space(4))) MultiArgs* KMulti;
+// The plan, the block map and the pointer tables as the kernel reads them:
+// through the constant address space.  The kernel never writes them, and a
+// uniform read there is always a scalar load.  Through plain pointers the
+// reads are scalar only while the compiler can prove that nothing before
+// them writes memory; anything it cannot see through (an s_sleep, an empty
+// asm volatile) turns them into vector loads that wait behind the tiles'
+// data, which measured 20-25% slower.
+typedef const __attribute__((address_space(4))) ddp_tensor_tiles* CTiles;
+typedef const __attribute__((address_space(4))) int32_t* CInts;
+typedef const void* const __attribute__((address_space(4)))* CPtrs;
 
 // Non-temporal loads through global-address-space pointers.  The tensors'
 // addresses come from device tables, so the compiler cannot tell that they
@@ -133,6 +143,12 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     const KMulti a = multi_args();
     const int T = a->T;
     const int64_t b = blockIdx.x;
+    const CTiles tiles = (CTiles)(a->tiles);
+    const CInts block_first = (CInts)(a->block_first);
+    const CPtrs in_tab = (CPtrs)(a->in);
+    const CPtrs out_tab = (CPtrs)(a->out);
+    const CPtrs w_tab = (CPtrs)(a->w);
+    const CPtrs v_tab = (CPtrs)(a->v);
 
     // The tensor whose tile run holds this workgroup: largest t with
     // first_tile <= b, by a binary search over the plan.  With the block
@@ -143,20 +159,23 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     // level in one round trip measured 7-20% slower).
     int lo = 0;
     int hi = T - 1;
-    if (a->block_first != nullptr) {
+    if (block_first != nullptr) {
         const uint32_t k = static_cast<uint32_t>(b) / kMultiBlockTiles;
-        const int f = a->block_first[k];
-        const int g = (k + 1) * kMultiBlockTiles < gridDim.x ? a->block_first[k + 1] : T - 1;
+        const int f = block_first[k];
+        const int g = (k + 1) * kMultiBlockTiles < gridDim.x ? block_first[k + 1] : T - 1;
         // Clamped, so that a map of another plan reads only entries of this one.
         lo = f < 0 ? 0 : (f > T - 1 ? T - 1 : f);
         hi = g < lo ? lo : (g > T - 1 ? T - 1 : g);
     }
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a->tiles[mid].first_tile <= b) lo = mid; else hi = mid - 1;
+        if (tiles[mid].first_tile <= b) lo = mid; else hi = mid - 1;
     }
     const int t = lo;
-    const ddp_tensor_tiles tt = a->tiles[t];
+    ddp_tensor_tiles tt;
+    tt.numel = tiles[t].numel;
+    tt.first_tile = tiles[t].first_tile;
+    tt.lead = tiles[t].lead;
     // Tile k of the tensor: with a lead, [0, lead) and then whole tiles
     // from `lead` on (each on a 128-byte line of the address the plan was
     // aligned to); without, whole tiles from element 0.
@@ -188,17 +207,17 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     char* dst[P];
 #pragma unroll
     for (int k = 0; k < P; ++k)
-        src[k] = static_cast<const char*>(a->in[static_cast<int64_t>(rr::rank_at(s0, k, P)) * T + t]);
+        src[k] = static_cast<const char*>(in_tab[static_cast<int64_t>(rr::rank_at(s0, k, P)) * T + t]);
     if (write_out) {
 #pragma unroll
         for (int q = 0; q < P; ++q)
-            dst[q] = static_cast<char*>(a->out[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]);
+            dst[q] = static_cast<char*>(const_cast<void*>(out_tab[static_cast<int64_t>(rr::rank_at(rot, q, P)) * T + t]));
     }
     char* wp = nullptr;
     char* vp = nullptr;
     if constexpr (SGD) {
-        wp = reinterpret_cast<char*>(a->w[t]);
-        vp = reinterpret_cast<char*>(a->v[t]);
+        wp = static_cast<char*>(const_cast<void*>(w_tab[t]));
+        vp = static_cast<char*>(const_cast<void*>(v_tab[t]));
     }
 
     uintptr_t align = 0;
@@ -244,22 +263,22 @@ __global__ __launch_bounds__(kBlock) void multi_ring_kernel(MultiArgs) {
     // the end (nothing uses them).  Up to P = 8: at P = 16 the 33 extra
     // pointers crowd the scalar registers and the launch got 2-6% slower.
     uint64_t warm = 0;
-    if (P <= 8 && a->block_first != nullptr) {
+    if (P <= 8 && block_first != nullptr) {
         const uint32_t ahead = static_cast<uint32_t>(b) + kMultiPrefetchTiles;
         if (ahead < gridDim.x) {
-            const int f = a->block_first[ahead / kMultiBlockTiles];
+            const int f = block_first[ahead / kMultiBlockTiles];
             const int tw = f < 0 ? 0 : (f > T - 1 ? T - 1 : f);
             constexpr int NW = 2 * P + 1 + (SGD ? 2 : 0);
             uint64_t w[NW];
-            w[0] = static_cast<uint64_t>(a->tiles[tw].numel);
+            w[0] = static_cast<uint64_t>(tiles[tw].numel);
 #pragma unroll
             for (int r = 0; r < P; ++r) {
-                w[1 + r] = reinterpret_cast<uint64_t>(a->in[static_cast<int64_t>(r) * T + tw]);
-                w[1 + P + r] = write_out ? reinterpret_cast<uint64_t>(a->out[static_cast<int64_t>(r) * T + tw]) : 0;
+                w[1 + r] = reinterpret_cast<uint64_t>(in_tab[static_cast<int64_t>(r) * T + tw]);
+                w[1 + P + r] = write_out ? reinterpret_cast<uint64_t>(out_tab[static_cast<int64_t>(r) * T + tw]) : 0;
             }
             if constexpr (SGD) {
-                w[2 * P + 1] = reinterpret_cast<uint64_t>(a->w[tw]);
-                w[2 * P + 2] = reinterpret_cast<uint64_t>(a->v[tw]);
+                w[2 * P + 1] = reinterpret_cast<uint64_t>(w_tab[tw]);
+                w[2 * P + 2] = reinterpret_cast<uint64_t>(v_tab[tw]);
             }
 #pragma unroll
             for (int i = 0; i < NW; ++i) warm |= w[i];
