@@ -80,10 +80,19 @@ constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
 // a little after the one it replaces finished.  bf16 -> f32 at P = 8 and 5
 // workgroups per CU, on 100 MiB buckets: 6,389 GB/s with no pause, 6,505-6,512
 // with 3, 4 or 5, 6,451 with 8; at 6 per CU a pause of 12 came to 6,477.
-// The same pause for the other type pairs and the optimizer step was level
-// or slower at their caps.
+// For bf16 -> f32 at other rank counts (100 MiB buckets, C = P, the caps
+// above; pauses 0, 2, 4, 8, 12, 16, 24 tried) the best pause and its gain:
+// P = 3: 12 (+1.0%), P = 4: 4 (+0.7%), P = 6: 16 (+2.9%), P = 12: 12
+// (+2.7%), P = 16: 8 (+4.6%); P = 2: none helped.  The best length does not
+// follow P smoothly (at P = 16 a pause of 4 was slower than none), so rank
+// counts not measured keep none.  The same pause for the other type pairs
+// and the optimizer step was level or slower at their caps.
+constexpr signed char kRingStartSleepBf16F32[17] = {
+    //   P: 1  2   3  4  5   6  7  8  9 10 11  12 13 14 15 16
+    0, 0, 0, 12, 4, 0, 16, 0, 4, 0, 0, 0, 12, 0, 0, 0, 8,
+};
 constexpr int ring_start_sleep(int P, bool in_bf16, bool out_bf16, bool sgd) {
-    return (P == 8 && in_bf16 && !out_bf16 && !sgd) ? 4 : 0;
+    return (in_bf16 && !out_bf16 && !sgd) ? kRingStartSleepBf16F32[P] : 0;
 }
 
 // The tree strategies measured best one workgroup above the ring (5 at

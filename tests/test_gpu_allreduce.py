@@ -66,7 +66,7 @@ def test_sweep_f32(P):
 
 
 @pytest.mark.parametrize("pair", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16")])
-@pytest.mark.parametrize("P", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("P", [2, 3, 4, 6, 8, 12, 16])
 def test_sweep_mixed_types(pair, P):
     it, ot = pair
     for n in (1, 7, 9, 1000, 16391, 70001):
