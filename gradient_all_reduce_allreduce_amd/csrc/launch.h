@@ -85,8 +85,9 @@ constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
 // P = 3: 12 (+1.0%), P = 4: 4 (+0.7%), P = 6: 16 (+2.9%), P = 12: 12
 // (+2.7%), P = 16: 8 (+4.6%); P = 2: none helped.  The best length does not
 // follow P smoothly (at P = 16 a pause of 4 was slower than none), so rank
-// counts not measured keep none.  The same pause for the other type pairs
-// and the optimizer step was level or slower at their caps.
+// counts not measured keep none.  For the other type pairs the best pause
+// gained under 0.3% at most rank counts (0.6-1.2% at P = 12 and 16 only),
+// and with the optimizer step it was level or slower: they keep none.
 constexpr signed char kRingStartSleepBf16F32[17] = {
     //   P: 1  2   3  4  5   6  7  8  9 10 11  12 13 14 15 16
     0, 0, 0, 12, 4, 0, 16, 0, 4, 0, 0, 0, 12, 0, 0, 0, 8,
