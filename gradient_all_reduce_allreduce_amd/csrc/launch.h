@@ -87,7 +87,7 @@ constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
 // follow P smoothly (at P = 16 a pause of 4 was slower than none), so rank
 // counts not measured keep none.  For the other type pairs the best pause
 // gained under 0.3% at most rank counts (0.6-1.2% at P = 12 and 16 only),
-// and with the optimizer step it was level or slower: they keep none.
+// and with the optimizer step under 0.7% (one isolated 2%): they keep none.
 constexpr signed char kRingStartSleepBf16F32[17] = {
     //   P: 1  2   3  4  5   6  7  8  9 10 11  12 13 14 15 16
     0, 0, 0, 12, 4, 0, 16, 0, 4, 0, 0, 0, 12, 0, 0, 0, 8,
