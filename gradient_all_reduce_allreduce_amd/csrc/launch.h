@@ -82,15 +82,16 @@ constexpr int sgd_wg_per_cu(int P, bool grad_bf16, bool writes_ranks) {
 // with 3, 4 or 5, 6,451 with 8; at 6 per CU a pause of 12 came to 6,477.
 // For bf16 -> f32 at other rank counts (100 MiB buckets, C = P, the caps
 // above; pauses 0, 2, 4, 8, 12, 16, 24 tried) the best pause and its gain:
-// P = 3: 12 (+1.0%), P = 4: 4 (+0.7%), P = 6: 16 (+2.9%), P = 12: 12
-// (+2.7%), P = 16: 8 (+4.6%); P = 2: none helped.  The best length does not
-// follow P smoothly (at P = 16 a pause of 4 was slower than none), so rank
-// counts not measured keep none.  For the other type pairs the best pause
+// P = 3: 12 (+1.0%), 4: 4 (+0.7%), 5: 16 (+1.6%), 6: 16 (+2.9%), 7: 8
+// (+3.8%), 9: 12 (+3.1%), 10: 8 (+3.6%), 11: 8 (+3.4%), 12: 12 (+2.7%),
+// 13: 8 (+4.5%), 14: 8 (+5.4%), 15: 12 (+3.7%), 16: 8 (+4.6%); P = 2: none
+// helped.  The best length does not follow P smoothly (at P = 16 a pause of
+// 4 was slower than none), so each is the measured one.  For the other type pairs the best pause
 // gained under 0.3% at most rank counts (0.6-1.2% at P = 12 and 16 only),
 // and with the optimizer step under 0.7% (one isolated 2%): they keep none.
 constexpr signed char kRingStartSleepBf16F32[17] = {
-    //   P: 1  2   3  4  5   6  7  8  9 10 11  12 13 14 15 16
-    0, 0, 0, 12, 4, 0, 16, 0, 4, 0, 0, 0, 12, 0, 0, 0, 8,
+    //   P: 1  2   3  4   5   6  7  8   9 10 11  12 13 14  15 16
+    0, 0, 0, 12, 4, 16, 16, 8, 4, 12, 8, 8, 12, 8, 8, 12, 8,
 };
 constexpr int ring_start_sleep(int P, bool in_bf16, bool out_bf16, bool sgd) {
     return (in_bf16 && !out_bf16 && !sgd) ? kRingStartSleepBf16F32[P] : 0;

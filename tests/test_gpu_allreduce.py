@@ -78,6 +78,19 @@ def test_sweep_mixed_types(pair, P):
                 assert_same_bits(got, want, f"{it}->{ot} P={P} n={n} C={C} {op}")
 
 
+@pytest.mark.parametrize("P", list(range(1, 17)))
+def test_bf16_to_f32_every_rank_count(P):
+    """bf16 -> float32, the type pair whose kernels pause at each
+    workgroup's start by rank count: bit-exact against the oracle for every
+    P, across tiles, chunk boundaries and a ragged tail."""
+    for n in (9, 70001):
+        for C in sorted({1, P, 2 * P + 1}):
+            X = draw(P, n, "bf16", seed=P * 131 + n + C)
+            got = gpu_ring(X, "mean", C, "bf16", "f32")
+            want = oracle_ring(X, "mean", C, in_dtype="bf16", out_dtype="f32")
+            assert_same_bits(got, want, f"bf16->f32 P={P} n={n} C={C}")
+
+
 def test_many_tiles_and_chunk_boundaries():
     """Sizes where chunk boundaries fall inside tiles and inside vectors."""
     for P, n, C in ((8, 1_000_003, 8), (8, 1_048_576 + 12, 16), (4, 524_287, 4),
