@@ -21,14 +21,17 @@
 //   * one one-wave workgroup (64 lanes) per tile and as many workgroups as
 //     tiles, with the number resident per CU capped (launch.h): this mix of
 //     reads and writes streams fastest with few waves per CU, and the
-//     dispatcher balances tiles over the CUs and XCDs as they free up;
+//     dispatcher balances tiles over the CUs and XCDs as they free up.  For
+//     bf16 -> float32 every workgroup first pauses 256-1024 clocks,
+//     which acts as a fraction of a workgroup below the cap;
 //   * each lane loads U vectors of V elements from each of the P ranks (P*U
 //     loads in flight) with non-temporal hints, folds them in registers and
 //     stores the result with device-scope buffer stores.  Every lane store is
 //     16 bytes wide when the output or the momentum state is float32 (V = 4),
 //     so a wave writes 1 KiB contiguous per instruction; bf16 -> bf16 moves 8
-//     elements per lane.  The data is touched once, so nothing is staged in
-//     LDS;
+//     elements per lane.  The data is touched once: tiles staged in LDS
+//     through direct global-to-LDS loads measured slower for float32 and
+//     level for bf16 -> float32, so tiles stay in registers;
 //   * addresses are a per-rank base in SGPRs plus one 32-bit lane offset
 //     shared by all ranks (the host splits buffers over 2^29 elements into
 //     several launches), which keeps VGPRs for data;
@@ -564,9 +567,10 @@ __global__ __launch_bounds__(kBlock) void ring_reduce_scalar_kernel(RingArgs) {
 // Reduce-scatter: element i's finished reduction is written to its owner
 // only, owner = (s + P - 1) mod P, the rank where the chunk's reduce-scatter
 // ends -- in the rotated load order that is register P-1.  The owner's copy
-// is stored with ordinary (cache-allocating) stores, so an all-gather that
-// follows finds it in the last-level cache.  All-gather: every rank other
-// than the owner receives the owner's value.  Tiles that straddle a chunk
+// goes out with the fused kernel's device-scope buffer stores, which
+// measured faster than ordinary stores both alone and followed by an
+// all-gather.  All-gather: every rank other than the owner receives the
+// owner's value.  Tiles that straddle a chunk
 // boundary take the per-element path (at most C-1 tiles per call).
 
 template <int P, bool INB, bool OUTB>
