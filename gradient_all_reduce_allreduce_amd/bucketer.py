@@ -69,9 +69,10 @@ class GradBucketer:
     def alloc_arena(self, P, dtype=None):
         """A [P, n_buckets * E] view holding every rank's gradients in bucket
         order (DDP's "gradients as bucket views" layout: no pack or unpack
-        copies).  Each rank's row is padded to whole buckets plus 4 KiB, so
-        rank r's copy of bucket k starts at r * (n_buckets * bucket_bytes +
-        4096) + k * bucket_bytes.  Every row starts 4 KiB-aligned, so the
+        copies).  Each rank's row is padded to whole buckets, rounded up to
+        a multiple of 4 KiB, plus 4 KiB, so with buckets of a whole number of
+        KiB rank r's copy of bucket k starts at r * (n_buckets * bucket_bytes
+        + 4096) + k * bucket_bytes.  Every row starts 4 KiB-aligned, so the
         all-reduce's 1 KiB wave accesses never split a 128-byte line, and
         the 4 KiB stagger keeps the P copies the all-reduce reads at the
         same offset from lining up in memory (measured about 1% faster than
@@ -83,8 +84,27 @@ class GradBucketer:
         import torch
         dtype = dtype or self.dtype
         cols = max(1, self.n_buckets) * self.bucket_elems
-        stride = cols + self.ROW_STAGGER // torch.empty(0, dtype=dtype).element_size()
+        es = torch.empty(0, dtype=dtype).element_size()
+        line = self.ROW_STAGGER // es
+        stride = -(-cols // line) * line + line
         return torch.empty(P, stride, dtype=dtype, device=self.device)[:, :cols]
+
+    def alloc_state(self, count=2):
+        """``count`` float32 buffers of ``total`` elements in bucket order,
+        e.g. the master weights and momentum of the fused optimizer step
+        (bucket b's state is ``x[b * bucket_elems:][:bucket_len(b)]``).  They
+        share one allocation laid out like ``alloc_arena`` rows, so each
+        starts 4 KiB-aligned.  The fused step's tiles start at the
+        gradients' 128-byte lines; a state buffer that starts inside a line
+        leaves two partly written lines at every wave store.  Carving both
+        from one flat buffer of 2 * total floats does that whenever total is
+        not a multiple of 32: with the ViT-B/16 set (P = 8, bf16 gradients,
+        no gradient output) momentum 32 bytes into a line ran 7.6% slower
+        one call per bucket and 11% slower as one bucketed call, 64 bytes
+        into a line 3.5% and 7.4%."""
+        import torch
+        rows = self.alloc_arena(count, torch.float32)
+        return [rows[i, :self.total] for i in range(count)]
 
     def bucket_view(self, arena_row, b):
         """Bucket b of one rank's arena row (its live elements only)."""

@@ -430,6 +430,26 @@ def test_bucket_views_match_pack_layout():
             assert np.array_equal(b.bucket_view(arena[r], k).numpy(), want[k])
 
 
+def test_state_buffers_start_on_lines_in_bucket_order():
+    """alloc_state gives float32 buffers of the plan's total, each starting
+    4 KiB into its allocation's rows (so on a 128-byte line whatever the
+    total), disjoint, with bucket b at b * bucket_elems (host-only: CPU
+    tensors)."""
+    import torch
+    for shapes in ([(3, 5), (7,), (1,), (33,)], [(1000,), (17, 3)], [(8,)]):
+        b = ddp.GradBucketer(shapes, torch.bfloat16, 256, device="cpu")
+        w, v = b.alloc_state()
+        base = w.data_ptr()
+        for x in (w, v):
+            assert x.dtype == torch.float32 and x.is_contiguous() and x.numel() == b.total
+            assert (x.data_ptr() - base) % 4096 == 0
+        assert v.data_ptr() - w.data_ptr() >= 4 * b.total
+        w.fill_(1.0)
+        v.fill_(2.0)
+        assert torch.all(w == 1.0) and torch.all(v == 2.0)
+        assert len(b.alloc_state(3)) == 3
+
+
 def test_bucketer_rejects_tables_and_buffers_that_do_not_fit(monkeypatch):
     """pack/unpack check the tensor table and the bucket buffers before
     calling the library; the library itself is replaced by a recorder, so
