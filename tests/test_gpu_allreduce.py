@@ -317,6 +317,55 @@ def test_fused_sgd_sum_and_zero_momentum():
     assert np.array_equal(v.cpu().numpy(), g)
 
 
+@pytest.mark.parametrize("layout", ["flat buffer, off lines", "alloc_state"])
+@pytest.mark.parametrize("bucketed", [False, True])
+def test_fused_sgd_state_layouts(layout, bucketed):
+    """Master weights and momentum 16-byte aligned but inside 128-byte lines
+    (w 16 bytes in, v 32 bytes in, both carved from one flat buffer, the
+    gradients 16 bytes in), and the buffers GradBucketer.alloc_state lays
+    out, as one call and as a bucketed call: bit for bit the oracle's ring
+    Mean and momentum step, every bucket its own ring."""
+    P, n, C = 8, 262_147, 8
+    E = 65_536                          # bf16 elements per bucket of the bucketed call
+    X = draw(P, n, "bf16", seed=41, dist="normal")
+    w0 = workloads.rank_buffers(1, n, "normal", 0.02, seed=42)[0]
+    v0 = workloads.rank_buffers(1, n, "normal", 1e-3, seed=43)[0]
+    rows = [torch.empty(n + 64, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    grads = [r[8:8 + n] for r in rows]
+    for g, h in zip(grads, to_device(X, "bf16")):
+        g.copy_(h)
+    if layout == "alloc_state":
+        plan = ddp.GradBucketer([(n,)], torch.bfloat16, 2 * E, device=DEV)
+        w, v = plan.alloc_state()
+        assert w.data_ptr() % 128 == 0 and v.data_ptr() % 128 == 0
+    else:
+        flat = torch.empty(2 * n + 64, dtype=torch.float32, device=DEV)
+        vo = -(-(4 + n) // 4) * 4
+        w, v = flat[4:4 + n], flat[vo:vo + n]
+        assert w.data_ptr() % 128 == 16 and v.data_ptr() % 128 == 32
+    w.copy_(torch.from_numpy(w0))
+    v.copy_(torch.from_numpy(v0))
+    outs = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    ddp.allreduce_sgd(grads, w, v, 1e-3, 0.9, "mean", C, out=outs, bucket_elems=E if bucketed else None)
+    w2, v2 = w.clone(), v.clone()
+    ddp.allreduce_sgd(grads, w, v, 1e-3, 0.9, "mean", C, bucket_elems=E if bucketed else None)
+    torch.cuda.synchronize()
+    if bucketed:
+        g = np.concatenate([oracle_ring(X[:, lo:lo + E], "mean", C, in_dtype="bf16", out_dtype="f32")[0]
+                            for lo in range(0, n, E)])
+    else:
+        g = oracle_ring(X, "mean", C, in_dtype="bf16", out_dtype="f32")[0]
+    ow, ov = oracle.sgd_momentum(g, w0, v0, 1e-3, 0.9)
+    ow2, ov2 = oracle.sgd_momentum(g, ow, ov, 1e-3, 0.9)
+    tag = f"{layout}, {'bucketed' if bucketed else 'one call'}"
+    assert_same_bits(w2.cpu().numpy(), ow, "w, first step, " + tag)
+    assert_same_bits(v2.cpu().numpy(), ov, "v, first step, " + tag)
+    assert_same_bits(w.cpu().numpy(), ow2, "w, second step, " + tag)
+    assert_same_bits(v.cpu().numpy(), ov2, "v, second step, " + tag)
+    for r in range(P):
+        assert_same_bits(outs[r].cpu().numpy(), g, f"gradient out rank {r}, " + tag)
+
+
 def test_fused_steps_round_every_operation_once():
     """The two hand-worked cases where a fused multiply-add would differ
     (mu * v a tie that rounds to even and is then cancelled by g; lr * v
