@@ -403,6 +403,25 @@ def _w_step(ctx):
                 note="moves 35n floats per bucket against 16n")
 
 
+@work("stepwise-resnet50-merged", "resnet")
+def _w_step_merged(ctx):
+    import gradient_all_reduce_allreduce_amd as ddp
+    plan, _, rows = _resnet(ctx)
+    E, nb = plan.bucket_elems, plan.n_buckets
+    full = nb - 1 if plan.bucket_len(nb - 1) < E else nb
+
+    def step(i):
+        o = rows[i % 2][1]
+        ddp.allreduce_stepwise([r[:full * E] for r in o], "mean", 8 * full)
+        if full < nb:
+            ddp.allreduce_stepwise([r[full * E:plan.total] for r in o], "mean", 8)
+    return Work(f"resnet50 p8 f32 mean, stepwise ring, the {full} full buckets as one ring of {full} x 8 chunks "
+                "and the tail bucket (in place)",
+                step, 8 * plan.total * 8, "ring_step_kernel<8>", 14 * (2 if full < nb else 1), steps=20,
+                note="C a multiple of P and buckets a multiple of C: every chunk keeps its start rank and length, "
+                     "the same bits and per-rank sends as one call per bucket")
+
+
 @work("multi-resnet50", "resnet_tensors")
 def _w_multi(ctx):
     import torch

@@ -63,3 +63,30 @@ def test_stepwise_equals_fused_at_bucket_size():
     torch.cuda.synchronize()
     assert_same_bits(got, to_host(fused), "25 MiB bucket")
     assert np.all(sent * P == 2 * (P - 1) * n)
+
+
+@pytest.mark.parametrize("P,C", [(8, 8), (4, 8), (3, 6)])
+def test_full_buckets_as_one_call_equal_one_call_per_bucket(P, C):
+    """With C a multiple of P and the bucket length a multiple of C,
+    consecutive full buckets form one ring with chunking (buckets x C):
+    every chunk keeps its start rank and length, so one stepwise call over
+    three full buckets gives the bits of one call per bucket, and every rank
+    sends the same number of elements."""
+    E, nb = 4096 * C, 3
+    n = nb * E
+    X = workloads.rank_buffers(P, n, "normal", 0.01, seed=70 + P)
+    per = to_device(X, "f32")
+    one = to_device(X, "f32")
+    sent_per = torch.zeros(P, dtype=torch.int64, device=DEV)
+    sent_one = torch.zeros(P, dtype=torch.int64, device=DEV)
+    for k in range(nb):
+        ddp.allreduce_stepwise([x[k * E:(k + 1) * E] for x in per], "mean", C, sent=sent_per)
+    ddp.allreduce_stepwise(one, "mean", nb * C, sent=sent_one)
+    torch.cuda.synchronize()
+    for r in range(P):
+        assert torch.equal(per[r].view(torch.int32), one[r].view(torch.int32)), r
+    assert torch.equal(sent_per, sent_one)
+    for k in range(nb):
+        want, _ = oracle.ring_allreduce(X[:, k * E:(k + 1) * E], "mean", C)
+        assert_same_bits(to_host([t[k * E:(k + 1) * E] for t in one]), want, f"bucket {k}")
+
