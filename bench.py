@@ -393,6 +393,43 @@ def _w_ag(ctx):
                 note="reads n, writes (P-1)*n")
 
 
+def _merged_calls(plan, rows, C, call):
+    """The full buckets of the arena rows as one ring of buckets x C chunks
+    (C a multiple of P, buckets a multiple of C: every chunk keeps its start
+    rank and length), then the tail bucket; call(ins, outs, chunking)."""
+    E, nb = plan.bucket_elems, plan.n_buckets
+    full = nb - 1 if plan.bucket_len(nb - 1) < E else nb
+    g, o = rows
+    call([r[:full * E] for r in g], [r[:full * E] for r in o], C * full)
+    if full < nb:
+        call([r[full * E:plan.total] for r in g], [r[full * E:plan.total] for r in o], C)
+    return 2 if full < nb else 1
+
+
+@work("rs-resnet50-merged", "resnet")
+def _w_rs_merged(ctx):
+    import gradient_all_reduce_allreduce_amd as ddp
+    plan, _, rows = _resnet(ctx)
+    rs = (lambda a, o, c: ddp.reduce_scatter(a, "mean", c, out=o))
+    return Work("resnet50 p8 f32 mean, reduce-scatter alone, the full buckets as one ring of buckets x 8 chunks "
+                "and the tail bucket",
+                lambda i: _merged_calls(plan, rows[i % 2], 8, rs),
+                8 * plan.total * 4 + plan.total * 4, "ring_rs_kernel<8, false, false>", 2,
+                note="the same bits as one call per bucket")
+
+
+@work("ag-resnet50-merged", "resnet")
+def _w_ag_merged(ctx):
+    import gradient_all_reduce_allreduce_amd as ddp
+    plan, _, rows = _resnet(ctx)
+    ag = (lambda a, o, c: ddp.all_gather(o, c))
+    return Work("resnet50 p8 f32, all-gather alone, the full buckets as one ring of buckets x 8 chunks and the "
+                "tail bucket",
+                lambda i: _merged_calls(plan, rows[i % 2], 8, ag),
+                plan.total * 4 + 7 * plan.total * 4, "ring_ag_kernel<8, 4>", 2,
+                note="the same bits as one call per bucket")
+
+
 @work("stepwise-resnet50", "resnet")
 def _w_step(ctx):
     import gradient_all_reduce_allreduce_amd as ddp
@@ -407,17 +444,12 @@ def _w_step(ctx):
 def _w_step_merged(ctx):
     import gradient_all_reduce_allreduce_amd as ddp
     plan, _, rows = _resnet(ctx)
-    E, nb = plan.bucket_elems, plan.n_buckets
-    full = nb - 1 if plan.bucket_len(nb - 1) < E else nb
-
-    def step(i):
-        o = rows[i % 2][1]
-        ddp.allreduce_stepwise([r[:full * E] for r in o], "mean", 8 * full)
-        if full < nb:
-            ddp.allreduce_stepwise([r[full * E:plan.total] for r in o], "mean", 8)
-    return Work(f"resnet50 p8 f32 mean, stepwise ring, the {full} full buckets as one ring of {full} x 8 chunks "
+    step = (lambda a, o, c: ddp.allreduce_stepwise(o, "mean", c))
+    calls = 2 if plan.bucket_len(plan.n_buckets - 1) < plan.bucket_elems else 1
+    return Work("resnet50 p8 f32 mean, stepwise ring, the full buckets as one ring of buckets x 8 chunks "
                 "and the tail bucket (in place)",
-                step, 8 * plan.total * 8, "ring_step_kernel<8>", 14 * (2 if full < nb else 1), steps=20,
+                lambda i: _merged_calls(plan, rows[i % 2], 8, step), 8 * plan.total * 8, "ring_step_kernel<8>",
+                14 * calls, steps=20,
                 note="C a multiple of P and buckets a multiple of C: every chunk keeps its start rank and length, "
                      "the same bits and per-rank sends as one call per bucket")
 
