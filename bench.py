@@ -393,41 +393,27 @@ def _w_ag(ctx):
                 note="reads n, writes (P-1)*n")
 
 
-def _merged_calls(plan, rows, C, call):
-    """The full buckets of the arena rows as one ring of buckets x C chunks
-    (C a multiple of P, buckets a multiple of C: every chunk keeps its start
-    rank and length), then the tail bucket; call(ins, outs, chunking)."""
-    E, nb = plan.bucket_elems, plan.n_buckets
-    full = nb - 1 if plan.bucket_len(nb - 1) < E else nb
-    g, o = rows
-    call([r[:full * E] for r in g], [r[:full * E] for r in o], C * full)
-    if full < nb:
-        call([r[full * E:plan.total] for r in g], [r[full * E:plan.total] for r in o], C)
-    return 2 if full < nb else 1
-
-
-@work("rs-resnet50-merged", "resnet")
-def _w_rs_merged(ctx):
+@work("rs-resnet50-bucketed", "resnet")
+def _w_rs_b(ctx):
     import gradient_all_reduce_allreduce_amd as ddp
     plan, _, rows = _resnet(ctx)
-    rs = (lambda a, o, c: ddp.reduce_scatter(a, "mean", c, out=o))
-    return Work("resnet50 p8 f32 mean, reduce-scatter alone, the full buckets as one ring of buckets x 8 chunks "
-                "and the tail bucket",
-                lambda i: _merged_calls(plan, rows[i % 2], 8, rs),
+    return Work("resnet50 p8 f32 mean, reduce-scatter alone, all buckets in one bucketed call",
+                lambda i: ddp.reduce_scatter(rows[i % 2][0], "mean", 8, out=rows[i % 2][1],
+                                             bucket_elems=plan.bucket_elems),
                 8 * plan.total * 4 + plan.total * 4, "ring_rs_kernel<8, false, false>", 2,
-                note="the same bits as one call per bucket")
+                note="every bucket its own ring, the same bits; the full buckets go out as one ring of "
+                     "buckets x 8 chunks")
 
 
-@work("ag-resnet50-merged", "resnet")
-def _w_ag_merged(ctx):
+@work("ag-resnet50-bucketed", "resnet")
+def _w_ag_b(ctx):
     import gradient_all_reduce_allreduce_amd as ddp
     plan, _, rows = _resnet(ctx)
-    ag = (lambda a, o, c: ddp.all_gather(o, c))
-    return Work("resnet50 p8 f32, all-gather alone, the full buckets as one ring of buckets x 8 chunks and the "
-                "tail bucket",
-                lambda i: _merged_calls(plan, rows[i % 2], 8, ag),
+    return Work("resnet50 p8 f32, all-gather alone, all buckets in one bucketed call",
+                lambda i: ddp.all_gather(rows[i % 2][1], 8, bucket_elems=plan.bucket_elems),
                 plan.total * 4 + 7 * plan.total * 4, "ring_ag_kernel<8, 4>", 2,
-                note="the same bits as one call per bucket")
+                note="every bucket its own ring, the same bits; the full buckets go out as one ring of "
+                     "buckets x 8 chunks")
 
 
 @work("stepwise-resnet50", "resnet")
@@ -440,18 +426,15 @@ def _w_step(ctx):
                 note="moves 35n floats per bucket against 16n")
 
 
-@work("stepwise-resnet50-merged", "resnet")
-def _w_step_merged(ctx):
+@work("stepwise-resnet50-bucketed", "resnet")
+def _w_step_b(ctx):
     import gradient_all_reduce_allreduce_amd as ddp
     plan, _, rows = _resnet(ctx)
-    step = (lambda a, o, c: ddp.allreduce_stepwise(o, "mean", c))
-    calls = 2 if plan.bucket_len(plan.n_buckets - 1) < plan.bucket_elems else 1
-    return Work("resnet50 p8 f32 mean, stepwise ring, the full buckets as one ring of buckets x 8 chunks "
-                "and the tail bucket (in place)",
-                lambda i: _merged_calls(plan, rows[i % 2], 8, step), 8 * plan.total * 8, "ring_step_kernel<8>",
-                14 * calls, steps=20,
-                note="C a multiple of P and buckets a multiple of C: every chunk keeps its start rank and length, "
-                     "the same bits and per-rank sends as one call per bucket")
+    return Work("resnet50 p8 f32 mean, stepwise ring, all buckets in one bucketed call (in place)",
+                lambda i: ddp.allreduce_stepwise(rows[i % 2][1], "mean", 8, bucket_elems=plan.bucket_elems),
+                8 * plan.total * 8, "ring_step_kernel<8>", 28, steps=20,
+                note="every bucket its own ring, the same bits and per-rank sends; the full buckets go out as "
+                     "one ring of buckets x 8 chunks: 2(P-1) launches for them and 2(P-1) for the tail")
 
 
 @work("multi-resnet50", "resnet_tensors")

@@ -95,6 +95,15 @@ _SIGNATURES = {
     "allreduce_ring_stepwise": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p]),
+    "reducescatter_ring_buckets": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "allgather_ring_buckets": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p]),
+    "allreduce_ring_stepwise_buckets": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "allreduce_tree_emulated": (ctypes.c_int, [
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp,
         ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]),

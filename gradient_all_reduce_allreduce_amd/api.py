@@ -8,8 +8,9 @@ Python ints, stream as an int handle or None):
     allreduce_ring_emulated, allreduce_fused_sgd, allreduce_ring_buckets,
     allreduce_fused_sgd_buckets, zero1_sgd_step_emulated, zero1_sgd_step_buckets,
     ddp_buckets_launch_count,
-    reducescatter_ring_emulated,
-    allgather_ring_emulated, allreduce_ring_stepwise, allreduce_tree_emulated,
+    reducescatter_ring_emulated, reducescatter_ring_buckets,
+    allgather_ring_emulated, allgather_ring_buckets, allreduce_ring_stepwise,
+    allreduce_ring_stepwise_buckets, allreduce_tree_emulated,
     allreduce_hierarchical_emulated, ddp_multi_plan, ddp_multi_block_map, allreduce_multi_ring_emulated,
     allreduce_multi_fused_sgd, ddp_set_wg_per_cu
 Tensor-level helpers:
@@ -173,6 +174,23 @@ def reducescatter_ring_emulated(op, P, chunking, rank_in, in_dtype, rank_out, ou
     _check(N.lib().reducescatter_ring_emulated(_op(op), P, chunking, N.pointer_array(rank_in),
                                                in_dtype, N.pointer_array(rank_out), out_dtype, n,
                                                stream))
+
+
+def reducescatter_ring_buckets(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, bucket_elems,
+                               stream=None):
+    _check(N.lib().reducescatter_ring_buckets(_op(op), P, chunking, N.pointer_array(rank_in), in_dtype,
+                                              N.pointer_array(rank_out), out_dtype, n, bucket_elems, stream))
+
+
+def allgather_ring_buckets(P, chunking, rank_buf, dtype, n, bucket_elems, stream=None):
+    _check(N.lib().allgather_ring_buckets(P, chunking, N.pointer_array(rank_buf), dtype, n, bucket_elems,
+                                          stream))
+
+
+def allreduce_ring_stepwise_buckets(op, P, chunking, rank_buf, dtype, n, bucket_elems, sent_dev=None,
+                                    stream=None):
+    _check(N.lib().allreduce_ring_stepwise_buckets(_op(op), P, chunking, N.pointer_array(rank_buf), dtype, n,
+                                                   bucket_elems, sent_dev, stream))
 
 
 def allgather_ring_emulated(P, chunking, rank_buf, dtype, n, stream=None):
@@ -404,10 +422,11 @@ def allreduce_hierarchical(tensors, nodes, op="sum", local=("ring", None), globa
     return out
 
 
-def reduce_scatter(tensors, op="sum", chunking=None, out=None, out_dtype=None):
+def reduce_scatter(tensors, op="sum", chunking=None, out=None, out_dtype=None, bucket_elems=None):
     """Reduce-scatter: out[owner(i)][i] receives element i's reduction
     (owner = the rank where the chunk's ring ends); every other element of
-    ``out`` is left as it was.  Returns ``out``."""
+    ``out`` is left as it was.  ``bucket_elems``: every bucket of that many
+    elements its own ring, as for ``allreduce``.  Returns ``out``."""
     import torch
     tensors = _rank_tensors(tensors, "reduce_scatter")
     P = len(tensors)
@@ -418,37 +437,47 @@ def reduce_scatter(tensors, op="sum", chunking=None, out=None, out_dtype=None):
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("reduce_scatter: out must match the inputs")
     _same_device(tensors, out, "reduce_scatter")
-    reducescatter_ring_emulated(op, P, chunking or P, [t.data_ptr() for t in tensors],
-                                torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
-                                torch_dtype_code(out[0].dtype), tensors[0].numel(),
-                                current_stream(tensors[0].device))
+    args = (op, P, chunking or P, [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
+            [t.data_ptr() for t in out], torch_dtype_code(out[0].dtype), tensors[0].numel())
+    if bucket_elems is not None:
+        reducescatter_ring_buckets(*args, bucket_elems, current_stream(tensors[0].device))
+    else:
+        reducescatter_ring_emulated(*args, current_stream(tensors[0].device))
     return out
 
 
-def all_gather(tensors, chunking=None):
+def all_gather(tensors, chunking=None, bucket_elems=None):
     """All-gather in place: every rank receives each element from the rank
-    that owns it.  Returns the tensors."""
+    that owns it.  ``bucket_elems``: every bucket of that many elements its
+    own ring, as for ``allreduce``.  Returns the tensors."""
     tensors = _rank_tensors(tensors, "all_gather")
-    allgather_ring_emulated(len(tensors), chunking or len(tensors),
-                            [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
-                            tensors[0].numel(), current_stream(tensors[0].device))
+    args = (len(tensors), chunking or len(tensors), [t.data_ptr() for t in tensors],
+            torch_dtype_code(tensors[0].dtype), tensors[0].numel())
+    if bucket_elems is not None:
+        allgather_ring_buckets(*args, bucket_elems, current_stream(tensors[0].device))
+    else:
+        allgather_ring_emulated(*args, current_stream(tensors[0].device))
     return tensors
 
 
-def allreduce_stepwise(tensors, op="sum", chunking=None, sent=None):
+def allreduce_stepwise(tensors, op="sum", chunking=None, sent=None, bucket_elems=None):
     """All-reduce fp32 rank tensors in place, one ring step per launch.
     ``sent``: optional int64 GPU tensor of P counters, increased by the
-    elements each rank sends.  Returns the tensors."""
+    elements each rank sends.  ``bucket_elems``: every bucket of that many
+    elements its own ring, as for ``allreduce``.  Returns the tensors."""
     import torch
     tensors = _rank_tensors(tensors, "allreduce_stepwise")
     if sent is not None and (sent.dtype != torch.int64 or sent.numel() != len(tensors)
                              or sent.device != tensors[0].device or not sent.is_contiguous()):
         raise ValueError("allreduce_stepwise: sent must be a contiguous int64 tensor of P on the "
                          "tensors' device")
-    allreduce_ring_stepwise(op, len(tensors), chunking or len(tensors),
-                            [t.data_ptr() for t in tensors], torch_dtype_code(tensors[0].dtype),
-                            tensors[0].numel(), sent.data_ptr() if sent is not None else None,
-                            current_stream(tensors[0].device))
+    args = (op, len(tensors), chunking or len(tensors), [t.data_ptr() for t in tensors],
+            torch_dtype_code(tensors[0].dtype), tensors[0].numel())
+    sent_ptr = sent.data_ptr() if sent is not None else None
+    if bucket_elems is not None:
+        allreduce_ring_stepwise_buckets(*args, bucket_elems, sent_ptr, current_stream(tensors[0].device))
+    else:
+        allreduce_ring_stepwise(*args, sent_ptr, current_stream(tensors[0].device))
     return tensors
 
 

@@ -172,7 +172,8 @@ std::vector<BucketPart> bucket_parts(const ddp::RingLaunch& l, int64_t E) {
     // and no tile straddles them.
     const int64_t tile = ddp::ring_tile_elems(l);
     const int64_t first_chunks = joint ? full * l.chunking : l.chunking;
-    if ((joint || full == 1) && tail > 0 && l.n <= ddp::kMaxLaunchElems && (full * E) % tile == 0 &&
+    if (l.mode == ddp::kAllReduce && (joint || full == 1) && tail > 0 && l.n <= ddp::kMaxLaunchElems &&
+        (full * E) % tile == 0 &&
         (E + l.chunking - 1) / l.chunking >= tile && (tail + l.chunking - 1) / l.chunking >= tile) {
         parts.push_back({0, l.n, static_cast<int>(first_chunks), full * E, l.chunking});
         return parts;
@@ -202,6 +203,25 @@ int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
         b.seg2 = p.seg2;
         b.seg2_chunking = p.seg2_chunking;
         if (const int e = ddp::launch_ring_reduce(b, msg)) return e;
+    }
+    return 0;
+}
+
+// The stepwise ring over every bucket: the same parts as launch_buckets
+// (whole buckets as one ring where that keeps every chunk), each part its
+// 2(P-1) launches; the send counters keep adding up across parts.
+int launch_step_buckets(const ddp::StepLaunch& l, int64_t E, const char** msg) {
+    ddp::RingLaunch shape{};
+    shape.mode = ddp::kReduceScatter;
+    shape.P = l.P;
+    shape.chunking = l.chunking;
+    shape.n = l.n;
+    for (const BucketPart& p : bucket_parts(shape, E)) {
+        ddp::StepLaunch b = l;
+        for (int r = 0; r < l.P; ++r) b.buf[r] = l.buf[r] + p.first;
+        b.n = p.count;
+        b.chunking = p.chunking;
+        if (const int e = ddp::launch_ring_stepwise(b, msg)) return e;
     }
     return 0;
 }
@@ -641,11 +661,17 @@ int zero1_sgd_step_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const
                      param_dtype, 2, stream);
 }
 
-int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
-                                ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// reducescatter_ring_emulated (bucket_elems 0) and reducescatter_ring_buckets.
+int reduce_scatter_call(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
+                        ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                        int64_t bucket_elems, void* stream) {
     int s = validate_reduce(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, true);
     if (s) return s;
+    if (bucket_elems != 0 && (s = check_bucket_elems(bucket_elems, in_dtype, out_dtype))) return s;
     std::vector<Buf> bufs;
     add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
     add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
@@ -666,18 +692,20 @@ int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, c
     l.n = n;
     l.stream = stream;
     const char* msg = nullptr;
-    const int e = ddp::launch_ring_reduce(l, &msg);
+    const int e = bucket_elems != 0 ? launch_buckets(l, bucket_elems, &msg) : ddp::launch_ring_reduce(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
 }
 
-int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf, ddp_dtype dtype, int64_t n,
-                            void* stream) {
+// allgather_ring_emulated (bucket_elems 0) and allgather_ring_buckets.
+int all_gather_call(int32_t P, int32_t chunking, void* const* rank_buf, ddp_dtype dtype, int64_t n,
+                    int64_t bucket_elems, void* stream) {
     int s = check_ranks(P);
     if (s) return s;
     if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
     if (int e = check_length(n, "n")) return e;
     if (!valid_dtype(dtype)) return fail(DDP_E_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (bucket_elems != 0 && (s = check_bucket_elems(bucket_elems, dtype, dtype))) return s;
     if ((s = check_ptr_array(const_cast<const void* const*>(rank_buf), P, "rank_buf"))) return s;
     std::vector<Buf> bufs;
     add_rank_bufs(bufs, const_cast<const void* const*>(rank_buf), P, n, elem_bytes(dtype), "rank_buf");
@@ -698,13 +726,14 @@ int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf, 
     l.n = n;
     l.stream = stream;
     const char* msg = nullptr;
-    const int e = ddp::launch_ring_reduce(l, &msg);
+    const int e = bucket_elems != 0 ? launch_buckets(l, bucket_elems, &msg) : ddp::launch_ring_reduce(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
 }
 
-int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void* const* rank_buf,
-                            ddp_dtype dtype, int64_t n, uint64_t* sent_dev, void* stream) {
+// allreduce_ring_stepwise (bucket_elems 0) and allreduce_ring_stepwise_buckets.
+int stepwise_call(ddp_reduce_op op, int32_t P, int32_t chunking, void* const* rank_buf, ddp_dtype dtype,
+                  int64_t n, int64_t bucket_elems, uint64_t* sent_dev, void* stream) {
     if (op != DDP_SUM && op != DDP_MEAN) return fail(DDP_E_ARG, "unknown reduce op %d", op);
     int s = check_ranks(P);
     if (s) return s;
@@ -714,6 +743,7 @@ int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void*
     if (dtype != DDP_F32)
         return fail(DDP_E_UNSUPPORTED, "the stepwise ring keeps partial sums in the rank buffers, "
                                        "which must therefore be float32");
+    if (bucket_elems != 0 && (s = check_bucket_elems(bucket_elems, dtype, dtype))) return s;
     if ((s = check_ptr_array(const_cast<const void* const*>(rank_buf), P, "rank_buf"))) return s;
     std::vector<Buf> bufs;
     add_rank_bufs(bufs, const_cast<const void* const*>(rank_buf), P, n, 4, "rank_buf");
@@ -738,9 +768,49 @@ int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void*
     l.n = n;
     l.stream = stream;
     const char* msg = nullptr;
-    const int e = ddp::launch_ring_stepwise(l, &msg);
+    const int e = bucket_elems != 0 ? launch_step_buckets(l, bucket_elems, &msg) : ddp::launch_ring_stepwise(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int reducescatter_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
+                                ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                                void* stream) {
+    return reduce_scatter_call(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, 0, stream);
+}
+
+int reducescatter_ring_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, const void* const* rank_in,
+                               ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype, int64_t n,
+                               int64_t bucket_elems, void* stream) {
+    if (bucket_elems == 0) return fail(DDP_E_ARG, "bucket_elems = 0, must be >= 1");
+    return reduce_scatter_call(op, P, chunking, rank_in, in_dtype, rank_out, out_dtype, n, bucket_elems, stream);
+}
+
+int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf, ddp_dtype dtype, int64_t n,
+                            void* stream) {
+    return all_gather_call(P, chunking, rank_buf, dtype, n, 0, stream);
+}
+
+int allgather_ring_buckets(int32_t P, int32_t chunking, void* const* rank_buf, ddp_dtype dtype, int64_t n,
+                           int64_t bucket_elems, void* stream) {
+    if (bucket_elems == 0) return fail(DDP_E_ARG, "bucket_elems = 0, must be >= 1");
+    return all_gather_call(P, chunking, rank_buf, dtype, n, bucket_elems, stream);
+}
+
+int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking, void* const* rank_buf,
+                            ddp_dtype dtype, int64_t n, uint64_t* sent_dev, void* stream) {
+    return stepwise_call(op, P, chunking, rank_buf, dtype, n, 0, sent_dev, stream);
+}
+
+int allreduce_ring_stepwise_buckets(ddp_reduce_op op, int32_t P, int32_t chunking, void* const* rank_buf,
+                                    ddp_dtype dtype, int64_t n, int64_t bucket_elems, uint64_t* sent_dev,
+                                    void* stream) {
+    if (bucket_elems == 0) return fail(DDP_E_ARG, "bucket_elems = 0, must be >= 1");
+    return stepwise_call(op, P, chunking, rank_buf, dtype, n, bucket_elems, sent_dev, stream);
 }
 
 int allreduce_tree_emulated(ddp_reduce_op op, int32_t P, int32_t branching, const void* const* rank_in,

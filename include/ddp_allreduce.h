@@ -421,6 +421,37 @@ int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf,
                             ddp_dtype dtype, int64_t n, void* stream);
 
 /*
+ * reducescatter_ring_buckets / allgather_ring_buckets -- the two halves over
+ * every bucket of a flat buffer in one call.
+ *
+ * Bucket k is elements [k * E, min((k + 1) * E, n)) of every rank buffer,
+ * as for allreduce_ring_buckets ("Distributed Training", "Data parallelism
+ * and all-reduce"; FSDP reduce-scatters gradients and all-gathers
+ * parameters unit by unit, same page, "Sharded data parallelism").  Each
+ * bucket is reduce-scattered (all-gathered) exactly as the single-bucket
+ * call does it: its own C chunks of ceil(len_k / C) elements, its own
+ * owners, the same bits, untouched elements left untouched.  When C is a
+ * multiple of P and E a multiple of C, consecutive full buckets are one
+ * ring of (full buckets x C) chunks with the same chunks and owners and go
+ * out as one launch sequence; otherwise each bucket is its own.
+ *
+ *   bucket_elems  E >= 1, with E * element size a multiple of 16 bytes for
+ *                 every element type of the call
+ *   n             elements per rank buffer (all its buckets), >= 0
+ *   other arguments, layout, ownership and errors as for
+ *   reducescatter_ring_emulated and allgather_ring_emulated.
+ * Errors: those of the single-bucket calls; DDP_E_ARG for bucket_elems < 1,
+ * DDP_E_ALIGN for a bucket size that misaligns the buckets.
+ */
+int reducescatter_ring_buckets(ddp_reduce_op op, int32_t P, int32_t chunking,
+                               const void* const* rank_in, ddp_dtype in_dtype,
+                               void* const* rank_out, ddp_dtype out_dtype,
+                               int64_t n, int64_t bucket_elems, void* stream);
+int allgather_ring_buckets(int32_t P, int32_t chunking, void* const* rank_buf,
+                           ddp_dtype dtype, int64_t n, int64_t bucket_elems,
+                           void* stream);
+
+/*
  * allreduce_ring_stepwise -- the same all-reduce, one ring step per launch.
  *
  * The ring as the pages describe it: peers pass slices of the tensor around
@@ -448,6 +479,29 @@ int allgather_ring_emulated(int32_t P, int32_t chunking, void* const* rank_buf,
 int allreduce_ring_stepwise(ddp_reduce_op op, int32_t P, int32_t chunking,
                             void* const* rank_buf, ddp_dtype dtype, int64_t n,
                             uint64_t* sent_dev, void* stream);
+
+/*
+ * allreduce_ring_stepwise_buckets -- the stepwise ring over every bucket of
+ * a flat buffer in one call.
+ *
+ * Each bucket (as for allreduce_ring_buckets) goes through its own P-1
+ * reduce-scatter and P-1 all-gather steps, with its own chunks, exactly as
+ * allreduce_ring_stepwise runs it alone: the same bits and the same send
+ * counts.  When C is a multiple of P and E a multiple of C, consecutive full
+ * buckets are one ring of (full buckets x C) chunks whose step t moves every
+ * chunk of every full bucket in one launch: 2(P-1) launches for the full
+ * buckets together instead of 2(P-1) each.
+ *
+ *   bucket_elems  E >= 1, with 4 * E a multiple of 16 bytes
+ *   other arguments, layout, ownership and errors as for
+ *   allreduce_ring_stepwise (sent_dev accumulates over all buckets).
+ * Errors: those of allreduce_ring_stepwise; DDP_E_ARG for bucket_elems < 1,
+ * DDP_E_ALIGN for a bucket size that misaligns the buckets.
+ */
+int allreduce_ring_stepwise_buckets(ddp_reduce_op op, int32_t P, int32_t chunking,
+                                    void* const* rank_buf, ddp_dtype dtype, int64_t n,
+                                    int64_t bucket_elems, uint64_t* sent_dev,
+                                    void* stream);
 
 /*
  * allreduce_tree_emulated -- the all-reduce along a tree instead of a ring.

@@ -221,6 +221,39 @@ def test_bucketed_calls_errors():
     assert bz(4, n=0) == N.DDP_OK
 
 
+def test_bucketed_halves_and_stepwise_errors():
+    """reducescatter_ring_buckets, allgather_ring_buckets and
+    allreduce_ring_stepwise_buckets validate as their single-bucket calls
+    do, plus the bucket size (no launch: fake addresses)."""
+    lib = N.lib()
+    ins = N.pointer_array([A, A + MB])
+    outs = N.pointer_array([A + 64 * MB, A + 65 * MB])
+
+    def rs(E, it=0, ot=0, n=1024, o=outs, C=2):
+        return lib.reducescatter_ring_buckets(1, 2, C, ins, it, o, ot, n, E, None)
+
+    def ag(E, dt=0, n=1024, b=outs, P=2):
+        return lib.allgather_ring_buckets(P, 2, b, dt, n, E, None)
+
+    def st(E, dt=0, n=1024, b=outs, sent=None):
+        return lib.allreduce_ring_stepwise_buckets(1, 2, 2, b, dt, n, E, sent, None)
+
+    for f in (rs, ag, st):
+        assert f(0) == N.DDP_E_ARG and "bucket_elems" in N.last_error()
+        assert f(-4) == N.DDP_E_ARG
+        assert f(6) == N.DDP_E_ALIGN                   # 24 bytes of float32
+        assert f(4, n=0) == N.DDP_OK                   # nothing to do, nothing launched
+    assert rs(4, it=1) == N.DDP_E_ALIGN                # 8 bytes of bf16 input
+    assert rs(4, o=N.pointer_array([A + 16, A + 65 * MB])) == N.DDP_E_OVERLAP
+    assert rs(4, C=0) == N.DDP_E_ARG
+    assert ag(4, dt=1) == N.DDP_E_ALIGN
+    assert ag(4, b=N.pointer_array([A, A + 16])) == N.DDP_E_OVERLAP
+    assert ag(4, P=0) == N.DDP_E_ARG
+    assert st(4, dt=1) == N.DDP_E_UNSUPPORTED          # the stepwise ring is float32 only
+    assert st(4, sent=A + 4) == N.DDP_E_ALIGN
+    assert st(4, b=N.pointer_array([A, A + 16])) == N.DDP_E_OVERLAP
+
+
 def test_buckets_launch_count():
     """The launch count the bucketed calls report, by the rule of their
     declaration: one launch when the full buckets form one ring and the

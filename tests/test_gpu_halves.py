@@ -124,3 +124,38 @@ def test_full_buckets_as_one_call_equal_one_call_per_bucket(P, C):
         want, _ = oracle.ring_allreduce(X[:, k * E:(k + 1) * E], "mean", C)
         got = to_host([t[k * E:(k + 1) * E] for t in one_ag])
         assert_same_bits(got, want, f"bucket {k}")
+
+
+@pytest.mark.parametrize("P,C,E,n,dt", [
+    (8, 8, 8192 * 8, 3 * 8192 * 8 + 12_345, "f32"),   # full buckets merged, a partial tail
+    (4, 8, 4096 * 8, 3 * 4096 * 8, "f32"),            # merged, no tail
+    (3, 4, 10_000, 35_555, "f32"),                    # C not a multiple of P: bucket by bucket
+    (2, 6, 6_004, 2 * 6_004 + 17, "f32"),             # E not a multiple of C
+    (5, 5, 4_096, 3, "f32"),                          # one partial bucket
+    (8, 8, 8192 * 8, 2 * 8192 * 8 + 999, "bf16"),
+])
+def test_bucketed_halves_equal_one_call_per_bucket(P, C, E, n, dt):
+    """reducescatter_ring_buckets and allgather_ring_buckets: every bucket
+    exactly as the single-bucket calls handle it (the same bits, untouched
+    elements untouched), merged into one ring or not."""
+    X = draw(P, n, dt, seed=P * 13 + n)
+    ins = to_device(X, dt)
+    per, _ = sentinel_tensors(P, n, dt)
+    one, _ = sentinel_tensors(P, n, dt)
+    for k in range(0, n, E):
+        ddp.reduce_scatter([x[k:k + E] for x in ins], "mean", C, out=[y[k:k + E] for y in per])
+    ddp.reduce_scatter(ins, "mean", C, out=one, bucket_elems=E)
+    torch.cuda.synchronize()
+    for r in range(P):
+        assert np.array_equal(raw(to_host([per[r]])[0]), raw(to_host([one[r]])[0])), f"reduce-scatter rank {r}"
+    for k in range(0, n, E):
+        ddp.all_gather([y[k:k + E] for y in per], C)
+    ddp.all_gather(one, C, bucket_elems=E)
+    torch.cuda.synchronize()
+    got = to_host(one)
+    for r in range(P):
+        assert np.array_equal(raw(to_host([per[r]])[0]), raw(got[r])), f"all-gather rank {r}"
+    for k in range(0, n, E):
+        want, _ = oracle.ring_allreduce(X[:, k:k + E], "mean", C, in_dtype=dt, out_dtype=dt)
+        assert_same_bits(got[:, k:k + E], want, f"bucket at {k}")
+

@@ -90,3 +90,29 @@ def test_full_buckets_as_one_call_equal_one_call_per_bucket(P, C):
         want, _ = oracle.ring_allreduce(X[:, k * E:(k + 1) * E], "mean", C)
         assert_same_bits(to_host([t[k * E:(k + 1) * E] for t in one]), want, f"bucket {k}")
 
+
+@pytest.mark.parametrize("P,C,E,n", [
+    (8, 8, 4096 * 8, 3 * 4096 * 8 + 5_001),   # full buckets merged, a partial tail
+    (3, 4, 10_000, 35_555),                   # C not a multiple of P: bucket by bucket
+    (4, 4, 8_192, 8_192),                     # one full bucket
+    (2, 2, 4_096, 5),                         # one partial bucket
+])
+def test_stepwise_buckets_equal_one_call_per_bucket(P, C, E, n):
+    """allreduce_ring_stepwise_buckets: the bits and the per-rank send counts
+    of one stepwise call per bucket, merged into one ring or not."""
+    X = workloads.rank_buffers(P, n, "normal", 0.01, seed=90 + P + n)
+    per = to_device(X, "f32")
+    one = to_device(X, "f32")
+    sent_per = torch.zeros(P, dtype=torch.int64, device=DEV)
+    sent_one = torch.zeros(P, dtype=torch.int64, device=DEV)
+    for k in range(0, n, E):
+        ddp.allreduce_stepwise([x[k:k + E] for x in per], "mean", C, sent=sent_per)
+    ddp.allreduce_stepwise(one, "mean", C, sent=sent_one, bucket_elems=E)
+    torch.cuda.synchronize()
+    got = to_host(one)
+    assert_same_bits(got, to_host(per), "one call per bucket")
+    assert torch.equal(sent_per, sent_one)
+    for k in range(0, n, E):
+        want, _ = oracle.ring_allreduce(X[:, k:k + E], "mean", C)
+        assert_same_bits(got[:, k:k + E], want, f"bucket at {k}")
+
