@@ -363,6 +363,18 @@ def _w_hier1(ctx):
                 8 * plan.total * 8, TREE, plan.n_buckets)
 
 
+@work("hier-resnet50-2x4-ring-ring-bucketed", "resnet")
+def _w_hier1_b(ctx):
+    import gradient_all_reduce_allreduce_amd as ddp
+    plan, _, rows = _resnet(ctx)
+    return Work("resnet50 p8 f32 mean, two-level 2 nodes x 4: ring in the nodes, ring over them, all buckets in "
+                "one bucketed call",
+                lambda i: ddp.allreduce_hierarchical(rows[i % 2][0], 2, "mean", ("ring", None), ("ring", None),
+                                                     out=rows[i % 2][1], bucket_elems=plan.bucket_elems),
+                8 * plan.total * 8, TREE, 2,
+                note="every bucket its own two-level ring, the same bits; the full buckets go out as one")
+
+
 @work("hier-resnet50-4x2-tree-ring", "resnet")
 def _w_hier2(ctx):
     import gradient_all_reduce_allreduce_amd as ddp

@@ -18,7 +18,7 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   allreduce_multi_fused_sgd, ddp_set_wg_per_cu, KERNEL_FAMILIES,
                   allreduce_ring_buckets, allreduce_fused_sgd_buckets, zero1_sgd_step_buckets,
                   ddp_buckets_launch_count, reducescatter_ring_buckets, allgather_ring_buckets,
-                  allreduce_ring_stepwise_buckets)
+                  allreduce_ring_stepwise_buckets, allreduce_hierarchical_buckets)
 from .bucketer import GradBucketer
 
 __all__ = [
@@ -34,5 +34,5 @@ __all__ = [
     "allreduce_multi_fused_sgd", "ddp_set_wg_per_cu", "KERNEL_FAMILIES",
     "allreduce_ring_buckets", "allreduce_fused_sgd_buckets", "zero1_sgd_step_buckets",
     "ddp_buckets_launch_count", "reducescatter_ring_buckets", "allgather_ring_buckets",
-    "allreduce_ring_stepwise_buckets",
+    "allreduce_ring_stepwise_buckets", "allreduce_hierarchical_buckets",
 ]

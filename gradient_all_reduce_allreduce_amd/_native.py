@@ -111,6 +111,10 @@ _SIGNATURES = {
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int,
         ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp, ctypes.c_int, ctypes.c_int64,
         ctypes.c_void_p]),
+    "allreduce_hierarchical_buckets": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int,
+        ctypes.c_int32, _c_void_pp, ctypes.c_int, _c_void_pp, ctypes.c_int, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p]),
     "ddp_multi_plan": (ctypes.c_int, [
         ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
         _c_void_pp, ctypes.POINTER(TensorTiles), ctypes.POINTER(ctypes.c_int64),

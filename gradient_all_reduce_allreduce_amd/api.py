@@ -10,7 +10,7 @@ Python ints, stream as an int handle or None):
     ddp_buckets_launch_count,
     reducescatter_ring_emulated, reducescatter_ring_buckets,
     allgather_ring_emulated, allgather_ring_buckets, allreduce_ring_stepwise,
-    allreduce_ring_stepwise_buckets, allreduce_tree_emulated,
+    allreduce_ring_stepwise_buckets, allreduce_tree_emulated, allreduce_hierarchical_buckets,
     allreduce_hierarchical_emulated, ddp_multi_plan, ddp_multi_block_map, allreduce_multi_ring_emulated,
     allreduce_multi_fused_sgd, ddp_set_wg_per_cu
 Tensor-level helpers:
@@ -229,6 +229,15 @@ def allreduce_hierarchical_emulated(op, nodes, local_ranks, local_strategy, loca
         N.pointer_array(rank_out), out_dtype, n, stream))
 
 
+def allreduce_hierarchical_buckets(op, nodes, local_ranks, local_strategy, local_param,
+                                   global_strategy, global_param, rank_in, in_dtype, rank_out,
+                                   out_dtype, n, bucket_elems, stream=None):
+    _check(N.lib().allreduce_hierarchical_buckets(
+        _op(op), nodes, local_ranks, _strategy(local_strategy), local_param or 0,
+        _strategy(global_strategy), global_param or 0, N.pointer_array(rank_in), in_dtype,
+        N.pointer_array(rank_out), out_dtype, n, bucket_elems, stream))
+
+
 TILES_DTYPE = np.dtype([("numel", "<i8"), ("first_tile", "<i4"), ("lead", "<i4")])
 
 
@@ -396,12 +405,13 @@ def allreduce_tree(tensors, op="sum", branching=2, out=None, out_dtype=None):
 
 
 def allreduce_hierarchical(tensors, nodes, op="sum", local=("ring", None), global_=("ring", None),
-                           out=None, out_dtype=None):
+                           out=None, out_dtype=None, bucket_elems=None):
     """Two-level all-reduce: ``nodes`` nodes of len(tensors) / nodes ranks
     (node-major), each level with its own strategy, given as (name,
     parameter) with name "ring" (parameter: chunk count, None = the level's
     member count), "tree" (branching) or "centralized".  Other arguments as
-    for ``allreduce``."""
+    for ``allreduce`` (``bucket_elems``: every bucket its own two-level
+    all-reduce)."""
     import torch
     tensors = _rank_tensors(tensors, "allreduce_hierarchical")
     P = len(tensors)
@@ -414,11 +424,13 @@ def allreduce_hierarchical(tensors, nodes, op="sum", local=("ring", None), globa
     if len(out) != P or out[0].numel() != tensors[0].numel():
         raise ValueError("allreduce_hierarchical: out must match the inputs")
     _same_device(tensors, out, "allreduce_hierarchical")
-    allreduce_hierarchical_emulated(op, nodes, P // nodes, local[0], local[1], global_[0], global_[1],
-                                    [t.data_ptr() for t in tensors],
-                                    torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out],
-                                    torch_dtype_code(out[0].dtype), tensors[0].numel(),
-                                    current_stream(tensors[0].device))
+    args = (op, nodes, P // nodes, local[0], local[1], global_[0], global_[1], [t.data_ptr() for t in tensors],
+            torch_dtype_code(tensors[0].dtype), [t.data_ptr() for t in out], torch_dtype_code(out[0].dtype),
+            tensors[0].numel())
+    if bucket_elems is not None:
+        allreduce_hierarchical_buckets(*args, bucket_elems, current_stream(tensors[0].device))
+    else:
+        allreduce_hierarchical_emulated(*args, current_stream(tensors[0].device))
     return out
 
 

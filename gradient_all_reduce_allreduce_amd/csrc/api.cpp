@@ -880,11 +880,52 @@ int check_strategy(ddp_strategy st, int32_t param, const char* level) {
 
 }  // namespace
 
-int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t local_ranks,
-                                    ddp_strategy local_strategy, int32_t local_param,
-                                    ddp_strategy global_strategy, int32_t global_param,
-                                    const void* const* rank_in, ddp_dtype in_dtype, void* const* rank_out,
-                                    ddp_dtype out_dtype, int64_t n, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The two-level fold over every bucket of a flat buffer.  A ring level's
+// chunk j starts at member j mod M, so consecutive full buckets form one
+// ring at that level, with the same chunks and start members, when the
+// level's chunking is a multiple of M and the bucket length a multiple of
+// the chunking; levels of fixed order (trees, centralized) always do.  When
+// both levels allow it the full buckets go out as one launch sequence with
+// both chunkings scaled by their count; otherwise each bucket is its own.
+int launch_tree_buckets(const ddp::RingLaunch& l, int64_t E, int local_members, int global_members,
+                        const char** msg) {
+    const int64_t full = l.n / E;
+    const int64_t tail = l.n - full * E;
+    auto joins = [&](int chunking, int members) {
+        return chunking == 0 || (chunking % members == 0 && E % chunking == 0 && full * chunking <= INT32_MAX);
+    };
+    const bool joint = full > 1 && joins(l.local_chunking, local_members) && joins(l.global_chunking, global_members);
+    const int ies = l.in_bf16 ? 2 : 4;
+    const int oes = l.out_bf16 ? 2 : 4;
+    auto launch = [&](int64_t first, int64_t count, int64_t scale) {
+        ddp::RingLaunch b = l;
+        for (int r = 0; r < l.P; ++r) {
+            b.in[r] = static_cast<const char*>(l.in[r]) + first * ies;
+            b.out[r] = static_cast<char*>(l.out[r]) + first * oes;
+        }
+        b.n = count;
+        b.local_chunking = static_cast<int>(l.local_chunking * scale);
+        b.global_chunking = static_cast<int>(l.global_chunking * scale);
+        return ddp::launch_ring_reduce(b, msg);
+    };
+    if (joint) {
+        if (const int e = launch(0, full * E, full)) return e;
+    } else {
+        for (int64_t k = 0; k < full; ++k)
+            if (const int e = launch(k * E, E, 1)) return e;
+    }
+    return tail > 0 ? launch(full * E, tail, 1) : 0;
+}
+
+// allreduce_hierarchical_emulated (bucket_elems 0) and allreduce_hierarchical_buckets.
+int hierarchical_call(ddp_reduce_op op, int32_t nodes, int32_t local_ranks, ddp_strategy local_strategy,
+                      int32_t local_param, ddp_strategy global_strategy, int32_t global_param,
+                      const void* const* rank_in, ddp_dtype in_dtype, void* const* rank_out, ddp_dtype out_dtype,
+                      int64_t n, int64_t bucket_elems, void* stream) {
     if (nodes < 1 || local_ranks < 1 || nodes > DDP_MAX_RANKS || local_ranks > DDP_MAX_RANKS ||
         nodes * local_ranks > DDP_MAX_RANKS)
         return fail(DDP_E_ARG, "nodes = %d x local_ranks = %d, need both >= 1 and a product <= %d", nodes,
@@ -894,6 +935,7 @@ int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t loc
     if ((s = check_strategy(global_strategy, global_param, "global"))) return s;
     const int P = nodes * local_ranks;
     if ((s = validate_reduce(op, P, 1, rank_in, in_dtype, rank_out, out_dtype, n, true))) return s;
+    if (bucket_elems != 0 && (s = check_bucket_elems(bucket_elems, in_dtype, out_dtype))) return s;
     std::vector<Buf> bufs;
     add_rank_bufs(bufs, rank_in, P, n, elem_bytes(in_dtype), "rank_in");
     add_rank_bufs(bufs, const_cast<const void* const*>(rank_out), P, n, elem_bytes(out_dtype), "rank_out");
@@ -922,9 +964,33 @@ int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t loc
     l.n = n;
     l.stream = stream;
     const char* msg = nullptr;
-    const int e = ddp::launch_ring_reduce(l, &msg);
+    const int e = bucket_elems != 0 ? launch_tree_buckets(l, bucket_elems, local_ranks, nodes, &msg)
+                                    : ddp::launch_ring_reduce(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t local_ranks,
+                                    ddp_strategy local_strategy, int32_t local_param,
+                                    ddp_strategy global_strategy, int32_t global_param,
+                                    const void* const* rank_in, ddp_dtype in_dtype, void* const* rank_out,
+                                    ddp_dtype out_dtype, int64_t n, void* stream) {
+    return hierarchical_call(op, nodes, local_ranks, local_strategy, local_param, global_strategy, global_param,
+                             rank_in, in_dtype, rank_out, out_dtype, n, 0, stream);
+}
+
+int allreduce_hierarchical_buckets(ddp_reduce_op op, int32_t nodes, int32_t local_ranks,
+                                   ddp_strategy local_strategy, int32_t local_param,
+                                   ddp_strategy global_strategy, int32_t global_param,
+                                   const void* const* rank_in, ddp_dtype in_dtype, void* const* rank_out,
+                                   ddp_dtype out_dtype, int64_t n, int64_t bucket_elems, void* stream) {
+    if (bucket_elems == 0) return fail(DDP_E_ARG, "bucket_elems = 0, must be >= 1");
+    return hierarchical_call(op, nodes, local_ranks, local_strategy, local_param, global_strategy, global_param,
+                             rank_in, in_dtype, rank_out, out_dtype, n, bucket_elems, stream);
 }
 
 int ddp_multi_plan(const int64_t* numels, int32_t n_tensors, int32_t P, ddp_dtype in_dtype,

@@ -577,6 +577,35 @@ int allreduce_hierarchical_emulated(ddp_reduce_op op, int32_t nodes, int32_t loc
                                     int64_t n, void* stream);
 
 /*
+ * allreduce_hierarchical_buckets -- the two-level all-reduce over every
+ * bucket of a flat buffer in one call.
+ *
+ * Bucket k is elements [k * E, min((k + 1) * E, n)) of every rank buffer,
+ * as for allreduce_ring_buckets ("Distributed Training", "Data parallelism
+ * and all-reduce"), and each bucket is reduced exactly as
+ * allreduce_hierarchical_emulated reduces it alone: its own chunks at each
+ * ring level, the same bits.  A ring level's chunk j starts at member
+ * j mod M (M its member count), so when every ring level's chunking is a
+ * multiple of its M and E a multiple of that chunking, consecutive full
+ * buckets are one two-level ring and go out as one launch sequence; levels
+ * of fixed order (tree, centralized) never prevent it.  Otherwise each
+ * bucket is its own.
+ *
+ *   bucket_elems  E >= 1, with E * element size a multiple of 16 bytes for
+ *                 both element types
+ *   other arguments, layout, ownership and errors as for
+ *   allreduce_hierarchical_emulated.
+ * Errors: those of allreduce_hierarchical_emulated; DDP_E_ARG for
+ * bucket_elems < 1, DDP_E_ALIGN for a bucket size that misaligns the buckets.
+ */
+int allreduce_hierarchical_buckets(ddp_reduce_op op, int32_t nodes, int32_t local_ranks,
+                                   ddp_strategy local_strategy, int32_t local_param,
+                                   ddp_strategy global_strategy, int32_t global_param,
+                                   const void* const* rank_in, ddp_dtype in_dtype,
+                                   void* const* rank_out, ddp_dtype out_dtype,
+                                   int64_t n, int64_t bucket_elems, void* stream);
+
+/*
  * ddp_multi_plan -- host only: lay out the tiles of a multi-tensor
  * all-reduce.
  *

@@ -254,6 +254,26 @@ def test_bucketed_halves_and_stepwise_errors():
     assert st(4, b=N.pointer_array([A, A + 16])) == N.DDP_E_OVERLAP
 
 
+def test_hierarchical_buckets_errors():
+    """allreduce_hierarchical_buckets validates as the single call does,
+    plus the bucket size (no launch: fake addresses)."""
+    lib = N.lib()
+    ins = N.pointer_array([A + k * MB for k in range(4)])
+    outs = N.pointer_array([A + (64 + k) * MB for k in range(4)])
+
+    def h(E, nodes=2, local=2, ls=0, lp=0, gs=0, gp=0, n=1024, it=0):
+        return lib.allreduce_hierarchical_buckets(1, nodes, local, ls, lp, gs, gp, ins, it, outs, 0, n, E, None)
+
+    assert h(0) == N.DDP_E_ARG and "bucket_elems" in N.last_error()
+    assert h(-4) == N.DDP_E_ARG
+    assert h(6) == N.DDP_E_ALIGN
+    assert h(4, it=1) == N.DDP_E_ALIGN
+    assert h(4, nodes=0) == N.DDP_E_ARG
+    assert h(4, ls=7) == N.DDP_E_ARG
+    assert h(4, lp=-1) == N.DDP_E_ARG
+    assert h(4, n=0) == N.DDP_OK
+
+
 def test_buckets_launch_count():
     """The launch count the bucketed calls report, by the rule of their
     declaration: one launch when the full buckets form one ring and the

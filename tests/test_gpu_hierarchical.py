@@ -169,3 +169,26 @@ def test_two_level_across_launches():
     assert_same_bits(got, want_, "two-level across launches")
     del bufs, outs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("P,G,local,glob,E,n,it,ot", [
+    (8, 2, ("ring", None), ("ring", None), 8192 * 4, 3 * 8192 * 4 + 777, "f32", "f32"),   # both levels join
+    (8, 4, ("tree", 2), ("ring", 8), 8192 * 8, 3 * 8192 * 8 + 5, "f32", "f32"),           # tree + joining ring
+    (8, 2, ("ring", 3), ("ring", None), 9_000, 3 * 9_000 + 1_234, "f32", "f32"),         # 3 % 4: bucket by bucket
+    (6, 3, ("centralized", None), ("ring", 5), 10_000, 25_001, "f32", "f32"),            # 5 % 3: bucket by bucket
+    (16, 4, ("ring", 8), ("tree", 1), 4096 * 8, 2 * 4096 * 8, "bf16", "f32"),             # join, no tail
+    (4, 2, ("ring", None), ("centralized", None), 8_192, 100, "bf16", "bf16"),           # one partial bucket
+])
+def test_buckets_equal_one_call_per_bucket(P, G, local, glob, E, n, it, ot):
+    """allreduce_hierarchical_buckets: every bucket exactly as the single
+    two-level call reduces it (the oracle's bits), whether the full buckets
+    join into one two-level ring or go bucket by bucket."""
+    X = draw(P, n, it, seed=P * 7 + G + n)
+    got = ddp.allreduce_hierarchical(to_device(X, it), G, "mean", local, glob, out_dtype=torch_dtype(ot),
+                                     bucket_elems=E)
+    torch.cuda.synchronize()
+    got = to_host(got)
+    for k in range(0, n, E):
+        what = f"P={P} G={G} {local} {glob} bucket at {k}"
+        assert_same_bits(got[:, k:k + E], want(X[:, k:k + E], it, ot, "mean", G, local, glob), what)
+
