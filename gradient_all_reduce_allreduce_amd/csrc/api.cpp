@@ -193,7 +193,7 @@ int launch_buckets(const ddp::RingLaunch& l, int64_t E, const char** msg) {
     for (const BucketPart& p : bucket_parts(l, E)) {
         ddp::RingLaunch b = l;
         for (int r = 0; r < l.P; ++r) {
-            b.in[r] = static_cast<const char*>(l.in[r]) + p.first * ies;
+            b.in[r] = l.in[r] ? static_cast<const char*>(l.in[r]) + p.first * ies : nullptr;
             b.out[r] = l.out[r] ? static_cast<char*>(l.out[r]) + p.first * oes : nullptr;
         }
         if (l.w) b.w = l.w + p.first;
