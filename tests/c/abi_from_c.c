@@ -61,6 +61,13 @@ int main(void) {
               ddp_last_error()[0] == '\0', "n = 0 is a no-op");
     CHECK(allreduce_ring_buckets(DDP_SUM, 2, 2, in, DDP_F32, out, DDP_F32, 1024, 6, NULL) == DDP_E_ALIGN,
           "bucket size that misaligns the buckets rejected");
+    CHECK(reducescatter_ring_buckets(DDP_SUM, 2, 2, in, DDP_F32, out, DDP_F32, 1024, 0, NULL) == DDP_E_ARG &&
+              allgather_ring_buckets(2, 2, out, DDP_BF16, 1024, 4, NULL) == DDP_E_ALIGN &&
+              allreduce_ring_stepwise_buckets(DDP_SUM, 2, 2, out, DDP_F32, 0, 4, NULL, NULL) == DDP_OK,
+          "bucketed halves and stepwise ring validation");
+    CHECK(allreduce_hierarchical_buckets(DDP_MEAN, 2, 1, DDP_STRATEGY_RING, 0, DDP_STRATEGY_TREE, 2, in, DDP_F32,
+                                         out, DDP_F32, 1024, 6, NULL) == DDP_E_ALIGN,
+          "bucketed two-level call validation");
     CHECK(ddp_set_wg_per_cu(DDP_KF_RING, 1) == DDP_E_ARG && ddp_set_wg_per_cu(DDP_KF_RING, -1) == DDP_OK,
           "occupancy knob validation");
     /* Pack and unpack check the segment table against the plan before
