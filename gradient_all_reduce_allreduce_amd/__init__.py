@@ -15,7 +15,7 @@ from .api import (SUM, MEAN, F32, BF16, MAX_RANKS, DdpError, ddp_bucket_plan, dd
                   allreduce, allreduce_stepwise, allreduce_tree, MultiAllReduce,
                   allreduce_sgd, reduce_scatter, all_gather, allreduce_hierarchical_emulated,
                   allreduce_hierarchical, zero1_sgd_step_emulated, zero1_sgd_step,
-                  allreduce_multi_fused_sgd, ddp_set_wg_per_cu, KERNEL_FAMILIES,
+                  allreduce_multi_fused_sgd, allreduce_multi_ring_noalloc, ddp_set_wg_per_cu, KERNEL_FAMILIES,
                   allreduce_ring_buckets, allreduce_fused_sgd_buckets, zero1_sgd_step_buckets,
                   ddp_buckets_launch_count, reducescatter_ring_buckets, allgather_ring_buckets,
                   allreduce_ring_stepwise_buckets, allreduce_hierarchical_buckets)
@@ -31,7 +31,7 @@ __all__ = [
     "allreduce_sgd",
     "reduce_scatter", "all_gather", "GradBucketer", "allreduce_hierarchical_emulated",
     "allreduce_hierarchical", "zero1_sgd_step_emulated", "zero1_sgd_step",
-    "allreduce_multi_fused_sgd", "ddp_set_wg_per_cu", "KERNEL_FAMILIES",
+    "allreduce_multi_fused_sgd", "allreduce_multi_ring_noalloc", "ddp_set_wg_per_cu", "KERNEL_FAMILIES",
     "allreduce_ring_buckets", "allreduce_fused_sgd_buckets", "zero1_sgd_step_buckets",
     "ddp_buckets_launch_count", "reducescatter_ring_buckets", "allgather_ring_buckets",
     "allreduce_ring_stepwise_buckets", "allreduce_hierarchical_buckets",

@@ -131,6 +131,10 @@ _SIGNATURES = {
         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_void_p]),
+    "allreduce_multi_ring_noalloc": (ctypes.c_int, [
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.POINTER(ctypes.c_int64), _c_void_pp, ctypes.c_int, _c_void_pp, ctypes.c_int,
+        ctypes.c_void_p]),
     "ddp_set_wg_per_cu": (ctypes.c_int, [ctypes.c_int, ctypes.c_int32]),
     "ddp_last_error": (ctypes.c_char_p, []),
 }

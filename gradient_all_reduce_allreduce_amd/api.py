@@ -12,7 +12,7 @@ Python ints, stream as an int handle or None):
     allgather_ring_emulated, allgather_ring_buckets, allreduce_ring_stepwise,
     allreduce_ring_stepwise_buckets, allreduce_tree_emulated, allreduce_hierarchical_buckets,
     allreduce_hierarchical_emulated, ddp_multi_plan, ddp_multi_block_map, allreduce_multi_ring_emulated,
-    allreduce_multi_fused_sgd, ddp_set_wg_per_cu
+    allreduce_multi_fused_sgd, allreduce_multi_ring_noalloc, ddp_set_wg_per_cu
 Tensor-level helpers:
     allreduce(tensors, op, chunking, out)            -> list of outputs
     allreduce_sgd(grads, w, v, lr, mu, op, chunking, out)
@@ -288,6 +288,21 @@ def allreduce_multi_fused_sgd(op, P, chunking, n_tensors, tiles_dev, total_tiles
                                              tile_elems, block_first_dev, in_ptrs_dev, grad_dtype,
                                              w_ptrs_dev, v_ptrs_dev, lr, mu, out_ptrs_dev, out_dtype,
                                              stream))
+
+
+def allreduce_multi_ring_noalloc(op, P, chunking, numels, in_ptrs, in_dtype, out_ptrs, out_dtype,
+                                 stream=None):
+    """The multi-tensor all-reduce from host arrays, with its tables in the
+    library's per-GPU scratch area (no device allocation).  ``numels``: T
+    element counts; ``in_ptrs``/``out_ptrs``: P * T device addresses,
+    rank-major."""
+    numels = np.ascontiguousarray(numels, dtype=np.int64)
+    T = numels.size
+    if len(in_ptrs) != P * T or len(out_ptrs) != P * T:
+        raise ValueError(f"need {P * T} input and output pointers")
+    _check(N.lib().allreduce_multi_ring_noalloc(
+        _op(op), P, chunking, T, numels.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        N.pointer_array(in_ptrs), in_dtype, N.pointer_array(out_ptrs), out_dtype, stream))
 
 
 def ddp_set_wg_per_cu(family, wg_per_cu):

@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -1141,6 +1142,125 @@ int allreduce_multi_ring_emulated(ddp_reduce_op op, int32_t P, int32_t chunking,
     l.stream = stream;
     const char* msg = nullptr;
     const int e = ddp::launch_multi_ring(l, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    return ok();
+}
+
+static_assert(DDP_NOALLOC_SCRATCH_BYTES == ddp::kNoAllocScratchBytes, "scratch size in the header");
+
+namespace {
+
+static constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// The allocation-free call's host staging area, a static array held by one
+// call at a time (calls from several threads take turns).  Its contents are
+// copied out of host memory before each call returns.
+alignas(256) static unsigned char g_noalloc_stage[DDP_NOALLOC_SCRATCH_BYTES];
+static std::mutex g_noalloc_mutex;
+
+}  // namespace
+
+int allreduce_multi_ring_noalloc(ddp_reduce_op op, int32_t P, int32_t chunking, int32_t n_tensors,
+                                 const int64_t* numels, const void* const* in_ptrs, ddp_dtype in_dtype,
+                                 void* const* out_ptrs, ddp_dtype out_dtype, void* stream) {
+    if (op != DDP_SUM && op != DDP_MEAN) return fail(DDP_E_ARG, "unknown reduce op %d", op);
+    int s = check_ranks(P);
+    if (s) return s;
+    if (chunking < 1) return fail(DDP_E_ARG, "chunking = %d, must be >= 1", chunking);
+    if (n_tensors < 1) return fail(DDP_E_ARG, "n_tensors = %d, must be >= 1", n_tensors);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DDP_E_ARG, "unknown dtype");
+    if (numels == nullptr || in_ptrs == nullptr || out_ptrs == nullptr)
+        return fail(DDP_E_ARG, "NULL pointer argument");
+    const int ies = elem_bytes(in_dtype);
+    const int oes = elem_bytes(out_dtype);
+    const int64_t T = n_tensors;
+    // Sizes first, so that a request beyond the scratch area is refused
+    // before anything else is read or written.
+    const size_t ptr_bytes = static_cast<size_t>(P) * static_cast<size_t>(T) * sizeof(void*);
+    const size_t tiles_bytes = static_cast<size_t>(T) * sizeof(ddp_tensor_tiles);
+    if (tiles_bytes + 2 * ptr_bytes > static_cast<size_t>(DDP_NOALLOC_SCRATCH_BYTES))
+        return fail(DDP_E_UNSUPPORTED,
+                    "%d tensors x %d ranks need %zu bytes of tables, over the %d-byte scratch area", n_tensors,
+                    P, tiles_bytes + 2 * ptr_bytes, DDP_NOALLOC_SCRATCH_BYTES);
+    std::vector<Buf> bufs;
+    for (int64_t t = 0; t < T; ++t) {
+        if ((s = check_length(numels[t], "numels[t]"))) return s;
+        if (numels[t] > (int64_t(1) << 29))
+            return fail(DDP_E_UNSUPPORTED, "numels[%lld] = %lld is over 2^29 elements", static_cast<long long>(t),
+                        static_cast<long long>(numels[t]));
+        for (int r = 0; r < P; ++r) {
+            const void* a = in_ptrs[r * T + t];
+            const void* b = out_ptrs[r * T + t];
+            if (numels[t] > 0 && (a == nullptr || b == nullptr))
+                return fail(DDP_E_ARG, "rank %d's pointer of tensor %lld is NULL", r, static_cast<long long>(t));
+            if ((reinterpret_cast<uintptr_t>(a) % ies) || (reinterpret_cast<uintptr_t>(b) % oes))
+                return fail(DDP_E_ALIGN, "rank %d's tensor %lld is not aligned to its element size", r,
+                            static_cast<long long>(t));
+            if (numels[t] == 0) continue;
+            const uintptr_t ia = reinterpret_cast<uintptr_t>(a);
+            const uintptr_t ib = reinterpret_cast<uintptr_t>(b);
+            bufs.push_back({ia, ia + static_cast<uintptr_t>(numels[t]) * ies, ies, "in", r});
+            // In place (output = input, same element size) is the one alias.
+            if (ib != ia || oes != ies)
+                bufs.push_back({ib, ib + static_cast<uintptr_t>(numels[t]) * oes, oes, "out", r});
+        }
+    }
+    // Every other pair of buffers must be disjoint: sorted by start, each
+    // must begin at or after the furthest end seen so far.
+    std::sort(bufs.begin(), bufs.end(), [](const Buf& x, const Buf& y) { return x.lo < y.lo; });
+    uintptr_t reach = 0;
+    for (size_t i = 0; i < bufs.size(); ++i) {
+        if (i > 0 && bufs[i].lo < reach)
+            return fail(DDP_E_OVERLAP, "a %s buffer of rank %d overlaps another tensor's buffer", bufs[i].what,
+                        bufs[i].index);
+        reach = std::max(reach, bufs[i].hi);
+    }
+
+    // Tables, laid out in the host stage as they will sit in the scratch
+    // area: plan | block map | input pointers | output pointers.
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    unsigned char* stage = g_noalloc_stage;
+    auto* tiles = reinterpret_cast<ddp_tensor_tiles*>(stage);
+    int64_t total_tiles = 0, tile_elems = 0;
+    if ((s = ddp_multi_plan(numels, n_tensors, P, in_dtype, out_dtype, in_ptrs, tiles, &total_tiles, &tile_elems)))
+        return s;
+    if (total_tiles == 0) return ok();
+    const size_t map_off = align_up(tiles_bytes, 256);
+    const int64_t n_blocks = (total_tiles + ddp::kMultiBlockTiles - 1) / ddp::kMultiBlockTiles;
+    const size_t in_off = align_up(map_off + static_cast<size_t>(n_blocks) * sizeof(int32_t), 256);
+    const size_t out_off = align_up(in_off + ptr_bytes, 256);
+    const size_t total_bytes = out_off + ptr_bytes;
+    if (total_bytes > static_cast<size_t>(DDP_NOALLOC_SCRATCH_BYTES))
+        return fail(DDP_E_UNSUPPORTED, "the tables need %zu bytes, over the %d-byte scratch area", total_bytes,
+                    DDP_NOALLOC_SCRATCH_BYTES);
+    int64_t nb = 0;
+    if ((s = ddp_multi_block_map(tiles, n_tensors, total_tiles, reinterpret_cast<int32_t*>(stage + map_off), n_blocks,
+                                 &nb)))
+        return s;
+    std::memcpy(stage + in_off, in_ptrs, ptr_bytes);
+    std::memcpy(stage + out_off, out_ptrs, ptr_bytes);
+
+    void* dev = nullptr;
+    const char* msg = nullptr;
+    int e = ddp::noalloc_scratch(stream, &dev, &msg);
+    if (e != 0) return hip_fail(e, msg);
+    unsigned char* d = static_cast<unsigned char*>(dev);
+    if ((e = ddp::copy_to_scratch(d, stage, total_bytes, stream, &msg)) != 0) return hip_fail(e, msg);
+
+    ddp::MultiLaunch l{};
+    l.P = P;
+    l.chunking = chunking;
+    l.op = op;
+    l.in_bf16 = in_dtype == DDP_BF16;
+    l.out_bf16 = out_dtype == DDP_BF16;
+    l.T = n_tensors;
+    l.tiles = reinterpret_cast<const ddp_tensor_tiles*>(d);
+    l.block_first = reinterpret_cast<const int32_t*>(d + map_off);
+    l.in = reinterpret_cast<const void* const*>(d + in_off);
+    l.out = reinterpret_cast<void* const*>(d + out_off);
+    l.total_tiles = total_tiles;
+    l.stream = stream;
+    e = ddp::launch_multi_ring(l, &msg);
     if (e != 0) return hip_fail(e, msg);
     return ok();
 }

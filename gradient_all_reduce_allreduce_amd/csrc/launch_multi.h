@@ -46,7 +46,17 @@ struct MultiLaunch {
     void* stream;
 };
 
+// Size of the per-GPU scratch area of allreduce_multi_ring_noalloc (its
+// tables: plan, block map, input and output pointer tables).
+constexpr int64_t kNoAllocScratchBytes = int64_t(1) << 20;
+
 int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16);
+// The device address of this GPU's scratch area (the GPU of `stream`, or
+// the current one for the null stream), looked up once per device.
+int noalloc_scratch(void* stream, void** ptr, const char** msg);
+// Copies `bytes` of host memory into device memory in stream order (the
+// host buffer may be reused when this returns).
+int copy_to_scratch(void* dst, const void* src, size_t bytes, void* stream, const char** msg);
 int launch_multi_ring(const MultiLaunch& l, const char** msg);
 
 }  // namespace ddp

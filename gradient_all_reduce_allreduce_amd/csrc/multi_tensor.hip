@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch_multi.h"
 #include "ring_reduce_impl.h"
 
@@ -349,6 +351,70 @@ const void* multi_kernel_for(int P) {
 }
 
 }  // namespace
+
+// The allocation-free multi-tensor call's tables (plan, block map, pointer
+// tables) live here: one copy per GPU, loaded with the code object, held
+// until the process ends.  Host code never names this array in a launch or
+// copy: its name is a host-side stand-in, not a device address.  It uses the
+// address hipGetSymbolAddress gives on each device instead.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+}  // namespace
+
+int noalloc_scratch(void* stream, void** ptr, const char** msg) {
+    int dev = -1;
+    hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                     : hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *msg = "hipStreamGetDevice/hipGetDevice (scratch)";
+        return static_cast<int>(e);
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) {
+        *msg = "device ordinal beyond the scratch table";
+        return static_cast<int>(hipErrorInvalidDevice);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // Look the address up once per device, with that device current.
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) {
+            *msg = "hipGetDevice (scratch)";
+            return static_cast<int>(e);
+        }
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) {
+            *msg = "hipSetDevice (scratch)";
+            return static_cast<int>(e);
+        }
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess || p == nullptr) {
+            *msg = "hipGetSymbolAddress(scratch)";
+            return static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return 0;
+}
+
+int copy_to_scratch(void* dst, const void* src, size_t bytes, void* stream, const char** msg) {
+    const hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        *msg = "hipMemcpyAsync (scratch tables)";
+        return static_cast<int>(e);
+    }
+    return 0;
+}
 
 int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16) {
     return static_cast<int64_t>(kBlock) * ring_vectors_per_lane(P, false) * ring_lane_elems(in_bf16, out_bf16, false);

@@ -740,6 +740,56 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
                               float lr, float mu, void* const* out_ptrs_dev,
                               ddp_dtype out_dtype, void* stream);
 
+/* Bytes of the per-GPU scratch area of allreduce_multi_ring_noalloc. */
+#define DDP_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+/*
+ * allreduce_multi_ring_noalloc -- allreduce_multi_ring_emulated for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It takes host arrays and
+ * builds the plan (ddp_multi_plan, tiles on rank 0's input lines), its block
+ * map and the two pointer tables itself, in a scratch area of
+ * DDP_NOALLOC_SCRATCH_BYTES that the library holds in device memory on every
+ * GPU it runs on until the process ends; it calls no hipMalloc, hipFree or
+ * other allocating device routine.  Results are, bit for bit, those of
+ * allreduce_multi_ring_emulated on the same tensors (tensor t reduced alone,
+ * in the ring order, with its own chunk length).
+ *
+ *   op, P, chunking      as for allreduce_multi_ring_emulated
+ *   n_tensors            tensors per rank, >= 1
+ *   numels               HOST array [n_tensors], each 0 .. 2^29 elements
+ *   in_ptrs              HOST array [P * n_tensors] of device pointers,
+ *                        rank-major (entry r * n_tensors + t = rank r's
+ *                        tensor t), each aligned to its element size; may be
+ *                        NULL where numels[t] = 0
+ *   out_ptrs             HOST array [P * n_tensors], same layout, elements of
+ *                        out_dtype; an output may be its own input when the
+ *                        element types match (in place)
+ *   stream               the stream to enqueue on (NULL: the null stream);
+ *                        its GPU's scratch area is used
+ * Host arrays are read during the call only.  Apart from the in-place alias,
+ * every buffer must be disjoint from every other (checked).  The tables
+ * (16 bytes per tensor, 2 * 8 * P bytes per tensor of pointers, 4 bytes per
+ * 64 tiles of block map, each part rounded to 256 bytes) must fit the
+ * scratch area: about 7,700 tensors at P = 8.
+ *
+ * Every call on one GPU shares that GPU's scratch area, which keeps the last
+ * call's tables: a call copies its tables in, in stream order, then
+ * launches.  Calls on one stream follow each other safely; calls that
+ * overlap on one GPU (other streams, other threads' streams) race on the
+ * tables and give undefined results.  Nothing in the area needs clearing:
+ * every byte a launch reads was written by its own call's copy.
+ * Errors: DDP_E_ARG (counts, NULL arrays or pointers, op, dtypes),
+ * DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_UNSUPPORTED (a tensor over 2^29
+ * elements; tables larger than the scratch area), DDP_E_HIP.  On any error
+ * nothing has been enqueued.
+ */
+int allreduce_multi_ring_noalloc(ddp_reduce_op op, int32_t P, int32_t chunking,
+                                 int32_t n_tensors, const int64_t* numels,
+                                 const void* const* in_ptrs, ddp_dtype in_dtype,
+                                 void* const* out_ptrs, ddp_dtype out_dtype,
+                                 void* stream);
+
 /* Kernel families whose launch shape ddp_set_wg_per_cu can override. */
 typedef enum ddp_kernel_family {
     DDP_KF_RING = 0,            /* allreduce_ring_emulated */

@@ -338,6 +338,42 @@ def test_multi_fused_sgd_errors():
     assert f(1, 8, 8, 1, A, 0, tile, None, A, 0, A, A, 1e-3, 0.9, None, 0, None) == N.DDP_OK
 
 
+def test_multi_noalloc_errors():
+    """The allocation-free multi-tensor call refuses, before any HIP call,
+    bad arguments, overlapping buffers and tables beyond its scratch area."""
+    f = N.lib().allreduce_multi_ring_noalloc
+
+    def call(numels, ins, outs, op=0, P=2, C=2, it=0, ot=0):
+        arr = (ctypes.c_int64 * len(numels))(*numels)
+        return f(op, P, C, len(numels), arr, N.pointer_array(ins), it, N.pointer_array(outs), ot, None)
+
+    numels = [100, 37]
+    ins = [A + i * MB for i in range(4)]
+    outs = [A + 64 * MB + i * MB for i in range(4)]
+    assert call(numels, ins, outs, op=7) == N.DDP_E_ARG
+    assert call(numels, ins, outs, C=0) == N.DDP_E_ARG
+    assert call(numels, ins, outs, it=5) == N.DDP_E_ARG
+    assert call([100, -1], ins, outs) == N.DDP_E_ARG
+    assert f(0, 2, 2, 0, None, None, 0, None, 0, None) == N.DDP_E_ARG
+    arr = (ctypes.c_int64 * 2)(*numels)
+    assert f(0, 2, 2, 2, arr, None, 0, N.pointer_array(outs), 0, None) == N.DDP_E_ARG
+    assert call(numels, [A, 0, A + 2 * MB, A + 3 * MB], outs) == N.DDP_E_ARG      # NULL, numel > 0
+    assert call(numels, [A + 2] + ins[1:], outs) == N.DDP_E_ALIGN                 # f32 at +2 bytes
+    assert call(numels, [A, A + 200] + ins[2:], outs) == N.DDP_E_OVERLAP          # 100 floats from A
+    assert "overlaps" in N.last_error()
+    assert call(numels, ins, [ins[0]] + outs[1:], ot=1) == N.DDP_E_OVERLAP        # bf16 out over f32 in
+    assert call([(1 << 29) + 1, 1], ins, outs) == N.DDP_E_UNSUPPORTED               # tensor over 2^29
+    # Tables over the scratch area: 5,000 tensors at P = 16 need 2.6 MB.
+    T, P = 5000, 16
+    big_in = [A + i * 64 for i in range(P * T)]
+    big_out = [A + 1024 * MB + i * 64 for i in range(P * T)]
+    assert call([1] * T, big_in, big_out, P=P) == N.DDP_E_UNSUPPORTED
+    assert "scratch" in N.last_error()
+    # Zero elements everywhere: nothing to launch, NULL pointers allowed.
+    assert call([0, 0], [0] * 4, [0] * 4) == N.DDP_OK
+    assert getattr(ddp, "allreduce_multi_ring_noalloc") is not None
+
+
 def _pack_case(numels, bucket_bytes, P=2, es=4):
     """A real plan's first bucket with fake, never dereferenced tensor and
     bucket addresses: (segments of bucket 0, numels array, tensor address
