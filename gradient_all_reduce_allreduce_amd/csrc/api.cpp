@@ -1157,6 +1157,13 @@ static constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * 
 // copied out of host memory before each call returns.
 alignas(256) static unsigned char g_noalloc_stage[DDP_NOALLOC_SCRATCH_BYTES];
 static std::mutex g_noalloc_mutex;
+// What the last call copied into a scratch area, and on which device: a
+// call whose tables are the same bytes on the same device skips its copy
+// (the area keeps the last call's tables, and calls on one GPU are ordered
+// by contract), so a loop over the same tensors costs one launch per call.
+alignas(256) static unsigned char g_noalloc_last[DDP_NOALLOC_SCRATCH_BYTES];
+static size_t g_noalloc_last_bytes = 0;
+static void* g_noalloc_last_area = nullptr;
 
 }  // namespace
 
@@ -1245,7 +1252,15 @@ int allreduce_multi_ring_noalloc(ddp_reduce_op op, int32_t P, int32_t chunking, 
     int e = ddp::noalloc_scratch(stream, &dev, &msg);
     if (e != 0) return hip_fail(e, msg);
     unsigned char* d = static_cast<unsigned char*>(dev);
-    if ((e = ddp::copy_to_scratch(d, stage, total_bytes, stream, &msg)) != 0) return hip_fail(e, msg);
+    const bool same = g_noalloc_last_area == dev && g_noalloc_last_bytes == total_bytes &&
+                      std::memcmp(g_noalloc_last, stage, total_bytes) == 0;
+    if (!same) {
+        g_noalloc_last_area = nullptr;
+        if ((e = ddp::copy_to_scratch(d, stage, total_bytes, stream, &msg)) != 0) return hip_fail(e, msg);
+        std::memcpy(g_noalloc_last, stage, total_bytes);
+        g_noalloc_last_bytes = total_bytes;
+        g_noalloc_last_area = dev;
+    }
 
     ddp::MultiLaunch l{};
     l.P = P;

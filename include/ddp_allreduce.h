@@ -775,6 +775,8 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
  *
  * Every call on one GPU shares that GPU's scratch area, which keeps the last
  * call's tables: a call copies its tables in, in stream order, then
+ * launches; when its tables are byte for byte the ones the last call on
+ * that GPU copied (the same tensors again), it skips the copy and only
  * launches.  Calls on one stream follow each other safely; calls that
  * overlap on one GPU (other streams, other threads' streams) race on the
  * tables and give undefined results.  Nothing in the area needs clearing:

@@ -117,6 +117,31 @@ def test_no_alloc_equals_device_table_call_twice(case):
                              f"oracle case {case} call {call} tensor {t}")
 
 
+def test_no_alloc_repeated_tables():
+    """The same tensors again right after (the call finds its tables already
+    in the scratch area and skips the copy), then other tensors, then the
+    first ones again: every call equals the oracle."""
+    P, C = 8, 8
+    sets = [[4097, 9, 70001, 1], [33, 129 * 7]]
+    data = [make(P, n, torch.float32, seed=40 + k) for k, n in enumerate(sets)]
+    # One output list per set, reused, so that a repeat has the same tables.
+    out_sets = [[[torch.empty((n,), device=DEV) for n in numels] for _ in range(P)] for numels in sets]
+    for k in (0, 0, 1, 0, 1, 1):
+        numels = sets[k]
+        host, ins = data[k]
+        outs = out_sets[k]
+        print(f"no-alloc repeated: set {k}", flush=True)
+        for row in outs:
+            for x in row:
+                x.fill_(-3.0)
+        no_alloc(N.DDP_MEAN, P, C, numels, ins, N.DDP_F32, outs, N.DDP_F32)
+        torch.cuda.synchronize()
+        for t in range(len(numels)):
+            X = np.stack([host[r][t] for r in range(P)])
+            g = np.stack([bits_of(outs[r][t]) for r in range(P)])
+            assert_same_bits(g, oracle_ring(X, "mean", C), f"set {k} tensor {t}")
+
+
 def test_no_alloc_in_place():
     """Output = input (in place) on the allocation-free call."""
     P, C, numels = 4, 4, [4097, 9, 70001]
