@@ -461,33 +461,51 @@ def _w_multi(ctx):
                 lambda i: run("mean"), 8 * plan.total * 8, "multi_ring_kernel<8, false, false, false>", 1)
 
 
-@work("multi-noalloc-resnet50", "resnet_tensors")
-def _w_multi_noalloc(ctx):
-    """The same 161 tensors through the allocation-free entry point: every
-    call plans on the host and copies its tables into the library's scratch
-    area before its launch (arguments marshalled once, smallest tensor
-    first as MultiAllReduce orders them)."""
+def _noalloc_runner(ctx, shapes, tensors, n_out):
+    """fn(i) calling allreduce_multi_ring_noalloc on the tensors (smallest
+    first, as MultiAllReduce orders them), into output set i % n_out."""
     import ctypes
 
     import numpy as np
     import torch
 
     from gradient_all_reduce_allreduce_amd import _native as N
-    plan, shapes, tensors = _resnet_tensors(ctx)
-    outs = [[torch.empty(s_, device=_dev()) for s_ in shapes] for _ in range(8)]
     numels = [int(np.prod(s_, dtype=np.int64)) for s_ in shapes]
     order = sorted(range(len(numels)), key=lambda t: numels[t])
     c_numels = (ctypes.c_int64 * len(order))(*[numels[t] for t in order])
     c_in = N.pointer_array([tensors[r][t].data_ptr() for r in range(8) for t in order])
-    c_out = N.pointer_array([outs[r][t].data_ptr() for r in range(8) for t in order])
+    outs = [[[torch.empty(s_, device=_dev()) for s_ in shapes] for _ in range(8)] for _ in range(n_out)]
+    c_outs = [N.pointer_array([o[r][t].data_ptr() for r in range(8) for t in order]) for o in outs]
+    ctx.setdefault("noalloc_outs", []).append(outs)
 
     def run(i):
         stream = ctypes.c_void_p(torch.cuda.current_stream(_dev()).cuda_stream)
         st = N.lib().allreduce_multi_ring_noalloc(N.DDP_MEAN, 8, 8, len(order), c_numels, c_in, N.DDP_F32,
-                                                  c_out, N.DDP_F32, stream)
+                                                  c_outs[i % n_out], N.DDP_F32, stream)
         if st != N.DDP_OK:
             raise RuntimeError(N.last_error())
+    return run
 
+
+@work("multi-noalloc-resnet50-alternating", "resnet_tensors")
+def _w_multi_noalloc_alt(ctx):
+    """As multi-noalloc-resnet50, alternating between two output sets, so
+    that every call writes its tables (4 fill launches of 30,016 bytes)."""
+    plan, shapes, tensors = _resnet_tensors(ctx)
+    run = _noalloc_runner(ctx, shapes, tensors, 2)
+    return Work("resnet50 p8 f32 mean, 161 separate tensors, allocation-free multi-tensor call, tables "
+                "written on every call (two output sets alternating)", run, 8 * plan.total * 8,
+                "multi_ring_kernel<8, false, false, false>", 1, host_timing=True,
+                note="against multi-noalloc-resnet50: the cost of writing the tables on every call")
+
+
+@work("multi-noalloc-resnet50", "resnet_tensors")
+def _w_multi_noalloc(ctx):
+    """The same 161 tensors through the allocation-free entry point, the
+    same outputs every call: the tables are written on the first call only,
+    later calls plan on the host and launch."""
+    plan, shapes, tensors = _resnet_tensors(ctx)
+    run = _noalloc_runner(ctx, shapes, tensors, 1)
     return Work("resnet50 p8 f32 mean, 161 separate tensors, allocation-free multi-tensor call (host plan, "
                 "tables in the scratch area, one launch)", run, 8 * plan.total * 8,
                 "multi_ring_kernel<8, false, false, false>", 1, host_timing=True,

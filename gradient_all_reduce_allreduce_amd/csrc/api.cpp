@@ -1164,6 +1164,10 @@ static std::mutex g_noalloc_mutex;
 alignas(256) static unsigned char g_noalloc_last[DDP_NOALLOC_SCRATCH_BYTES];
 static size_t g_noalloc_last_bytes = 0;
 static void* g_noalloc_last_area = nullptr;
+// Per device: a call was captured into a graph there.  Its replays rewrite
+// the area whenever they run, so the last copy is no longer known and no
+// later call on that device skips its copy.
+static bool g_noalloc_captured[ddp::kMaxScratchDevices] = {};
 
 }  // namespace
 
@@ -1248,15 +1252,19 @@ int allreduce_multi_ring_noalloc(ddp_reduce_op op, int32_t P, int32_t chunking, 
     std::memcpy(stage + out_off, out_ptrs, ptr_bytes);
 
     void* dev = nullptr;
+    int ordinal = -1;
+    bool capturing = false;
     const char* msg = nullptr;
-    int e = ddp::noalloc_scratch(stream, &dev, &msg);
+    int e = ddp::noalloc_scratch(stream, &dev, &ordinal, &msg);
     if (e != 0) return hip_fail(e, msg);
+    if ((e = ddp::stream_capturing(stream, &capturing, &msg)) != 0) return hip_fail(e, msg);
+    if (capturing) g_noalloc_captured[ordinal] = true;
     unsigned char* d = static_cast<unsigned char*>(dev);
-    const bool same = g_noalloc_last_area == dev && g_noalloc_last_bytes == total_bytes &&
-                      std::memcmp(g_noalloc_last, stage, total_bytes) == 0;
+    const bool same = !g_noalloc_captured[ordinal] && g_noalloc_last_area == dev &&
+                      g_noalloc_last_bytes == total_bytes && std::memcmp(g_noalloc_last, stage, total_bytes) == 0;
     if (!same) {
         g_noalloc_last_area = nullptr;
-        if ((e = ddp::copy_to_scratch(d, stage, total_bytes, stream, &msg)) != 0) return hip_fail(e, msg);
+        if ((e = ddp::fill_scratch(d, stage, total_bytes, stream, &msg)) != 0) return hip_fail(e, msg);
         std::memcpy(g_noalloc_last, stage, total_bytes);
         g_noalloc_last_bytes = total_bytes;
         g_noalloc_last_area = dev;

@@ -49,14 +49,21 @@ struct MultiLaunch {
 // Size of the per-GPU scratch area of allreduce_multi_ring_noalloc (its
 // tables: plan, block map, input and output pointer tables).
 constexpr int64_t kNoAllocScratchBytes = int64_t(1) << 20;
+// Devices (ordinals 0 .. kMaxScratchDevices - 1) the call can run on.
+constexpr int kMaxScratchDevices = 64;
 
 int64_t multi_tile_elems(int P, bool in_bf16, bool out_bf16);
-// The device address of this GPU's scratch area (the GPU of `stream`, or
-// the current one for the null stream), looked up once per device.
-int noalloc_scratch(void* stream, void** ptr, const char** msg);
-// Copies `bytes` of host memory into device memory in stream order (the
-// host buffer may be reused when this returns).
-int copy_to_scratch(void* dst, const void* src, size_t bytes, void* stream, const char** msg);
+// The device address of the scratch area of the GPU of `stream` (the
+// current GPU for the null stream), looked up once per device, and that
+// device's ordinal.
+int noalloc_scratch(void* stream, void** ptr, int* device, const char** msg);
+// Whether `stream` is capturing a graph.
+int stream_capturing(void* stream, bool* capturing, const char** msg);
+// Writes `bytes` (a multiple of 8) of host data to device memory at `dst`
+// in stream order, with kernels that carry the data in their arguments
+// (so a captured call's graph rewrites it at every replay); the host data
+// may be reused when this returns.
+int fill_scratch(void* dst, const void* src, size_t bytes, void* stream, const char** msg);
 int launch_multi_ring(const MultiLaunch& l, const char** msg);
 
 }  // namespace ddp

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "launch_multi.h"
@@ -361,13 +362,12 @@ static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
-constexpr int kMaxScratchDevices = 64;
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxScratchDevices] = {};
 
 }  // namespace
 
-int noalloc_scratch(void* stream, void** ptr, const char** msg) {
+int noalloc_scratch(void* stream, void** ptr, int* device, const char** msg) {
     int dev = -1;
     hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
                                      : hipGetDevice(&dev);
@@ -404,14 +404,71 @@ int noalloc_scratch(void* stream, void** ptr, const char** msg) {
         g_scratch_ptr[dev] = p;
     }
     *ptr = g_scratch_ptr[dev];
+    *device = dev;
     return 0;
 }
 
-int copy_to_scratch(void* dst, const void* src, size_t bytes, void* stream, const char** msg) {
-    const hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+int stream_capturing(void* stream, bool* capturing, const char** msg) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &st);
     if (e != hipSuccess) {
-        *msg = "hipMemcpyAsync (scratch tables)";
+        *msg = "hipStreamIsCapturing";
         return static_cast<int>(e);
+    }
+    *capturing = st != hipStreamCaptureStatusNone;
+    return 0;
+}
+
+namespace {
+
+// The tables reach the scratch area as kernel arguments: each fill launch
+// carries up to kFillWords 8-byte words, one per lane over ceil(n / 64)
+// one-wave workgroups (a single wave looping over them waited out a load
+// per word: 7.4 us per launch), and writes them with vector stores.  A
+// launch captured into a graph keeps its arguments, so every replay
+// writes the same tables again.
+constexpr int kFillWords = 944;
+
+struct FillArgs {
+    uint64_t* dst;
+    int32_t n;          // words, 1 .. kFillWords
+    int32_t unused;
+    uint64_t w[kFillWords];
+};
+static_assert(sizeof(FillArgs) <= 7800, "the fill's kernel arguments must stay under the 8,000 bytes measured to pass");
+
+typedef const __attribute__((address_space(4))) FillArgs* KFill;
+
+__global__ __launch_bounds__(kBlock) void table_fill_kernel(FillArgs) {
+    const KFill a = (KFill)(__builtin_amdgcn_kernarg_segment_ptr());
+    const int i = static_cast<int>(blockIdx.x) * kBlock + static_cast<int>(threadIdx.x);
+    if (i < a->n) a->dst[i] = a->w[i];
+}
+
+}  // namespace
+
+int fill_scratch(void* dst, const void* src, size_t bytes, void* stream, const char** msg) {
+    if (bytes % sizeof(uint64_t) != 0) {
+        *msg = "table bytes not a whole number of 8-byte words";
+        return static_cast<int>(hipErrorInvalidValue);
+    }
+    const uint64_t* w = static_cast<const uint64_t*>(src);
+    const size_t words = bytes / sizeof(uint64_t);
+    FillArgs a;
+    for (size_t k = 0; k < words; k += kFillWords) {
+        const size_t n = words - k < static_cast<size_t>(kFillWords) ? words - k : static_cast<size_t>(kFillWords);
+        a.dst = static_cast<uint64_t*>(dst) + k;
+        a.n = static_cast<int32_t>(n);
+        a.unused = 0;
+        std::memcpy(a.w, w + k, n * sizeof(uint64_t));
+        void* args[] = {&a};
+        const unsigned grid = static_cast<unsigned>((n + kBlock - 1) / kBlock);
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&table_fill_kernel), dim3(grid),
+                                             dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) {
+            *msg = "hipLaunchKernel(table_fill)";
+            return static_cast<int>(e);
+        }
     }
     return 0;
 }

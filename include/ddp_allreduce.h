@@ -774,13 +774,19 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
  * scratch area: about 7,700 tensors at P = 8.
  *
  * Every call on one GPU shares that GPU's scratch area, which keeps the last
- * call's tables: a call copies its tables in, in stream order, then
- * launches; when its tables are byte for byte the ones the last call on
- * that GPU copied (the same tensors again), it skips the copy and only
- * launches.  Calls on one stream follow each other safely; calls that
- * overlap on one GPU (other streams, other threads' streams) race on the
- * tables and give undefined results.  Nothing in the area needs clearing:
- * every byte a launch reads was written by its own call's copy.
+ * call's tables: a call writes its tables in, in stream order, with small
+ * kernels that carry them in their arguments, then launches; when its
+ * tables are byte for byte the ones the last call on that GPU wrote (the
+ * same tensors again), it skips the writes and only launches.  Under HIP
+ * graph capture the writes are captured with the launch, so every replay
+ * rewrites the area with its own tables first; from a GPU's first captured
+ * call on, no call on that GPU skips its writes (replays change the area
+ * when they run).  Calls and replays on one stream follow each other
+ * safely; calls that
+ * overlap on one GPU (other streams, other threads' streams, replays on
+ * other streams) race on the tables and give undefined results.  Nothing in the area needs clearing:
+ * every byte a launch reads was written by its own call (or by an earlier
+ * call with the same tables).
  * Errors: DDP_E_ARG (counts, NULL arrays or pointers, op, dtypes),
  * DDP_E_ALIGN, DDP_E_OVERLAP, DDP_E_UNSUPPORTED (a tensor over 2^29
  * elements; tables larger than the scratch area), DDP_E_HIP.  On any error

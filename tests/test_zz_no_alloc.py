@@ -142,6 +142,56 @@ def test_no_alloc_repeated_tables():
             assert_same_bits(g, oracle_ring(X, "mean", C), f"set {k} tensor {t}")
 
 
+def _want(host, numels, P, C):
+    return [oracle_ring(np.stack([host[r][t] for r in range(P)]), "mean", C) for t in range(len(numels))]
+
+
+def _check(outs, want, what):
+    for t, w in enumerate(want):
+        g = np.stack([bits_of(outs[r][t]) for r in range(len(outs))])
+        assert_same_bits(g, w, f"{what} tensor {t}")
+
+
+def test_no_alloc_graph_replays():
+    """Captured in a HIP graph, the call's table writes are captured with its
+    launch, so every replay rewrites the scratch area first: replays between
+    eager calls on other tensors (which rewrite the area, and which must not
+    skip their writes once a replay may have run) each give the oracle's
+    result, and so does every eager call."""
+    P, C = 8, 8
+    na, nb = [4097, 9, 70001, 1], [33, 129 * 7, 5]
+    host_a, ins_a = make(P, na, torch.float32, seed=61)
+    host_b, ins_b = make(P, nb, torch.float32, seed=62)
+    out_a = [[torch.empty((n,), device=DEV) for n in na] for _ in range(P)]
+    out_b = [[torch.empty((n,), device=DEV) for n in nb] for _ in range(P)]
+    want_a, want_b = _want(host_a, na, P, C), _want(host_b, nb, P, C)
+    print("no-alloc graph: eager call before capture", flush=True)
+    no_alloc(N.DDP_MEAN, P, C, na, ins_a, N.DDP_F32, out_a, N.DDP_F32)
+    torch.cuda.synchronize()
+    _check(out_a, want_a, "eager a")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        no_alloc(N.DDP_MEAN, P, C, na, ins_a, N.DDP_F32, out_a, N.DDP_F32)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        print(f"no-alloc graph: replay {rep}", flush=True)
+        for row in out_a + out_b:
+            for x in row:
+                x.fill_(-3.0)
+        no_alloc(N.DDP_MEAN, P, C, nb, ins_b, N.DDP_F32, out_b, N.DDP_F32)
+        torch.cuda.synchronize()
+        _check(out_b, want_b, f"eager b before replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        _check(out_a, want_a, f"replay {rep}")
+        for row in out_b:
+            for x in row:
+                x.fill_(-3.0)
+        no_alloc(N.DDP_MEAN, P, C, nb, ins_b, N.DDP_F32, out_b, N.DDP_F32)
+        torch.cuda.synchronize()
+        _check(out_b, want_b, f"eager b after replay {rep}")
+
+
 def test_no_alloc_in_place():
     """Output = input (in place) on the allocation-free call."""
     P, C, numels = 4, 4, [4097, 9, 70001]
