@@ -1260,15 +1260,30 @@ int allreduce_multi_ring_noalloc(ddp_reduce_op op, int32_t P, int32_t chunking, 
     if ((e = ddp::stream_capturing(stream, &capturing, &msg)) != 0) return hip_fail(e, msg);
     if (capturing) g_noalloc_captured[ordinal] = true;
     unsigned char* d = static_cast<unsigned char*>(dev);
-    const bool same = !g_noalloc_captured[ordinal] && g_noalloc_last_area == dev &&
-                      g_noalloc_last_bytes == total_bytes && std::memcmp(g_noalloc_last, stage, total_bytes) == 0;
-    if (!same) {
-        g_noalloc_last_area = nullptr;
-        if ((e = ddp::fill_scratch(d, stage, total_bytes, stream, &msg)) != 0) return hip_fail(e, msg);
-        std::memcpy(g_noalloc_last, stage, total_bytes);
-        g_noalloc_last_bytes = total_bytes;
-        g_noalloc_last_area = dev;
+    // The area's bytes [0, known) are those of the host shadow; a run of
+    // one fill launch's worth of bytes that the shadow already holds is not
+    // written again (the tensors of a loop that alternates output buffers
+    // change only the output pointer table).
+    const size_t known = !g_noalloc_captured[ordinal] && g_noalloc_last_area == dev ? g_noalloc_last_bytes : 0;
+    const size_t run = static_cast<size_t>(ddp::kFillWords) * sizeof(uint64_t);
+    g_noalloc_last_area = nullptr;
+    size_t pending = 0, pending_len = 0;    // consecutive runs that differ, written together
+    for (size_t off = 0; off < total_bytes; off += run) {
+        const size_t len = std::min(run, total_bytes - off);
+        const bool held = off + len <= known && std::memcmp(g_noalloc_last + off, stage + off, len) == 0;
+        if (!held) {
+            if (pending_len == 0) pending = off;
+            pending_len += len;
+        }
+        if ((held || off + len == total_bytes) && pending_len > 0) {
+            if ((e = ddp::fill_scratch(d + pending, stage + pending, pending_len, stream, &msg)) != 0)
+                return hip_fail(e, msg);
+            pending_len = 0;
+        }
     }
+    std::memcpy(g_noalloc_last, stage, total_bytes);
+    g_noalloc_last_bytes = std::max(total_bytes, known);
+    g_noalloc_last_area = dev;
 
     ddp::MultiLaunch l{};
     l.P = P;

@@ -49,6 +49,8 @@ struct MultiLaunch {
 // Size of the per-GPU scratch area of allreduce_multi_ring_noalloc (its
 // tables: plan, block map, input and output pointer tables).
 constexpr int64_t kNoAllocScratchBytes = int64_t(1) << 20;
+// 8-byte words of table one fill launch carries in its arguments.
+constexpr int kFillWords = 944;
 // Devices (ordinals 0 .. kMaxScratchDevices - 1) the call can run on.
 constexpr int kMaxScratchDevices = 64;
 

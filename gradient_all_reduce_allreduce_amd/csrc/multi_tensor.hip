@@ -427,7 +427,6 @@ namespace {
 // per word: 7.4 us per launch), and writes them with vector stores.  A
 // launch captured into a graph keeps its arguments, so every replay
 // writes the same tables again.
-constexpr int kFillWords = 944;
 
 struct FillArgs {
     uint64_t* dst;

@@ -775,9 +775,9 @@ int allreduce_multi_fused_sgd(ddp_reduce_op op, int32_t P, int32_t chunking,
  *
  * Every call on one GPU shares that GPU's scratch area, which keeps the last
  * call's tables: a call writes its tables in, in stream order, with small
- * kernels that carry them in their arguments, then launches; when its
- * tables are byte for byte the ones the last call on that GPU wrote (the
- * same tensors again), it skips the writes and only launches.  Under HIP
+ * kernels that carry them in their arguments, then launches.  It writes
+ * only the parts that differ from what the last call on that GPU wrote, so
+ * the same tensors again write nothing and only launch.  Under HIP
  * graph capture the writes are captured with the launch, so every replay
  * rewrites the area with its own tables first; from a GPU's first captured
  * call on, no call on that GPU skips its writes (replays change the area

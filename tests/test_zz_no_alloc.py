@@ -152,6 +152,27 @@ def _check(outs, want, what):
         assert_same_bits(g, w, f"{what} tensor {t}")
 
 
+def test_no_alloc_alternating_outputs():
+    """The same inputs into two output sets in turn, with enough tensors for
+    several fill launches: only the output pointer table changes between
+    calls, and only the launches' runs that changed are written again.
+    Every call equals the oracle."""
+    P, C = 8, 8
+    rng = np.random.default_rng(7)
+    numels = [int(x) for x in rng.integers(1, 3000, 300)]   # tables of 300 tensors: 43,520 bytes, 6 fill runs
+    host, ins = make(P, numels, torch.float32, seed=71)
+    want = _want(host, numels, P, C)
+    outs = [[[torch.empty((n,), device=DEV) for n in numels] for _ in range(P)] for _ in range(2)]
+    for k in (0, 1, 0, 1, 1, 0):
+        print(f"no-alloc alternating outputs: set {k}", flush=True)
+        for row in outs[k]:
+            for x in row:
+                x.fill_(-3.0)
+        no_alloc(N.DDP_MEAN, P, C, numels, ins, N.DDP_F32, outs[k], N.DDP_F32)
+        torch.cuda.synchronize()
+        _check(outs[k], want, f"output set {k}")
+
+
 def test_no_alloc_graph_replays():
     """Captured in a HIP graph, the call's table writes are captured with its
     launch, so every replay rewrites the scratch area first: replays between
