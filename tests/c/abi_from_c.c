@@ -96,6 +96,30 @@ int main(void) {
     b1[0].bucket = 0;
     CHECK(ddp_bucket_pack(2, DDP_F32, b1, 3, numels, 3, tens, bk, 16, NULL) == DDP_E_PLAN,
           "pack: segments of two buckets are rejected");
+    /* The allocation-free multi-tensor call: host arrays, checked before any HIP call. */
+    {
+        const int64_t mn[2] = {100, 37};
+        const int64_t big[2] = {((int64_t)1 << 29) + 1, 1};
+        const void* mi[4] = {(const void*)0x7f0030000000ull, (const void*)0x7f0030100000ull,
+                             (const void*)0x7f0030200000ull, (const void*)0x7f0030300000ull};
+        void* mo[4] = {(void*)0x7f0031000000ull, (void*)0x7f0031100000ull, (void*)0x7f0031200000ull,
+                       (void*)0x7f0031300000ull};
+        void* mo_over[4] = {(void*)0x7f0030000040ull, (void*)0x7f0031100000ull, (void*)0x7f0031200000ull,
+                            (void*)0x7f0031300000ull};
+        const int64_t none[2] = {0, 0};
+        const void* nulls[4] = {NULL, NULL, NULL, NULL};
+        void* onulls[4] = {NULL, NULL, NULL, NULL};
+        CHECK(allreduce_multi_ring_noalloc(DDP_MEAN, 2, 0, 2, mn, mi, DDP_F32, mo, DDP_F32, NULL) == DDP_E_ARG,
+              "no-alloc: chunking 0 is rejected");
+        CHECK(allreduce_multi_ring_noalloc(DDP_MEAN, 2, 2, 2, NULL, mi, DDP_F32, mo, DDP_F32, NULL) == DDP_E_ARG,
+              "no-alloc: NULL numels is rejected");
+        CHECK(allreduce_multi_ring_noalloc(DDP_MEAN, 2, 2, 2, big, mi, DDP_F32, mo, DDP_F32, NULL) ==
+                  DDP_E_UNSUPPORTED, "no-alloc: a tensor over 2^29 elements is rejected");
+        CHECK(allreduce_multi_ring_noalloc(DDP_MEAN, 2, 2, 2, mn, mi, DDP_F32, mo_over, DDP_F32, NULL) ==
+                  DDP_E_OVERLAP, "no-alloc: an output inside another input is rejected");
+        CHECK(allreduce_multi_ring_noalloc(DDP_MEAN, 2, 2, 2, none, nulls, DDP_F32, onulls, DDP_F32, NULL) ==
+                  DDP_OK, "no-alloc: empty tensors launch nothing");
+    }
     printf("all checks passed\n");
     return 0;
 }
